@@ -1,0 +1,383 @@
+"""Plain CPU oracle for the forward pass of a dropless top-k mixture-of-experts FFN layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import this module. The GPU path never imports, links or calls it,
+and this module imports nothing from the GPU package: the two share no code.
+
+Everything here is NumPy float64, evaluated per token, on exactly the values the GPU sees
+(bf16 inputs are widened to float64 exactly; there is no intermediate rounding here).
+
+Pages cited (by title, section / table / figure):
+  [L7.8]   "Mixture of Experts: routing, sorted dispatch, Switch aux loss, aux-free bias"
+           (openlearn course module L7.8): §2 symbol table, §2.1 routers table and output
+           equation, §2.2 sorted dispatch, §2.3 load-balancing loss, §2.5 aux-free bias,
+           §3 worked example, §4 interface and "Your graded tests" (the oracle recipe:
+           a per-token loop in float64, top-k sorted with an explicit (score, id) key).
+  [RB-15]  "15. Mixture of Experts" (RustingBrain tutorial): §15.2 routing and renormalised
+           gates, "Dropless", §15.3 the z-loss, §15.4 the shared expert.
+  [GPT2-MoE] "Extending Raschka's GPT-2: an MoE trained from scratch on an RTX 3090":
+           the router walk-through (Diagram 4, all experts active; Diagrams 10-12, top-k of
+           one context vector), the per-expert masked loop (Diagrams 13-19), and the
+           router-loss function.
+  [nanoMoE] "nanoMoE: Mixture-of-Experts (MoE) LLMs from Scratch in PyTorch": the MLP and
+           MLPExperts listings (nn.GELU, optional biases), "Expert Capacity", the z-loss.
+
+Readings taken where the pages are silent or ambiguous (each also listed in the design doc):
+  * selection for the softmax routers uses the logits z (softmax is monotone, so the chosen
+    set equals "top k of p"); ties go to the lowest expert id; the k chosen experts are
+    stored largest first.
+  * GELU is the exact erf form (nn.GELU's default in [nanoMoE]'s listings).
+  * SwiGLU is h = silu(x Wg^T) * (x Wu^T), y = h W2^T, no biases.  PARITY UNPINNED: the
+    pages name SwiGLU / GatedMLP but print no formula.
+  * P_e always averages p = softmax(z), with any logit offset included and without the
+    sigmoid router's selection bias ([L7.8] §2 symbol table).
+
+Pins (tests/test_oracle_pins.py): the [L7.8] §3 worked example in exact rationals, the
+[GPT2-MoE] router printouts, the [RB-15] §15.2 gate example, textbook normal-CDF values for
+GELU, brute-force top-k over all subsets, the L = k balance construction, collapse, counting
+identities, sorted dispatch == per-token loop == [GPT2-MoE] masked loop, k = E dense mixture,
+shared-weight and zero-W2 reductions, and a mutation self-check that plants each [L7.8] §5
+pitfall here and requires a pin to fail.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Any, Mapping, Optional
+
+import numpy as np
+
+try:  # scipy's erf is a vectorised library routine; math.erf is the fallback
+    from scipy.special import erf as _erf
+except Exception:  # pragma: no cover
+    _erf = np.vectorize(math.erf, otypes=[np.float64])
+
+ROUTERS = ("softmax_topk", "topk_softmax", "sigmoid")
+ACTS = ("gelu", "swiglu")
+
+f64 = np.float64
+
+
+@dataclass
+class Spec:
+    """Layer hyper-parameters, named as in [L7.8] §4 (the MoE constructor)."""
+
+    n_experts: int
+    top_k: int
+    router: str = "softmax_topk"
+    norm_topk: bool = True
+    routed_scaling: float = 1.0
+    act: str = "swiglu"
+
+    def __post_init__(self):
+        # [L7.8] §4 "What the tests check": bad top_k / router fail loudly.
+        if self.router not in ROUTERS:
+            raise ValueError(f"unknown router {self.router!r}")
+        if self.act not in ACTS:
+            raise ValueError(f"unknown act {self.act!r}")
+        if not (1 <= self.top_k <= self.n_experts):
+            raise ValueError(f"top_k={self.top_k} must be in [1, n_experts={self.n_experts}]")
+
+
+@dataclass
+class Route:
+    """Routing of N tokens: ids [N,k] largest first, weights [N,k], probs p [N,E]."""
+
+    z: np.ndarray
+    p: np.ndarray
+    scores: np.ndarray
+    ids: np.ndarray
+    w: np.ndarray
+    gap: np.ndarray = field(default=None)        # s_(k) - s_(k+1), +inf when k == E
+    intra_gap: np.ndarray = field(default=None)  # smallest adjacent gap inside the top k
+
+
+# ----------------------------------------------------------------------------------------
+# Router: [L7.8] §2 symbol table (z_n = W_g x_n, p_n = softmax(z_n)), §2.1 routers table.
+# ----------------------------------------------------------------------------------------
+
+def router_logits(x, w_g, logit_bias=None) -> np.ndarray:
+    """z = x W_g^T (+ a per-expert logit offset). [L7.8] §2; [RB-15] §15.2 (bias-free
+    d_model -> n_experts projection). The offset, when given, is part of the logits."""
+    z = np.asarray(x, f64) @ np.asarray(w_g, f64).T
+    if logit_bias is not None:
+        z = z + np.asarray(logit_bias, f64)[None, :]
+    return z
+
+
+def softmax(z) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first. [L7.8] §2; [GPT2-MoE] Diagram 4."""
+    z = np.asarray(z, f64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def sigmoid(z) -> np.ndarray:
+    """Logistic function, evaluated without overflow for either sign."""
+    z = np.asarray(z, f64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def selection_scores(z, router: str, sel_bias=None) -> np.ndarray:
+    """The score the top-k is taken over ([L7.8] §2.1 "chooses by" column).
+
+    softmax_topk / topk_softmax: the logits z (same order as p, since softmax is monotone).
+    sigmoid: sigma(z) + b, where b is the aux-free bias of [L7.8] §2.5 (selection only).
+    A selection bias on the softmax routers is added to z, again for selection only.
+    """
+    z = np.asarray(z, f64)
+    s = sigmoid(z) if router == "sigmoid" else z.copy()
+    if sel_bias is not None:
+        s = s + np.asarray(sel_bias, f64)[None, :]
+    return s
+
+
+def topk_ids(scores, k: int) -> np.ndarray:
+    """[N,k] ids, largest score first, ties to the lowest id ([L7.8] §2.1 and §4).
+
+    Per token, the experts are sorted by the explicit key (-score, id), as the [L7.8] §4
+    oracle recipe asks, and the first k are kept.
+    """
+    s = np.asarray(scores, f64)
+    n, e = s.shape
+    if not (1 <= k <= e):
+        raise ValueError(f"top_k={k} must be in [1, {e}]")
+    out = np.empty((n, k), dtype=np.int64)
+    for t in range(n):
+        row = s[t]
+        order = sorted(range(e), key=lambda i: (-row[i], i))
+        out[t] = order[:k]
+    return out
+
+
+def topk_gaps(scores, ids):
+    """gap_n = s_(k) - s_(k+1) (+inf when k == E) and the smallest adjacent gap within the
+    chosen k. They mark tokens whose choice or order a rounding difference could flip."""
+    s = np.asarray(scores, f64)
+    n, e = s.shape
+    k = ids.shape[1]
+    gap = np.full(n, np.inf)
+    intra = np.full(n, np.inf)
+    for t in range(n):
+        chosen = s[t, ids[t]]
+        if k < e:
+            rest = np.delete(s[t], ids[t])
+            gap[t] = chosen[-1] - rest.max()
+        if k > 1:
+            intra[t] = np.min(chosen[:-1] - chosen[1:])
+    return gap, intra
+
+
+def gate_weights(z, ids, spec: Spec) -> np.ndarray:
+    """w_{n,j} for the chosen ids, by the [L7.8] §2.1 "weights" column, then x routed_scaling.
+
+    softmax_topk: p_{n,e} over the chosen set, divided by their sum when norm_topk
+                  ([RB-15] §15.2 "renormalized to sum to one").
+    topk_softmax: a softmax over the chosen logits only.
+    sigmoid:      sigma(z_{n,e}) of the UNBIASED logit, divided by their sum when norm_topk.
+    """
+    z = np.asarray(z, f64)
+    n, k = ids.shape
+    w = np.empty((n, k), f64)
+    for t in range(n):
+        zt = z[t, ids[t]]
+        if spec.router == "softmax_topk":
+            p = softmax(z[t][None, :])[0]
+            u = p[ids[t]]
+            w[t] = u / u.sum() if spec.norm_topk else u
+        elif spec.router == "topk_softmax":
+            w[t] = softmax(zt[None, :])[0]
+        else:
+            u = sigmoid(zt)
+            w[t] = u / u.sum() if spec.norm_topk else u
+    return w * f64(spec.routed_scaling)
+
+
+def route(x, w_g, spec: Spec, logit_bias=None, sel_bias=None) -> Route:
+    """Routing of every token: logits, probabilities, choice, gates and tie margins."""
+    z = router_logits(x, w_g, logit_bias)
+    p = softmax(z)
+    s = selection_scores(z, spec.router, sel_bias)
+    ids = topk_ids(s, spec.top_k)
+    w = gate_weights(z, ids, spec)
+    gap, intra = topk_gaps(s, ids)
+    return Route(z=z, p=p, scores=s, ids=ids, w=w, gap=gap, intra_gap=intra)
+
+
+# ----------------------------------------------------------------------------------------
+# Experts: GELU MLP ([nanoMoE] MLP / MLPExperts listings) and SwiGLU (named in [L7.8] §4).
+# ----------------------------------------------------------------------------------------
+
+def gelu_erf(u) -> np.ndarray:
+    """GELU(u) = u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), the exact (erf) form."""
+    u = np.asarray(u, f64)
+    return 0.5 * u * (1.0 + _erf(u / math.sqrt(2.0)))
+
+
+def silu(u) -> np.ndarray:
+    """silu(u) = u * sigma(u)."""
+    u = np.asarray(u, f64)
+    return u * sigmoid(u)
+
+
+def expert_ffn(xr, act: str, w1, w2, w3=None, b1=None, b2=None) -> np.ndarray:
+    """One expert applied to rows xr [m, d]; weights in [out, in] (nn.Linear) layout.
+
+    gelu:   y = gelu(xr W1^T + b1) W2^T + b2          (biases optional)
+    swiglu: y = (silu(xr W1^T) * (xr W3^T)) W2^T       (W1 = gate, W3 = up; no biases)
+    """
+    xr = np.asarray(xr, f64)
+    if act == "gelu":
+        u = xr @ np.asarray(w1, f64).T
+        if b1 is not None:
+            u = u + np.asarray(b1, f64)[None, :]
+        h = gelu_erf(u)
+        y = h @ np.asarray(w2, f64).T
+        if b2 is not None:
+            y = y + np.asarray(b2, f64)[None, :]
+        return y
+    if act == "swiglu":
+        g = xr @ np.asarray(w1, f64).T
+        u = xr @ np.asarray(w3, f64).T
+        return (silu(g) * u) @ np.asarray(w2, f64).T
+    raise ValueError(f"unknown act {act!r}")
+
+
+def _expert(params: Mapping[str, Any], e: int):
+    """Expert e's weights from a params mapping whose per-expert tensors support [e]."""
+    get = lambda name: None if params.get(name) is None else params[name][e]
+    return dict(w1=get("w1"), w2=get("w2"), w3=get("w3"), b1=get("b1"), b2=get("b2"))
+
+
+# ----------------------------------------------------------------------------------------
+# The oracle proper: y_n = sum_{e in T_n} w_{n,e} Expert_e(x_n)  ([L7.8] §2.1 equation).
+# ----------------------------------------------------------------------------------------
+
+def forward_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_bias=None):
+    """Per-token loop over the chosen experts, j ascending ([L7.8] §4 oracle recipe).
+
+    params: w_g [E,d]; w1 [E,d_ff,d]; w3 [E,d_ff,d] (swiglu); w2 [E,d,d_ff];
+            b1 [E,d_ff], b2 [E,d] (optional, gelu only). Returns (y [N,d], Route).
+    """
+    x = np.asarray(x, f64)
+    r = route(x, params["w_g"], spec, logit_bias, sel_bias)
+    n, d = x.shape
+    y = np.zeros((n, d), f64)
+    for t in range(n):
+        for j in range(spec.top_k):
+            e = int(r.ids[t, j])
+            y[t] += r.w[t, j] * expert_ffn(x[t][None, :], spec.act, **_expert(params, e))[0]
+    return y, r
+
+
+# ----------------------------------------------------------------------------------------
+# Sorted dispatch and combine: [L7.8] §2.2, §3 (worked example), §4 interface.
+# ----------------------------------------------------------------------------------------
+
+def dispatch(ids, n_experts: int):
+    """Dispatch arrays for ids [N,k]: assignment a = n k + j is stably sorted by expert.
+
+    Returns perm [A] (sorted position -> assignment), inv_perm [A] (inv_perm[perm[i]] = i),
+    counts [E] and offsets [E+1] (offsets[e] is the START of expert e's slice, offsets[E]
+    = A). The token of sorted row i is perm[i] // k.
+    """
+    ids = np.asarray(ids)
+    n, k = ids.shape
+    expert_of = ids.reshape(-1).astype(np.int64)
+    if expert_of.size and (expert_of.min() < 0 or expert_of.max() >= n_experts):
+        raise ValueError("expert id out of range")  # [L7.8] §4: bad expert ids fail loudly
+    perm = np.argsort(expert_of, kind="stable")
+    counts = np.bincount(expert_of, minlength=n_experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    inv_perm = np.empty_like(perm)
+    inv_perm[perm] = np.arange(perm.size)
+    return perm, inv_perm, counts, offsets
+
+
+def combine(y_sorted, w, inv_perm) -> np.ndarray:
+    """y_n = sum_j w_{n,j} y_sorted[inv_perm[n k + j]], j ascending ([L7.8] §2.2)."""
+    y_sorted = np.asarray(y_sorted, f64)
+    w = np.asarray(w, f64)
+    n, k = w.shape
+    out = np.zeros((n,) + y_sorted.shape[1:], f64)
+    for j in range(k):
+        out += w[:, j].reshape((n,) + (1,) * (y_sorted.ndim - 1)) * y_sorted[inv_perm[np.arange(n) * k + j]]
+    return out
+
+
+def forward_sorted(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_bias=None):
+    """The same output by sorted dispatch: each expert runs once on its contiguous slice
+    ([L7.8] §2.2), then combine. Pinned equal to forward_loop."""
+    x = np.asarray(x, f64)
+    r = route(x, params["w_g"], spec, logit_bias, sel_bias)
+    y = expert_output_sorted(x, r.ids, r.w, params, spec)
+    return y, r
+
+
+def expert_output_sorted(x, ids, w, params, spec: Spec) -> np.ndarray:
+    """sum_j w_{n,j} FFN_{ids[n,j]}(x_n) computed via dispatch -> per-slice FFN -> combine."""
+    x = np.asarray(x, f64)
+    k = ids.shape[1]
+    perm, inv_perm, counts, offsets = dispatch(ids, spec.n_experts)
+    x_sorted = x[perm // k]
+    y_sorted = np.zeros((perm.size, x.shape[1]), f64)
+    for e in range(spec.n_experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:  # an idle expert runs nothing and its weights are never read
+            y_sorted[lo:hi] = expert_ffn(x_sorted[lo:hi], spec.act, **_expert(params, e))
+    return combine(y_sorted, w, inv_perm)
+
+
+def forward_masked_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_bias=None):
+    """[GPT2-MoE] Diagrams 13-19 form: a dense [N,E] weight matrix that is zero off the
+    chosen set; for each expert, the rows with a non-zero weight are gathered, run through
+    the expert, scaled by their weight and accumulated. Pinned equal to forward_loop."""
+    x = np.asarray(x, f64)
+    r = route(x, params["w_g"], spec, logit_bias, sel_bias)
+    n = x.shape[0]
+    dense_w = np.zeros((n, spec.n_experts), f64)
+    for t in range(n):
+        dense_w[t, r.ids[t]] = r.w[t]
+    y = np.zeros_like(x)
+    for e in range(spec.n_experts):
+        mask = dense_w[:, e] > 0
+        if mask.any():
+            y[mask] += expert_ffn(x[mask], spec.act, **_expert(params, e)) * dense_w[mask, e][:, None]
+    return y, r
+
+
+# ----------------------------------------------------------------------------------------
+# Switch load-balance statistics: [L7.8] §2.3; [GPT2-MoE] router-loss function.
+# ----------------------------------------------------------------------------------------
+
+def load_balance(p, ids, n_experts: int):
+    """f_e = (assignments to e) / N, P_e = mean_n p_{n,e}, L = E sum_e f_e P_e.
+
+    f counts assignments (never probabilities); sum_e f_e = k, so L = k at perfect balance.
+    """
+    p = np.asarray(p, f64)
+    n = p.shape[0]
+    counts = np.bincount(np.asarray(ids).reshape(-1), minlength=n_experts)
+    f = counts.astype(f64) / n
+    P = p.mean(axis=0)
+    L = n_experts * float(np.dot(f, P))
+    return f, P, L
+
+
+def z_loss(z) -> float:
+    """Router z-loss: mean_n (logsumexp_e z_{n,e})^2 ([RB-15] §15.3; [nanoMoE] z-loss)."""
+    z = np.asarray(z, f64)
+    m = z.max(axis=-1)
+    lse = m + np.log(np.exp(z - m[:, None]).sum(axis=-1))
+    return float(np.mean(lse ** 2))
+
+
+def update_bias(b, load, rate: float) -> np.ndarray:
+    """Aux-free balancing step b_e <- b_e + gamma sign(mean(load) - load_e) ([L7.8] §2.5)."""
+    load = np.asarray(load, f64)
+    return np.asarray(b, f64) + f64(rate) * np.sign(load.mean() - load)
