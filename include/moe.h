@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of a dropless top-k mixture-of-experts FFN layer forward for AMD MI355X
+ * (gfx950, CDNA4). Every step runs in hand-written HIP kernels; this header carries no HIP
+ * or framework types, only plain pointers and sizes.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [L7.8]  "Mixture of Experts: routing, sorted dispatch, Switch aux loss, aux-free bias"
+ *           (openlearn course module L7.8): §2 symbols, §2.1 routers table and output
+ *           equation, §2.2 sorted dispatch, §2.3 load-balancing loss, §2.5 aux-free bias,
+ *           §3 worked example, §4 interface, §5 pitfalls.
+ *   [RB-15] "15. Mixture of Experts" (RustingBrain tutorial): §15.2 routing and "Dropless",
+ *           §15.3 the z-loss.
+ *   [nanoMoE] "nanoMoE: Mixture-of-Experts (MoE) LLMs from Scratch in PyTorch": the MLP /
+ *           MLPExperts listings (GELU expert with optional biases).
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *     never allocates, frees or keeps device memory, and keeps no state between calls:
+ *     scratch memory comes from the caller's workspace `ws` of `ws_bytes` bytes.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *     enqueue kernels on it and return without synchronising (moe_get_device_error is the
+ *     one exception). Outputs are valid once the stream reaches that point.
+ *   - Layout: row-major everywhere. Expert weights are stacked per expert in nn.Linear's
+ *     [out, in] layout, so both operands of every product are contiguous along the
+ *     reduction axis. Index tensors are int32, gates and statistics float32.
+ *   - Element type T (cfg->dtype): float32 or bfloat16 for x, all weights and biases,
+ *     x_sorted, y_sorted and y. Accumulation is always float32. With bfloat16 the
+ *     intermediate expert activation h and y_sorted are rounded to bfloat16
+ *     (round-to-nearest-even); the combine sums in float32 and rounds once.
+ *   - Assignments: token n's j-th choice is assignment a = n*k + j; A = N*k ([L7.8] §2.2).
+ *   - Errors: arguments are validated on the host before anything is enqueued; an invalid
+ *     call returns a non-zero moe_status and leaves every output untouched. Errors never
+ *     cross the ABI as exceptions. A failed kernel launch returns MOE_ERR_HIP.
+ *   - Limits: 0 <= N*k < 2^31, 1 <= E <= 1024, 1 <= k <= min(E, 32), d and d_ff in
+ *     [8, 65536] and multiples of 8, every pointer 16-byte aligned (MOE_ERR_UNSUPPORTED
+ *     otherwise). N = 0 is valid: counts and statistics are written as zeros.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* bad k, E, N, enum, flag combination or a NULL pointer */
+  MOE_ERR_UNSUPPORTED = 2,   /* outside the limits above (sizes, alignment) */
+  MOE_ERR_WORKSPACE = 3,     /* ws_bytes < moe_workspace_size(cfg, op) or ws == NULL */
+  MOE_ERR_BAD_EXPERT_ID = 4, /* device-detected expert id outside [0, E) */
+  MOE_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+/* [L7.8] §2.1 routers table. */
+typedef enum {
+  MOE_ROUTER_SOFTMAX_TOPK = 0, /* choose top k of p = softmax(z); w = p_T (renormalised if norm_topk) */
+  MOE_ROUTER_TOPK_SOFTMAX = 1, /* choose top k of z; w = softmax over the k chosen logits */
+  MOE_ROUTER_SIGMOID = 2       /* choose top k of sigmoid(z) + b; w = sigmoid(z_T) (renormalised if norm_topk) */
+} moe_router;
+
+/* Expert FFN. GELU (exact erf form): y = W2 gelu(W1 x + b1) + b2, biases optional
+ * ([nanoMoE] MLPExperts). SwiGLU: y = W2 (silu(W1 x) * (W3 x)), W1 = gate, W3 = up, no biases. */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+  MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_COMBINE = 3, MOE_OP_FORWARD = 4
+} moe_op;
+
+typedef struct {
+  int64_t n_tokens;     /* N: tokens, every leading axis flattened ([L7.8] §2) */
+  int32_t d_model;      /* d */
+  int32_t n_experts;    /* E */
+  int32_t top_k;        /* k */
+  int32_t d_ff;         /* expert hidden width */
+  int32_t router;       /* moe_router */
+  int32_t norm_topk;    /* 1: renormalise the chosen gates to sum to 1; 0: keep them raw */
+  int32_t act;          /* moe_act */
+  int32_t has_bias;     /* 1: b1 [E,d_ff] and b2 [E,d] are given (GELU only) */
+  int32_t dtype;        /* moe_dtype: element type T */
+  float routed_scaling; /* every gate is multiplied by this after renormalisation ([L7.8] §2.1) */
+} moe_config;
+
+/* Number of statistics floats moe_route / moe_forward write: f[E], P[E], L, z_loss. */
+#define MOE_STATS_LEN(E) (2 * (size_t)(E) + 2)
+
+/* Workspace bytes that call `op` needs for this config (256-byte aligned sizes), or 0 when
+ * the config is invalid. The first 256 bytes of every workspace hold the device error word
+ * read by moe_get_device_error; a workspace may be reused by later calls on the same stream. */
+size_t moe_workspace_size(const moe_config* cfg, int op);
+
+/* Routing of N tokens ([L7.8] §2, §2.1; [RB-15] §15.2):
+ *   z = x W_g^T + logit_bias                      (logit_bias [E] float32 or NULL: a fixed
+ *                                                   per-expert offset that is part of z)
+ *   p = softmax(z)                                 (float32, max-subtracted)
+ *   s = z (+ sel_bias) for the softmax routers, sigmoid(z) + sel_bias for sigmoid
+ *   T = the k largest s, largest first, ties to the lowest expert id
+ *   w = gates by the routers table, times routed_scaling; sel_bias never enters w.
+ * Switch statistics ([L7.8] §2.3): counts_e = assignments to e; f_e = counts_e / N;
+ * P_e = mean_n p_{n,e}; L = E sum_e f_e P_e; and the router z-loss ([RB-15] §15.3)
+ * z_loss = mean_n (logsumexp z_n)^2. The final reductions run in a fixed order, so the
+ * statistics are bitwise reproducible.
+ * In:  x [N,d] T; w_router [E,d] T; logit_bias, sel_bias [E] float32 or NULL.
+ * Out: topk_ids [N,k] int32; topk_w [N,k] float32; counts [E] int32;
+ *      stats [2E+2] float32 = f[0..E), P[E..2E), L at [2E], z_loss at [2E+1];
+ *      logits_out [N,E] float32 (z) or NULL; gap_out [N] float32 or NULL, the margin
+ *      s_(k) - s_(k+1) between the last chosen and the best unchosen score (+inf if k = E).
+ * ws: moe_workspace_size(cfg, MOE_OP_ROUTE) bytes. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* sel_bias,
+                     int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                     float* logits_out, float* gap_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Sorted dispatch ([L7.8] §2.2, §3): assignment a = n*k + j is stably sorted by expert id.
+ * Out: perm [A] int32 (sorted position i -> assignment a; the token is a / k);
+ *      inv_perm [A] int32 (inv_perm[perm[i]] = i); counts [E] int32;
+ *      offsets [E+1] int32 (offsets[e] is the START of expert e's slice, offsets[E] = A);
+ *      x_sorted [A,d] T with x_sorted[i] = x[perm[i] / k] (a bit copy);
+ *      gate_sorted [A] float32 = topk_w.flat[perm[i]] when both topk_w and gate_sorted are
+ *      given (either may be NULL otherwise; x_sorted may be NULL to skip the row copy).
+ * Ids outside [0, E) are dropped (no slot; inv_perm = -1; not counted) and set the device
+ * error word in ws, which moe_get_device_error reports as MOE_ERR_BAD_EXPERT_ID.
+ * ws: moe_workspace_size(cfg, MOE_OP_DISPATCH) bytes. */
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_ids,
+                        const float* topk_w, void* x_sorted, int32_t* perm, int32_t* inv_perm,
+                        int32_t* counts, int32_t* offsets, float* gate_sorted,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN over ragged per-expert slices ([L7.8] §2.2 "each expert runs once on its
+ * slice"; [RB-15] "Dropless"): for every expert e and every row i in
+ * [offsets[e], offsets[e+1]):  y_sorted[i] = FFN_e(x_sorted[i]) * gate_sorted[i].
+ * Experts with an empty slice run nothing and their weights are never read.
+ * In:  x_sorted [A,d] T; offsets [E+1] int32 (non-decreasing, offsets[0] = 0, offsets[E] <= A);
+ *      w1 [E,d_ff,d] T (GELU fc or SwiGLU gate); w3 [E,d_ff,d] T (SwiGLU up; NULL for GELU);
+ *      b1 [E,d_ff] T and b2 [E,d] T (has_bias only); w2 [E,d,d_ff] T;
+ *      gate_sorted [A] float32 or NULL (NULL: no scaling).
+ * Out: y_sorted [A,d] T (rows at or past offsets[E] are not written).
+ * ws: moe_workspace_size(cfg, MOE_OP_EXPERT_FFN) bytes (holds h [A,d_ff] T). */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int32_t* offsets,
+                          const void* w1, const void* w3, const void* b1,
+                          const void* w2, const void* b2, const float* gate_sorted,
+                          void* y_sorted, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine ([L7.8] §2.2, §3): y[n] = sum_{j<k} g_{n,j} y_sorted[inv_perm[n*k+j]], summed in
+ * float32 with j ascending and rounded to T once; g = topk_w [N,k] float32, or 1 when
+ * topk_w is NULL (y_sorted already gate-scaled). Assignments with inv_perm outside [0, A)
+ * contribute nothing. */
+moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const float* topk_w,
+                       const int32_t* inv_perm, void* y, void* stream);
+
+/* The whole layer ([L7.8] §2.1 output equation): route -> dispatch -> expert FFN (gate
+ * applied in the down-projection epilogue) -> combine -> statistics, on one stream with no
+ * host synchronisation. Inputs and outputs as in the calls above; y [N,d] T.
+ * stage_events: NULL, or 6 hipEvent_t (as void*) recorded on `stream` at the start, after
+ * routing, after dispatch, after the up projection, after the down projection and at the end.
+ * ws: moe_workspace_size(cfg, MOE_OP_FORWARD) bytes. */
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logit_bias, const float* sel_bias,
+                       const void* w1, const void* w3, const void* b1,
+                       const void* w2, const void* b2,
+                       void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                       void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* Synchronises `stream`, then reads and clears the device error word at the start of `ws`:
+ * MOE_ERR_BAD_EXPERT_ID if a dispatch on this workspace met an out-of-range id,
+ * MOE_ERR_HIP if the synchronisation or copy failed, else MOE_OK. */
+moe_status moe_get_device_error(void* ws, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

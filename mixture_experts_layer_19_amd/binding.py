@@ -1,0 +1,355 @@
+"""Thin ctypes binding over libmoe_mi355x.so, with the C ABI's names.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and contiguity,
+outputs are allocated with torch (device memory is PyTorch's job here), and every step of
+the layer runs in the library's HIP kernels on torch's current stream. There is no
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_BAD_EXPERT_ID, MOE_ERR_HIP = range(6)
+ROUTERS = {"softmax_topk": 0, "topk_softmax": 1, "sigmoid": 2}
+ACTS = {"gelu": 0, "swiglu": 1}
+DTYPES = {"f32": 0, "bf16": 1}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class Op(enum.IntEnum):
+    ROUTE = 0
+    DISPATCH = 1
+    EXPERT_FFN = 2
+    COMBINE = 3
+    FORWARD = 4
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class MoeConfigStruct(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("d_model", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("router", ctypes.c_int32),
+        ("norm_topk", ctypes.c_int32),
+        ("act", ctypes.c_int32),
+        ("has_bias", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("routed_scaling", ctypes.c_float),
+    ]
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    """Hyper-parameters of one layer call (mirrors moe_config)."""
+
+    n_tokens: int
+    d_model: int
+    n_experts: int
+    top_k: int
+    d_ff: int
+    router: str = "softmax_topk"
+    norm_topk: bool = True
+    act: str = "swiglu"
+    has_bias: bool = False
+    dtype: str = "bf16"
+    routed_scaling: float = 1.0
+
+    def struct(self) -> MoeConfigStruct:
+        if self.router not in ROUTERS or self.act not in ACTS or self.dtype not in DTYPES:
+            raise ValueError(f"unknown router/act/dtype in {self}")
+        return MoeConfigStruct(self.n_tokens, self.d_model, self.n_experts, self.top_k, self.d_ff,
+                               ROUTERS[self.router], int(self.norm_topk), ACTS[self.act],
+                               int(self.has_bias), DTYPES[self.dtype], float(self.routed_scaling))
+
+    @property
+    def torch_dtype(self):
+        return TORCH_DTYPES[self.dtype]
+
+    @property
+    def n_assign(self) -> int:
+        return self.n_tokens * self.top_k
+
+    def with_tokens(self, n: int) -> "LayerConfig":
+        return LayerConfig(n, self.d_model, self.n_experts, self.top_k, self.d_ff, self.router,
+                           self.norm_topk, self.act, self.has_bias, self.dtype, self.routed_scaling)
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: run `python -m mixture_experts_layer_19_amd.build` first")
+    L = ctypes.CDLL(LIB_PATH)
+    S = ctypes.POINTER(MoeConfigStruct)
+    L.moe_workspace_size.argtypes = [S, ctypes.c_int]
+    L.moe_workspace_size.restype = ctypes.c_size_t
+    L.moe_route.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.moe_dispatch.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.moe_expert_ffn.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.moe_combine.argtypes = [S, _P, _P, _P, _P, _P]
+    L.moe_forward.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              ctypes.c_size_t, _P, _P]
+    L.moe_get_device_error.argtypes = [_P, _P]
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        if status in (MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE):
+            raise ValueError(f"{what}: {status_string(status)} (status {status})")
+        raise MoeError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _want(t, name, shape, dtype, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_workspace_size(cfg: LayerConfig, op: Op) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(cfg.struct()), int(op)))
+
+
+def workspace(cfg: LayerConfig, op: Op, device="cuda") -> torch.Tensor:
+    n = moe_workspace_size(cfg, op)
+    if n == 0:
+        raise ValueError(f"invalid configuration {cfg}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_route(cfg: LayerConfig, x, w_router, logit_bias=None, sel_bias=None, *, want_logits=False,
+              want_gap=False, ws=None):
+    """Routing and Switch statistics. Returns a dict of device tensors: topk_ids [N,k] int32,
+    topk_w [N,k] f32, counts [E] int32, stats [2E+2] f32 (f, P, L, z_loss) and, on request,
+    logits [N,E] f32 and gap [N] f32."""
+    N, d, E, k = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k
+    T = cfg.torch_dtype
+    _want(x, "x", (N, d), T)
+    _want(w_router, "w_router", (E, d), T)
+    _want(logit_bias, "logit_bias", (E,), torch.float32, optional=True)
+    _want(sel_bias, "sel_bias", (E,), torch.float32, optional=True)
+    dev = w_router.device
+    out = {
+        "topk_ids": torch.empty((N, k), dtype=torch.int32, device=dev),
+        "topk_w": torch.empty((N, k), dtype=torch.float32, device=dev),
+        "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+        "stats": torch.empty((2 * E + 2,), dtype=torch.float32, device=dev),
+    }
+    out["logits"] = torch.empty((N, E), dtype=torch.float32, device=dev) if want_logits else None
+    out["gap"] = torch.empty((N,), dtype=torch.float32, device=dev) if want_gap else None
+    ws = workspace(cfg, Op.ROUTE, dev) if ws is None else ws
+    st = lib().moe_route(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(sel_bias),
+                         _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]),
+                         _ptr(out["logits"]), _ptr(out["gap"]), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_route")
+    return out
+
+
+def moe_dispatch(cfg: LayerConfig, x, topk_ids, topk_w=None, *, want_x_sorted=True, ws=None):
+    """Sorted dispatch. Returns x_sorted [A,d] (or None), perm [A], inv_perm [A], counts [E],
+    offsets [E+1], gate_sorted [A] (when topk_w is given), and the workspace used (its first
+    word carries the device error flag, see moe_get_device_error)."""
+    N, d, E, k = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k
+    A = N * k
+    _want(topk_ids, "topk_ids", (N, k), torch.int32)
+    _want(topk_w, "topk_w", (N, k), torch.float32, optional=True)
+    if want_x_sorted:
+        _want(x, "x", (N, d), cfg.torch_dtype)
+    dev = topk_ids.device
+    out = {
+        "x_sorted": torch.empty((A, d), dtype=cfg.torch_dtype, device=dev) if want_x_sorted else None,
+        "perm": torch.empty((A,), dtype=torch.int32, device=dev),
+        "inv_perm": torch.empty((A,), dtype=torch.int32, device=dev),
+        "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+        "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+        "gate_sorted": torch.empty((A,), dtype=torch.float32, device=dev) if topk_w is not None else None,
+    }
+    ws = workspace(cfg, Op.DISPATCH, dev) if ws is None else ws
+    st = lib().moe_dispatch(ctypes.byref(cfg.struct()), _ptr(x) if want_x_sorted else None, _ptr(topk_ids),
+                            _ptr(topk_w), _ptr(out["x_sorted"]), _ptr(out["perm"]), _ptr(out["inv_perm"]),
+                            _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["gate_sorted"]),
+                            _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_dispatch")
+    out["ws"] = ws
+    return out
+
+
+def moe_expert_ffn(cfg: LayerConfig, x_sorted, offsets, w1, w3, b1, w2, b2, gate_sorted=None, *, ws=None):
+    """Expert FFN over the ragged slices; returns y_sorted [A,d] (rows past offsets[E] unwritten)."""
+    N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
+    A = N * k
+    T = cfg.torch_dtype
+    _want(x_sorted, "x_sorted", (A, d), T)
+    _want(offsets, "offsets", (E + 1,), torch.int32)
+    _want(w1, "w1", (E, f, d), T)
+    _want(w2, "w2", (E, d, f), T)
+    _want(w3, "w3", (E, f, d), T, optional=cfg.act != "swiglu")
+    _want(b1, "b1", (E, f), T, optional=not cfg.has_bias)
+    _want(b2, "b2", (E, d), T, optional=not cfg.has_bias)
+    _want(gate_sorted, "gate_sorted", (A,), torch.float32, optional=True)
+    y_sorted = torch.empty((A, d), dtype=T, device=w1.device)
+    ws = workspace(cfg, Op.EXPERT_FFN, w1.device) if ws is None else ws
+    st = lib().moe_expert_ffn(ctypes.byref(cfg.struct()), _ptr(x_sorted), _ptr(offsets), _ptr(w1), _ptr(w3),
+                              _ptr(b1), _ptr(w2), _ptr(b2), _ptr(gate_sorted), _ptr(y_sorted),
+                              _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_expert_ffn")
+    return y_sorted
+
+
+def moe_combine(cfg: LayerConfig, y_sorted, topk_w, inv_perm):
+    """Gate-weighted combine back through inv_perm; returns y [N,d]."""
+    N, d, k = cfg.n_tokens, cfg.d_model, cfg.top_k
+    _want(y_sorted, "y_sorted", (N * k, d), cfg.torch_dtype)
+    _want(topk_w, "topk_w", (N, k), torch.float32, optional=True)
+    _want(inv_perm, "inv_perm", (N * k,), torch.int32)
+    y = torch.empty((N, d), dtype=cfg.torch_dtype, device=inv_perm.device)
+    st = lib().moe_combine(ctypes.byref(cfg.struct()), _ptr(y_sorted), _ptr(topk_w), _ptr(inv_perm), _ptr(y), _stream())
+    _check(st, "moe_combine")
+    return y
+
+
+def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, logit_bias=None, sel_bias=None,
+                *, ws=None, out=None, stage_events: Optional[Sequence[int]] = None):
+    """The whole layer. Returns dict y [N,d], topk_ids, topk_w, counts, stats. `out` may hold
+    preallocated outputs (same keys) and `ws` a preallocated workspace, so that repeated calls
+    allocate nothing. stage_events: 6 raw hipEvent_t handles (ints) or None."""
+    N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
+    T = cfg.torch_dtype
+    if out is None:
+        _want(x, "x", (N, d), T)
+        _want(w_router, "w_router", (E, d), T)
+        _want(w1, "w1", (E, f, d), T)
+        _want(w2, "w2", (E, d, f), T)
+        _want(w3, "w3", (E, f, d), T, optional=cfg.act != "swiglu")
+        _want(b1, "b1", (E, f), T, optional=not cfg.has_bias)
+        _want(b2, "b2", (E, d), T, optional=not cfg.has_bias)
+        _want(logit_bias, "logit_bias", (E,), torch.float32, optional=True)
+        _want(sel_bias, "sel_bias", (E,), torch.float32, optional=True)
+        dev = w_router.device
+        out = {
+            "y": torch.empty((N, d), dtype=T, device=dev),
+            "topk_ids": torch.empty((N, k), dtype=torch.int32, device=dev),
+            "topk_w": torch.empty((N, k), dtype=torch.float32, device=dev),
+            "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+            "stats": torch.empty((2 * E + 2,), dtype=torch.float32, device=dev),
+        }
+    if ws is None:
+        ws = workspace(cfg, Op.FORWARD, w_router.device)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in stage_events])
+    st = lib().moe_forward(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(sel_bias),
+                           _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out["y"]), _ptr(out["topk_ids"]),
+                           _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]), _ptr(ws), ws.numel(),
+                           ev, _stream())
+    _check(st, "moe_forward")
+    return out
+
+
+def moe_get_device_error(ws: torch.Tensor) -> int:
+    """Synchronises the current stream and returns (and clears) the workspace's device error
+    status: MOE_OK, MOE_ERR_BAD_EXPERT_ID or MOE_ERR_INVALID_ARG."""
+    return int(lib().moe_get_device_error(_ptr(ws), _stream()))
+
+
+# HIP events for stage timing, straight from the HIP runtime (torch.cuda.Event only times
+# work on torch's streams; these are recorded by the library itself on the call's stream).
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        for name in ("libamdhip64.so", "libamdhip64.so.7", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise RuntimeError("libamdhip64 not found")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+        _hip.hipEventSynchronize.argtypes = [_P]
+        _hip.hipEventDestroy.argtypes = [_P]
+    return _hip
+
+
+class HipEvents:
+    """A handful of raw hipEvent_t handles (timing enabled)."""
+
+    def __init__(self, n: int):
+        h = _hiprt()
+        self.handles = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(e.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        h = _hiprt()
+        h.hipEventSynchronize(ctypes.c_void_p(self.handles[j]))
+        ms = ctypes.c_float()
+        if h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handles[i]), ctypes.c_void_p(self.handles[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            h = _hiprt()
+            for e in self.handles:
+                h.hipEventDestroy(ctypes.c_void_p(e))
+        except Exception:
+            pass

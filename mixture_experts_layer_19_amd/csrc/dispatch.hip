@@ -1,0 +1,189 @@
+// Sorted dispatch ("Mixture of Experts: routing, sorted dispatch, Switch aux loss, aux-free
+// bias" (L7.8) §2.2 and §3): assignment a = n*k + j is stably sorted by expert id as a
+// two-level counting sort, with no atomics deciding any position:
+//   1. histogram:  per chunk of kChunk assignments, the count of each expert;
+//   2. scan:       counts, offsets (exclusive prefix sum, offsets[E] = A), and for every
+//                  chunk the first sorted slot of its run of each expert;
+//   3. scatter:    within a chunk, an assignment's slot is its chunk base plus the number of
+//                  earlier assignments of the same expert in the chunk (wave ballots), so the
+//                  order inside each expert's slice is ascending in a (stable);
+//   4. row copy:   token-major, each row of x is read once and written to its k slots.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kChunk = 2048;  // assignments per workgroup in the histogram / scatter passes
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(
+    const int32_t* __restrict__ ids, int A, int E, int* __restrict__ hist, int* __restrict__ bad) {
+  __shared__ int s_hist[kMaxExperts];
+  __shared__ int s_bad;
+  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * kChunk;
+  const int a1 = min(A, a0 + kChunk);
+  int my_bad = 0;
+  for (int a = a0 + threadIdx.x; a < a1; a += 256) {
+    const int e = ids[a];
+    if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);  // integer counts: order-independent
+    else my_bad = 1;
+  }
+  if (my_bad) s_bad = 1;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = s_hist[e];
+  if (threadIdx.x == 0) bad[blockIdx.x] = s_bad;
+}
+
+// One workgroup: per-expert totals over the chunks (chunk order), exclusive scan over
+// experts, chunk bases, and the device error word (written, not accumulated).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    const int* __restrict__ hist, const int* __restrict__ bad, int n_chunks, int E,
+    int* __restrict__ base, int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ err) {
+  __shared__ int s_scan[kMaxExperts];
+  __shared__ int s_bad;
+  const int e = threadIdx.x;
+  if (e == 0) s_bad = 0;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < n_chunks; ++b) total += hist[(size_t)b * E + e];
+    s_scan[e] = total;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < n_chunks; b += blockDim.x)
+    if (bad[b]) s_bad = 1;
+  // inclusive Hillis-Steele scan over the experts
+  for (int o = 1; o < E; o <<= 1) {
+    int v = 0;
+    if (e < E && e >= o) v = s_scan[e - o];
+    __syncthreads();
+    if (e < E) s_scan[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int start = s_scan[e] - total;
+    counts[e] = total;
+    offsets[e] = start;
+    if (e == E - 1) offsets[E] = s_scan[e];
+    int run = start;
+    for (int b = 0; b < n_chunks; ++b) {
+      base[(size_t)b * E + e] = run;
+      run += hist[(size_t)b * E + e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && err) err[0] = s_bad ? MOE_ERR_BAD_EXPERT_ID : 0;
+}
+
+// Stable scatter. The chunk is walked in order, 256 assignments (4 waves) at a time. For an
+// assignment of expert e in wave w: slot = running[e] + (count of e in waves < w of this
+// step) + (count of e in lower lanes of wave w). Per-wave counts are published in LDS
+// tagged with the step number, so stale entries read as zero without clearing.
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int A, int E, int id_bits,
+    const int* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    float* __restrict__ gate_sorted) {
+  __shared__ int s_run[kMaxExperts];
+  __shared__ int s_cnt[4][kMaxExperts];  // (step << 16) | count
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    s_run[e] = base[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s_cnt[w][e] = -1;
+  }
+  __syncthreads();
+  const int a0 = blockIdx.x * kChunk;
+  const int a1 = min(A, a0 + kChunk);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int step = 0, as = a0; as < a1; ++step, as += 256) {
+    const int a = as + threadIdx.x;
+    const int e = (a < a1) ? ids[a] : -1;
+    const bool valid = e >= 0 && e < E;
+    // lanes of this wave holding the same expert id
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+      const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    const int cnt = __popcll(peers);
+    const bool leader = valid && rank == 0;
+    if (leader) s_cnt[wave][e] = (step << 16) | cnt;
+    __syncthreads();
+    if (valid) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) {
+        const int v = s_cnt[w][e];
+        if ((v >> 16) == step) before += v & 0xffff;
+      }
+      const int pos = s_run[e] + before + rank;
+      perm[pos] = a;
+      inv_perm[a] = pos;
+      if (gate_sorted) gate_sorted[pos] = topk_w[a];
+    } else if (a < a1) {
+      inv_perm[a] = -1;
+    }
+    __syncthreads();
+    if (leader) atomicAdd(&s_run[e], cnt);  // integer adds: the final run is order-independent
+    __syncthreads();
+  }
+}
+
+// Token-major row copy: x_sorted[inv_perm[n*k + j]] = x[n] for j < k, 16 bytes per lane.
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ inv_perm, uint4* __restrict__ x_sorted,
+    long long n_tokens, int k, int vec_per_row) {
+  const long long total = n_tokens * vec_per_row;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    const long long n = i / vec_per_row;
+    const int c = (int)(i - n * vec_per_row);
+    const uint4 v = x[i];
+    for (int j = 0; j < k; ++j) {
+      const int dst = inv_perm[n * k + j];
+      if (dst >= 0) x_sorted[(size_t)dst * vec_per_row + c] = v;
+    }
+  }
+}
+
+void carve_dispatch(const moe_config& c, WsCarver& w, WsLayout* L) {
+  const long long A = c.n_tokens * c.top_k;
+  const int n_chunks = (int)((A + kChunk - 1) / kChunk);
+  const size_t E = (size_t)c.n_experts;
+  int* hist = w.take_t<int>((size_t)n_chunks * E);
+  int* base = w.take_t<int>((size_t)n_chunks * E);
+  int* bad = w.take_t<int>((size_t)n_chunks);
+  if (L) {
+    L->d_hist = hist;
+    L->d_base = base;
+    L->d_bad = bad;
+  }
+}
+
+hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x,
+                           const int32_t* topk_ids, const float* topk_w, void* x_sorted,
+                           int32_t* perm, int32_t* inv_perm, int32_t* counts, int32_t* offsets,
+                           float* gate_sorted, hipStream_t stream) {
+  const int A = (int)(c.n_tokens * c.top_k);
+  const int E = c.n_experts;
+  const int n_chunks = (A + kChunk - 1) / kChunk;
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  if (n_chunks > 0) dispatch_hist_kernel<<<n_chunks, 256, 0, stream>>>(topk_ids, A, E, L.d_hist, L.d_bad);
+  dispatch_scan_kernel<<<1, 1024, 0, stream>>>(L.d_hist, L.d_bad, n_chunks, E, L.d_base, counts, offsets, L.err);
+  if (n_chunks > 0) {
+    dispatch_scatter_kernel<<<n_chunks, 256, 0, stream>>>(topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr,
+                                                          A, E, id_bits, L.d_base, perm, inv_perm,
+                                                          (gate_sorted && topk_w) ? gate_sorted : nullptr);
+    if (x_sorted) {
+      const int vpr = (int)(c.d_model * elem_size(c) / 16);
+      const long long total = c.n_tokens * vpr;
+      const int grid = (int)std::min<long long>((total + 255) / 256, 1 << 16);
+      dispatch_copy_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(x), inv_perm,
+                                                     static_cast<uint4*>(x_sorted), c.n_tokens, c.top_k, vpr);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

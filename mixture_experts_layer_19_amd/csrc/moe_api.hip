@@ -1,0 +1,276 @@
+// C ABI of the MoE layer forward: host-side validation, workspace carving and the launch
+// sequences. Nothing here allocates, frees or synchronises (except moe_get_device_error),
+// and no HIP call is made before the first launch, so the library loads without a GPU.
+#include <cmath>
+#include <cstdint>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Checks of the configuration itself. needs_ff: the call uses d_ff.
+moe_status check_config(const moe_config* c, bool needs_ff) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->n_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts) return MOE_ERR_INVALID_ARG;
+  if (c->router < MOE_ROUTER_SOFTMAX_TOPK || c->router > MOE_ROUTER_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->act < MOE_ACT_GELU || c->act > MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if ((c->norm_topk != 0 && c->norm_topk != 1) || (c->has_bias != 0 && c->has_bias != 1)) return MOE_ERR_INVALID_ARG;
+  if (c->has_bias && c->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->routed_scaling)) return MOE_ERR_INVALID_ARG;
+  if (c->n_experts > kMaxExperts || c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->n_tokens * (long long)c->top_k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model < 8 || c->d_model > 65536 || c->d_model % 8) return MOE_ERR_UNSUPPORTED;
+  if (needs_ff && (c->d_ff < 8 || c->d_ff > 65536 || c->d_ff % 8)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// A required tensor of the element type: non-null and 16-byte aligned.
+moe_status need_t(const void* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  return aligned16(p) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+moe_status opt_t(const void* p) { return (!p || aligned16(p)) ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+// A required int32 / float32 tensor: non-null and 4-byte aligned.
+moe_status need_4(const void* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  return aligned4(p) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+moe_status opt_4(const void* p) { return (!p || aligned4(p)) ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+
+#define MOE_TRY(expr)                  \
+  do {                                 \
+    const moe_status s_ = (expr);      \
+    if (s_ != MOE_OK) return s_;       \
+  } while (0)
+
+// Forward-only buffers placed after the stage regions.
+void carve_forward_buffers(const moe_config& c, WsCarver& w, WsLayout* L) {
+  const size_t A = (size_t)(c.n_tokens * c.top_k);
+  const size_t row = (size_t)c.d_model * elem_size(c);
+  int* perm = w.take_t<int>(A);
+  int* inv = w.take_t<int>(A);
+  int* off = w.take_t<int>((size_t)c.n_experts + 1);
+  int* cnt = w.take_t<int>((size_t)c.n_experts);
+  float* gs = w.take_t<float>(A);
+  void* xs = w.take(A * row);
+  void* ys = w.take(A * row);
+  if (L) {
+    L->perm = perm;
+    L->inv_perm = inv;
+    L->offsets = off;
+    L->counts_tmp = cnt;
+    L->gate_sorted = gs;
+    L->x_sorted = xs;
+    L->y_sorted = ys;
+  }
+}
+
+size_t layout(const moe_config& c, int op, char* base, WsLayout* L) {
+  WsCarver w(base);
+  int* err = w.take_t<int>(kErrWordBytes / sizeof(int));
+  if (L) {
+    L->base = base;
+    L->err = err;
+  }
+  switch (op) {
+    case MOE_OP_ROUTE: carve_route(c, w, L); break;
+    case MOE_OP_DISPATCH: carve_dispatch(c, w, L); break;
+    case MOE_OP_EXPERT_FFN: carve_ffn(c, w, L); break;
+    case MOE_OP_COMBINE: break;
+    case MOE_OP_FORWARD:
+      carve_route(c, w, L);
+      carve_dispatch(c, w, L);
+      carve_ffn(c, w, L);
+      carve_forward_buffers(c, w, L);
+      break;
+    default: return 0;
+  }
+  return w.used();
+}
+
+moe_status check_ws(const moe_config& c, int op, void* ws, size_t ws_bytes, WsLayout* L) {
+  if (!ws || !aligned16(ws)) return MOE_ERR_WORKSPACE;
+  const size_t need = layout(c, op, nullptr, nullptr);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  layout(c, op, static_cast<char*>(ws), L);
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg, int op) {
+  const bool needs_ff = op == MOE_OP_EXPERT_FFN || op == MOE_OP_FORWARD;
+  if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD) return 0;
+  if (check_config(cfg, needs_ff) != MOE_OK) return 0;
+  return layout(*cfg, op, nullptr, nullptr);
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* sel_bias, int32_t* topk_ids,
+                     float* topk_w, int32_t* counts, float* stats, float* logits_out,
+                     float* gap_out, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg, false));
+  const bool has_tokens = cfg->n_tokens > 0;
+  if (has_tokens) {
+    MOE_TRY(need_t(x));
+    MOE_TRY(need_4(topk_ids));
+    MOE_TRY(need_4(topk_w));
+  }
+  MOE_TRY(need_t(w_router));
+  MOE_TRY(need_4(counts));
+  MOE_TRY(need_4(stats));
+  MOE_TRY(opt_4(logit_bias));
+  MOE_TRY(opt_4(sel_bias));
+  MOE_TRY(opt_4(logits_out));
+  MOE_TRY(opt_4(gap_out));
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_ROUTE, ws, ws_bytes, &L));
+  return hip_status(launch_route(*cfg, L, x, w_router, logit_bias, sel_bias, topk_ids, topk_w, counts,
+                                 stats, logits_out, gap_out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_ids,
+                        const float* topk_w, void* x_sorted, int32_t* perm, int32_t* inv_perm,
+                        int32_t* counts, int32_t* offsets, float* gate_sorted,
+                        void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg, false));
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_4(topk_ids));
+    MOE_TRY(need_4(perm));
+    MOE_TRY(need_4(inv_perm));
+    MOE_TRY(opt_t(x_sorted));
+    if (x_sorted) MOE_TRY(need_t(x));
+    MOE_TRY(opt_4(topk_w));
+    MOE_TRY(opt_4(gate_sorted));
+  }
+  MOE_TRY(need_4(counts));
+  MOE_TRY(need_4(offsets));
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_DISPATCH, ws, ws_bytes, &L));
+  return hip_status(launch_dispatch(*cfg, L, x, topk_ids, topk_w, x_sorted, perm, inv_perm, counts, offsets,
+                                    gate_sorted, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int32_t* offsets,
+                          const void* w1, const void* w3, const void* b1, const void* w2,
+                          const void* b2, const float* gate_sorted, void* y_sorted, void* ws,
+                          size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg, true));
+  MOE_TRY(need_4(offsets));
+  MOE_TRY(need_t(w1));
+  MOE_TRY(need_t(w2));
+  if (cfg->act == MOE_ACT_SWIGLU) MOE_TRY(need_t(w3));
+  if (cfg->has_bias) {
+    MOE_TRY(need_t(b1));
+    MOE_TRY(need_t(b2));
+  }
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_t(x_sorted));
+    MOE_TRY(need_t(y_sorted));
+    MOE_TRY(opt_4(gate_sorted));
+  }
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_EXPERT_FFN, ws, ws_bytes, &L));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(hip_status(launch_ffn_up(*cfg, L, x_sorted, offsets, w1, w3, b1, s)));
+  return hip_status(launch_ffn_down(*cfg, L, offsets, w2, b2, gate_sorted, y_sorted, s));
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const float* topk_w,
+                       const int32_t* inv_perm, void* y, void* stream) {
+  MOE_TRY(check_config(cfg, false));
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_t(y_sorted));
+    MOE_TRY(need_4(inv_perm));
+    MOE_TRY(need_t(y));
+    MOE_TRY(opt_4(topk_w));
+  }
+  return hip_status(launch_combine(*cfg, y_sorted, topk_w, inv_perm, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logit_bias, const float* sel_bias, const void* w1,
+                       const void* w3, const void* b1, const void* w2, const void* b2, void* y,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, void* ws,
+                       size_t ws_bytes, void* const* stage_events, void* stream) {
+  MOE_TRY(check_config(cfg, true));
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_t(x));
+    MOE_TRY(need_t(y));
+    MOE_TRY(need_4(topk_ids));
+    MOE_TRY(need_4(topk_w));
+  }
+  MOE_TRY(need_t(w_router));
+  MOE_TRY(need_t(w1));
+  MOE_TRY(need_t(w2));
+  if (cfg->act == MOE_ACT_SWIGLU) MOE_TRY(need_t(w3));
+  if (cfg->has_bias) {
+    MOE_TRY(need_t(b1));
+    MOE_TRY(need_t(b2));
+  }
+  MOE_TRY(need_4(counts));
+  MOE_TRY(need_4(stats));
+  MOE_TRY(opt_4(logit_bias));
+  MOE_TRY(opt_4(sel_bias));
+  if (stage_events)
+    for (int i = 0; i < 6; ++i)
+      if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_FORWARD, ws, ws_bytes, &L));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> moe_status {
+    if (!stage_events) return MOE_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s));
+  };
+  MOE_TRY(mark(0));
+  MOE_TRY(hip_status(launch_route(*cfg, L, x, w_router, logit_bias, sel_bias, topk_ids, topk_w, counts, stats,
+                                  nullptr, nullptr, s)));
+  MOE_TRY(mark(1));
+  MOE_TRY(hip_status(launch_dispatch(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
+                                     L.counts_tmp, L.offsets, L.gate_sorted, s)));
+  MOE_TRY(mark(2));
+  MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s)));
+  MOE_TRY(mark(3));
+  MOE_TRY(hip_status(launch_ffn_down(*cfg, L, L.offsets, w2, b2, L.gate_sorted, L.y_sorted, s)));
+  MOE_TRY(mark(4));
+  MOE_TRY(hip_status(launch_combine(*cfg, L.y_sorted, nullptr, L.inv_perm, y, s)));
+  return mark(5);
+}
+
+moe_status moe_get_device_error(void* ws, void* stream) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int v = 0;
+  const int zero = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  if (hipMemcpyAsync(ws, &zero, sizeof(int), hipMemcpyHostToDevice, s) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  if (v == MOE_ERR_BAD_EXPERT_ID || v == MOE_ERR_INVALID_ARG) return static_cast<moe_status>(v);
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or alignment";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_BAD_EXPERT_ID: return "expert id out of range";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

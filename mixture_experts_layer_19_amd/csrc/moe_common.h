@@ -1,0 +1,90 @@
+// Device-side helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bfloat16 is carried as its 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+MOE_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Element-type traits: load/store one element as float.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPer16B = 4;
+  MOE_DEV static float load(const float* p) { return *p; }
+  MOE_DEV static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kPer16B = 8;
+  MOE_DEV static float load(const bf16_t* p) { return bf16_to_f32(p->bits); }
+  MOE_DEV static void store(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
+};
+
+// 16 bytes of T unpacked to float (4 floats or 8 bf16 -> 8 floats).
+MOE_DEV void unpack16(const uint4& v, float* out, float) {
+  out[0] = __uint_as_float(v.x);
+  out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z);
+  out[3] = __uint_as_float(v.w);
+}
+MOE_DEV void unpack16(const uint4& v, float* out, bf16_t) {
+  out[0] = __uint_as_float(v.x << 16);
+  out[1] = __uint_as_float(v.x & 0xffff0000u);
+  out[2] = __uint_as_float(v.y << 16);
+  out[3] = __uint_as_float(v.y & 0xffff0000u);
+  out[4] = __uint_as_float(v.z << 16);
+  out[5] = __uint_as_float(v.z & 0xffff0000u);
+  out[6] = __uint_as_float(v.w << 16);
+  out[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+MOE_DEV uint4 pack16(const float* in, float) {
+  return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                    __float_as_uint(in[3]));
+}
+MOE_DEV uint4 pack16(const float* in, bf16_t) {
+  auto p2 = [](float lo, float hi) { return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16); };
+  return make_uint4(p2(in[0], in[1]), p2(in[2], in[3]), p2(in[4], in[5]), p2(in[6], in[7]));
+}
+
+MOE_DEV float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752440f)); }
+MOE_DEV float sigmoid_f(float u) { return 1.0f / (1.0f + expf(-u)); }
+MOE_DEV float silu_f(float u) { return u / (1.0f + expf(-u)); }
+
+MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Wave-wide sums / maxima through cross-lane shuffles (fixed butterfly order, so every lane
+// gets the same bitwise result).
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+MOE_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+}  // namespace moe

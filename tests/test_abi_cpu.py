@@ -1,0 +1,125 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/moe.h declares,
+sizes workspaces, and rejects invalid calls on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_19_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+               "moe_workspace_size", "moe_get_device_error", "moe_status_string"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(lib, fn), f"{fn} declared in moe.h but not exported"
+
+
+def test_status_strings():
+    assert B.status_string(0) == "ok"
+    assert "expert id" in B.status_string(4)
+    assert B.status_string(99) == "unknown status"
+
+
+MIXTRAL = B.LayerConfig(8192, 4096, 8, 2, 14336)
+
+
+def test_workspace_sizes():
+    sizes = {op: B.moe_workspace_size(MIXTRAL, op) for op in B.Op}
+    assert all(s > 0 and s % 256 == 0 for s in sizes.values())
+    A = 8192 * 2
+    # forward holds x_sorted, y_sorted and h: 2 A d + A d_ff bf16 at least
+    assert sizes[B.Op.FORWARD] >= (2 * A * 4096 + A * 14336) * 2
+    assert sizes[B.Op.FORWARD] > sizes[B.Op.EXPERT_FFN] > sizes[B.Op.ROUTE]
+    assert B.moe_workspace_size(MIXTRAL.with_tokens(0), B.Op.FORWARD) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(top_k=0), dict(top_k=9), dict(n_experts=0), dict(router="argmax"), dict(act="relu"),
+    dict(has_bias=True), dict(n_tokens=-1),
+])
+def test_invalid_configs_have_no_workspace(bad):
+    import dataclasses
+    kw = dataclasses.asdict(MIXTRAL)
+    kw.update(bad)
+    if kw["router"] not in B.ROUTERS or kw["act"] not in B.ACTS:
+        with pytest.raises(ValueError):
+            B.LayerConfig(**kw).struct()
+        return
+    assert B.moe_workspace_size(B.LayerConfig(**kw), B.Op.FORWARD) == 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(d_model=100), B.MOE_ERR_UNSUPPORTED), (dict(d_ff=12), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=2048, top_k=2), B.MOE_ERR_UNSUPPORTED), (dict(top_k=33, n_experts=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_tokens=2 ** 30, top_k=2), B.MOE_ERR_UNSUPPORTED), (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+])
+def test_host_validation_codes(bad, status):
+    """Invalid calls return their status before any HIP call (so this runs without a GPU)."""
+    import dataclasses
+    kw = dataclasses.asdict(MIXTRAL)
+    kw.update(bad)
+    cfg = B.LayerConfig(**kw).struct()
+    lib = B.lib()
+    fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+    st = lib.moe_forward(ctypes.byref(cfg), fake, fake, None, None, fake, fake, None, fake, None, fake, fake,
+                         fake, fake, fake, fake, 1 << 40, None, None)
+    assert st == status
+
+
+def test_null_and_misaligned_pointers_and_small_workspace():
+    lib = B.lib()
+    cfg = MIXTRAL.struct()
+    f = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)
+    args = lambda **o: [o.get(n, f) for n in ("x", "wg", "lb", "sb", "ids", "w", "cnt", "st", "lo", "gap", "ws")]
+    call = lambda a, n=1 << 40: lib.moe_route(ctypes.byref(cfg), *a[:10], a[10], n, None)
+    assert call(args(x=None)) == B.MOE_ERR_INVALID_ARG
+    assert call(args(x=mis)) == B.MOE_ERR_UNSUPPORTED
+    assert call(args(ws=None)) == B.MOE_ERR_WORKSPACE
+    assert call(args(), 16) == B.MOE_ERR_WORKSPACE
+    # SwiGLU needs w3; GELU with biases needs b1 and b2
+    st = lib.moe_expert_ffn(ctypes.byref(cfg), f, f, f, None, None, f, None, None, f, f, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    gcfg = B.LayerConfig(8192, 768, 6, 2, 3072, act="gelu", has_bias=True).struct()
+    st = lib.moe_expert_ffn(ctypes.byref(gcfg), f, f, f, None, None, f, f, None, f, f, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    # stage events must all be given when the array is
+    ev = (ctypes.c_void_p * 6)(f, f, f, None, f, f)
+    st = lib.moe_forward(ctypes.byref(cfg), f, f, None, None, f, f, None, f, None, f, f, f, f, f, f, 1 << 40, ev, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+
+
+def test_workload_recipes_are_seeded_and_shaped():
+    from mixture_experts_layer_19_amd.workload import WORKLOADS, make_inputs
+    w = WORKLOADS["fine_grained"].scaled(n_tokens=64, d_model=32, d_ff=16)
+    a = make_inputs(w, seed=0, device="cpu")
+    b = make_inputs(w, seed=0, device="cpu")
+    assert a["x"].shape == (64, 32) and a["w1"].shape == (128, 16, 32) and a["w3"].shape == (128, 16, 32)
+    assert all(torch_equal(a[k], b[k]) for k in a if a[k] is not None)
+    r = sorted((-a["logit_bias"].double() / 1.2).exp().round().long().tolist())
+    assert r == list(range(1, 129)), "Zipf offset must be -1.2 ln r over a permutation r of 1..E"
+    d = make_inputs(WORKLOADS["deepseek_v3"].scaled(n_tokens=8, d_model=16, d_ff=8, n_experts=16), device="cpu")
+    assert d["sel_bias"].abs().max() <= 0.1 and d["logit_bias"] is None
+    assert abs(float(a["w1"].float().std()) - 0.02) < 0.002
+
+
+def torch_equal(x, y):
+    import torch
+    return torch.equal(x, y)

@@ -1,0 +1,299 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on the same seeded
+inputs, at sizes the oracle finishes in seconds that span several tiles and ragged tails,
+plus edge cases. Bar: bit-exact ids / perm / inv_perm / counts / offsets (near-ties
+excluded and counted), max|err| <= 1e-4 max|y| (f32) or 2e-2 max|y| (bf16)."""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (NEAR_TIE, TOL, assert_close_rel, check_dispatch_valid, compare_ids, f64,
+                         oracle_params, spec_of)
+from mixture_experts_layer_19_amd import binding as B
+from mixture_experts_layer_19_amd import workload as W
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def run_forward_and_check(w: W.Workload, seed=0, check_stats=True):
+    cfg = w.cfg
+    say(f"[forward] {w.name} {cfg}")
+    inp = W.make_inputs(w, seed=seed)
+    out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
+                        inp["logit_bias"], inp["sel_bias"])
+    torch.cuda.synchronize()
+    params = oracle_params(inp)
+    spec = spec_of(cfg)
+    y_ref, r = O.forward_loop(f64(inp["x"]), params, spec, f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    ids = out["topk_ids"].cpu().numpy()
+    near, intra, agree = compare_ids(ids, r, cfg.top_k)
+    gw = out["topk_w"].cpu().numpy()
+    if agree.any():
+        np.testing.assert_allclose(gw[agree], r.w[agree], rtol=1e-5, atol=1e-6)
+    counts = out["counts"].cpu().numpy()
+    assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=cfg.n_experts))
+    if agree.all():
+        assert np.array_equal(counts, np.bincount(r.ids.reshape(-1), minlength=cfg.n_experts))
+    if check_stats:
+        f, P, L = O.load_balance(r.p, r.ids, cfg.n_experts)
+        st = out["stats"].cpu().numpy().astype(np.float64)
+        E = cfg.n_experts
+        if agree.all():
+            np.testing.assert_allclose(st[:E], f, rtol=1e-6, atol=1e-7)
+            np.testing.assert_allclose(st[2 * E], L, rtol=1e-5)
+        np.testing.assert_allclose(st[E:2 * E], P, rtol=1e-5, atol=1e-7)
+        np.testing.assert_allclose(st[2 * E + 1], O.z_loss(r.z), rtol=1e-5, atol=1e-6)
+    y = f64(out["y"])
+    err, scale = assert_close_rel(y[agree], y_ref[agree], TOL[cfg.dtype], f"y ({w.name})")
+    say(f"    near-ties {int(near.sum())} intra {int(intra.sum())} max|err| {err:.3e} max|y| {scale:.3e}")
+    return out, r
+
+
+# ---------------------------------------------------------------------------------------
+# L7.8 §3 worked example through the device path
+# ---------------------------------------------------------------------------------------
+
+def test_worked_example_on_device():
+    d = 8
+    cfg = B.LayerConfig(2, d, 4, 2, 8, dtype="f32", act="gelu")
+    z = np.log(np.array([[2, 4, 1, 1], [3, 1, 3, 2]], np.float64))
+    x = torch.zeros((2, d), dtype=torch.float32)
+    x[:, :4] = torch.from_numpy(z).float()
+    wg = torch.zeros((4, d), dtype=torch.float32)
+    wg[:, :4] = torch.eye(4)
+    r = B.moe_route(cfg, x.cuda(), wg.cuda(), want_logits=True, want_gap=True)
+    assert r["topk_ids"].cpu().tolist() == [[1, 0], [0, 2]]
+    np.testing.assert_allclose(r["topk_w"].cpu().numpy(), [[2 / 3, 1 / 3], [1 / 2, 1 / 2]], rtol=1e-6)
+    assert r["counts"].cpu().tolist() == [2, 1, 1, 0]
+    st = r["stats"].cpu().numpy()
+    np.testing.assert_allclose(st[:4], [1, 0.5, 0.5, 0], rtol=1e-6)
+    np.testing.assert_allclose(st[4:8], [7 / 24, 11 / 36, 11 / 48, 25 / 144], rtol=1e-6)
+    np.testing.assert_allclose(st[8], 161 / 72, rtol=1e-6)
+    dsp = B.moe_dispatch(cfg, x.cuda(), r["topk_ids"], r["topk_w"])
+    assert dsp["perm"].cpu().tolist() == [1, 2, 0, 3]
+    assert dsp["inv_perm"].cpu().tolist() == [2, 0, 1, 3]
+    assert dsp["offsets"].cpu().tolist() == [0, 2, 3, 4, 4]
+    assert dsp["counts"].cpu().tolist() == [2, 1, 1, 0]
+    np.testing.assert_allclose(dsp["gate_sorted"].cpu().numpy(), [1 / 3, 1 / 2, 2 / 3, 1 / 2], rtol=1e-6)
+    assert torch.equal(dsp["x_sorted"].cpu(), x[[0, 1, 0, 1]])
+    ys = torch.tensor([10.0, 20.0, 30.0, 40.0]).repeat_interleave(d).reshape(4, d).cuda()
+    y = B.moe_combine(cfg, ys, r["topk_w"], dsp["inv_perm"]).cpu().numpy()
+    np.testing.assert_allclose(y[:, 0], [70 / 3, 30], rtol=1e-6)
+    assert B.moe_get_device_error(dsp["ws"]) == B.MOE_OK
+
+
+# ---------------------------------------------------------------------------------------
+# Stage-level parity on seeded stage inputs
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,E,k,zipf", [(1, 4, 2, 0), (777, 5, 2, 0), (3000, 64, 6, 1.3), (4100, 256, 8, 1.1),
+                                        (2500, 1024, 32, 0.8), (513, 3, 3, 0), (1000, 1, 1, 0)])
+def test_dispatch_bit_exact(N, E, k, zipf):
+    cfg = B.LayerConfig(N, 64, E, k, 64, dtype="bf16")
+    say(f"[dispatch] N={N} E={E} k={k} zipf={zipf}")
+    ids = W.random_ids(N, E, k, seed=3, zipf=zipf)
+    x = W.random_rows(N, 64, torch.bfloat16, seed=3)
+    gw = W.random_gates(N, k, seed=3)
+    out = B.moe_dispatch(cfg, x, ids, gw)
+    perm, inv, counts, offsets = O.dispatch(ids.cpu().numpy(), E)
+    assert np.array_equal(out["perm"].cpu().numpy(), perm)
+    assert np.array_equal(out["inv_perm"].cpu().numpy(), inv)
+    assert np.array_equal(out["counts"].cpu().numpy(), counts)
+    assert np.array_equal(out["offsets"].cpu().numpy(), offsets)
+    assert torch.equal(out["x_sorted"].cpu(), x.cpu()[torch.from_numpy(perm // k)])
+    assert np.array_equal(out["gate_sorted"].cpu().numpy(), gw.cpu().numpy().reshape(-1)[perm])
+    assert B.moe_get_device_error(out["ws"]) == B.MOE_OK
+
+
+def test_dispatch_flags_bad_ids():
+    N, E, k = 300, 8, 2
+    cfg = B.LayerConfig(N, 64, E, k, 64)
+    ids = W.random_ids(N, E, k, seed=4)
+    ids[17, 1] = E        # out of range: dropped and flagged
+    ids[200, 0] = -3
+    out = B.moe_dispatch(cfg, None, ids, want_x_sorted=False)
+    assert B.moe_get_device_error(out["ws"]) == B.MOE_ERR_BAD_EXPERT_ID
+    inv = out["inv_perm"].cpu().numpy()
+    assert inv[17 * k + 1] == -1 and inv[200 * k] == -1
+    assert int(out["offsets"][-1]) == N * k - 2
+    assert B.moe_get_device_error(out["ws"]) == B.MOE_OK  # cleared by the read
+
+
+@pytest.mark.parametrize("dtype,act,bias,rows,E,d,f,empty", [
+    ("bf16", "swiglu", False, 600, 5, 200, 264, 1),
+    ("bf16", "gelu", True, 1000, 6, 256, 392, 2),
+    ("bf16", "gelu", False, 389, 3, 72, 136, 0),
+    ("bf16", "swiglu", False, 1300, 16, 128, 96, 9),
+    ("f32", "gelu", True, 500, 4, 64, 256, 1),
+    ("f32", "swiglu", False, 333, 7, 40, 72, 3),
+])
+def test_expert_ffn(dtype, act, bias, rows, E, d, f, empty):
+    """Ragged slices (empty experts, tails shorter than a tile, widths off the tile grid)."""
+    say(f"[ffn] {dtype} {act} bias={bias} rows={rows} E={E} d={d} f={f} empty={empty}")
+    k = 1
+    cfg = B.LayerConfig(rows, d, E, k, f, act=act, has_bias=bias, dtype=dtype)
+    wl = W.Workload("ffn", cfg, weight_std=0.1)
+    inp = W.make_inputs(wl, seed=5)
+    counts = W.random_counts(rows, E, seed=5, empty=empty)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=5)
+    gate = W.random_gates(rows, 1, seed=5).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    xs64, g64 = f64(xs), f64(gate)
+    p = oracle_params(inp)
+    ref = np.zeros((rows, d))
+    off = offsets.cpu().numpy()
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            ex = {n: (None if p[n] is None else p[n][e]) for n in ("w1", "w2", "w3", "b1", "b2")}
+            ref[lo:hi] = O.expert_ffn(xs64[lo:hi], act, **ex) * g64[lo:hi, None]
+    err, scale = assert_close_rel(f64(ys), ref, TOL[dtype], "y_sorted")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
+@pytest.mark.parametrize("dtype,N,k,d", [("bf16", 1000, 2, 256), ("bf16", 77, 8, 7168), ("f32", 300, 3, 64)])
+def test_combine(dtype, N, k, d):
+    cfg = B.LayerConfig(N, d, max(k, 8), k, 64, dtype=dtype)
+    T = cfg.torch_dtype
+    ys = W.random_rows(N * k, d, T, seed=6)
+    gw = W.random_gates(N, k, seed=6)
+    inv = W.random_perm(N * k, seed=6)
+    y = B.moe_combine(cfg, ys, gw, inv)
+    ref = O.combine(f64(ys), f64(gw), inv.cpu().numpy())
+    assert_close_rel(f64(y), ref, 1e-6 if dtype == "f32" else 8e-3, "combine")
+    y1 = B.moe_combine(cfg, ys, None, inv)   # gates already applied upstream
+    ref1 = O.combine(f64(ys), np.ones((N, k)), inv.cpu().numpy())
+    assert_close_rel(f64(y1), ref1, 1e-6 if dtype == "f32" else 8e-3, "combine without gates")
+
+
+# ---------------------------------------------------------------------------------------
+# Routing parity (all three routers, with and without renormalisation, scaling, offsets)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("router,norm,scale,E,k,dtype", [
+    ("softmax_topk", True, 1.0, 8, 2, "bf16"), ("softmax_topk", False, 1.0, 6, 2, "bf16"),
+    ("topk_softmax", True, 1.0, 16, 4, "bf16"), ("sigmoid", True, 2.5, 256, 8, "bf16"),
+    ("sigmoid", False, 1.0, 64, 6, "f32"), ("softmax_topk", True, 1.0, 128, 8, "bf16"),
+    ("softmax_topk", True, 1.0, 1000, 32, "bf16"), ("topk_softmax", True, 1.0, 5, 5, "f32"),
+])
+def test_route(router, norm, scale, E, k, dtype):
+    N, d = 1500, 384
+    cfg = B.LayerConfig(N, d, E, k, 64, router=router, norm_topk=norm, routed_scaling=scale, dtype=dtype)
+    wl = W.Workload("route", cfg, logit_offset="zipf1.2" if E == 128 else None,
+                    sel_bias="uniform0.1" if router == "sigmoid" else None)
+    say(f"[route] {cfg}")
+    inp = W.make_inputs(wl, seed=7)
+    out = B.moe_route(cfg, inp["x"], inp["w_router"], inp["logit_bias"], inp["sel_bias"], want_logits=True, want_gap=True)
+    r = O.route(f64(inp["x"]), f64(inp["w_router"]), spec_of(cfg), f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    np.testing.assert_allclose(out["logits"].cpu().numpy(), r.z, rtol=1e-5, atol=2e-6)
+    near, intra, agree = compare_ids(out["topk_ids"].cpu().numpy(), r, k)
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy()[agree], r.w[agree], rtol=1e-5, atol=1e-6)
+    gap = out["gap"].cpu().numpy()
+    fin = np.isfinite(r.gap)
+    np.testing.assert_allclose(gap[fin & agree], r.gap[fin & agree], atol=2e-5)
+    assert np.all(np.isinf(gap[~fin]))
+    f, P, L = O.load_balance(r.p, r.ids, E)
+    st = out["stats"].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(st[E:2 * E], P, rtol=1e-5, atol=1e-7)
+    if agree.all():
+        assert np.array_equal(out["counts"].cpu().numpy(), np.bincount(r.ids.reshape(-1), minlength=E))
+        np.testing.assert_allclose(st[2 * E], L, rtol=1e-5)
+    say(f"    near-ties {int(near.sum())} intra {int(intra.sum())}")
+
+
+# ---------------------------------------------------------------------------------------
+# The whole layer on every recipe at oracle-sized shapes, and edge cases
+# ---------------------------------------------------------------------------------------
+
+SMALL = {
+    "tiny_f32": {},  # full size: the oracle runs it in well under a second
+    "gpt2_small": dict(n_tokens=700, d_model=192, d_ff=392),
+    "mixtral": dict(n_tokens=640, d_model=256, d_ff=456),
+    "fine_grained": dict(n_tokens=900, d_model=128, d_ff=96),
+    "deepseek_v3": dict(n_tokens=300, d_model=256, d_ff=128),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    run_forward_and_check(W.WORKLOADS[name].scaled(**SMALL[name]))
+
+
+@pytest.mark.parametrize("case", ["n1", "k_eq_e", "e1", "k1", "identical_tokens", "skip_experts", "no_norm_scaled"])
+def test_forward_edge_cases(case):
+    base = W.WORKLOADS["mixtral"].scaled(n_tokens=260, d_model=128, d_ff=200)
+    if case == "n1":
+        w = base.scaled(n_tokens=1)
+    elif case == "k_eq_e":
+        w = base.scaled(n_experts=4, top_k=4)
+    elif case == "e1":
+        w = base.scaled(n_experts=1, top_k=1)
+    elif case == "k1":
+        w = dataclasses.replace(W.WORKLOADS["gpt2_small"].scaled(n_tokens=300, d_model=64, d_ff=128, top_k=1))
+    elif case == "no_norm_scaled":
+        w = base.scaled(router="sigmoid", norm_topk=False, routed_scaling=2.5, n_experts=16, top_k=4)
+    else:
+        w = base
+    if case == "identical_tokens":
+        cfg = w.cfg
+        inp = W.make_inputs(w, seed=0)
+        inp["x"][:] = inp["x"][0]
+        out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"])
+        ids = out["topk_ids"].cpu().numpy()
+        assert (ids == ids[0]).all()
+        counts = out["counts"].cpu().numpy()
+        assert sorted(counts.tolist())[-cfg.top_k:] == [cfg.n_tokens] * cfg.top_k
+        y = f64(out["y"])
+        y_ref, _ = O.forward_loop(f64(inp["x"][:1]), oracle_params(inp), spec_of(cfg))
+        assert_close_rel(y, np.repeat(y_ref, cfg.n_tokens, axis=0), TOL["bf16"], "collapsed y")
+        return
+    if case == "skip_experts":
+        # a large negative logit offset keeps experts 1 and 5 idle: their weights are never read
+        cfg = w.cfg
+        inp = W.make_inputs(w, seed=1)
+        lb = torch.zeros(cfg.n_experts, dtype=torch.float32, device="cuda")
+        lb[1] = lb[5] = -1e4
+        inp["w1"][1].fill_(float("nan"))
+        inp["w2"][5].fill_(float("nan"))
+        out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], logit_bias=lb)
+        counts = out["counts"].cpu().numpy()
+        assert counts[1] == 0 and counts[5] == 0
+        assert torch.isfinite(out["y"].float()).all(), "an idle expert's weights were read"
+        return
+    run_forward_and_check(w)
+
+
+def test_forward_empty_input():
+    cfg = W.WORKLOADS["mixtral"].scaled(n_tokens=0, d_model=64, d_ff=64).cfg
+    inp = W.make_inputs(W.Workload("empty", cfg))
+    out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"])
+    torch.cuda.synchronize()
+    assert out["counts"].cpu().tolist() == [0] * cfg.n_experts
+    assert not out["stats"].cpu().any()
+
+
+def test_forward_is_deterministic():
+    w = W.WORKLOADS["fine_grained"].scaled(n_tokens=2000, d_model=256, d_ff=128)
+    inp = W.make_inputs(w)
+    args = (w.cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], None, None, inp["logit_bias"])
+    a = B.moe_forward(*args)
+    for _ in range(5):
+        b = B.moe_forward(*args)
+        for key in a:
+            assert torch.equal(a[key], b[key]), f"{key} differs between identical runs"
