@@ -1,0 +1,211 @@
+"""MoE layer forward benchmark on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
+
+A step is one whole layer forward (moe_forward: route, dispatch, expert up and down
+projections, combine, statistics) over one batch of synthetic tokens already resident in
+HBM. Prints ONE JSON line: tokens/s plus the roofline of the dominant kernel (the fused
+gate/up expert projection) timed with HIP events that the library records on its own stream,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector / matrix)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+STAGES = ("route", "dispatch", "expert_up", "expert_down", "combine")
+
+
+def algorithmic(cfg):
+    """Algorithmic work per layer call (what the method itself must compute / move)."""
+    N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
+    A = N * k
+    b = 2 if cfg.dtype == "bf16" else 4
+    m_up = 2 if cfg.act == "swiglu" else 1
+    return {
+        "router_flops": 2 * N * d * E,
+        "up_flops": 2 * A * d * f * m_up,
+        "down_flops": 2 * A * f * d,
+        # dispatch: read x once, write x_sorted, ids in / perm / inv_perm (int32)
+        "dispatch_bytes": N * d * b + A * d * b + 3 * A * 4,
+        # combine (gates already applied upstream): read y_sorted and inv_perm, write y
+        "combine_bytes": A * d * b + A * 4 + N * d * b,
+    }
+
+
+def file_sha(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_src, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha") != file_sha(kernel_src):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, n_sample=0, target_s=15.0):
+    """The float64 CPU oracle, as it stands, on the first n_sample tokens of the workload
+    (n_sample = 0: sized from an 8-token probe to take about target_s seconds)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    f64 = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+    cfg = w.cfg
+    params = {"w_g": f64(inp["w_router"])}
+    for name in ("w1", "w3", "w2", "b1", "b2"):
+        params[name] = None if inp[name] is None else [f64(inp[name][e]) for e in range(cfg.n_experts)]
+    spec = O.Spec(n_experts=cfg.n_experts, top_k=cfg.top_k, router=cfg.router, norm_topk=cfg.norm_topk,
+                  routed_scaling=cfg.routed_scaling, act=cfg.act)
+    lb, sb = f64(inp["logit_bias"]), f64(inp["sel_bias"])
+    if not n_sample:
+        t0 = time.perf_counter()
+        O.forward_loop(f64(inp["x"][:8]), params, spec, lb, sb)
+        per_tok = (time.perf_counter() - t0) / 8
+        n_sample = int(min(cfg.n_tokens, max(8, target_s / max(per_tok, 1e-9))))
+    x = f64(inp["x"][:n_sample])
+    t0 = time.perf_counter()
+    O.forward_loop(x, params, spec, lb, sb)
+    dt = time.perf_counter() - t0
+    return {"value": n_sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"per-token float64 oracle (routing, {cfg.top_k} expert FFNs per token, combine) on the "
+                       f"first {n_sample} of {cfg.n_tokens} tokens; {dt:.1f} s; weights widened to float64 "
+                       f"before the timed region")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer has no multi-GPU "
+              f"path in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_19_amd import binding as B
+    from mixture_experts_layer_19_amd import workload as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "elementwise copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
+        return
+    w = W.WORKLOADS[args.workload]
+    cfg = w.cfg
+    inp = W.make_inputs(w, seed=0, device="cuda")
+    ws = B.workspace(cfg, B.Op.FORWARD)
+    dev = inp["x"].device
+    out = {
+        "y": torch.empty((cfg.n_tokens, cfg.d_model), dtype=cfg.torch_dtype, device=dev),
+        "topk_ids": torch.empty((cfg.n_tokens, cfg.top_k), dtype=torch.int32, device=dev),
+        "topk_w": torch.empty((cfg.n_tokens, cfg.top_k), dtype=torch.float32, device=dev),
+        "counts": torch.empty((cfg.n_experts,), dtype=torch.int32, device=dev),
+        "stats": torch.empty((2 * cfg.n_experts + 2,), dtype=torch.float32, device=dev),
+    }
+    call = lambda ev=None: B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"],
+                                         inp["b1"], inp["b2"], inp["logit_bias"], inp["sel_bias"],
+                                         ws=ws, out=out, stage_events=ev)
+    for _ in range(args.warmup):
+        call()
+    events = [B.HipEvents(6) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(events[i].handles)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    for ev in events:
+        for j, s in enumerate(STAGES):
+            stage_ms[s] += ev.elapsed_ms(j, j + 1) / args.steps
+    fwd_ms_events = sum(stage_ms.values())
+    ms_per_step = wall * 1e3 / args.steps
+    work = algorithmic(cfg)
+    flops = work["router_flops"] + work["up_flops"] + work["down_flops"]
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    up_tflops = work["up_flops"] / (stage_ms["expert_up"] * 1e-3) / 1e12
+    stats = out["stats"].cpu().numpy()
+    E = cfg.n_experts
+    counts = out["counts"].cpu().numpy()
+
+    src = os.path.join(ROOT, "mixture_experts_layer_19_amd", "csrc", "expert_ffn.hip")
+    res = {
+        "metric": "MoE layer fwd tokens/s + active TFLOP/s (% bf16 MFMA peak), 8\u00d7top-2 SwiGLU",
+        "value": cfg.n_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={cfg.n_tokens} d={cfg.d_model} E={E} k={cfg.top_k} "
+                               f"d_ff={cfg.d_ff} {cfg.act} {cfg.router}{'+norm' if cfg.norm_topk else ''} {cfg.dtype}",
+                   "global_batch": cfg.n_tokens, "parallelism": "single GPU"},
+        "active_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "active_frac_of_peak": flops / (ms_per_step * 1e-3) / 1e12 / peak,
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "stage_rates": {
+            "expert_up_tflops": up_tflops,
+            "expert_down_tflops": work["down_flops"] / (stage_ms["expert_down"] * 1e-3) / 1e12,
+            "dispatch_gbs": work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9,
+            "combine_gbs": work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9,
+        },
+        "roofline": {
+            "kernel": "expert_gemm_bf16_kernel<SwiGLU up>" if cfg.act == "swiglu" else "expert_gemm up",
+            "bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
+            "frac": up_tflops / peak, "traffic": traffic_for(src, w.name),
+            "flops_per_launch": work["up_flops"], "avg_launch_ms": stage_ms["expert_up"],
+        },
+        "switch_loss": float(stats[2 * E]),
+        "z_loss": float(stats[2 * E + 1]),
+        "expert_rows": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
+        "events_vs_wall": fwd_ms_events / ms_per_step,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

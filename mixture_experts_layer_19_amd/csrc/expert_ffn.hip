@@ -329,12 +329,18 @@ void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   }
 }
 
+hipError_t launch_ffn_tiles(const moe_config& c, const WsLayout& L, const int32_t* offsets, hipStream_t stream) {
+  const int A = (int)(c.n_tokens * c.top_k);
+  if (A == 0) return hipGetLastError();
+  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, tile_rows(c), max_m_tiles(c), L.tiles, L.err);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_sorted,
                          const int32_t* offsets, const void* w1, const void* w3, const void* b1,
                          hipStream_t stream) {
   const int A = (int)(c.n_tokens * c.top_k);
   if (A == 0) return hipGetLastError();
-  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, tile_rows(c), max_m_tiles(c), L.tiles, L.err);
   GemmArgs g{};
   g.a = x_sorted;
   g.b0 = w1;

@@ -183,6 +183,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int
   WsLayout L{};
   MOE_TRY(check_ws(*cfg, MOE_OP_EXPERT_FFN, ws, ws_bytes, &L));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(hip_status(launch_ffn_tiles(*cfg, L, offsets, s)));
   MOE_TRY(hip_status(launch_ffn_up(*cfg, L, x_sorted, offsets, w1, w3, b1, s)));
   return hip_status(launch_ffn_down(*cfg, L, offsets, w2, b2, gate_sorted, y_sorted, s));
 }
@@ -239,6 +240,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   MOE_TRY(mark(1));
   MOE_TRY(hip_status(launch_dispatch(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
                                      L.counts_tmp, L.offsets, L.gate_sorted, s)));
+  MOE_TRY(hip_status(launch_ffn_tiles(*cfg, L, L.offsets, s)));
   MOE_TRY(mark(2));
   MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s)));
   MOE_TRY(mark(3));

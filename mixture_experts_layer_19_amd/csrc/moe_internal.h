@@ -96,6 +96,8 @@ hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x
                            const int32_t* topk_ids, const float* topk_w, void* x_sorted,
                            int32_t* perm, int32_t* inv_perm, int32_t* counts, int32_t* offsets,
                            float* gate_sorted, hipStream_t stream);
+// Builds the per-call m-tile list from offsets (must precede the up and down launches).
+hipError_t launch_ffn_tiles(const moe_config& c, const WsLayout& L, const int32_t* offsets, hipStream_t stream);
 hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_sorted,
                          const int32_t* offsets, const void* w1, const void* w3, const void* b1,
                          hipStream_t stream);

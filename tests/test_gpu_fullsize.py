@@ -1,0 +1,95 @@
+"""Full-size parity on every workload, in the launch configuration bench.py times
+(moe_forward with one preallocated workspace). Routing, statistics and dispatch are checked
+on all N tokens; the output on a seeded sample that contains the first and the last row of
+every non-empty expert's slice (tile edges) plus random tokens, which the oracle computes
+one by one."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (TOL, assert_close_rel, check_dispatch_valid, compare_ids, f64, oracle_params,
+                         spec_of)
+from mixture_experts_layer_19_amd import binding as B
+from mixture_experts_layer_19_amd import workload as W
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = {"tiny_f32": 256, "gpt2_small": 256, "mixtral": 192, "fine_grained": 256, "deepseek_v3": 48}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_fullsize(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = W.WORKLOADS[name]
+    cfg = w.cfg
+    say(f"[fullsize] {name} {cfg}")
+    inp = W.make_inputs(w, seed=0)
+    ws = B.workspace(cfg, B.Op.FORWARD)
+    out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
+                        inp["logit_bias"], inp["sel_bias"], ws=ws)
+    torch.cuda.synchronize()
+    E, k, N = cfg.n_experts, cfg.top_k, cfg.n_tokens
+
+    # routing of every token
+    spec = spec_of(cfg)
+    x64 = f64(inp["x"])
+    r = O.route(x64, f64(inp["w_router"]), spec, f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    ids = out["topk_ids"].cpu().numpy()
+    near, intra, agree = compare_ids(ids, r, k)
+    say(f"    near-ties {int(near.sum())}, intra-top-k near-ties {int(intra.sum())}, "
+        f"tokens routed differently {int((~agree).sum())}")
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy()[agree], r.w[agree], rtol=1e-5, atol=1e-6)
+
+    # statistics
+    counts = out["counts"].cpu().numpy()
+    assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=E))
+    f, P, L = O.load_balance(r.p, r.ids, E)
+    st = out["stats"].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(st[E:2 * E], P, rtol=1e-5, atol=1e-8)
+    np.testing.assert_allclose(st[2 * E + 1], O.z_loss(r.z), rtol=1e-5)
+    if agree.all():
+        assert np.array_equal(counts, np.bincount(r.ids.reshape(-1), minlength=E))
+        np.testing.assert_allclose(st[:E], f, rtol=1e-6)
+        np.testing.assert_allclose(st[2 * E], L, rtol=1e-5)
+    say(f"    Switch L = {st[2 * E]:.6f} (oracle {L:.6f}), rows per expert min {counts.min()} max {counts.max()} "
+        f"empty {(counts == 0).sum()}")
+
+    # dispatch of the device's ids by the same kernels
+    d = B.moe_dispatch(cfg, inp["x"], out["topk_ids"], out["topk_w"])
+    perm, inv = d["perm"].cpu().numpy(), d["inv_perm"].cpu().numpy()
+    dc, doff = d["counts"].cpu().numpy(), d["offsets"].cpu().numpy()
+    if agree.all():
+        operm, oinv, ocounts, ooff = O.dispatch(r.ids, E)
+        assert np.array_equal(perm, operm) and np.array_equal(inv, oinv)
+        assert np.array_equal(dc, ocounts) and np.array_equal(doff, ooff)
+    else:
+        check_dispatch_valid(ids, perm, inv, dc, doff, E)
+    rows = np.random.default_rng(1).choice(N * k, size=min(64, N * k), replace=False)
+    assert torch.equal(d["x_sorted"][torch.from_numpy(rows).cuda()].cpu(),
+                       inp["x"].cpu()[torch.from_numpy(perm[rows] // k)])
+
+    # output on a stratified sample of tokens
+    rng = np.random.default_rng(2)
+    operm, _, _, ooff = O.dispatch(r.ids, E)
+    edge = set()
+    for e in range(E):
+        if ooff[e + 1] > ooff[e]:
+            edge.add(int(operm[ooff[e]] // k))
+            edge.add(int(operm[ooff[e + 1] - 1] // k))
+    n_extra = max(0, SAMPLE[name] - len(edge))
+    sample = np.array(sorted(edge | set(rng.choice(N, size=min(N, n_extra), replace=False).tolist())))
+    sample = sample[agree[sample]]
+    params = oracle_params(inp, lazy=True)
+    y_ref = O.expert_output_sorted(x64[sample], r.ids[sample], r.w[sample], params, spec)
+    y = f64(out["y"][torch.from_numpy(sample).cuda()])
+    err, scale = assert_close_rel(y, y_ref, TOL[cfg.dtype], f"y ({name})")
+    say(f"    output sample {sample.size} tokens: max|err| {err:.3e}, max|y| {scale:.3e}, "
+        f"ratio {err / scale:.2e} (bound {TOL[cfg.dtype]:.0e})")
