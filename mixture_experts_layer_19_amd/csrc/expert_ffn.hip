@@ -17,10 +17,14 @@ namespace moe {
 enum Epi { kEpiGelu = 0, kEpiSwiglu = 1, kEpiDown = 2 };
 
 // ---------------------------------------------------------------------------------------
-// Tile table: tiles[0] = number of m-tiles; tile t is tiles[4 + 4t ..] = (expert, first
-// row, rows in the tile). Offsets outside [0, rows] or decreasing are clamped, the list is
+// Tile table. tiles[0] = number of m-tiles, tiles[4..7] = 16 zero bytes (the source of
+// every load past the end of the reduction axis), and m-tile t is described by
+// tiles[8 + 8t ..] = (expert, first row, rows in the tile, the expert's first m-tile, the
+// expert's m-tile count). Offsets outside [0, rows] or decreasing are clamped, the list is
 // capped at max_tiles (so no access leaves the buffers) and the error word is set.
 // ---------------------------------------------------------------------------------------
+constexpr int kTileHdr = 8, kTileInts = 8;
+
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict__ offsets, int E, int rows,
                                                           int bm, int max_tiles, int* __restrict__ tiles,
                                                           int* __restrict__ err) {
@@ -28,6 +32,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict_
   __shared__ int s_bad;
   const int e = threadIdx.x;
   if (e == 0) s_bad = 0;
+  if (e < 4) tiles[4 + e] = 0;
   __syncthreads();
   int lo = 0, hi = 0, n = 0;
   if (e < E) {
@@ -51,10 +56,12 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict_
     const int start = s_scan[e] - n;
     for (int t = 0; t < n && start + t < max_tiles; ++t) {
       const int r0 = lo + t * bm;
-      int* q = tiles + 4 + 4 * (start + t);
+      int* q = tiles + kTileHdr + kTileInts * (start + t);
       q[0] = e;
       q[1] = r0;
       q[2] = min(bm, hi - r0);
+      q[3] = start;
+      q[4] = min(n, max_tiles - start);
     }
     if (e == E - 1) {
       if (s_scan[e] > max_tiles) s_bad = 1;
@@ -73,153 +80,258 @@ struct GemmArgs {
   const float* gate;    // [rows] or null (down only)
   void* c;              // [rows][N_out] T: h (up) or y_sorted (down)
   const int* tiles;     // tile table
-  int K, n_out;
+  int K, n_out;         // reduction length; output columns (= rows of each B matrix)
+  int n_tiles_n;        // output column tiles
 };
 
 // ---------------------------------------------------------------------------------------
 // bfloat16 grouped GEMM on MFMA (v_mfma_f32_16x16x32_bf16), float32 accumulation.
-// Workgroup tile: 128 rows x 128 B-rows (GELU / down: 128 output columns; SwiGLU: 64 gate
-// rows and the 64 matching up rows -> 64 output columns), K staged 64 at a time in LDS with
-// rows padded to 72 elements so that 16-byte reads of 8 consecutive rows hit distinct banks.
-// 4 waves in a 2 x 2 grid; each wave owns 64 rows x 64 B-rows = 4 x 4 MFMA blocks.
+//
+// Workgroup tile: 256 rows x 256 B-rows, 4 waves in a 2 x 2 grid, each wave 128 x 128 B-rows
+// (8 x 8 blocks of 16 x 16). GELU / down: 256 output columns per tile. SwiGLU: each wave's
+// 128 B-rows are 64 gate rows then the 64 up rows of the same columns, so the gate and the
+// up value of an output land in the same lane and the activation is applied in registers
+// (128 output columns per tile).
+//
+// K is staged 64 at a time through two LDS stages (A 32 KiB + B 32 KiB each) written by
+// global_load_lds_dwordx4 (memory straight to LDS, no VGPR staging); 16-byte chunks of a
+// 128-byte row are XOR-swizzled by (row mod 8) so the 16-byte MFMA operand reads of 8
+// consecutive rows hit distinct banks. The next stage's loads are in flight while the
+// current stage is multiplied.
+//
+// Scheduling: a persistent grid of one workgroup per CU. The tile sequence is split into 8
+// contiguous chunks, one per XCD (workgroup i runs on XCD i mod 8), so tiles that share
+// operands share an L2. Within an expert, tiles are ordered in supertiles of 8 m-tiles x 4
+// n-tiles (m fastest), so the ~32 tiles an XCD runs at once reuse 8 A and 4 B slices.
+// Rows past an expert's slice and columns past N are clamped to a valid row (their results
+// are never stored); reduction chunks past K read the table's zero bytes.
 // ---------------------------------------------------------------------------------------
-constexpr int kBM = 128, kBNB = 128, kBK = 64, kLdsRow = kBK + 8;
+constexpr int kBM = 256, kBNB = 256, kBK = 64;
+constexpr int kGM = 8, kGN = 4;
+constexpr int kStageElems = kBM * kBK;  // bf16 elements of one operand stage (32 KiB)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+MOE_DEV void lds_dma16(const void* src, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+MOE_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), others untouched
 
 template <int EPI>
-__global__ __launch_bounds__(256) void expert_gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kBNB * kLdsRow];
-
-  const int n_tiles_m = g.tiles[0];
-  const int mt = blockIdx.x;
-  if (mt >= n_tiles_m) return;
-  const int e = g.tiles[4 + 4 * mt];
-  const int row0 = g.tiles[5 + 4 * mt];
-  const int rows_valid = g.tiles[6 + 4 * mt];
-  const int K = g.K;
-  const int n_out = g.n_out;
-  constexpr int kColsPerTile = (EPI == kEpiSwiglu) ? 64 : 128;
-  const int n0 = blockIdx.y * kColsPerTile;
-  const int nb_rows = (EPI == kEpiSwiglu) ? n_out : n_out;  // rows of each B matrix
+__global__ __launch_bounds__(256, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sB1[kStageElems];
+  __shared__ float s_gate[kBM];  // this tile's per-row gates (down projection)
+  __shared__ float s_bias[kBNB]; // this tile's per-column biases
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
+  const int K = g.K, n_out = g.n_out, NT = g.n_tiles_n;
+  constexpr int kCols = (EPI == kEpiSwiglu) ? 128 : 256;  // output columns per tile
 
-  const uint16_t* A = static_cast<const uint16_t*>(g.a);
-  const uint16_t* B0 = static_cast<const uint16_t*>(g.b0) + (size_t)e * nb_rows * K;
-  const uint16_t* B1 = (EPI == kEpiSwiglu) ? static_cast<const uint16_t*>(g.b1) + (size_t)e * nb_rows * K : nullptr;
+  const int n_mt = g.tiles[0];
+  const long long S = (long long)n_mt * NT;
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int per_xcd = gridDim.x >> 3;
+  const long long chunk = (S + 7) / 8;
+  const long long s_begin = (long long)xcd * chunk;
+  const long long s_end = min(S, s_begin + chunk);
+  const int nk = (K + kBK - 1) / kBK;
+  const bool k_tail = (K % kBK) != 0;
 
-  // Per-thread global chunks: chunk c = tid + 256 q, row = c / 8, 16-byte column = c % 8.
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
-  bool a_ok[4], b_ok[4];
+  // Load geometry shared by every tile: instruction i of this wave fills the 8 LDS rows
+  // (8 * wave + i) * 8 .. +7; lane l writes row (l >> 3) of them, physical chunk l & 7,
+  // which holds the logical chunk (l & 7) ^ (row & 7).
+  const int lrow = lane >> 3;
+  const int lchunk = ((lane & 7) ^ (lrow & 7)) * 8;
+  // MFMA operand reads: row (lane & 31) of a 32-row block, logical chunk 2 ks + (lane >> 5),
+  // physical chunk = logical ^ (lane & 7); element offsets for ks = 0..3.
+  int rd32[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + 256 * q;
-    const int r = c >> 3, kc = (c & 7) * 8;
-    a_ok[q] = r < rows_valid;
-    a_src[q] = A + (size_t)(row0 + (a_ok[q] ? r : 0)) * K + kc;
-    int col;
-    const uint16_t* base;
-    if (EPI == kEpiSwiglu) {
-      const int wq = r >> 6, qq = r & 63;
-      col = n0 + wq * 32 + (qq & 31);
-      base = (qq >= 32) ? B1 : B0;
-    } else {
-      col = n0 + r;
-      base = B0;
-    }
-    b_ok[q] = col < nb_rows;
-    b_src[q] = base + (size_t)(b_ok[q] ? col : 0) * K + kc;
-  }
+  for (int ks = 0; ks < 4; ++ks) rd32[ks] = (lane & 31) * kBK + (((2 * ks + (lane >> 5)) ^ (lane & 7)) * 8);
+  const int a_rd = wm * 128 * kBK;
+  const int b_rd = wn * 128 * kBK;
 
-  uint4 ra[4], rb[4];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kc = ((tid + 256 * q) & 7) * 8;
-      const bool kin = (k0 + kc) < K;
-      ra[q] = (a_ok[q] && kin) ? *reinterpret_cast<const uint4*>(a_src[q] + k0) : make_uint4(0, 0, 0, 0);
-      rb[q] = (b_ok[q] && kin) ? *reinterpret_cast<const uint4*>(b_src[q] + k0) : make_uint4(0, 0, 0, 0);
-    }
-  };
+  for (long long s = s_begin + slot; s < s_end; s += per_xcd) {
+    // ---- tile decode: expert-major, then supertiles of kGM m-tiles x kGN n-tiles
+    const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
+    const int e = probe[0], ts = probe[3], me = probe[4];
+    const long long l = s - (long long)ts * NT;
+    const int band = (int)(l / ((long long)kGM * NT));
+    const int lb = (int)(l - (long long)band * kGM * NT);
+    const int bm = min(kGM, me - kGM * band);
+    const int grp = lb / (kGN * bm);
+    const int r = lb - grp * kGN * bm;
+    const int mt = ts + kGM * band + r % bm;
+    const int nt = grp * kGN + r / bm;
+    const int* tq = g.tiles + kTileHdr + kTileInts * mt;
+    const int row0 = tq[1], rows = tq[2];
+    const int n0 = nt * kCols;
 
-  f32x4 acc[4][4];
+    // uniform bases (bytes) and 32-bit per-lane offsets of the 8 A and 8 B load rows
+    const char* a_base = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
+    const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
+    const char* b1_base = (EPI == kEpiSwiglu) ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : nullptr;
+    uint32_t a_off[8], b_off[8];
+    bool b_up[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_tile(0);
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = tid + 256 * q;
-      const int r = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&sA[r * kLdsRow + kc]) = ra[q];
-      *reinterpret_cast<uint4*>(&sB[r * kLdsRow + kc]) = rb[q];
-    }
-    __syncthreads();
-    if (k0 + kBK < K) load_tile(k0 + kBK);
-#pragma unroll
-    for (int ks = 0; ks < kBK; ks += 32) {
-      const int kq = ks + (lane >> 4) * 8;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + (lane & 15);
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sA[r * kLdsRow + kq]));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + j * 16 + (lane & 15);
-        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sB[r * kLdsRow + kq]));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // Epilogue: lane holds rows (lane >> 4) * 4 + r and column lane & 15 of each 16 x 16 block.
-  uint16_t* C = static_cast<uint16_t*>(g.c);
-  const uint16_t* bias = g.bias ? static_cast<const uint16_t*>(g.bias) + (size_t)e * n_out : nullptr;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lr = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-      if (lr >= rows_valid) continue;
-      const int row = row0 + lr;
+    for (int i = 0; i < 8; ++i) {
+      const int rr = (wave * 8 + i) * 8 + lrow;  // tile row / B-row 0..255
+      a_off[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
+      int cl;  // B-row's column relative to n0
       if (EPI == kEpiSwiglu) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 32 + j * 16 + (lane & 15);
-          if (col < n_out) {
-            const float gv = acc[i][j][r], uv = acc[i][j + 2][r];
-            C[(size_t)row * n_out + col] = f32_to_bf16(silu_f(gv) * uv);
-          }
-        }
+        const int half = rr >> 7, qq = rr & 127;  // B-rows of wave column `half`
+        cl = half * 64 + (qq & 63);
+        b_up[i] = (((wave * 8 + i) * 8) & 127) >= 64;  // uniform: a load group never straddles 64
       } else {
-        const float gs = (EPI == kEpiDown && g.gate) ? g.gate[row] : 1.0f;
+        cl = rr;
+        b_up[i] = false;
+      }
+      b_off[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
+    }
+    // k0 beyond the last full slab: lanes past K read a valid chunk (clamped) and are zeroed
+    // in LDS after the copy lands.
+    auto issue = [&](uint16_t* sa, uint16_t* sb, int k0) {
+      int kb = k0;
+      if (k_tail && k0 + kBK > K) kb = k0;  // offsets clamp below
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-          if (col < n_out) {
-            float v = acc[i][j][r];
-            if (bias) v += bf16_to_f32(bias[col]);
-            if (EPI == kEpiGelu) v = gelu_erf(v);
-            else v *= gs;
-            C[(size_t)row * n_out + col] = f32_to_bf16(v);
+      for (int i = 0; i < 8; ++i) {
+        uint32_t ka = (uint32_t)kb * 2u;
+        if (k_tail && k0 + lchunk >= K) ka = (uint32_t)(K - 8 - lchunk) * 2u;  // stays inside the row
+        uint16_t* da = sa + (wave * 8 + i) * 8 * kBK;
+        uint16_t* db = sb + (wave * 8 + i) * 8 * kBK;
+        lds_dma16(a_base + a_off[i] + ka, da);
+        const char* bb = (EPI == kEpiSwiglu && b_up[i]) ? b1_base : b0_base;
+        lds_dma16(bb + b_off[i] + ka, db);
+      }
+    };
+    // zero this lane's chunks that lie past K (last slab only), once its copies have landed
+    auto zero_tail = [&](uint16_t* sa, uint16_t* sb, int k0) {
+      if (!k_tail || k0 + kBK <= K || k0 + lchunk < K) return;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int off = (wave * 8 + i) * 8 * kBK + lane * 8;
+        *reinterpret_cast<uint4*>(sa + off) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(sb + off) = make_uint4(0, 0, 0, 0);
+      }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // v_mfma_f32_32x32x16_bf16: lane l supplies row (l & 31) of A / column (l & 31) of B
+    // with the 8 reduction elements of logical chunk 2 ks + (l >> 5).
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+      // operands of reduction step ks + 1 are read while step ks multiplies
+      bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[0][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + a_rd + t * 32 * kBK + rd32[0]));
+        bfr[0][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + b_rd + t * 32 * kBK + rd32[0]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks < 3) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            af[nxt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + a_rd + t * 32 * kBK + rd32[ks + 1]));
+            bfr[nxt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + b_rd + t * 32 * kBK + rd32[ks + 1]));
           }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    issue(sA0, sB0, 0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      wait_vm0();
+      zero_tail(sA0, sB0, kt * kBK);
+      __syncthreads();
+      issue(sA1, sB1, (kt + 1) * kBK);
+      compute(sA0, sB0);
+      wait_vm0();
+      zero_tail(sA1, sB1, (kt + 1) * kBK);
+      __syncthreads();
+      if (kt + 2 < nk) issue(sA0, sB0, (kt + 2) * kBK);
+      compute(sA1, sB1);
+    }
+    if (kt < nk) {  // odd number of slabs: the last one is in stage 0
+      wait_vm0();
+      zero_tail(sA0, sB0, kt * kBK);
+      __syncthreads();
+      compute(sA0, sB0);
+    }
+    // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
+    // (1 and 0 when absent, so the epilogue has no branches)
+    s_gate[tid] = (EPI == kEpiDown && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
+    s_bias[tid] = (EPI != kEpiSwiglu && g.bias && n0 + tid < n_out)
+                      ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
+    __syncthreads();  // every wave is done reading the stages: reuse them for the epilogue
+
+    // ---- epilogue: activation / bias / gate in registers, the wave's bf16 tile staged in its
+    // own LDS region (rows padded by 16 bytes: the two half-waves, 4 rows apart, hit disjoint
+    // banks), then 16-byte coalesced row stores. 128-column waves go in two 64-row passes.
+    uint16_t* C = static_cast<uint16_t*>(g.c);
+    constexpr int kWCols = (EPI == kEpiSwiglu) ? 64 : 128;   // wave output columns
+    constexpr int kStride = kWCols + 8;                       // staged row length (elements)
+    constexpr int kPassRows = (EPI == kEpiSwiglu) ? 128 : 64; // rows staged per pass
+    constexpr int kWChunks = kWCols / 8;                      // 16-byte chunks per row
+    uint16_t* stage = (wave == 0) ? sA0 : (wave == 1) ? sB0 : (wave == 2) ? sA1 : sB1;
+    const int col_base = n0 + wn * kWCols;                    // first output column of the wave
+    // lane's element in a 32 x 32 block: column lane & 31, rows 8 g + 4 (lane >> 5) + r
+    uint16_t* st_lane = stage + ((lane >> 5) * 4) * kStride + (lane & 31);
+#pragma unroll
+    for (int pass = 0; pass < 128 / kPassRows; ++pass) {
+#pragma unroll
+      for (int ii = 0; ii < kPassRows / 32; ++ii) {
+        const int i = pass * (kPassRows / 32) + ii;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int prow = ii * 32 + (v >> 2) * 8 + (v & 3);            // pass row, minus 4 (lane >> 5)
+          const float gs = s_gate[wm * 128 + pass * kPassRows + prow + (lane >> 5) * 4];
+          if (EPI == kEpiSwiglu) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              st_lane[prow * kStride + j * 32] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float val = acc[i][j][v] + s_bias[wn * kWCols + j * 32 + (lane & 31)];
+              val = (EPI == kEpiGelu) ? gelu_erf(val) : val * gs;
+              st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep each 32-row group's registers short-lived
+      }
+      // each lane stores whole 16-byte chunks of the pass's rows
+#pragma unroll 4
+      for (int it = 0; it < kPassRows * kWChunks / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int prow = idx / kWChunks, ch = idx % kWChunks;
+        const int trow = wm * 128 + pass * kPassRows + prow;
+        const int col = col_base + ch * 8;
+        const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
+        if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(C + (size_t)(row0 + trow) * n_out + col) = val;
       }
     }
+    __syncthreads();  // the staging area is the next tile's first stage
   }
 }
 
@@ -238,9 +350,9 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(GemmArgs g) {
   const int n_tiles_m = g.tiles[0];
   const int mt = blockIdx.x;
   if (mt >= n_tiles_m) return;
-  const int e = g.tiles[4 + 4 * mt];
-  const int row0 = g.tiles[5 + 4 * mt];
-  const int rows_valid = g.tiles[6 + 4 * mt];
+  const int e = g.tiles[kTileHdr + kTileInts * mt];
+  const int row0 = g.tiles[kTileHdr + kTileInts * mt + 1];
+  const int rows_valid = g.tiles[kTileHdr + kTileInts * mt + 2];
   const int K = g.K, n_out = g.n_out;
   const int n0 = blockIdx.y * kFBN;
   const int tid = threadIdx.x;
@@ -313,6 +425,19 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------
 static int tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM; }
 
+// One persistent workgroup per CU (a multiple of 8, so every XCD gets the same count).
+static int persistent_grid() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = (n + 7) / 8 * 8;
+  }
+  return cus[dev];
+}
+
 static int max_m_tiles(const moe_config& c) {
   const long long A = c.n_tokens * c.top_k;
   const int bm = tile_rows(c);
@@ -321,7 +446,7 @@ static int max_m_tiles(const moe_config& c) {
 
 void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   const size_t A = (size_t)(c.n_tokens * c.top_k);
-  int* tiles = w.take_t<int>(4 + 4 * (size_t)max_m_tiles(c));
+  int* tiles = w.take_t<int>(kTileHdr + kTileInts * (size_t)max_m_tiles(c));
   void* h = w.take(A * (size_t)c.d_ff * elem_size(c));
   if (L) {
     L->tiles = tiles;
@@ -352,13 +477,10 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
   g.n_out = c.d_ff;
   const int mt = max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
-    if (c.act == MOE_ACT_SWIGLU) {
-      dim3 grid(mt, (c.d_ff + 63) / 64);
-      expert_gemm_bf16_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
-    } else {
-      dim3 grid(mt, (c.d_ff + 127) / 128);
-      expert_gemm_bf16_kernel<kEpiGelu><<<grid, 256, 0, stream>>>(g);
-    }
+    g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
+    const int grid = persistent_grid();
+    if (c.act == MOE_ACT_SWIGLU) expert_gemm_bf16_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
+    else expert_gemm_bf16_kernel<kEpiGelu><<<grid, 256, 0, stream>>>(g);
   } else {
     dim3 grid(mt, (c.d_ff + kFBN - 1) / kFBN);
     if (c.act == MOE_ACT_SWIGLU) expert_gemm_f32_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
@@ -383,8 +505,8 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
   g.n_out = c.d_model;
   const int mt = max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
-    dim3 grid(mt, (c.d_model + 127) / 128);
-    expert_gemm_bf16_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);
+    g.n_tiles_n = (c.d_model + 255) / 256;
+    expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), 256, 0, stream>>>(g);
   } else {
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);

@@ -21,13 +21,8 @@ struct bf16_t {
 
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays a (quiet) NaN.
-MOE_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// float32 -> bfloat16, round to nearest, ties to even (gfx950's v_cvt_pk_bf16_f32).
+MOE_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Element-type traits: load/store one element as float.
 template <typename T> struct Elem;
@@ -63,8 +58,13 @@ MOE_DEV uint4 pack16(const float* in, float) {
   return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
                     __float_as_uint(in[3]));
 }
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 MOE_DEV uint4 pack16(const float* in, bf16_t) {
-  auto p2 = [](float lo, float hi) { return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16); };
+  auto p2 = [](float lo, float hi) { return pack_bf16x2(lo, hi); };
   return make_uint4(p2(in[0], in[1]), p2(in[2], in[3]), p2(in[4], in[5]), p2(in[6], in[7]));
 }
 
