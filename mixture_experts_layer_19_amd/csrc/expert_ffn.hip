@@ -85,51 +85,84 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------------------------------
-// bfloat16 grouped GEMM on MFMA (v_mfma_f32_16x16x32_bf16), float32 accumulation.
+// bfloat16 grouped GEMM on MFMA (v_mfma_f32_32x32x16_bf16), float32 accumulation.
 //
-// Workgroup tile: 256 rows x 256 B-rows, 4 waves in a 2 x 2 grid, each wave 128 x 128 B-rows
-// (8 x 8 blocks of 16 x 16). GELU / down: 256 output columns per tile. SwiGLU: each wave's
-// 128 B-rows are 64 gate rows then the 64 up rows of the same columns, so the gate and the
-// up value of an output land in the same lane and the activation is applied in registers
-// (128 output columns per tile).
+// Workgroup tile: 256 rows x 256 B-rows, 8 waves = 2 per SIMD, each wave 128 rows x 64
+// B-rows (4 x 2 blocks of 32 x 32, 128 accumulators per lane). GELU / down: 256 output
+// columns per tile. SwiGLU: each wave's 64 B-rows are 32 gate rows then the 32 up rows of
+// the same columns, so the gate and up value of an output land in the same lane and the
+// activation is applied in registers (128 output columns per tile).
 //
-// K is staged 64 at a time through two LDS stages (A 32 KiB + B 32 KiB each) written by
-// global_load_lds_dwordx4 (memory straight to LDS, no VGPR staging); 16-byte chunks of a
-// 128-byte row are XOR-swizzled by (row mod 8) so the 16-byte MFMA operand reads of 8
-// consecutive rows hit distinct banks. The next stage's loads are in flight while the
-// current stage is multiplied.
+// Operands stream through four LDS stages of 32 reduction elements (A 16 KiB + B 16 KiB)
+// written by global_load_lds_dwordx4 (memory straight to LDS, no VGPR staging), three
+// stages ahead. The four 16-byte chunks of a 64-byte LDS row are XOR-swizzled by
+// (row >> 2) mod 4, so the 16 rows one 256-byte LDS cycle of a 16-byte operand read serves
+// (rows r .. r+15 at one logical chunk) fall in 16 distinct bank slots.
+//
+// Ping-pong: the waves form two groups offset by half a step. In every phase one group's
+// wave on a SIMD issues its 16 multiplies back to back while the other group's wave reads
+// the next slab's operands from LDS and refills a free stage, then a barrier swaps the
+// roles; so the MFMA pipe is fed by one wave while the other's memory latency is hidden.
+//   phase 2k:   group 0 multiplies slab k      group 1 reads slab k, loads slab k+3
+//   phase 2k+1: group 0 reads slab k+1, loads slab k+4      group 1 multiplies slab k
+// Each wave issues 4 of the 32 copies of a slab per refill and keeps two refills in
+// flight, so at every phase boundary `vmcnt(8)` guarantees that the next slab to be read
+// has landed for every wave. Refills past the last slab copy the last slab again into a
+// stage that is never read, which keeps that count exact.
 //
 // Scheduling: a persistent grid of one workgroup per CU. The tile sequence is split into 8
 // contiguous chunks, one per XCD (workgroup i runs on XCD i mod 8), so tiles that share
 // operands share an L2. Within an expert, tiles are ordered in supertiles of 8 m-tiles x 4
 // n-tiles (m fastest), so the ~32 tiles an XCD runs at once reuse 8 A and 4 B slices.
 // Rows past an expert's slice and columns past N are clamped to a valid row (their results
-// are never stored); reduction chunks past K read the table's zero bytes.
+// are never stored); reduction chunks past K are loaded from inside the row and zeroed in
+// LDS once they have landed.
 // ---------------------------------------------------------------------------------------
-constexpr int kBM = 256, kBNB = 256, kBK = 64;
+constexpr int kBM = 256, kBNB = 256, kBK = 32;
 constexpr int kGM = 8, kGN = 4;
-constexpr int kStageElems = kBM * kBK;  // bf16 elements of one operand stage (32 KiB)
+constexpr int kStageElems = kBM * kBK;  // bf16 elements of one operand stage (16 KiB)
+constexpr int kGemmThreads = 512;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; M0 holds the wave-uniform LDS base). Written as asm so the
+// compiler's wait insertion, which cannot tell the four stage buffers apart once more than a
+// few copies are in flight, does not stall every LDS read on every copy: the kernel waits
+// for each stage explicitly. The instruction has no register outputs.
 MOE_DEV void lds_dma16(const void* src, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
-MOE_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), others untouched
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's loads older than its last N have landed in LDS
+// and its own LDS accesses are done.
+template <int N> MOE_DEV void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+// Workgroup barrier without a memory fence: __syncthreads() would also wait for every load
+// in flight (the stages still being prefetched). The waits each phase needs are explicit;
+// the clobber keeps the compiler from moving memory accesses across it.
+MOE_DEV void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t sB0[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t sA1[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t sB1[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sA3[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sB3[kStageElems];
   __shared__ float s_gate[kBM];  // this tile's per-row gates (down projection)
   __shared__ float s_bias[kBNB]; // this tile's per-column biases
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const int grp = wave >> 2;                                  // ping-pong group
+  const int wm = wave & 1;                                    // 128-row half of the tile
+  const int wc = grp * 2 + ((wave >> 1) & 1);                 // 64-B-row block 0..3
   const int K = g.K, n_out = g.n_out, NT = g.n_tiles_n;
   constexpr int kCols = (EPI == kEpiSwiglu) ? 128 : 256;  // output columns per tile
 
@@ -144,20 +177,25 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
   const int nk = (K + kBK - 1) / kBK;
   const bool k_tail = (K % kBK) != 0;
 
-  // Load geometry shared by every tile: instruction i of this wave fills the 8 LDS rows
-  // (8 * wave + i) * 8 .. +7; lane l writes row (l >> 3) of them, physical chunk l & 7,
-  // which holds the logical chunk (l & 7) ^ (row & 7).
-  const int lrow = lane >> 3;
-  const int lchunk = ((lane & 7) ^ (lrow & 7)) * 8;
-  // MFMA operand reads: row (lane & 31) of a 32-row block, logical chunk 2 ks + (lane >> 5),
-  // physical chunk = logical ^ (lane & 7); element offsets for ks = 0..3.
-  int rd32[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) rd32[ks] = (lane & 31) * kBK + (((2 * ks + (lane >> 5)) ^ (lane & 7)) * 8);
-  const int a_rd = wm * 128 * kBK;
-  const int b_rd = wn * 128 * kBK;
-
   for (long long s = s_begin + slot; s < s_end; s += per_xcd) {
+    // The lane index is made opaque per tile: otherwise the compiler hoists every
+    // lane-dependent address out of the tile loop and spills them across it.
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    // Load geometry: copy instruction i (0, 1) of this wave fills the 16 LDS rows
+    // (2 wave + i) * 16 .. +15 of a stage; lane l writes row (l >> 2) of them at physical
+    // chunk l & 3, which holds the logical chunk (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
+    const int lrow = lane >> 2;
+    const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+    // MFMA operand reads: row (lane & 31) of a 32-row block, logical chunk 2 ks + (lane >> 5),
+    // physical chunk = logical ^ ((row >> 2) & 3); element offsets for ks = 0, 1.
+    int rdk[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) rdk[ks] = (lane & 31) * kBK + (((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3)) * 8);
+    const int a_rd = wm * 128 * kBK;
+    const int b_rd = wc * 64 * kBK;
+
+
     // ---- tile decode: expert-major, then supertiles of kGM m-tiles x kGN n-tiles
     const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
     const int e = probe[0], ts = probe[3], me = probe[4];
@@ -165,171 +203,205 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
     const int band = (int)(l / ((long long)kGM * NT));
     const int lb = (int)(l - (long long)band * kGM * NT);
     const int bm = min(kGM, me - kGM * band);
-    const int grp = lb / (kGN * bm);
-    const int r = lb - grp * kGN * bm;
+    const int grpn = lb / (kGN * bm);
+    const int r = lb - grpn * kGN * bm;
     const int mt = ts + kGM * band + r % bm;
-    const int nt = grp * kGN + r / bm;
+    const int nt = grpn * kGN + r / bm;
     const int* tq = g.tiles + kTileHdr + kTileInts * mt;
     const int row0 = tq[1], rows = tq[2];
     const int n0 = nt * kCols;
 
-    // uniform bases (bytes) and 32-bit per-lane offsets of the 8 A and 8 B load rows
+    // uniform bases (bytes) and 32-bit per-lane offsets of this wave's 2 A and 2 B copies
     const char* a_base = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
     const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
-    const char* b1_base = (EPI == kEpiSwiglu) ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : nullptr;
-    uint32_t a_off[8], b_off[8];
-    bool b_up[8];
+    const char* b1_base = (EPI == kEpiSwiglu) ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
+    uint32_t a_off[2], b_off[2];
+    const char* b_src[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = (wave * 8 + i) * 8 + lrow;  // tile row / B-row 0..255
+    for (int i = 0; i < 2; ++i) {
+      const int rr = (wave * 2 + i) * 16 + lrow;  // stage row / B-row 0..255
       a_off[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
-      int cl;  // B-row's column relative to n0
+      int cl;  // B-row's output column relative to n0
       if (EPI == kEpiSwiglu) {
-        const int half = rr >> 7, qq = rr & 127;  // B-rows of wave column `half`
-        cl = half * 64 + (qq & 63);
-        b_up[i] = (((wave * 8 + i) * 8) & 127) >= 64;  // uniform: a load group never straddles 64
+        // B-rows 64 c .. 64 c + 31: gate of columns 32 c ..; the next 32: up of the same
+        cl = (rr >> 6) * 32 + (rr & 31);
+        b_src[i] = ((((wave * 2 + i) * 16) & 63) >= 32) ? b1_base : b0_base;  // uniform per copy
       } else {
         cl = rr;
-        b_up[i] = false;
+        b_src[i] = b0_base;
       }
       b_off[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
     }
-    // k0 beyond the last full slab: lanes past K read a valid chunk (clamped) and are zeroed
-    // in LDS after the copy lands.
-    auto issue = [&](uint16_t* sa, uint16_t* sb, int k0) {
-      int kb = k0;
-      if (k_tail && k0 + kBK > K) kb = k0;  // offsets clamp below
+    auto dma_k = [&](int k0) -> uint32_t {  // lanes past K read inside the row (zeroed later)
+      return (k_tail && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
+    };
+    auto refill = [&](uint16_t* sa, uint16_t* sb, int slab) {
+      const uint32_t ka = dma_k(slab * kBK);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t ka = (uint32_t)kb * 2u;
-        if (k_tail && k0 + lchunk >= K) ka = (uint32_t)(K - 8 - lchunk) * 2u;  // stays inside the row
-        uint16_t* da = sa + (wave * 8 + i) * 8 * kBK;
-        uint16_t* db = sb + (wave * 8 + i) * 8 * kBK;
-        lds_dma16(a_base + a_off[i] + ka, da);
-        const char* bb = (EPI == kEpiSwiglu && b_up[i]) ? b1_base : b0_base;
-        lds_dma16(bb + b_off[i] + ka, db);
+      for (int i = 0; i < 2; ++i) {
+        lds_dma16(a_base + a_off[i] + ka, sa + (wave * 2 + i) * 16 * kBK);
+        lds_dma16(b_src[i] + b_off[i] + ka, sb + (wave * 2 + i) * 16 * kBK);
       }
     };
-    // zero this lane's chunks that lie past K (last slab only), once its copies have landed
-    auto zero_tail = [&](uint16_t* sa, uint16_t* sb, int k0) {
-      if (!k_tail || k0 + kBK <= K || k0 + lchunk < K) return;
+    // zero this wave's copied chunks of the last slab that lie past K (after they landed)
+    auto zero_tail = [&](uint16_t* sa, uint16_t* sb, int slab) {
+      if (!k_tail || slab != nk - 1 || slab * kBK + lchunk < K) return;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int off = (wave * 8 + i) * 8 * kBK + lane * 8;
+      for (int i = 0; i < 2; ++i) {
+        const int off = (wave * 2 + i) * 16 * kBK + lane * 8;
         *reinterpret_cast<uint4*>(sa + off) = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(sb + off) = make_uint4(0, 0, 0, 0);
       }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // v_mfma_f32_32x32x16_bf16: lane l supplies row (l & 31) of A / column (l & 31) of B
-    // with the 8 reduction elements of logical chunk 2 ks + (l >> 5).
-    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
-      // operands of reduction step ks + 1 are read while step ks multiplies
-      bf16x8 af[2][4], bfr[2][4];
+    bf16x8 fa[2][4], fb[2][2];  // operands of one slab: [ks][block]
+    auto read_slab = [&](const uint16_t* sa, const uint16_t* sb) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[0][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + a_rd + t * 32 * kBK + rd32[0]));
-        bfr[0][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + b_rd + t * 32 * kBK + rd32[0]));
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          fa[ks][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + a_rd + t * 32 * kBK + rdk[ks]));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          fb[ks][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + b_rd + t * 32 * kBK + rdk[ks]));
       }
+    };
+    auto multiply = [&]() {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int cur = ks & 1, nxt = cur ^ 1;
-        if (ks < 3) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            af[nxt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + a_rd + t * 32 * kBK + rd32[ks + 1]));
-            bfr[nxt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + b_rd + t * 32 * kBK + rd32[ks + 1]));
-          }
-        }
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
-      }
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+    };
+    // phase boundary; `next` = the slab group 0 reads in the coming phase (its K tail is
+    // zeroed here, once every wave's copies of it have landed)
+    auto boundary = [&](uint16_t* na, uint16_t* nb, int next) {
+      __builtin_amdgcn_sched_barrier(0);  // the phase's multiplies / reads stay in the phase
+      wait_vm_lds<8>();
+      zero_tail(na, nb, next);
+      wait_vm_lds<63>();
+      stage_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Slab k lives in stage k mod 4. Each group runs its own straight-line loop; both pass
+    // the same sequence of barriers (two per slab plus one before the first).
+    //   group 0: [read 0] | mult 0 | read 1 | mult 1 | read 2 | ...      (reads in odd phases)
+    //   group 1: [ idle ] | read 0 | mult 0 | read 1 | mult 1 | ...      (reads in even phases)
+    // read k also refills stage (k + 3) mod 4 (free: both groups are done with slab k - 1).
+    auto mem = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k3, uint16_t* b_k3, int k) {
+      refill(a_k3, b_k3, min(k + 3, nk - 1));
+      read_slab(a_k, b_k);
+    };
+    // group 0, slab k: multiply k | read k+1 (the phase boundary before the read publishes
+    // slab k+1, whose K tail is zeroed there)
+    auto g0_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1, int k) {
+      multiply();
+      boundary(a_k1, b_k1, k + 1);
+      if (k + 1 < nk) mem(a_k1, b_k1, a_k, b_k, k + 1);
+      boundary(a_k1, b_k1, -1);
+    };
+    // group 1, slab k: read k | multiply k
+    auto g1_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1,
+                       uint16_t* a_k3, uint16_t* b_k3, int k) {
+      mem(a_k, b_k, a_k3, b_k3, k);
+      boundary(a_k1, b_k1, k + 1);
+      multiply();
+      boundary(a_k1, b_k1, -1);
     };
 
-    issue(sA0, sB0, 0);
+    // prologue: slabs 0..2 in flight, slab 0 published, group 0 reads it
+    refill(sA0, sB0, 0);
+    refill(sA1, sB1, min(1, nk - 1));
+    refill(sA2, sB2, min(2, nk - 1));
+    boundary(sA0, sB0, 0);
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      wait_vm0();
-      zero_tail(sA0, sB0, kt * kBK);
-      __syncthreads();
-      issue(sA1, sB1, (kt + 1) * kBK);
-      compute(sA0, sB0);
-      wait_vm0();
-      zero_tail(sA1, sB1, (kt + 1) * kBK);
-      __syncthreads();
-      if (kt + 2 < nk) issue(sA0, sB0, (kt + 2) * kBK);
-      compute(sA1, sB1);
+    if (grp == 0) {
+      mem(sA0, sB0, sA3, sB3, 0);
+      boundary(sA0, sB0, -1);
+      for (; kt + 4 <= nk; kt += 4) {
+        g0_step(sA0, sB0, sA1, sB1, kt);
+        g0_step(sA1, sB1, sA2, sB2, kt + 1);
+        g0_step(sA2, sB2, sA3, sB3, kt + 2);
+        g0_step(sA3, sB3, sA0, sB0, kt + 3);
+      }
+      const int rem = nk - kt;
+      if (rem > 0) g0_step(sA0, sB0, sA1, sB1, kt);
+      if (rem > 1) g0_step(sA1, sB1, sA2, sB2, kt + 1);
+      if (rem > 2) g0_step(sA2, sB2, sA3, sB3, kt + 2);
+    } else {
+      boundary(sA0, sB0, -1);
+      for (; kt + 4 <= nk; kt += 4) {
+        g1_step(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+        g1_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+        g1_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+        g1_step(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
+      }
+      const int rem = nk - kt;
+      if (rem > 0) g1_step(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+      if (rem > 1) g1_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+      if (rem > 2) g1_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
     }
-    if (kt < nk) {  // odd number of slabs: the last one is in stage 0
-      wait_vm0();
-      zero_tail(sA0, sB0, kt * kBK);
-      __syncthreads();
-      compute(sA0, sB0);
-    }
+    wait_vm_lds<0>();  // copies past the end land before the stages are reused
+
     // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
     // (1 and 0 when absent, so the epilogue has no branches)
-    s_gate[tid] = (EPI == kEpiDown && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
-    s_bias[tid] = (EPI != kEpiSwiglu && g.bias && n0 + tid < n_out)
-                      ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
+    if (tid < kBM) {
+      s_gate[tid] = (EPI == kEpiDown && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
+      s_bias[tid] = (EPI != kEpiSwiglu && g.bias && n0 + tid < n_out)
+                        ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
+    }
     __syncthreads();  // every wave is done reading the stages: reuse them for the epilogue
 
-    // ---- epilogue: activation / bias / gate in registers, the wave's bf16 tile staged in its
-    // own LDS region (rows padded by 16 bytes: the two half-waves, 4 rows apart, hit disjoint
-    // banks), then 16-byte coalesced row stores. 128-column waves go in two 64-row passes.
+    // ---- epilogue: activation / bias / gate in registers, then per 32-row block the wave's
+    // bf16 rows are staged in its own LDS buffer (rows padded by 16 bytes: the two
+    // half-waves, 4 rows apart, hit disjoint banks) and written with 16-byte row stores.
     uint16_t* C = static_cast<uint16_t*>(g.c);
-    constexpr int kWCols = (EPI == kEpiSwiglu) ? 64 : 128;   // wave output columns
+    constexpr int kWCols = (EPI == kEpiSwiglu) ? 32 : 64;    // wave output columns
     constexpr int kStride = kWCols + 8;                       // staged row length (elements)
-    constexpr int kPassRows = (EPI == kEpiSwiglu) ? 128 : 64; // rows staged per pass
     constexpr int kWChunks = kWCols / 8;                      // 16-byte chunks per row
-    uint16_t* stage = (wave == 0) ? sA0 : (wave == 1) ? sB0 : (wave == 2) ? sA1 : sB1;
-    const int col_base = n0 + wn * kWCols;                    // first output column of the wave
+    uint16_t* stage = (wave == 0) ? sA0 : (wave == 1) ? sB0 : (wave == 2) ? sA1 : (wave == 3) ? sB1
+                    : (wave == 4) ? sA2 : (wave == 5) ? sB2 : (wave == 6) ? sA3 : sB3;
+    const int col_base = n0 + wc * kWCols;                    // first output column of the wave
     // lane's element in a 32 x 32 block: column lane & 31, rows 8 g + 4 (lane >> 5) + r
     uint16_t* st_lane = stage + ((lane >> 5) * 4) * kStride + (lane & 31);
 #pragma unroll
-    for (int pass = 0; pass < 128 / kPassRows; ++pass) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int ii = 0; ii < kPassRows / 32; ++ii) {
-        const int i = pass * (kPassRows / 32) + ii;
+      for (int v = 0; v < 16; ++v) {
+        const int prow = (v >> 2) * 8 + (v & 3);  // block row, minus 4 (lane >> 5)
+        if (EPI == kEpiSwiglu) {
+          st_lane[prow * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+        } else {
+          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int prow = ii * 32 + (v >> 2) * 8 + (v & 3);            // pass row, minus 4 (lane >> 5)
-          const float gs = s_gate[wm * 128 + pass * kPassRows + prow + (lane >> 5) * 4];
-          if (EPI == kEpiSwiglu) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              st_lane[prow * kStride + j * 32] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float val = acc[i][j][v] + s_bias[wn * kWCols + j * 32 + (lane & 31)];
-              val = (EPI == kEpiGelu) ? gelu_erf(val) : val * gs;
-              st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
-            }
+          for (int j = 0; j < 2; ++j) {
+            float val = acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)];
+            val = (EPI == kEpiGelu) ? gelu_erf(val) : val * gs;
+            st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep each 32-row group's registers short-lived
       }
-      // each lane stores whole 16-byte chunks of the pass's rows
-#pragma unroll 4
-      for (int it = 0; it < kPassRows * kWChunks / 64; ++it) {
+      // each lane stores whole 16-byte chunks of the block's 32 rows
+#pragma unroll
+      for (int it = 0; it < 32 * kWChunks / 64; ++it) {
         const int idx = it * 64 + lane;
         const int prow = idx / kWChunks, ch = idx % kWChunks;
-        const int trow = wm * 128 + pass * kPassRows + prow;
+        const int trow = wm * 128 + i * 32 + prow;
         const int col = col_base + ch * 8;
         const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
         if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(C + (size_t)(row0 + trow) * n_out + col) = val;
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep each 32-row block's registers short-lived
     }
     __syncthreads();  // the staging area is the next tile's first stage
   }
@@ -479,8 +551,8 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
     const int grid = persistent_grid();
-    if (c.act == MOE_ACT_SWIGLU) expert_gemm_bf16_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
-    else expert_gemm_bf16_kernel<kEpiGelu><<<grid, 256, 0, stream>>>(g);
+    if (c.act == MOE_ACT_SWIGLU) expert_gemm_bf16_kernel<kEpiSwiglu><<<grid, kGemmThreads, 0, stream>>>(g);
+    else expert_gemm_bf16_kernel<kEpiGelu><<<grid, kGemmThreads, 0, stream>>>(g);
   } else {
     dim3 grid(mt, (c.d_ff + kFBN - 1) / kFBN);
     if (c.act == MOE_ACT_SWIGLU) expert_gemm_f32_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
@@ -506,7 +578,7 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
   const int mt = max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_model + 255) / 256;
-    expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), 256, 0, stream>>>(g);
+    expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
   } else {
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);
