@@ -155,8 +155,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
   __shared__ __attribute__((aligned(16))) uint16_t sB2[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t sA3[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t sB3[kStageElems];
-  __shared__ float s_gate[kBM];  // this tile's per-row gates (down projection)
-  __shared__ float s_bias[kBNB]; // this tile's per-column biases
+  __shared__ __attribute__((aligned(16))) uint16_t sA4[kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sB4[kStageElems];
+  // epilogue only: this tile's per-row gates (down projection) and per-column biases
+  float* s_gate = reinterpret_cast<float*>(sA4);
+  float* s_bias = reinterpret_cast<float*>(sA4) + kBM;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
@@ -287,23 +290,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     // zeroed here, once every wave's copies of it have landed)
     auto boundary = [&](uint16_t* na, uint16_t* nb, int next) {
       __builtin_amdgcn_sched_barrier(0);  // the phase's multiplies / reads stay in the phase
-      wait_vm_lds<8>();
+      wait_vm_lds<12>();
       zero_tail(na, nb, next);
       wait_vm_lds<63>();
       stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
     };
-    // Slab k lives in stage k mod 4. Each group runs its own straight-line loop; both pass
+    // Slab k lives in stage k mod 5. Each group runs its own straight-line loop; both pass
     // the same sequence of barriers (two per slab plus one before the first).
     //   group 0: [read 0] | mult 0 | read 1 | mult 1 | read 2 | ...      (reads in odd phases)
     //   group 1: [ idle ] | read 0 | mult 0 | read 1 | mult 1 | ...      (reads in even phases)
-    // read k also refills stage (k + 3) mod 4 (free: both groups are done with slab k - 1).
-    auto mem = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k3, uint16_t* b_k3, int k) {
-      refill(a_k3, b_k3, min(k + 3, nk - 1));
+    // read k also refills stage (k + 4) mod 5 (free: both groups are done with slab k - 1).
+    auto mem = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k4, uint16_t* b_k4, int k) {
+      refill(a_k4, b_k4, min(k + 4, nk - 1));
       read_slab(a_k, b_k);
     };
     // group 0, slab k: multiply k | read k+1 (the phase boundary before the read publishes
-    // slab k+1, whose K tail is zeroed there)
+    // slab k+1, whose K tail is zeroed there); read k+1 refills the stage of slab k
     auto g0_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1, int k) {
       multiply();
       boundary(a_k1, b_k1, k + 1);
@@ -312,44 +315,49 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     };
     // group 1, slab k: read k | multiply k
     auto g1_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1,
-                       uint16_t* a_k3, uint16_t* b_k3, int k) {
-      mem(a_k, b_k, a_k3, b_k3, k);
+                       uint16_t* a_k4, uint16_t* b_k4, int k) {
+      mem(a_k, b_k, a_k4, b_k4, k);
       boundary(a_k1, b_k1, k + 1);
       multiply();
       boundary(a_k1, b_k1, -1);
     };
 
-    // prologue: slabs 0..2 in flight, slab 0 published, group 0 reads it
+    // prologue: slabs 0..3 in flight, slab 0 published, group 0 reads it
     refill(sA0, sB0, 0);
     refill(sA1, sB1, min(1, nk - 1));
     refill(sA2, sB2, min(2, nk - 1));
+    refill(sA3, sB3, min(3, nk - 1));
     boundary(sA0, sB0, 0);
     int kt = 0;
     if (grp == 0) {
-      mem(sA0, sB0, sA3, sB3, 0);
+      mem(sA0, sB0, sA4, sB4, 0);
       boundary(sA0, sB0, -1);
-      for (; kt + 4 <= nk; kt += 4) {
+      for (; kt + 5 <= nk; kt += 5) {
         g0_step(sA0, sB0, sA1, sB1, kt);
         g0_step(sA1, sB1, sA2, sB2, kt + 1);
         g0_step(sA2, sB2, sA3, sB3, kt + 2);
-        g0_step(sA3, sB3, sA0, sB0, kt + 3);
+        g0_step(sA3, sB3, sA4, sB4, kt + 3);
+        g0_step(sA4, sB4, sA0, sB0, kt + 4);
       }
       const int rem = nk - kt;
       if (rem > 0) g0_step(sA0, sB0, sA1, sB1, kt);
       if (rem > 1) g0_step(sA1, sB1, sA2, sB2, kt + 1);
       if (rem > 2) g0_step(sA2, sB2, sA3, sB3, kt + 2);
+      if (rem > 3) g0_step(sA3, sB3, sA4, sB4, kt + 3);
     } else {
       boundary(sA0, sB0, -1);
-      for (; kt + 4 <= nk; kt += 4) {
-        g1_step(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+      for (; kt + 5 <= nk; kt += 5) {
+        g1_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
         g1_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
         g1_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-        g1_step(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
+        g1_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
+        g1_step(sA4, sB4, sA0, sB0, sA3, sB3, kt + 4);
       }
       const int rem = nk - kt;
-      if (rem > 0) g1_step(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+      if (rem > 0) g1_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
       if (rem > 1) g1_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
       if (rem > 2) g1_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+      if (rem > 3) g1_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
     }
     wait_vm_lds<0>();  // copies past the end land before the stages are reused
 
