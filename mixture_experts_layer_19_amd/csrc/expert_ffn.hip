@@ -93,20 +93,21 @@ struct GemmArgs {
 // the same columns, so the gate and up value of an output land in the same lane and the
 // activation is applied in registers (128 output columns per tile).
 //
-// Operands stream through four LDS stages of 32 reduction elements (A 16 KiB + B 16 KiB)
-// written by global_load_lds_dwordx4 (memory straight to LDS, no VGPR staging), three
-// stages ahead. The four 16-byte chunks of a 64-byte LDS row are XOR-swizzled by
-// (row >> 2) mod 4, so the 16 rows one 256-byte LDS cycle of a 16-byte operand read serves
-// (rows r .. r+15 at one logical chunk) fall in 16 distinct bank slots.
+// Operands stream through five LDS stages of 32 reduction elements (A 16 KiB + B 16 KiB, all
+// 160 KiB of the CU's LDS) written by global_load_lds_dwordx4 (memory straight to LDS, no
+// VGPR staging), four or five slabs ahead. The four 16-byte chunks of a 64-byte LDS row are
+// XOR-swizzled by (row >> 2) mod 4, so the 16 rows one 256-byte LDS cycle of a 16-byte
+// operand read serves (rows r .. r+15 at one logical chunk) fall in 16 distinct bank slots.
 //
 // Ping-pong: the waves form two groups offset by half a step. In every phase one group's
-// wave on a SIMD issues its 16 multiplies back to back while the other group's wave reads
-// the next slab's operands from LDS and refills a free stage, then a barrier swaps the
-// roles; so the MFMA pipe is fed by one wave while the other's memory latency is hidden.
-//   phase 2k:   group 0 multiplies slab k      group 1 reads slab k, loads slab k+3
-//   phase 2k+1: group 0 reads slab k+1, loads slab k+4      group 1 multiplies slab k
-// Each wave issues 4 of the 32 copies of a slab per refill and keeps two refills in
-// flight, so at every phase boundary `vmcnt(8)` guarantees that the next slab to be read
+// wave on a SIMD issues its 16 multiplies (with one LDS refill copy after every 4) while the
+// other group's wave reads the next slab's operands from LDS, then a barrier swaps the
+// roles; so the MFMA pipe is fed by one wave while the other's LDS latency is hidden, and
+// the copies are issued from the wave whose MFMAs keep the pipe busy meanwhile.
+//   phase 2k:   group 0 multiplies slab k, refills slab k+4   group 1 reads slab k
+//   phase 2k+1: group 0 reads slab k+1          group 1 multiplies slab k, refills slab k+5
+// Each wave issues 4 of the 32 copies of a slab per refill and keeps three refills in
+// flight, so at every phase boundary `vmcnt(12)` guarantees that the next slab to be read
 // has landed for every wave. Refills past the last slab copy the last slab again into a
 // stage that is never read, which keeps that count exact.
 //
@@ -297,32 +298,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       __builtin_amdgcn_sched_barrier(0);
     };
     // Slab k lives in stage k mod 5. Each group runs its own straight-line loop; both pass
-    // the same sequence of barriers (two per slab plus one before the first).
+    // the same sequence of barriers (two per slab plus one before the first):
     //   group 0: [read 0] | mult 0 | read 1 | mult 1 | read 2 | ...      (reads in odd phases)
     //   group 1: [ idle ] | read 0 | mult 0 | read 1 | mult 1 | ...      (reads in even phases)
-    // read k also refills stage (k + 4) mod 5 (free: both groups are done with slab k - 1).
-    auto mem = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k4, uint16_t* b_k4, int k) {
-      refill(a_k4, b_k4, min(k + 4, nk - 1));
-      read_slab(a_k, b_k);
+    // A stage is refilled only when both groups are done with its previous slab.
+    // multiply slab k while refilling stage (fa, fb) with `slab`: one copy after every 4 MFMAs
+    auto multiply_refill = [&](uint16_t* fa_, uint16_t* fb_, int slab) {
+      const uint32_t ka = dma_k(slab * kBK);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int mm = q * 4 + m, ks = mm >> 3, i = (mm >> 1) & 3, j = mm & 1;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+        }
+        const int ii = q >> 1;
+        if ((q & 1) == 0) lds_dma16(a_base + a_off[ii] + ka, fa_ + (wave * 2 + ii) * 16 * kBK);
+        else lds_dma16(b_src[ii] + b_off[ii] + ka, fb_ + (wave * 2 + ii) * 16 * kBK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
-    // group 0, slab k: multiply k | read k+1 (the phase boundary before the read publishes
-    // slab k+1, whose K tail is zeroed there); read k+1 refills the stage of slab k
-    auto g0_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1, int k) {
-      multiply();
-      boundary(a_k1, b_k1, k + 1);
-      if (k + 1 < nk) mem(a_k1, b_k1, a_k, b_k, k + 1);
-      boundary(a_k1, b_k1, -1);
-    };
-    // group 1, slab k: read k | multiply k
-    auto g1_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1,
+    // group 0: phase 2k multiplies k and refills stage (k+4)%5 with slab k+4; phase 2k+1 reads k+1
+    auto g0_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1,
                        uint16_t* a_k4, uint16_t* b_k4, int k) {
-      mem(a_k, b_k, a_k4, b_k4, k);
+      multiply_refill(a_k4, b_k4, min(k + 4, nk - 1));
       boundary(a_k1, b_k1, k + 1);
-      multiply();
+      if (k + 1 < nk) read_slab(a_k1, b_k1);
       boundary(a_k1, b_k1, -1);
     };
-
-    // prologue: slabs 0..3 in flight, slab 0 published, group 0 reads it
+    // group 1: phase 2k reads k; phase 2k+1 multiplies k and refills stage k%5 with slab k+5
+    auto g1_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1, int k) {
+      read_slab(a_k, b_k);
+      boundary(a_k1, b_k1, k + 1);
+      multiply_refill(a_k, b_k, min(k + 5, nk - 1));
+      boundary(a_k1, b_k1, -1);
+    };
     refill(sA0, sB0, 0);
     refill(sA1, sB1, min(1, nk - 1));
     refill(sA2, sB2, min(2, nk - 1));
@@ -330,34 +340,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     boundary(sA0, sB0, 0);
     int kt = 0;
     if (grp == 0) {
-      mem(sA0, sB0, sA4, sB4, 0);
+      read_slab(sA0, sB0);
       boundary(sA0, sB0, -1);
       for (; kt + 5 <= nk; kt += 5) {
-        g0_step(sA0, sB0, sA1, sB1, kt);
-        g0_step(sA1, sB1, sA2, sB2, kt + 1);
-        g0_step(sA2, sB2, sA3, sB3, kt + 2);
-        g0_step(sA3, sB3, sA4, sB4, kt + 3);
-        g0_step(sA4, sB4, sA0, sB0, kt + 4);
+        g0_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
+        g0_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+        g0_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+        g0_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
+        g0_step(sA4, sB4, sA0, sB0, sA3, sB3, kt + 4);
       }
       const int rem = nk - kt;
-      if (rem > 0) g0_step(sA0, sB0, sA1, sB1, kt);
-      if (rem > 1) g0_step(sA1, sB1, sA2, sB2, kt + 1);
-      if (rem > 2) g0_step(sA2, sB2, sA3, sB3, kt + 2);
-      if (rem > 3) g0_step(sA3, sB3, sA4, sB4, kt + 3);
+      if (rem > 0) g0_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
+      if (rem > 1) g0_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+      if (rem > 2) g0_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+      if (rem > 3) g0_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
     } else {
+      refill(sA4, sB4, min(4, nk - 1));
       boundary(sA0, sB0, -1);
       for (; kt + 5 <= nk; kt += 5) {
-        g1_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
-        g1_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-        g1_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-        g1_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
-        g1_step(sA4, sB4, sA0, sB0, sA3, sB3, kt + 4);
+        g1_step(sA0, sB0, sA1, sB1, kt);
+        g1_step(sA1, sB1, sA2, sB2, kt + 1);
+        g1_step(sA2, sB2, sA3, sB3, kt + 2);
+        g1_step(sA3, sB3, sA4, sB4, kt + 3);
+        g1_step(sA4, sB4, sA0, sB0, kt + 4);
       }
       const int rem = nk - kt;
-      if (rem > 0) g1_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
-      if (rem > 1) g1_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-      if (rem > 2) g1_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-      if (rem > 3) g1_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
+      if (rem > 0) g1_step(sA0, sB0, sA1, sB1, kt);
+      if (rem > 1) g1_step(sA1, sB1, sA2, sB2, kt + 1);
+      if (rem > 2) g1_step(sA2, sB2, sA3, sB3, kt + 2);
+      if (rem > 3) g1_step(sA3, sB3, sA4, sB4, kt + 3);
     }
     wait_vm_lds<0>();  // copies past the end land before the stages are reused
 
