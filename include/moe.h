@@ -32,8 +32,14 @@
  *     call returns a non-zero moe_status and leaves every output untouched. Errors never
  *     cross the ABI as exceptions. A failed kernel launch returns MOE_ERR_HIP.
  *   - Limits: 0 <= N*k < 2^31, 1 <= E <= 1024, 1 <= k <= min(E, 32), d and d_ff in
- *     [8, 65536] and multiples of 8, every pointer 16-byte aligned (MOE_ERR_UNSUPPORTED
- *     otherwise). N = 0 is valid: counts and statistics are written as zeros.
+ *     [8, 65536] and multiples of 8; the workspace and every T tensor 16-byte aligned, every
+ *     int32 / float32 tensor 4-byte aligned (MOE_ERR_UNSUPPORTED otherwise; MOE_ERR_WORKSPACE
+ *     for a misaligned workspace). N = 0 is valid: counts and statistics are written as zeros.
+ *   - Device error word: the first int of the workspace. moe_dispatch overwrites it (0, or
+ *     MOE_ERR_BAD_EXPERT_ID when it met an id outside [0, E)); moe_forward overwrites it with
+ *     0; moe_expert_ffn sets it to MOE_ERR_INVALID_ARG when offsets is not a non-decreasing
+ *     sequence in [0, A] starting at 0, and leaves it unchanged otherwise.
+ *     moe_get_device_error reads and clears it.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -156,7 +162,9 @@ moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const float*
 
 /* The whole layer ([L7.8] §2.1 output equation): route -> dispatch -> expert FFN (gate
  * applied in the down-projection epilogue) -> combine -> statistics, on one stream with no
- * host synchronisation. Inputs and outputs as in the calls above; y [N,d] T.
+ * host synchronisation. Inputs and outputs as in the calls above; y [N,d] T. Routing's final
+ * reduction also forms the dispatch offsets and per-block bases from its own histograms, so
+ * the dispatch stage is a scatter and a row copy; results equal the separate calls'.
  * stage_events: NULL, or 6 hipEvent_t (as void*) recorded on `stream` at the start, after
  * routing, after dispatch, after the up projection, after the down projection and at the end.
  * ws: moe_workspace_size(cfg, MOE_OP_FORWARD) bytes. */
@@ -168,8 +176,10 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 
 /* Synchronises `stream`, then reads and clears the device error word at the start of `ws`:
- * MOE_ERR_BAD_EXPERT_ID if a dispatch on this workspace met an out-of-range id,
- * MOE_ERR_HIP if the synchronisation or copy failed, else MOE_OK. */
+ * MOE_ERR_BAD_EXPERT_ID if the last dispatch on this workspace met an out-of-range id,
+ * MOE_ERR_INVALID_ARG if an expert FFN call on it met a malformed offsets array (the call
+ * clamped it, so no access left the buffers), MOE_ERR_HIP if the synchronisation or copy
+ * failed, else MOE_OK. */
 moe_status moe_get_device_error(void* ws, void* stream);
 
 /* A static, human-readable name for a status code. */

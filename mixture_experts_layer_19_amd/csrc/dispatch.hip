@@ -75,28 +75,30 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   if (threadIdx.x == 0 && err) err[0] = s_bad ? MOE_ERR_BAD_EXPERT_ID : 0;
 }
 
-// Stable scatter. The chunk is walked in order, 256 assignments (4 waves) at a time. For an
-// assignment of expert e in wave w: slot = running[e] + (count of e in waves < w of this
-// step) + (count of e in lower lanes of wave w). Per-wave counts are published in LDS
-// tagged with the step number, so stale entries read as zero without clearing.
+// Stable scatter. The chunk of `chunk` assignments is walked in order, blockDim.x (64, 128
+// or 256) at a time. For an assignment of expert e in wave w: slot = running[e] + (count of
+// e in waves < w of this step) + (count of e in lower lanes of wave w). Per-wave counts are
+// published in LDS tagged with the step number, so stale entries read as zero without
+// clearing. base[blockIdx.x][e] is the first slot of this chunk's run of expert e.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int A, int E, int id_bits,
+    const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int A, int E, int id_bits, int chunk,
     const int* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     float* __restrict__ gate_sorted) {
   __shared__ int s_run[kMaxExperts];
   __shared__ int s_cnt[4][kMaxExperts];  // (step << 16) | count
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) {
+  const int nthr = blockDim.x;
+  const int n_waves = nthr >> 6;
+  for (int e = threadIdx.x; e < E; e += nthr) {
     s_run[e] = base[(size_t)blockIdx.x * E + e];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) s_cnt[w][e] = -1;
+    for (int w = 0; w < n_waves; ++w) s_cnt[w][e] = -1;
   }
   __syncthreads();
-  const int a0 = blockIdx.x * kChunk;
-  const int a1 = min(A, a0 + kChunk);
+  const int a0 = blockIdx.x * chunk;
+  const int a1 = min(A, a0 + chunk);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int step = 0, as = a0; as < a1; ++step, as += 256) {
+  for (int step = 0, as = a0; as < a1; ++step, as += nthr) {
     const int a = as + threadIdx.x;
     const int e = (a < a1) ? ids[a] : -1;
     const bool valid = e >= 0 && e < E;
@@ -146,6 +148,22 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(
   }
 }
 
+static int id_bits_of(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+static void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted,
+                        hipStream_t stream) {
+  if (!x_sorted) return;
+  const int vpr = (int)(c.d_model * elem_size(c) / 16);
+  const long long total = c.n_tokens * vpr;
+  const int grid = (int)std::min<long long>((total + 255) / 256, 1 << 16);
+  dispatch_copy_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(x), inv_perm,
+                                                 static_cast<uint4*>(x_sorted), c.n_tokens, c.top_k, vpr);
+}
+
 void carve_dispatch(const moe_config& c, WsCarver& w, WsLayout* L) {
   const long long A = c.n_tokens * c.top_k;
   const int n_chunks = (int)((A + kChunk - 1) / kChunk);
@@ -167,22 +185,33 @@ hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x
   const int A = (int)(c.n_tokens * c.top_k);
   const int E = c.n_experts;
   const int n_chunks = (A + kChunk - 1) / kChunk;
-  int id_bits = 0;
-  while ((1 << id_bits) < E) ++id_bits;
+  const int id_bits = id_bits_of(E);
   if (n_chunks > 0) dispatch_hist_kernel<<<n_chunks, 256, 0, stream>>>(topk_ids, A, E, L.d_hist, L.d_bad);
   dispatch_scan_kernel<<<1, 1024, 0, stream>>>(L.d_hist, L.d_bad, n_chunks, E, L.d_base, counts, offsets, L.err);
   if (n_chunks > 0) {
     dispatch_scatter_kernel<<<n_chunks, 256, 0, stream>>>(topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr,
-                                                          A, E, id_bits, L.d_base, perm, inv_perm,
+                                                          A, E, id_bits, kChunk, L.d_base, perm, inv_perm,
                                                           (gate_sorted && topk_w) ? gate_sorted : nullptr);
-    if (x_sorted) {
-      const int vpr = (int)(c.d_model * elem_size(c) / 16);
-      const long long total = c.n_tokens * vpr;
-      const int grid = (int)std::min<long long>((total + 255) / 256, 1 << 16);
-      dispatch_copy_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(x), inv_perm,
-                                                     static_cast<uint4*>(x_sorted), c.n_tokens, c.top_k, vpr);
-    }
+    launch_copy(c, x, inv_perm, x_sorted, stream);
   }
+  return hipGetLastError();
+}
+
+// moe_forward's dispatch: the routing finalize already wrote offsets and the per-route-block
+// bases (L.fbase), so only the scatter (one chunk per routing block) and the copy remain.
+hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const void* x,
+                                   const int32_t* topk_ids, const float* topk_w, void* x_sorted,
+                                   int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream) {
+  const int A = (int)(c.n_tokens * c.top_k);
+  if (A == 0) return hipGetLastError();
+  const int E = c.n_experts;
+  const int chunk = route_tokens_per_block(c) * c.top_k;
+  const int n_chunks = (A + chunk - 1) / chunk;
+  const int threads = chunk <= 64 ? 64 : chunk <= 128 ? 128 : 256;
+  dispatch_scatter_kernel<<<n_chunks, threads, 0, stream>>>(topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr,
+                                                            A, E, id_bits_of(E), chunk, L.fbase, perm, inv_perm,
+                                                            (gate_sorted && topk_w) ? gate_sorted : nullptr);
+  launch_copy(c, x, inv_perm, x_sorted, stream);
   return hipGetLastError();
 }
 

@@ -16,15 +16,9 @@ namespace moe {
 
 enum Epi { kEpiGelu = 0, kEpiSwiglu = 1, kEpiDown = 2 };
 
-// ---------------------------------------------------------------------------------------
-// Tile table. tiles[0] = number of m-tiles, tiles[4..7] = 16 zero bytes (the source of
-// every load past the end of the reduction axis), and m-tile t is described by
-// tiles[8 + 8t ..] = (expert, first row, rows in the tile, the expert's first m-tile, the
-// expert's m-tile count). Offsets outside [0, rows] or decreasing are clamped, the list is
-// capped at max_tiles (so no access leaves the buffers) and the error word is set.
-// ---------------------------------------------------------------------------------------
-constexpr int kTileHdr = 8, kTileInts = 8;
-
+// Tile table (layout and clamping: build_tile_table) from offsets; a bad offsets array sets
+// the error word to MOE_ERR_INVALID_ARG and is otherwise clamped, so no access leaves the
+// buffers.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict__ offsets, int E, int rows,
                                                           int bm, int max_tiles, int* __restrict__ tiles,
                                                           int* __restrict__ err) {
@@ -32,43 +26,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict_
   __shared__ int s_bad;
   const int e = threadIdx.x;
   if (e == 0) s_bad = 0;
-  if (e < 4) tiles[4 + e] = 0;
   __syncthreads();
-  int lo = 0, hi = 0, n = 0;
-  if (e < E) {
-    lo = offsets[e];
-    hi = offsets[e + 1];
-    if (lo < 0 || hi > rows || hi < lo || (e == 0 && lo != 0)) s_bad = 1;
-    lo = min(max(lo, 0), rows);
-    hi = min(max(hi, lo), rows);
-    n = (hi - lo + bm - 1) / bm;
-    s_scan[e] = n;
-  }
-  __syncthreads();
-  for (int o = 1; o < E; o <<= 1) {
-    int v = 0;
-    if (e < E && e >= o) v = s_scan[e - o];
-    __syncthreads();
-    if (e < E) s_scan[e] += v;
-    __syncthreads();
-  }
-  if (e < E) {
-    const int start = s_scan[e] - n;
-    for (int t = 0; t < n && start + t < max_tiles; ++t) {
-      const int r0 = lo + t * bm;
-      int* q = tiles + kTileHdr + kTileInts * (start + t);
-      q[0] = e;
-      q[1] = r0;
-      q[2] = min(bm, hi - r0);
-      q[3] = start;
-      q[4] = min(n, max_tiles - start);
-    }
-    if (e == E - 1) {
-      if (s_scan[e] > max_tiles) s_bad = 1;
-      tiles[0] = min(s_scan[e], max_tiles);
-    }
-  }
-  __syncthreads();
+  const int lo = e < E ? offsets[e] : 0;
+  const int hi = e < E ? offsets[e + 1] : 0;
+  build_tile_table(lo, hi, E, rows, bm, max_tiles, tiles, s_scan, &s_bad);
   if (e == 0 && s_bad && err) err[0] = MOE_ERR_INVALID_ARG;
 }
 
@@ -514,7 +475,7 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------
-static int tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM; }
+int ffn_tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM; }
 
 // One persistent workgroup per CU (a multiple of 8, so every XCD gets the same count).
 static int persistent_grid() {
@@ -529,15 +490,15 @@ static int persistent_grid() {
   return cus[dev];
 }
 
-static int max_m_tiles(const moe_config& c) {
+int ffn_max_m_tiles(const moe_config& c) {
   const long long A = c.n_tokens * c.top_k;
-  const int bm = tile_rows(c);
+  const int bm = ffn_tile_rows(c);
   return (int)((A + bm - 1) / bm) + c.n_experts;
 }
 
 void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   const size_t A = (size_t)(c.n_tokens * c.top_k);
-  int* tiles = w.take_t<int>(kTileHdr + kTileInts * (size_t)max_m_tiles(c));
+  int* tiles = w.take_t<int>(kTileHdr + kTileInts * (size_t)ffn_max_m_tiles(c));
   void* h = w.take(A * (size_t)c.d_ff * elem_size(c));
   if (L) {
     L->tiles = tiles;
@@ -548,7 +509,7 @@ void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
 hipError_t launch_ffn_tiles(const moe_config& c, const WsLayout& L, const int32_t* offsets, hipStream_t stream) {
   const int A = (int)(c.n_tokens * c.top_k);
   if (A == 0) return hipGetLastError();
-  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, tile_rows(c), max_m_tiles(c), L.tiles, L.err);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, ffn_tile_rows(c), ffn_max_m_tiles(c), L.tiles, L.err);
   return hipGetLastError();
 }
 
@@ -566,7 +527,7 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
   g.tiles = L.tiles;
   g.K = c.d_model;
   g.n_out = c.d_ff;
-  const int mt = max_m_tiles(c);
+  const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
     const int grid = persistent_grid();
@@ -594,7 +555,7 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
   g.tiles = L.tiles;
   g.K = c.d_ff;
   g.n_out = c.d_model;
-  const int mt = max_m_tiles(c);
+  const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_model + 255) / 256;
     expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);

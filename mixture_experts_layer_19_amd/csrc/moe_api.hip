@@ -57,7 +57,7 @@ void carve_forward_buffers(const moe_config& c, WsCarver& w, WsLayout* L) {
   int* perm = w.take_t<int>(A);
   int* inv = w.take_t<int>(A);
   int* off = w.take_t<int>((size_t)c.n_experts + 1);
-  int* cnt = w.take_t<int>((size_t)c.n_experts);
+  int* fbase = w.take_t<int>(route_base_ints(c));
   float* gs = w.take_t<float>(A);
   void* xs = w.take(A * row);
   void* ys = w.take(A * row);
@@ -65,7 +65,7 @@ void carve_forward_buffers(const moe_config& c, WsCarver& w, WsLayout* L) {
     L->perm = perm;
     L->inv_perm = inv;
     L->offsets = off;
-    L->counts_tmp = cnt;
+    L->fbase = fbase;
     L->gate_sorted = gs;
     L->x_sorted = xs;
     L->y_sorted = ys;
@@ -86,7 +86,6 @@ size_t layout(const moe_config& c, int op, char* base, WsLayout* L) {
     case MOE_OP_COMBINE: break;
     case MOE_OP_FORWARD:
       carve_route(c, w, L);
-      carve_dispatch(c, w, L);
       carve_ffn(c, w, L);
       carve_forward_buffers(c, w, L);
       break;
@@ -137,7 +136,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   WsLayout L{};
   MOE_TRY(check_ws(*cfg, MOE_OP_ROUTE, ws, ws_bytes, &L));
   return hip_status(launch_route(*cfg, L, x, w_router, logit_bias, sel_bias, topk_ids, topk_w, counts,
-                                 stats, logits_out, gap_out, static_cast<hipStream_t>(stream)));
+                                 stats, logits_out, gap_out, false, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* topk_ids,
@@ -235,12 +234,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s));
   };
   MOE_TRY(mark(0));
+  // Routing's final reduction also writes offsets, the per-block dispatch bases and the
+  // m-tile table, so dispatch is a scatter and a row copy.
   MOE_TRY(hip_status(launch_route(*cfg, L, x, w_router, logit_bias, sel_bias, topk_ids, topk_w, counts, stats,
-                                  nullptr, nullptr, s)));
+                                  nullptr, nullptr, true, s)));
   MOE_TRY(mark(1));
-  MOE_TRY(hip_status(launch_dispatch(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
-                                     L.counts_tmp, L.offsets, L.gate_sorted, s)));
-  MOE_TRY(hip_status(launch_ffn_tiles(*cfg, L, L.offsets, s)));
+  MOE_TRY(hip_status(launch_dispatch_scanned(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
+                                             L.gate_sorted, s)));
   MOE_TRY(mark(2));
   MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s)));
   MOE_TRY(mark(3));

@@ -44,21 +44,91 @@ struct WsLayout {
   int* d_base = nullptr;   // [blocks][E] first sorted slot of each block's run of expert e
   int* d_bad = nullptr;    // [blocks] out-of-range id seen
   // expert FFN
-  int* tiles = nullptr;    // [1 + max_tiles][4]: count, then (expert, first row, rows) per m-tile
+  int* tiles = nullptr;    // m-tile table (kTileHdr + kTileInts per tile ints)
   void* h = nullptr;       // [A][d_ff] T
   // forward intermediates
   int* perm = nullptr;
   int* inv_perm = nullptr;
   int* offsets = nullptr;
-  int* counts_tmp = nullptr;
+  int* fbase = nullptr;    // [route blocks][E] dispatch bases from the routing histograms
   float* gate_sorted = nullptr;
   void* x_sorted = nullptr;
   void* y_sorted = nullptr;
 };
 
+// m-tile table of the grouped GEMMs: tiles[0] = number of m-tiles, tiles[4..7] = 16 zero
+// bytes, and m-tile t is tiles[kTileHdr + kTileInts t ..] = (expert, first row, rows in the
+// tile, the expert's first m-tile, the expert's m-tile count).
+constexpr int kTileHdr = 8, kTileInts = 8;
+
+// Builds the tile table with one workgroup of at least E threads (thread e owns expert e).
+// lo_e / hi_e are expert e's row range; ranges outside [0, rows] or decreasing are clamped,
+// the list is capped at max_tiles (so no access leaves the buffers) and *bad is set.
+// s_scan: kMaxExperts ints of LDS. Every thread of the block must call it.
+MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int max_tiles, int* tiles,
+                              int* s_scan, int* bad) {
+  const int e = threadIdx.x;
+  if (e < 4) tiles[4 + e] = 0;
+  int n = 0;
+  if (e < E) {
+    if (lo < 0 || hi > rows || hi < lo || (e == 0 && lo != 0)) *bad = 1;
+    lo = min(max(lo, 0), rows);
+    hi = min(max(hi, lo), rows);
+    n = (hi - lo + bm - 1) / bm;
+    s_scan[e] = n;
+  }
+  __syncthreads();
+  for (int o = 1; o < E; o <<= 1) {
+    int v = 0;
+    if (e < E && e >= o) v = s_scan[e - o];
+    __syncthreads();
+    if (e < E) s_scan[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int start = s_scan[e] - n;
+    for (int t = 0; t < n && start + t < max_tiles; ++t) {
+      const int r0 = lo + t * bm;
+      int* q = tiles + kTileHdr + kTileInts * (start + t);
+      q[0] = e;
+      q[1] = r0;
+      q[2] = min(bm, hi - r0);
+      q[3] = start;
+      q[4] = min(n, max_tiles - start);
+    }
+    if (e == E - 1) {
+      if (s_scan[e] > max_tiles) *bad = 1;
+      tiles[0] = min(s_scan[e], max_tiles);
+    }
+  }
+  __syncthreads();
+}
+
+// Routing launch shape. A token is handled by a group of lpt lanes (lpt = E rounded up to a
+// power of two, at most 64), each lane holding epl experts, so a wave routes 64/lpt tokens at
+// once; tokens_per_wave is a multiple of 64/lpt.
 struct RoutePlan {
+  int lpt, epl;
   int tokens_per_wave, tokens_per_block, n_blocks;
   int n_split, k_chunk;
+};
+
+// Final reduction of the routing partials; optionally (moe_forward) also the dispatch scan
+// over the same token blocks and the grouped-GEMM tile table.
+struct FinalizeArgs {
+  const float* part_p;
+  const int* part_hist;
+  const float* part_zl;
+  int n_blocks;
+  long long n_tokens;
+  int n_experts;
+  int32_t* counts;
+  float* stats;
+  int* offsets;   // [E+1] or null: no dispatch scan
+  int* base;      // [n_blocks][E] first sorted slot of each block's run of each expert
+  int* err;       // device error word (written 0: routed ids are always valid)
+  int* tiles;     // tile table or null
+  int tile_bm, max_tiles;
 };
 
 struct RouteArgs {
@@ -86,12 +156,21 @@ void carve_dispatch(const moe_config& c, WsCarver& w, WsLayout* L);
 void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L);
 
 RoutePlan plan_route(const moe_config& c);
+size_t route_base_ints(const moe_config& c);
+int route_tokens_per_block(const moe_config& c);
 
 // Launch sequences; none of them synchronises.
+// fuse_dispatch (moe_forward): the final routing reduction also writes L.offsets, L.fbase and
+// the tile table L.tiles, so dispatch runs only its scatter and copy (launch_dispatch_scanned).
 hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_router,
                         const float* logit_bias, const float* sel_bias, int32_t* topk_ids,
                         float* topk_w, int32_t* counts, float* stats, float* logits_out,
-                        float* gap_out, hipStream_t stream);
+                        float* gap_out, bool fuse_dispatch, hipStream_t stream);
+hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const void* x,
+                                   const int32_t* topk_ids, const float* topk_w, void* x_sorted,
+                                   int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream);
+int ffn_tile_rows(const moe_config& c);
+int ffn_max_m_tiles(const moe_config& c);
 hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x,
                            const int32_t* topk_ids, const float* topk_w, void* x_sorted,
                            int32_t* perm, int32_t* inv_perm, int32_t* counts, int32_t* offsets,

@@ -5,6 +5,8 @@
 // Follows "Mixture of Experts: routing, sorted dispatch, Switch aux loss, aux-free bias"
 // (L7.8) §2 symbol table and §2.1 routers table, §2.3 load-balancing loss, §2.5 (the bias
 // chooses, never weighs); "15. Mixture of Experts" (RustingBrain) §15.2 routing, §15.3 z-loss.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -59,6 +61,112 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   }
 }
 
+// Router projection for E > 64 experts, bfloat16 inputs: workgroup tile 64 tokens x 64 WE
+// experts, one wave per 64 experts (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), K walked in
+// slabs of 32 that are double-buffered in LDS with the next slab prefetched in registers.
+// Sharing each x slab across the workgroup's waves and each W_g slab across its 64 tokens
+// keeps the L2 traffic near one read of x plus one read of W_g per 64 tokens. grid.z splits
+// the reduction axis as in router_gemm_bf16_kernel.
+template <int WE>
+__global__ __launch_bounds__(64 * WE) void router_gemm_tiled_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, float* __restrict__ zpart,
+    int n_tokens, int d, int n_experts, int k_chunk) {
+  constexpr int kBMr = 64, kBEr = 64 * WE, kBKr = 32, kLd = kBKr + 8;  // LDS rows of 80 bytes
+  constexpr int kThreads = 64 * WE;
+  constexpr int kAPer = kBMr * 4 / kThreads;  // 16-byte chunks per thread per slab
+  constexpr int kBPer = kBEr * 4 / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBMr * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBEr * kLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kBMr, e0 = blockIdx.y * kBEr;
+  const int kb = blockIdx.z * k_chunk;
+  const int ke = min(d, kb + k_chunk);
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
+  const uint16_t* ws = reinterpret_cast<const uint16_t*>(wg);
+
+  uint4 ra[kAPer], rb[kBPer];
+  auto gload = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int idx = tid + i * kThreads, row = idx >> 2, kk = k + (idx & 3) * 8;
+      const int t = t0 + row;
+      ra[i] = (t < n_tokens && kk < ke) ? *reinterpret_cast<const uint4*>(xs + (size_t)t * d + kk)
+                                        : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int idx = tid + i * kThreads, row = idx >> 2, kk = k + (idx & 3) * 8;
+      const int e = e0 + row;
+      rb[i] = (e < n_experts && kk < ke) ? *reinterpret_cast<const uint4*>(ws + (size_t)e * d + kk)
+                                         : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kAPer; ++i) {
+      const int idx = tid + i * kThreads;
+      *reinterpret_cast<uint4*>(&sA[buf][(idx >> 2) * kLd + (idx & 3) * 8]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int idx = tid + i * kThreads;
+      *reinterpret_cast<uint4*>(&sB[buf][(idx >> 2) * kLd + (idx & 3) * 8]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  if (kb < ke) {
+    gload(kb);
+    lstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k = kb; k < ke; k += kBKr) {
+    const bool more = k + kBKr < ke;
+    if (more) gload(k + kBKr);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[2], fb[2];
+      const int kq = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(i * 32 + (lane & 31)) * kLd + kq]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wave * 64 + j * 32 + (lane & 31)) * kLd + kq]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // lane's element v of a 32 x 32 block: column lane & 31, row 8 (v >> 2) + 4 (lane >> 5) + (v & 3)
+  float* zp = zpart + (size_t)blockIdx.z * n_tokens * n_experts;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + wave * 64 + j * 32 + (lane & 31);
+    if (e >= n_experts) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (t < n_tokens) zp[(size_t)t * n_experts + e] = acc[i][j][v];
+      }
+  }
+}
+
 // Router projection for float32 inputs: one wave per token, lanes split the reduction axis,
 // float32 FMA accumulation, then a fixed butterfly sum per expert.
 __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
@@ -78,74 +186,100 @@ __global__ __launch_bounds__(256) void router_gemm_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-token routing. One wave per token; lane l holds experts l, l+64, ... (up to 16 each).
+// Per-token routing. A token is owned by a group of LPT lanes (LPT = E rounded up to a power
+// of two, at most 64); lane l of the group holds experts l, l + LPT, ... (EPL of them), so
+// one wave routes 64 / LPT tokens side by side and every cross-lane step stays in the group.
 // ---------------------------------------------------------------------------------------
-constexpr int kEpl = kMaxExperts / 64;  // experts per lane, upper bound
 
 // (score desc, id asc): a beats b when its score is larger, or equal with a lower id.
 MOE_DEV bool beats(float s, int id, float s2, int id2) { return s > s2 || (s == s2 && id < id2); }
 
-__global__ __launch_bounds__(256) void route_tokens_kernel(RouteArgs a) {
-  __shared__ float s_psum[4][kMaxExperts];
-  __shared__ int s_hist[kMaxExperts];
-  __shared__ float s_zl[4];
+template <int W> MOE_DEV float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+template <int W> MOE_DEV float group_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Waves per routing workgroup: 16, or 4 when every lane holds 16 experts (register budget).
+constexpr int route_waves(int epl) { return epl >= 16 ? 4 : 16; }
+
+template <int LPT, int EPL>
+__global__ __launch_bounds__(route_waves(EPL) * kWave) void route_tokens_kernel(RouteArgs a) {
+  constexpr int kRouteWaves = route_waves(EPL);
+  constexpr int kTpw = kWave / LPT;  // tokens routed side by side per wave
+  constexpr int kCols = LPT * EPL;   // expert slots of a token group
+  __shared__ float s_psum[kRouteWaves][kCols];
+  __shared__ int s_hist[kCols];
+  __shared__ float s_zl[kRouteWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int sub = lane & (LPT - 1);  // lane within the token's group
+  const int grp = lane / LPT;
   const int E = a.n_experts;
   const int k = a.top_k;
-  const int epl = (E + 63) >> 6;
+  const bool sigm = a.router == MOE_ROUTER_SIGMOID;
 
-  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += kRouteWaves * kWave) s_hist[e] = 0;
   __syncthreads();
 
-  float psum[kEpl];
+  float psum[EPL];
 #pragma unroll
-  for (int i = 0; i < kEpl; ++i) psum[i] = 0.f;
+  for (int i = 0; i < EPL; ++i) psum[i] = 0.f;
   float zl_acc = 0.f;
 
-  const int tok_begin = blockIdx.x * a.tokens_per_block + wave * a.tokens_per_wave;
-  const int tok_end = min((int)a.n_tokens, tok_begin + a.tokens_per_wave);
-  for (int t = tok_begin; t < tok_end; ++t) {
-    float z[kEpl], s[kEpl], ex[kEpl];
+  const int wave_tok0 = blockIdx.x * a.tokens_per_block + wave * a.tokens_per_wave;
+  // Uniform trip count over the wave: groups past the last token compute on zeros and
+  // write nothing.
+  for (int it = 0; it < a.tokens_per_wave; it += kTpw) {
+    const int t = wave_tok0 + it + grp;
+    const bool tok = t < a.n_tokens;
+    float z[EPL], s[EPL], ex[EPL];
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kEpl; ++i) {
-      const int e = lane + 64 * i;
-      z[i] = -INFINITY;
-      if (i < epl && e < E) {
-        float v = 0.f;
+    for (int i = 0; i < EPL; ++i) {
+      const int e = sub + LPT * i;
+      const bool ok = e < E;
+      float v = 0.f;
+      if (ok && tok) {
         for (int sp = 0; sp < a.n_split; ++sp) v += a.zpart[((size_t)sp * a.n_tokens + t) * E + e];
         if (a.logit_bias) v += a.logit_bias[e];
-        z[i] = v;
-        m = fmaxf(m, v);
         if (a.logits_out) a.logits_out[(size_t)t * E + e] = v;
       }
+      z[i] = ok ? v : -INFINITY;
+      m = fmaxf(m, z[i]);
     }
-    m = wave_max(m);
+    m = group_max<LPT>(m);
     float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kEpl; ++i) {
-      ex[i] = (i < epl && lane + 64 * i < E) ? expf(z[i] - m) : 0.f;
+    for (int i = 0; i < EPL; ++i) {
+      ex[i] = (sub + LPT * i < E) ? expf(z[i] - m) : 0.f;
       lsum += ex[i];
     }
-    const float sum = wave_sum(lsum);
+    const float sum = group_sum<LPT>(lsum);
     const float inv_sum = 1.0f / sum;
-    if (lane == 0) {
+    if (tok && sub == 0) {
       const float lse = m + logf(sum);
       zl_acc += lse * lse;
     }
 #pragma unroll
-    for (int i = 0; i < kEpl; ++i) {
-      const int e = lane + 64 * i;
-      const bool ok = i < epl && e < E;
-      psum[i] += ok ? ex[i] * inv_sum : 0.f;
-      float sc = (a.router == MOE_ROUTER_SIGMOID) ? sigmoid_f(z[i]) : z[i];
+    for (int i = 0; i < EPL; ++i) {
+      const int e = sub + LPT * i;
+      const bool ok = e < E;
+      psum[i] += (ok && tok) ? ex[i] * inv_sum : 0.f;
+      float sc = sigm ? sigmoid_f(z[i]) : z[i];
       if (ok && a.sel_bias) sc += a.sel_bias[e];
       if (sc != sc) sc = -INFINITY;  // a NaN score ranks last, so k valid ids are still chosen
       s[i] = ok ? sc : -INFINITY;
     }
 
-    // k rounds of a wave arg-max on (score desc, id asc); one more for the margin.
+    // k rounds of a group arg-max on (score desc, id asc); one more for the margin. Some
+    // lane of the group always holds an untaken valid expert (k <= E), and -inf loses
+    // only to a lower id, so the winner is always a valid id.
     uint32_t taken = 0;
     int my_id = -1;
     float my_u = 0.f, last_s = 0.f, gap = INFINITY;
@@ -154,17 +288,17 @@ __global__ __launch_bounds__(256) void route_tokens_kernel(RouteArgs a) {
       float bs = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int i = 0; i < kEpl; ++i) {
-        const int e = lane + 64 * i;
-        if (i < epl && e < E && !((taken >> i) & 1u) && beats(s[i], e, bs, bi)) {
+      for (int i = 0; i < EPL; ++i) {
+        const int e = sub + LPT * i;
+        if (e < E && !((taken >> i) & 1u) && beats(s[i], e, bs, bi)) {
           bs = s[i];
           bi = e;
         }
       }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float os = __shfl_xor(bs, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
+      for (int o = LPT / 2; o >= 1; o >>= 1) {
+        const float os = __shfl_xor(bs, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
         if (beats(os, oi, bs, bi)) {
           bs = os;
           bi = oi;
@@ -176,14 +310,15 @@ __global__ __launch_bounds__(256) void route_tokens_kernel(RouteArgs a) {
       }
       last_s = bs;
       // raw gate of the chosen expert: exp(z - m) for the softmax routers, sigmoid(z) else
-      const int slot = bi >> 6;
+      const int slot = bi / LPT;
+      const int owner = bi & (LPT - 1);
       float mine = 0.f;
 #pragma unroll
-      for (int i = 0; i < kEpl; ++i)
-        if (i == slot) mine = (a.router == MOE_ROUTER_SIGMOID) ? sigmoid_f(z[i]) : ex[i];
-      const float u = __shfl(mine, bi & 63, 64);
-      if (lane == (bi & 63)) taken |= 1u << slot;
-      if (lane == j) {
+      for (int i = 0; i < EPL; ++i)
+        if (i == slot) mine = sigm ? sigmoid_f(z[i]) : ex[i];
+      const float u = __shfl(mine, grp * LPT + owner, kWave);
+      if (sub == owner) taken |= 1u << slot;
+      if (sub == j) {
         my_id = bi;
         my_u = u;
       }
@@ -191,88 +326,203 @@ __global__ __launch_bounds__(256) void route_tokens_kernel(RouteArgs a) {
     // gates ([L7.8] §2.1): the softmax routers renormalise exp(z - m) over the chosen set
     // (= p_T / sum p_T = softmax over the chosen logits); without renormalisation the
     // softmax_topk gate is p itself. The sigmoid router renormalises sigmoid(z_T).
-    const float usum = wave_sum(lane < k ? my_u : 0.f);
-    if (lane < k) {
+    const float usum = group_sum<LPT>(sub < k ? my_u : 0.f);
+    if (tok && sub < k) {
       float w;
       if (a.router == MOE_ROUTER_TOPK_SOFTMAX || a.norm_topk) w = my_u / usum;
       else if (a.router == MOE_ROUTER_SOFTMAX_TOPK) w = my_u * inv_sum;
       else w = my_u;
       w *= a.routed_scaling;
-      a.topk_ids[(size_t)t * k + lane] = my_id;
-      a.topk_w[(size_t)t * k + lane] = w;
-      if (my_id >= 0 && my_id < E) atomicAdd(&s_hist[my_id], 1);  // integer adds: order-independent
+      a.topk_ids[(size_t)t * k + sub] = my_id;
+      a.topk_w[(size_t)t * k + sub] = w;
+      atomicAdd(&s_hist[my_id], 1);  // integer adds: order-independent
     }
-    if (a.gap_out && lane == 0) a.gap_out[t] = gap;
+    if (a.gap_out && tok && sub == 0) a.gap_out[t] = gap;
   }
 
-  // Deterministic block partials: waves' per-expert sums combined in wave order.
+  // Deterministic block partials: the groups of a wave combined by a fixed butterfly, then
+  // the waves in wave order.
 #pragma unroll
-  for (int i = 0; i < kEpl; ++i) {
-    const int e = lane + 64 * i;
-    if (i < epl && e < E) s_psum[wave][e] = psum[i];
+  for (int i = 0; i < EPL; ++i) {
+#pragma unroll
+    for (int o = 32; o >= LPT; o >>= 1) psum[i] += __shfl_xor(psum[i], o, kWave);
+    const int e = sub + LPT * i;
+    if (grp == 0 && e < E) s_psum[wave][e] = psum[i];
   }
-  if (lane == 0) s_zl[wave] = zl_acc;
+  const float zl = wave_sum(zl_acc);
+  if (lane == 0) s_zl[wave] = zl;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    a.part_p[(size_t)blockIdx.x * E + e] = ((s_psum[0][e] + s_psum[1][e]) + s_psum[2][e]) + s_psum[3][e];
+  for (int e = threadIdx.x; e < E; e += kRouteWaves * kWave) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) v += s_psum[w][e];
+    a.part_p[(size_t)blockIdx.x * E + e] = v;
     a.part_hist[(size_t)blockIdx.x * E + e] = s_hist[e];
   }
-  if (threadIdx.x == 0) a.part_zl[blockIdx.x] = ((s_zl[0] + s_zl[1]) + s_zl[2]) + s_zl[3];
+  if (threadIdx.x == 0) {
+    float v = 0.f;
+    for (int w = 0; w < kRouteWaves; ++w) v += s_zl[w];
+    a.part_zl[blockIdx.x] = v;
+  }
 }
 
-// Final statistics: counts, f, P, L = E sum f P and the z-loss, reduced over the block
-// partials in block order, in double precision, by one workgroup.
-__global__ __launch_bounds__(256) void route_finalize_kernel(
-    const float* __restrict__ part_p, const int* __restrict__ part_hist,
-    const float* __restrict__ part_zl, int n_blocks, long long n_tokens, int E,
-    int* __restrict__ counts, float* __restrict__ stats) {
-  __shared__ double s_red[256];
-  const double inv_n = n_tokens > 0 ? 1.0 / (double)n_tokens : 0.0;
-  double fp_acc = 0.0;
-  for (int e = threadIdx.x; e < E; e += 256) {
-    long long c = 0;
-    double p = 0.0;
-    for (int b = 0; b < n_blocks; ++b) {
-      c += part_hist[(size_t)b * E + e];
-      p += (double)part_p[(size_t)b * E + e];
-    }
-    counts[e] = (int)c;
-    const double f = (double)c * inv_n;
-    const double P = p * inv_n;
-    stats[e] = (float)f;
-    stats[E + e] = (float)P;
-    fp_acc += f * P;
-  }
-  s_red[threadIdx.x] = fp_acc;
+// ---------------------------------------------------------------------------------------
+// Final reduction over the routing blocks, one workgroup of 1024 threads. Thread (g, e)
+// with g < G = 1024 / E sums expert e's partials over a contiguous range of blocks
+// (coalesced over e); the G range sums are then combined in a fixed order, so counts, f, P,
+// L and the z-loss are bitwise reproducible. With offsets != null it goes on to the
+// dispatch scan of [L7.8] §2.2 over the same blocks: offsets = exclusive scan of counts,
+// and base[b][e] = offsets[e] + (assignments of expert e in blocks before b), the first
+// sorted slot of block b's run of expert e; then the grouped GEMM's m-tile table.
+// ---------------------------------------------------------------------------------------
+constexpr int kFinThreads = 1024;
+
+MOE_DEV double block_sum_f64(double v, double* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
-    if (threadIdx.x < o) s_red[threadIdx.x] += s_red[threadIdx.x + o];
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  double r = 0.0;
+  for (int w = 0; w < kFinThreads / kWave; ++w) r += s_red[w];
+  return r;
+}
+
+__global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArgs a) {
+  __shared__ double s_p[kFinThreads];
+  __shared__ int s_c[kFinThreads];
+  __shared__ int s_cs[kFinThreads];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_scan[kMaxExperts];
+  __shared__ double s_red[kFinThreads / kWave];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int E = a.n_experts;
+  const int nb = a.n_blocks;
+  const int G = kFinThreads / E;
+  const int g = tid / E;
+  const int e = tid - g * E;
+  const bool act = g < G;
+  const int b0 = act ? (int)((long long)nb * g / G) : 0;
+  const int b1 = act ? (int)((long long)nb * (g + 1) / G) : 0;
+  if (tid == 0) s_bad = 0;
+
+  int c = 0;
+  double p = 0.0;
+#pragma unroll 8
+  for (int b = b0; b < b1; ++b) {
+    c += a.part_hist[(size_t)b * E + e];
+    p += (double)a.part_p[(size_t)b * E + e];
+  }
+  s_c[tid] = c;
+  s_cs[tid] = c;
+  s_p[tid] = p;
+  __syncthreads();
+  // P: pairwise tree over the groups; counts: inclusive scan over the groups (integers).
+  int span = 1;
+  while (span < G) span <<= 1;
+  for (int h = span >> 1; h >= 1; h >>= 1) {
+    if (act && g < h && g + h < G) s_p[tid] += s_p[tid + h * E];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    stats[2 * E] = (float)((double)E * s_red[0]);
-    double zl = 0.0;
-    for (int b = 0; b < n_blocks; ++b) zl += (double)part_zl[b];
-    stats[2 * E + 1] = (float)(zl * inv_n);
+  for (int o = 1; o < G; o <<= 1) {
+    const int v = (act && g >= o) ? s_cs[tid - o * E] : 0;
+    __syncthreads();
+    s_cs[tid] += v;
+    __syncthreads();
   }
+  const double inv_n = a.n_tokens > 0 ? 1.0 / (double)a.n_tokens : 0.0;
+  int total = 0;
+  double fp = 0.0;
+  if (tid < E) {
+    total = s_cs[(G - 1) * E + tid];
+    const double f = (double)total * inv_n;
+    const double P = s_p[tid] * inv_n;
+    a.counts[tid] = total;
+    a.stats[tid] = (float)f;
+    a.stats[E + tid] = (float)P;
+    fp = f * P;
+  }
+  const double fp_sum = block_sum_f64(fp, s_red);
+  double zl = 0.0;
+  for (int b = tid; b < nb; b += kFinThreads) zl += (double)a.part_zl[b];
+  const double zl_sum = block_sum_f64(zl, s_red);
+  if (tid == 0) {
+    a.stats[2 * E] = (float)((double)E * fp_sum);
+    a.stats[2 * E + 1] = (float)(zl_sum * inv_n);
+  }
+  if (!a.offsets) return;  // uniform over the block
+
+  // offsets: exclusive scan of the counts over the experts
+  if (tid < E) s_scan[tid] = total;
+  __syncthreads();
+  for (int o = 1; o < E; o <<= 1) {
+    const int v = (tid < E && tid >= o) ? s_scan[tid - o] : 0;
+    __syncthreads();
+    if (tid < E) s_scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    s_off[tid] = s_scan[tid] - total;
+    a.offsets[tid] = s_scan[tid] - total;
+    if (tid == E - 1) {
+      s_off[E] = s_scan[tid];
+      a.offsets[E] = s_scan[tid];
+    }
+  }
+  __syncthreads();
+  // per-block bases: this thread's block range continues after the earlier groups' rows
+  if (act) {
+    int run = s_off[e] + (s_cs[tid] - s_c[tid]);
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
+      a.base[(size_t)b * E + e] = run;
+      run += a.part_hist[(size_t)b * E + e];
+    }
+  }
+  if (a.tiles) {
+    const int lo = tid < E ? s_off[tid] : 0;
+    const int hi = tid < E ? s_off[tid + 1] : 0;
+    build_tile_table(lo, hi, E, s_off[E], a.tile_bm, a.max_tiles, a.tiles, s_scan, &s_bad);
+  }
+  __syncthreads();
+  if (tid == 0 && a.err) a.err[0] = s_bad ? MOE_ERR_INVALID_ARG : 0;
 }
 
 // ---------------------------------------------------------------------------------------
 // Host-side launch sequence (no synchronisation).
 // ---------------------------------------------------------------------------------------
+// Experts per workgroup of the tiled router projection (E > 64).
+static int router_tile_experts(int E) { return E <= 128 ? 128 : 256; }
+
 RoutePlan plan_route(const moe_config& c) {
   RoutePlan p{};
   const long long N = c.n_tokens;
-  p.tokens_per_wave = 8;
-  p.tokens_per_block = 4 * p.tokens_per_wave;
+  const int E = c.n_experts;
+  p.lpt = 1;
+  while (p.lpt < E && p.lpt < kWave) p.lpt <<= 1;
+  p.epl = 1;
+  while (p.lpt * p.epl < E) p.epl <<= 1;
+  // Tokens per wave: enough that the per-block partial arrays ([blocks][E]) stay within
+  // 64K entries, which the single-workgroup final reduction reads twice.
+  const int tpw = kWave / p.lpt;
+  const int waves = route_waves(p.epl);
+  const long long per_block_min = (long long)waves * tpw;
+  long long iters = std::max<long long>(1, N * E / (65536ll * per_block_min));
+  while (((N + per_block_min * iters - 1) / (per_block_min * iters)) * E > 65536) ++iters;
+  p.tokens_per_wave = (int)(tpw * iters);
+  p.tokens_per_block = waves * p.tokens_per_wave;
   p.n_blocks = (int)((N + p.tokens_per_block - 1) / p.tokens_per_block);
   if (c.dtype == MOE_BF16) {
-    // Split the reduction so that the projection launches several waves of workgroups per
-    // CU even for a few thousand tokens; each split writes its own partial z.
-    const int e_blocks = (c.n_experts + 255) / 256;
+    // Split the reduction so that the projection launches several workgroups per CU even
+    // for a few thousand tokens; each split writes its own partial z.
+    const bool tiled = E > 64;
+    const int e_blocks = tiled ? (E + router_tile_experts(E) - 1) / router_tile_experts(E) : (E + 255) / 256;
     const long long base = ((N + 63) / 64) * e_blocks;
+    const long long want = tiled ? 512 : 1024;
     int split = 1;
-    while (split < 8 && base * split < 1024 && (c.d_model / (split * 2)) >= 256) split *= 2;
+    while (split < 8 && base * split < want && (c.d_model / (split * 2)) >= 256) split *= 2;
     p.n_split = split;
     p.k_chunk = ((c.d_model / split) + 31) / 32 * 32;
   } else {
@@ -297,24 +547,38 @@ void carve_route(const moe_config& c, WsCarver& w, WsLayout* L) {
   }
 }
 
+// Per-block dispatch bases of the fused path ([route blocks][E]), carved by moe_forward.
+size_t route_base_ints(const moe_config& c) { return (size_t)plan_route(c).n_blocks * c.n_experts; }
+int route_tokens_per_block(const moe_config& c) { return plan_route(c).tokens_per_block; }
+
+template <int LPT, int EPL>
+static void launch_tokens(const RoutePlan& p, const RouteArgs& ra, hipStream_t stream) {
+  route_tokens_kernel<LPT, EPL><<<p.n_blocks, route_waves(EPL) * kWave, 0, stream>>>(ra);
+}
+
 hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_router,
                         const float* logit_bias, const float* sel_bias, int32_t* topk_ids,
                         float* topk_w, int32_t* counts, float* stats, float* logits_out,
-                        float* gap_out, hipStream_t stream) {
+                        float* gap_out, bool fuse_dispatch, hipStream_t stream) {
   const RoutePlan p = plan_route(c);
   const int N = (int)c.n_tokens, E = c.n_experts, d = c.d_model;
   if (N > 0) {
     if (c.dtype == MOE_BF16) {
-      const int eb = (E <= 16) ? 1 : (E <= 32) ? 2 : (E <= 64) ? 4 : (E <= 128) ? 8 : 16;
-      dim3 grid((N + 63) / 64, (E + 16 * eb - 1) / (16 * eb), p.n_split);
       auto xb = static_cast<const bf16_t*>(x);
       auto wb = static_cast<const bf16_t*>(w_router);
-      switch (eb) {
-        case 1: router_gemm_bf16_kernel<1><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-        case 2: router_gemm_bf16_kernel<2><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-        case 4: router_gemm_bf16_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-        case 8: router_gemm_bf16_kernel<8><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-        default: router_gemm_bf16_kernel<16><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
+      if (E > 64) {
+        const int te = router_tile_experts(E);
+        dim3 grid((N + 63) / 64, (E + te - 1) / te, p.n_split);
+        if (te == 128) router_gemm_tiled_kernel<2><<<grid, 128, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk);
+        else router_gemm_tiled_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk);
+      } else {
+        const int eb = (E <= 16) ? 1 : (E <= 32) ? 2 : 4;
+        dim3 grid((N + 63) / 64, (E + 16 * eb - 1) / (16 * eb), p.n_split);
+        switch (eb) {
+          case 1: router_gemm_bf16_kernel<1><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
+          case 2: router_gemm_bf16_kernel<2><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
+          default: router_gemm_bf16_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
+        }
       }
     } else {
       router_gemm_f32_kernel<<<(N + 3) / 4, 256, 0, stream>>>(
@@ -340,10 +604,38 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
     ra.part_p = L.part_p;
     ra.part_hist = L.part_hist;
     ra.part_zl = L.part_zl;
-    route_tokens_kernel<<<p.n_blocks, 256, 0, stream>>>(ra);
+    switch (p.lpt * 100 + p.epl) {
+      case 101: launch_tokens<1, 1>(p, ra, stream); break;
+      case 201: launch_tokens<2, 1>(p, ra, stream); break;
+      case 401: launch_tokens<4, 1>(p, ra, stream); break;
+      case 801: launch_tokens<8, 1>(p, ra, stream); break;
+      case 1601: launch_tokens<16, 1>(p, ra, stream); break;
+      case 3201: launch_tokens<32, 1>(p, ra, stream); break;
+      case 6401: launch_tokens<64, 1>(p, ra, stream); break;
+      case 6402: launch_tokens<64, 2>(p, ra, stream); break;
+      case 6404: launch_tokens<64, 4>(p, ra, stream); break;
+      case 6408: launch_tokens<64, 8>(p, ra, stream); break;
+      default: launch_tokens<64, 16>(p, ra, stream); break;
+    }
   }
-  route_finalize_kernel<<<1, 256, 0, stream>>>(L.part_p, L.part_hist, L.part_zl, p.n_blocks,
-                                                c.n_tokens, E, counts, stats);
+  FinalizeArgs fa{};
+  fa.part_p = L.part_p;
+  fa.part_hist = L.part_hist;
+  fa.part_zl = L.part_zl;
+  fa.n_blocks = p.n_blocks;
+  fa.n_tokens = c.n_tokens;
+  fa.n_experts = E;
+  fa.counts = counts;
+  fa.stats = stats;
+  if (fuse_dispatch) {
+    fa.offsets = L.offsets;
+    fa.base = L.fbase;
+    fa.err = L.err;
+    fa.tiles = L.tiles;
+    fa.tile_bm = ffn_tile_rows(c);
+    fa.max_tiles = ffn_max_m_tiles(c);
+  }
+  route_finalize_kernel<<<1, kFinThreads, 0, stream>>>(fa);
   return hipGetLastError();
 }
 
