@@ -175,6 +175,17 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 
+/* Aux-free load balancing, one update step ([L7.8] §2.5): with load_e = counts[e] and
+ * mean = sum_e load_e / E,
+ *     sel_bias[e] <- sel_bias[e] + rate * sign(mean - load_e)
+ * so under-loaded experts become easier to select. The sign is decided exactly in integers
+ * (sign(sum - E load_e)); the add is one float32 addition per expert. The bias enters
+ * selection only (moe_route / moe_forward sel_bias), never the gates.
+ * In: counts [E] int32 (e.g. moe_route's output for the last batch); rate: finite.
+ * In/out: sel_bias [E] float32. No workspace. */
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float* sel_bias,
+                           float rate, void* stream);
+
 /* Synchronises `stream`, then reads and clears the device error word at the start of `ws`:
  * MOE_ERR_BAD_EXPERT_ID if the last dispatch on this workspace met an out-of-range id,
  * MOE_ERR_INVALID_ARG if an expert FFN call on it met a malformed offsets array (the call

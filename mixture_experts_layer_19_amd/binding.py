@@ -113,9 +113,11 @@ def lib():
     L.moe_forward.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               ctypes.c_size_t, _P, _P]
     L.moe_get_device_error.argtypes = [_P, _P]
+    L.moe_update_bias.argtypes = [S, _P, _P, ctypes.c_float, _P]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
-    for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error"):
+    for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
+                 "moe_update_bias"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -295,6 +297,15 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
                            ev, _stream())
     _check(st, "moe_forward")
     return out
+
+
+def moe_update_bias(cfg: LayerConfig, counts, sel_bias, rate: float):
+    """One aux-free balancing step on sel_bias in place (float32 [E]) from counts (int32 [E])."""
+    _want(counts, "counts", (cfg.n_experts,), torch.int32)
+    _want(sel_bias, "sel_bias", (cfg.n_experts,), torch.float32)
+    st = lib().moe_update_bias(ctypes.byref(cfg.struct()), _ptr(counts), _ptr(sel_bias), float(rate), _stream())
+    _check(st, "moe_update_bias")
+    return sel_bias
 
 
 def moe_get_device_error(ws: torch.Tensor) -> int:

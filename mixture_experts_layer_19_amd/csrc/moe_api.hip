@@ -250,6 +250,15 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   return mark(5);
 }
 
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float* sel_bias, float rate,
+                           void* stream) {
+  MOE_TRY(check_config(cfg, false));
+  MOE_TRY(need_4(counts));
+  MOE_TRY(need_4(sel_bias));
+  if (!std::isfinite(rate)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_update_bias(*cfg, counts, sel_bias, rate, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_get_device_error(void* ws, void* stream) {
   if (!ws) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

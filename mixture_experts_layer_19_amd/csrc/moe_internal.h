@@ -183,6 +183,8 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
 hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t* offsets,
                            const void* w2, const void* b2, const float* gate_sorted,
                            void* y_sorted, hipStream_t stream);
+hipError_t launch_update_bias(const moe_config& c, const int32_t* counts, float* bias, float rate,
+                              hipStream_t stream);
 hipError_t launch_combine(const moe_config& c, const void* y_sorted, const float* topk_w,
                           const int32_t* inv_perm, void* y, hipStream_t stream);
 

@@ -491,6 +491,35 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
 }
 
 // ---------------------------------------------------------------------------------------
+// Aux-free bias step ([L7.8] §2.5): b_e += rate * sign(mean load - load_e). One workgroup;
+// the sign is taken exactly as sign(sum - E load_e) in 64-bit integers.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void update_bias_kernel(const int32_t* __restrict__ counts, float* __restrict__ bias,
+                                                           int E, float rate) {
+  __shared__ long long s_part[1024 / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long c = 0;
+  for (int e = tid; e < E; e += 1024) c += counts[e];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, kWave);
+  if (lane == 0) s_part[wave] = c;
+  __syncthreads();
+  long long sum = 0;
+  for (int w = 0; w < 1024 / kWave; ++w) sum += s_part[w];
+  for (int e = tid; e < E; e += 1024) {
+    const long long d = sum - (long long)E * counts[e];
+    const float sg = d > 0 ? 1.f : (d < 0 ? -1.f : 0.f);
+    bias[e] = bias[e] + rate * sg;
+  }
+}
+
+hipError_t launch_update_bias(const moe_config& c, const int32_t* counts, float* bias, float rate,
+                              hipStream_t stream) {
+  update_bias_kernel<<<1, 1024, 0, stream>>>(counts, bias, c.n_experts, rate);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // Host-side launch sequence (no synchronisation).
 // ---------------------------------------------------------------------------------------
 // Experts per workgroup of the tiled router projection (E > 64).

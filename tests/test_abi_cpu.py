@@ -21,7 +21,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-               "moe_workspace_size", "moe_get_device_error", "moe_status_string"):
+               "moe_workspace_size", "moe_get_device_error", "moe_status_string", "moe_update_bias"):
         assert fn in names
 
 
@@ -104,6 +104,19 @@ def test_null_and_misaligned_pointers_and_small_workspace():
     ev = (ctypes.c_void_p * 6)(f, f, f, None, f, f)
     st = lib.moe_forward(ctypes.byref(cfg), f, f, None, None, f, f, None, f, None, f, f, f, f, f, f, 1 << 40, ev, None)
     assert st == B.MOE_ERR_INVALID_ARG
+
+
+def test_update_bias_host_validation():
+    lib = B.lib()
+    cfg = MIXTRAL.struct()
+    f = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10002)
+    assert lib.moe_update_bias(ctypes.byref(cfg), None, f, ctypes.c_float(0.1), None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(cfg), f, None, ctypes.c_float(0.1), None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(cfg), f, mis, ctypes.c_float(0.1), None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_update_bias(ctypes.byref(cfg), f, f, ctypes.c_float(float("inf")), None) == B.MOE_ERR_INVALID_ARG
+    bad = B.LayerConfig(8192, 4096, 2048, 2, 14336).struct()
+    assert lib.moe_update_bias(ctypes.byref(bad), f, f, ctypes.c_float(0.1), None) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_workload_recipes_are_seeded_and_shaped():

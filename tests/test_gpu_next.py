@@ -1,0 +1,88 @@
+"""GPU parity of the rows beyond the forward hot path: the aux-free bias update
+("Mixture of Experts: routing, sorted dispatch, Switch aux loss, aux-free bias" (L7.8) §2.5)
+against the CPU oracle, bit-exact."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import compare_ids, f64, spec_of
+from mixture_experts_layer_19_amd import binding as B
+from mixture_experts_layer_19_amd import workload as W
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+@pytest.mark.parametrize("E,rate,seed", [(1, 0.1, 0), (4, 0.01, 1), (128, 1e-3, 2), (256, 0.5, 3), (1024, 2.0, 4)])
+def test_update_bias_bit_exact(E, rate, seed):
+    say(f"[update_bias] E={E} rate={rate}")
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, 50, size=E).astype(np.int32)
+    counts[: E // 3] = counts[0]                 # ties with each other
+    if E % 2 == 0:
+        counts[-1] = counts.sum() // E           # possibly equal to the mean
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    cfg = B.LayerConfig(16, 64, E, 1, 64)
+    b_dev = torch.from_numpy(bias).cuda()
+    B.moe_update_bias(cfg, torch.from_numpy(counts).cuda(), b_dev, rate)
+    want = O.update_bias(bias.astype(np.float64), counts, float(np.float32(rate))).astype(np.float32)
+    assert np.array_equal(b_dev.cpu().numpy(), want)
+
+
+def test_update_bias_balanced_load_is_a_fixed_point():
+    E = 16
+    cfg = B.LayerConfig(16, 64, E, 2, 64)
+    b = torch.linspace(-0.2, 0.2, E, device="cuda")
+    before = b.clone()
+    B.moe_update_bias(cfg, torch.full((E,), 7, dtype=torch.int32, device="cuda"), b, 0.3)
+    assert torch.equal(b, before)
+
+
+def test_update_bias_rejects_bad_rate():
+    cfg = B.LayerConfig(16, 64, 8, 2, 64)
+    with pytest.raises(ValueError):
+        B.moe_update_bias(cfg, torch.zeros(8, dtype=torch.int32, device="cuda"),
+                          torch.zeros(8, device="cuda"), float("nan"))
+
+
+def test_bias_loop_spreads_a_skewed_sigmoid_router():
+    """Route -> counts -> bias step, repeated; each step the oracle routes with the device's
+    current bias, and the next bias must equal the oracle's update from the device's counts."""
+    w = W.WORKLOADS["deepseek_v3"].scaled(n_tokens=512, d_model=256, n_experts=32, top_k=4, d_ff=64)
+    cfg = w.cfg
+    inp = W.make_inputs(w, seed=5)
+    lb = torch.zeros(cfg.n_experts, dtype=torch.float32, device="cuda")
+    lb[:4] = 2.0                                  # four experts the router strongly prefers
+    bias = torch.zeros(cfg.n_experts, dtype=torch.float32, device="cuda")
+    spec = spec_of(cfg)
+    x64, wg64 = f64(inp["x"]), f64(inp["w_router"])
+    spreads = []
+    rate = 0.05
+    for step in range(40):
+        r_dev = B.moe_route(cfg, inp["x"], inp["w_router"], logit_bias=lb, sel_bias=bias, want_gap=True)
+        torch.cuda.synchronize()
+        counts = r_dev["counts"].cpu().numpy()
+        r = O.route(x64, wg64, spec, f64(lb), f64(bias))
+        near, intra, agree = compare_ids(r_dev["topk_ids"].cpu().numpy(), r, cfg.top_k)
+        if agree.all():
+            assert np.array_equal(counts, np.bincount(r.ids.reshape(-1), minlength=cfg.n_experts)), step
+        b_host = bias.cpu().numpy()
+        B.moe_update_bias(cfg, r_dev["counts"], bias, rate)
+        want = O.update_bias(b_host.astype(np.float64), counts, float(np.float32(rate))).astype(np.float32)
+        assert np.array_equal(bias.cpu().numpy(), want), step
+        spreads.append(int(counts.max() - counts.min()))
+    say(f"    max-min load per step: {spreads[:5]} ... {spreads[-5:]}")
+    assert np.mean(spreads[-10:]) < 0.5 * spreads[0]
