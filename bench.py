@@ -32,10 +32,12 @@ def algorithmic(cfg):
     A = N * k
     b = 2 if cfg.dtype == "bf16" else 4
     m_up = 2 if cfg.act == "swiglu" else 1
+    F = cfg.d_ff_shared
     return {
         "router_flops": 2 * N * d * E,
         "up_flops": 2 * A * d * f * m_up,
         "down_flops": 2 * A * f * d,
+        "shared_flops": 2 * N * d * F * m_up + 2 * N * F * d,
         # dispatch: read x once, write x_sorted, ids in / perm / inv_perm (int32)
         "dispatch_bytes": N * d * b + A * d * b + 3 * A * 4,
         # combine (gates already applied upstream): read y_sorted and inv_perm, write y
@@ -76,6 +78,8 @@ def cpu_baseline(w, inp, n_sample=0, target_s=15.0):
     params = {"w_g": f64(inp["w_router"])}
     for name in ("w1", "w3", "w2", "b1", "b2"):
         params[name] = None if inp[name] is None else [f64(inp[name][e]) for e in range(cfg.n_experts)]
+    for name, t in (inp.get("shared") or {}).items():
+        params[name] = f64(t)
     spec = O.Spec(n_experts=cfg.n_experts, top_k=cfg.top_k, router=cfg.router, norm_topk=cfg.norm_topk,
                   routed_scaling=cfg.routed_scaling, act=cfg.act)
     lb, sb = f64(inp["logit_bias"]), f64(inp["sel_bias"])
@@ -140,7 +144,7 @@ def main():
     }
     call = lambda ev=None: B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"],
                                          inp["b1"], inp["b2"], inp["logit_bias"], inp["sel_bias"],
-                                         ws=ws, out=out, stage_events=ev)
+                                         shared=inp["shared"], ws=ws, out=out, stage_events=ev)
     for _ in range(args.warmup):
         call()
     events = [B.HipEvents(6) for _ in range(args.steps)]
@@ -158,7 +162,7 @@ def main():
     fwd_ms_events = sum(stage_ms.values())
     ms_per_step = wall * 1e3 / args.steps
     work = algorithmic(cfg)
-    flops = work["router_flops"] + work["up_flops"] + work["down_flops"]
+    flops = work["router_flops"] + work["up_flops"] + work["down_flops"] + work["shared_flops"]
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
     up_tflops = work["up_flops"] / (stage_ms["expert_up"] * 1e-3) / 1e12
     stats = out["stats"].cpu().numpy()
@@ -187,7 +191,8 @@ def main():
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "stage_rates": {
             "expert_up_tflops": up_tflops,
-            "expert_down_tflops": work["down_flops"] / (stage_ms["expert_down"] * 1e-3) / 1e12,
+            # the down stage also runs the shared expert, when there is one
+            "expert_down_tflops": (work["down_flops"] + work["shared_flops"]) / (stage_ms["expert_down"] * 1e-3) / 1e12,
             "dispatch_gbs": work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9,
             "combine_gbs": work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9,
         },

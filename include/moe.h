@@ -75,7 +75,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Which call a workspace is sized for. */
 typedef enum {
-  MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_COMBINE = 3, MOE_OP_FORWARD = 4
+  MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_COMBINE = 3, MOE_OP_FORWARD = 4,
+  MOE_OP_SHARED_FFN = 5
 } moe_op;
 
 typedef struct {
@@ -90,6 +91,8 @@ typedef struct {
   int32_t has_bias;     /* 1: b1 [E,d_ff] and b2 [E,d] are given (GELU only) */
   int32_t dtype;        /* moe_dtype: element type T */
   float routed_scaling; /* every gate is multiplied by this after renormalisation ([L7.8] §2.1) */
+  int32_t d_ff_shared;  /* hidden width S f of the shared expert(s), 0 = none ([L7.8] §2.1:
+                           S shared experts of width f are one MLP of width S f; [RB-15] §15.4) */
 } moe_config;
 
 /* Number of statistics floats moe_route / moe_forward write: f[E], P[E], L, z_loss. */
@@ -153,25 +156,42 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int
                           const void* w2, const void* b2, const float* gate_sorted,
                           void* y_sorted, void* ws, size_t ws_bytes, void* stream);
 
-/* Combine ([L7.8] §2.2, §3): y[n] = sum_{j<k} g_{n,j} y_sorted[inv_perm[n*k+j]], summed in
- * float32 with j ascending and rounded to T once; g = topk_w [N,k] float32, or 1 when
- * topk_w is NULL (y_sorted already gate-scaled). Assignments with inv_perm outside [0, A)
- * contribute nothing. */
+/* Combine ([L7.8] §2.2, §3): y[n] = sum_{j<k} g_{n,j} y_sorted[inv_perm[n*k+j]] (+ y_add[n]),
+ * summed in float32 with j ascending, then y_add, and rounded to T once; g = topk_w [N,k]
+ * float32, or 1 when topk_w is NULL (y_sorted already gate-scaled). y_add [N,d] T or NULL:
+ * a term every token receives with weight 1 (the shared expert's output). Assignments with
+ * inv_perm outside [0, A) contribute nothing. */
 moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const float* topk_w,
-                       const int32_t* inv_perm, void* y, void* stream);
+                       const int32_t* inv_perm, const void* y_add, void* y, void* stream);
+
+/* The shared expert(s) ([L7.8] §2.1 Shared(x); [RB-15] §15.4): one dense MLP of width
+ * F = cfg->d_ff_shared (> 0) over all N tokens, same activation as the routed experts:
+ *   GELU:   y_shared = W2s gelu(W1s x + b1s) + b2s      (biases iff has_bias)
+ *   SwiGLU: y_shared = W2s (silu(W1s x) * (W3s x))
+ * In: x [N,d] T; s_w1 [F,d] T; s_w3 [F,d] T (SwiGLU) or NULL; s_b1 [F] T, s_b2 [d] T (GELU
+ * with has_bias) or NULL; s_w2 [d,F] T. Out: y_shared [N,d] T (bf16: h rounded to bf16, as
+ * for the routed experts). ws: moe_workspace_size(cfg, MOE_OP_SHARED_FFN) bytes. */
+moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* s_w1, const void* s_w3,
+                          const void* s_b1, const void* s_w2, const void* s_b2, void* y_shared,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* The whole layer ([L7.8] §2.1 output equation): route -> dispatch -> expert FFN (gate
  * applied in the down-projection epilogue) -> combine -> statistics, on one stream with no
  * host synchronisation. Inputs and outputs as in the calls above; y [N,d] T. Routing's final
  * reduction also forms the dispatch offsets and per-block bases from its own histograms, so
  * the dispatch stage is a scatter and a row copy; results equal the separate calls'.
+ * With cfg->d_ff_shared > 0 the shared expert's weights s_w1 .. s_b2 (as in moe_shared_ffn)
+ * are required and Shared(x) is added in the combine; otherwise they must be NULL.
  * stage_events: NULL, or 6 hipEvent_t (as void*) recorded on `stream` at the start, after
- * routing, after dispatch, after the up projection, after the down projection and at the end.
+ * routing, after dispatch, after the up projection, after the down projection (and the
+ * shared expert, when there is one) and at the end.
  * ws: moe_workspace_size(cfg, MOE_OP_FORWARD) bytes. */
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* logit_bias, const float* sel_bias,
                        const void* w1, const void* w3, const void* b1,
                        const void* w2, const void* b2,
+                       const void* s_w1, const void* s_w3, const void* s_b1,
+                       const void* s_w2, const void* s_b2,
                        void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     moe_forward,
     moe_get_device_error,
     moe_route,
+    moe_shared_ffn,
     moe_update_bias,
     moe_workspace_size,
     workspace,

@@ -31,6 +31,7 @@ class Op(enum.IntEnum):
     EXPERT_FFN = 2
     COMBINE = 3
     FORWARD = 4
+    SHARED_FFN = 5
 
 
 class MoeError(RuntimeError):
@@ -52,6 +53,7 @@ class MoeConfigStruct(ctypes.Structure):
         ("has_bias", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("routed_scaling", ctypes.c_float),
+        ("d_ff_shared", ctypes.c_int32),
     ]
 
 
@@ -70,13 +72,15 @@ class LayerConfig:
     has_bias: bool = False
     dtype: str = "bf16"
     routed_scaling: float = 1.0
+    d_ff_shared: int = 0     # width S f of the shared expert(s); 0 = none
 
     def struct(self) -> MoeConfigStruct:
         if self.router not in ROUTERS or self.act not in ACTS or self.dtype not in DTYPES:
             raise ValueError(f"unknown router/act/dtype in {self}")
         return MoeConfigStruct(self.n_tokens, self.d_model, self.n_experts, self.top_k, self.d_ff,
                                ROUTERS[self.router], int(self.norm_topk), ACTS[self.act],
-                               int(self.has_bias), DTYPES[self.dtype], float(self.routed_scaling))
+                               int(self.has_bias), DTYPES[self.dtype], float(self.routed_scaling),
+                               int(self.d_ff_shared))
 
     @property
     def torch_dtype(self):
@@ -88,7 +92,8 @@ class LayerConfig:
 
     def with_tokens(self, n: int) -> "LayerConfig":
         return LayerConfig(n, self.d_model, self.n_experts, self.top_k, self.d_ff, self.router,
-                           self.norm_topk, self.act, self.has_bias, self.dtype, self.routed_scaling)
+                           self.norm_topk, self.act, self.has_bias, self.dtype, self.routed_scaling,
+                           self.d_ff_shared)
 
 
 _lib = None
@@ -109,15 +114,15 @@ def lib():
     L.moe_route.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.moe_dispatch.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.moe_expert_ffn.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-    L.moe_combine.argtypes = [S, _P, _P, _P, _P, _P]
-    L.moe_forward.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                              ctypes.c_size_t, _P, _P]
+    L.moe_combine.argtypes = [S, _P, _P, _P, _P, _P, _P]
+    L.moe_shared_ffn.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.moe_forward.argtypes = [S] + [_P] * 20 + [ctypes.c_size_t, _P, _P]
     L.moe_get_device_error.argtypes = [_P, _P]
     L.moe_update_bias.argtypes = [S, _P, _P, ctypes.c_float, _P]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
-                 "moe_update_bias"):
+                 "moe_update_bias", "moe_shared_ffn"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -247,25 +252,49 @@ def moe_expert_ffn(cfg: LayerConfig, x_sorted, offsets, w1, w3, b1, w2, b2, gate
     return y_sorted
 
 
-def moe_combine(cfg: LayerConfig, y_sorted, topk_w, inv_perm):
-    """Gate-weighted combine back through inv_perm; returns y [N,d]."""
+def moe_combine(cfg: LayerConfig, y_sorted, topk_w, inv_perm, y_add=None):
+    """Gate-weighted combine back through inv_perm, plus y_add [N,d] (the shared expert's
+    output) with weight 1 when given; returns y [N,d]."""
     N, d, k = cfg.n_tokens, cfg.d_model, cfg.top_k
     _want(y_sorted, "y_sorted", (N * k, d), cfg.torch_dtype)
     _want(topk_w, "topk_w", (N, k), torch.float32, optional=True)
     _want(inv_perm, "inv_perm", (N * k,), torch.int32)
+    _want(y_add, "y_add", (N, d), cfg.torch_dtype, optional=True)
     y = torch.empty((N, d), dtype=cfg.torch_dtype, device=inv_perm.device)
-    st = lib().moe_combine(ctypes.byref(cfg.struct()), _ptr(y_sorted), _ptr(topk_w), _ptr(inv_perm), _ptr(y), _stream())
+    st = lib().moe_combine(ctypes.byref(cfg.struct()), _ptr(y_sorted), _ptr(topk_w), _ptr(inv_perm), _ptr(y_add),
+                           _ptr(y), _stream())
     _check(st, "moe_combine")
     return y
 
 
+def moe_shared_ffn(cfg: LayerConfig, x, s_w1, s_w3, s_w2, s_b1=None, s_b2=None, *, ws=None):
+    """The shared expert (dense MLP of width cfg.d_ff_shared) over all tokens; returns y [N,d]."""
+    N, d, F = cfg.n_tokens, cfg.d_model, cfg.d_ff_shared
+    T = cfg.torch_dtype
+    _want(x, "x", (N, d), T)
+    _want(s_w1, "s_w1", (F, d), T)
+    _want(s_w3, "s_w3", (F, d), T, optional=cfg.act != "swiglu")
+    _want(s_w2, "s_w2", (d, F), T)
+    _want(s_b1, "s_b1", (F,), T, optional=not cfg.has_bias)
+    _want(s_b2, "s_b2", (d,), T, optional=not cfg.has_bias)
+    y = torch.empty((N, d), dtype=T, device=s_w1.device)
+    ws = workspace(cfg, Op.SHARED_FFN, s_w1.device) if ws is None else ws
+    st = lib().moe_shared_ffn(ctypes.byref(cfg.struct()), _ptr(x), _ptr(s_w1), _ptr(s_w3), _ptr(s_b1), _ptr(s_w2),
+                              _ptr(s_b2), _ptr(y), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_shared_ffn")
+    return y
+
+
 def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, logit_bias=None, sel_bias=None,
-                *, ws=None, out=None, stage_events: Optional[Sequence[int]] = None):
-    """The whole layer. Returns dict y [N,d], topk_ids, topk_w, counts, stats. `out` may hold
-    preallocated outputs (same keys) and `ws` a preallocated workspace, so that repeated calls
-    allocate nothing. stage_events: 6 raw hipEvent_t handles (ints) or None."""
+                *, shared: Optional[dict] = None, ws=None, out=None, stage_events: Optional[Sequence[int]] = None):
+    """The whole layer. Returns dict y [N,d], topk_ids, topk_w, counts, stats. `shared`: the
+    shared expert's weights {s_w1, s_w3, s_w2, s_b1, s_b2} when cfg.d_ff_shared > 0. `out` may
+    hold preallocated outputs (same keys) and `ws` a preallocated workspace, so that repeated
+    calls allocate nothing. stage_events: 6 raw hipEvent_t handles (ints) or None."""
     N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
     T = cfg.torch_dtype
+    sh = shared or {}
+    s_w1, s_w3, s_w2, s_b1, s_b2 = (sh.get(n) for n in ("s_w1", "s_w3", "s_w2", "s_b1", "s_b2"))
     if out is None:
         _want(x, "x", (N, d), T)
         _want(w_router, "w_router", (E, d), T)
@@ -276,6 +305,13 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
         _want(b2, "b2", (E, d), T, optional=not cfg.has_bias)
         _want(logit_bias, "logit_bias", (E,), torch.float32, optional=True)
         _want(sel_bias, "sel_bias", (E,), torch.float32, optional=True)
+        if cfg.d_ff_shared:
+            F = cfg.d_ff_shared
+            _want(s_w1, "s_w1", (F, d), T)
+            _want(s_w3, "s_w3", (F, d), T, optional=cfg.act != "swiglu")
+            _want(s_w2, "s_w2", (d, F), T)
+            _want(s_b1, "s_b1", (F,), T, optional=not cfg.has_bias)
+            _want(s_b2, "s_b2", (d,), T, optional=not cfg.has_bias)
         dev = w_router.device
         out = {
             "y": torch.empty((N, d), dtype=T, device=dev),
@@ -292,7 +328,8 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
             raise ValueError("stage_events needs 6 events")
         ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(int(e)) for e in stage_events])
     st = lib().moe_forward(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(sel_bias),
-                           _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out["y"]), _ptr(out["topk_ids"]),
+                           _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1), _ptr(s_w3), _ptr(s_b1),
+                           _ptr(s_w2), _ptr(s_b2), _ptr(out["y"]), _ptr(out["topk_ids"]),
                            _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]), _ptr(ws), ws.numel(),
                            ev, _stream())
     _check(st, "moe_forward")

@@ -10,6 +10,8 @@
 // The m-tiles of every expert are listed once per call by tile_table_kernel from offsets,
 // so the GEMM grids are sized from the worst case on the host and idle experts cost
 // nothing: they own no tile and their weights are never read.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -490,6 +492,25 @@ static int persistent_grid() {
   return cus[dev];
 }
 
+// Tile table of one dense "expert" covering rows [0, n) (the shared expert).
+__global__ __launch_bounds__(256) void dense_tiles_kernel(int n, int bm, int* __restrict__ tiles) {
+  const int nt = (n + bm - 1) / bm;
+  if (threadIdx.x < 4) tiles[4 + threadIdx.x] = 0;
+  if (threadIdx.x == 0) tiles[0] = nt;
+  for (int t = threadIdx.x; t < nt; t += blockDim.x) {
+    int* q = tiles + kTileHdr + kTileInts * t;
+    q[0] = 0;
+    q[1] = t * bm;
+    q[2] = min(bm, n - t * bm);
+    q[3] = 0;
+    q[4] = nt;
+  }
+}
+
+static int shared_m_tiles(const moe_config& c) {
+  return c.d_ff_shared > 0 ? (int)((c.n_tokens + ffn_tile_rows(c) - 1) / ffn_tile_rows(c)) : 0;
+}
+
 int ffn_max_m_tiles(const moe_config& c) {
   const long long A = c.n_tokens * c.top_k;
   const int bm = ffn_tile_rows(c);
@@ -498,8 +519,11 @@ int ffn_max_m_tiles(const moe_config& c) {
 
 void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   const size_t A = (size_t)(c.n_tokens * c.top_k);
-  int* tiles = w.take_t<int>(kTileHdr + kTileInts * (size_t)ffn_max_m_tiles(c));
-  void* h = w.take(A * (size_t)c.d_ff * elem_size(c));
+  // the shared expert (run after the routed experts) reuses the tile table and h
+  const size_t tiles_n = (size_t)std::max(ffn_max_m_tiles(c), shared_m_tiles(c));
+  const size_t h_elems = std::max(A * (size_t)c.d_ff, (size_t)c.n_tokens * (size_t)std::max(c.d_ff_shared, 0));
+  int* tiles = w.take_t<int>(kTileHdr + kTileInts * tiles_n);
+  void* h = w.take(h_elems * elem_size(c));
   if (L) {
     L->tiles = tiles;
     L->h = h;
@@ -562,6 +586,52 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
   } else {
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, const void* s_w1,
+                         const void* s_w3, const void* s_b1, const void* s_w2, const void* s_b2,
+                         void* y_shared, hipStream_t stream) {
+  const int N = (int)c.n_tokens;
+  if (N == 0 || c.d_ff_shared <= 0) return hipGetLastError();
+  const int bm = ffn_tile_rows(c);
+  dense_tiles_kernel<<<1, 256, 0, stream>>>(N, bm, L.tiles);
+  const int mt = shared_m_tiles(c);
+  const bool bias = c.act == MOE_ACT_GELU && c.has_bias;
+  GemmArgs g{};
+  g.a = x;
+  g.b0 = s_w1;
+  g.b1 = s_w3;
+  g.bias = bias ? s_b1 : nullptr;
+  g.c = L.h;
+  g.tiles = L.tiles;
+  g.K = c.d_model;
+  g.n_out = c.d_ff_shared;
+  if (c.dtype == MOE_BF16) {
+    g.n_tiles_n = (c.d_ff_shared + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
+    if (c.act == MOE_ACT_SWIGLU) expert_gemm_bf16_kernel<kEpiSwiglu><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+    else expert_gemm_bf16_kernel<kEpiGelu><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+  } else {
+    dim3 grid(mt, (c.d_ff_shared + kFBN - 1) / kFBN);
+    if (c.act == MOE_ACT_SWIGLU) expert_gemm_f32_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
+    else expert_gemm_f32_kernel<kEpiGelu><<<grid, 256, 0, stream>>>(g);
+  }
+  GemmArgs d{};
+  d.a = L.h;
+  d.b0 = s_w2;
+  d.bias = bias ? s_b2 : nullptr;
+  d.gate = nullptr;
+  d.c = y_shared;
+  d.tiles = L.tiles;
+  d.K = c.d_ff_shared;
+  d.n_out = c.d_model;
+  if (c.dtype == MOE_BF16) {
+    d.n_tiles_n = (c.d_model + 255) / 256;
+    expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), kGemmThreads, 0, stream>>>(d);
+  } else {
+    dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
+    expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(d);
   }
   return hipGetLastError();
 }

@@ -28,6 +28,9 @@ moe_status check_config(const moe_config* c, bool needs_ff) {
   if (c->n_tokens * (long long)c->top_k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (c->d_model < 8 || c->d_model > 65536 || c->d_model % 8) return MOE_ERR_UNSUPPORTED;
   if (needs_ff && (c->d_ff < 8 || c->d_ff > 65536 || c->d_ff % 8)) return MOE_ERR_UNSUPPORTED;
+  if (c->d_ff_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (c->d_ff_shared > 0 && (c->d_ff_shared < 8 || c->d_ff_shared > 65536 || c->d_ff_shared % 8))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -43,6 +46,25 @@ moe_status need_4(const void* p) {
   return aligned4(p) ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 moe_status opt_4(const void* p) { return (!p || aligned4(p)) ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+
+// The shared expert's weights: required iff cfg->d_ff_shared > 0, NULL otherwise.
+moe_status check_shared(const moe_config* c, const void* s_w1, const void* s_w3, const void* s_b1,
+                        const void* s_w2, const void* s_b2) {
+  if (c->d_ff_shared == 0) return (s_w1 || s_w3 || s_b1 || s_w2 || s_b2) ? MOE_ERR_INVALID_ARG : MOE_OK;
+  moe_status st;
+  if ((st = need_t(s_w1)) != MOE_OK || (st = need_t(s_w2)) != MOE_OK) return st;
+  if (c->act == MOE_ACT_SWIGLU) {
+    if ((st = need_t(s_w3)) != MOE_OK) return st;
+  } else if (s_w3) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (c->has_bias) {
+    if ((st = need_t(s_b1)) != MOE_OK || (st = need_t(s_b2)) != MOE_OK) return st;
+  } else if (s_b1 || s_b2) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
 
 #define MOE_TRY(expr)                  \
   do {                                 \
@@ -84,6 +106,7 @@ size_t layout(const moe_config& c, int op, char* base, WsLayout* L) {
     case MOE_OP_DISPATCH: carve_dispatch(c, w, L); break;
     case MOE_OP_EXPERT_FFN: carve_ffn(c, w, L); break;
     case MOE_OP_COMBINE: break;
+    case MOE_OP_SHARED_FFN: carve_ffn(c, w, L); break;
     case MOE_OP_FORWARD:
       carve_route(c, w, L);
       carve_ffn(c, w, L);
@@ -109,9 +132,10 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 extern "C" {
 
 size_t moe_workspace_size(const moe_config* cfg, int op) {
-  const bool needs_ff = op == MOE_OP_EXPERT_FFN || op == MOE_OP_FORWARD;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_FORWARD) return 0;
+  const bool needs_ff = op == MOE_OP_EXPERT_FFN || op == MOE_OP_FORWARD || op == MOE_OP_SHARED_FFN;
+  if (op < MOE_OP_ROUTE || op > MOE_OP_SHARED_FFN) return 0;
   if (check_config(cfg, needs_ff) != MOE_OK) return 0;
+  if (op == MOE_OP_SHARED_FFN && cfg->d_ff_shared <= 0) return 0;
   return layout(*cfg, op, nullptr, nullptr);
 }
 
@@ -188,23 +212,42 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* y_sorted, const float* topk_w,
-                       const int32_t* inv_perm, void* y, void* stream) {
+                       const int32_t* inv_perm, const void* y_add, void* y, void* stream) {
   MOE_TRY(check_config(cfg, false));
   if (cfg->n_tokens > 0) {
     MOE_TRY(need_t(y_sorted));
     MOE_TRY(need_4(inv_perm));
     MOE_TRY(need_t(y));
     MOE_TRY(opt_4(topk_w));
+    MOE_TRY(opt_t(y_add));
   }
-  return hip_status(launch_combine(*cfg, y_sorted, topk_w, inv_perm, y, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_combine(*cfg, y_sorted, topk_w, inv_perm, y_add, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* s_w1, const void* s_w3,
+                          const void* s_b1, const void* s_w2, const void* s_b2, void* y_shared,
+                          void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg, true));
+  if (cfg->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_t(x));
+    MOE_TRY(need_t(y_shared));
+  }
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_SHARED_FFN, ws, ws_bytes, &L));
+  return hip_status(launch_shared(*cfg, L, x, s_w1, s_w3, s_b1, s_w2, s_b2, y_shared,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* logit_bias, const float* sel_bias, const void* w1,
-                       const void* w3, const void* b1, const void* w2, const void* b2, void* y,
-                       int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, void* ws,
-                       size_t ws_bytes, void* const* stage_events, void* stream) {
+                       const void* w3, const void* b1, const void* w2, const void* b2,
+                       const void* s_w1, const void* s_w3, const void* s_b1, const void* s_w2,
+                       const void* s_b2, void* y, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                       float* stats, void* ws, size_t ws_bytes, void* const* stage_events, void* stream) {
   MOE_TRY(check_config(cfg, true));
+  MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
   if (cfg->n_tokens > 0) {
     MOE_TRY(need_t(x));
     MOE_TRY(need_t(y));
@@ -245,8 +288,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s)));
   MOE_TRY(mark(3));
   MOE_TRY(hip_status(launch_ffn_down(*cfg, L, L.offsets, w2, b2, L.gate_sorted, L.y_sorted, s)));
+  // Shared(x) of the output equation: its output lands in x_sorted, free after the routed up
+  // projection (A >= N rows), and the combine adds it with weight 1.
+  const bool shared = cfg->d_ff_shared > 0;
+  if (shared) MOE_TRY(hip_status(launch_shared(*cfg, L, x, s_w1, s_w3, s_b1, s_w2, s_b2, L.x_sorted, s)));
   MOE_TRY(mark(4));
-  MOE_TRY(hip_status(launch_combine(*cfg, L.y_sorted, nullptr, L.inv_perm, y, s)));
+  MOE_TRY(hip_status(launch_combine(*cfg, L.y_sorted, nullptr, L.inv_perm, shared ? L.x_sorted : nullptr, y, s)));
   return mark(5);
 }
 

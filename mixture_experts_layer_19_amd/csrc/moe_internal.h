@@ -186,6 +186,11 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
 hipError_t launch_update_bias(const moe_config& c, const int32_t* counts, float* bias, float rate,
                               hipStream_t stream);
 hipError_t launch_combine(const moe_config& c, const void* y_sorted, const float* topk_w,
-                          const int32_t* inv_perm, void* y, hipStream_t stream);
+                          const int32_t* inv_perm, const void* y_add, void* y, hipStream_t stream);
+// The shared expert: dense MLP of width c.d_ff_shared over all N rows of x (tile table and
+// hidden activations in L.tiles / L.h, which must be free: after the routed down projection).
+hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, const void* s_w1,
+                         const void* s_w3, const void* s_b1, const void* s_w2, const void* s_b2,
+                         void* y_shared, hipStream_t stream);
 
 }  // namespace moe

@@ -12,6 +12,8 @@ Recipe (every draw seeded; seed 0 unless stated):
   * fine-grained: a Zipf(s = 1.2) per-expert logit offset, logit_bias_e = -1.2 ln r_e with
     r = 1 + a seeded permutation of 0..E-1, which makes the expert batches heavily ragged.
   * deepseek-v3: a selection-only bias b_e ~ U(-0.1, 0.1).
+  * a shared expert (d_ff_shared > 0) draws its weights like a routed expert's, from its own
+    streams.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ import torch
 
 from .binding import LayerConfig
 
-X, W_G, W1, W3, W2, B1, B2, ZIPF, SELB = range(9)  # tensor ids of the seed streams
+X, W_G, W1, W3, W2, B1, B2, ZIPF, SELB, SW1, SW3, SW2, SB1, SB2 = range(14)  # tensor ids of the seed streams
 
 
 @dataclass(frozen=True)
@@ -47,6 +49,10 @@ WORKLOADS: Dict[str, Workload] = {
                              logit_offset="zipf1.2"),
     "deepseek_v3": Workload("deepseek_v3", LayerConfig(4096, 7168, 256, 8, 2048, "sigmoid", True, "swiglu", False, "bf16"),
                             sel_bias="uniform0.1"),
+    # the same layer with its one shared expert of width f (the pages' DeepSeek setting)
+    "deepseek_v3_shared": Workload("deepseek_v3_shared",
+                                   LayerConfig(4096, 7168, 256, 8, 2048, "sigmoid", True, "swiglu", False, "bf16",
+                                               d_ff_shared=2048), sel_bias="uniform0.1"),
 }
 
 
@@ -70,7 +76,8 @@ def _normal(shape, std, seed, tensor_id, expert, device, dtype):
 
 def make_inputs(w: Workload, seed: int = 0, device="cuda") -> dict:
     """All inputs of one layer call on `device`: x, w_router, w1, w3, w2, b1, b2,
-    logit_bias, sel_bias (absent ones are None)."""
+    logit_bias, sel_bias and shared (a dict of the shared expert's weights) (absent ones are
+    None)."""
     c = w.cfg
     T = c.torch_dtype
     N, d, E, f = c.n_tokens, c.d_model, c.n_experts, c.d_ff
@@ -90,7 +97,15 @@ def make_inputs(w: Workload, seed: int = 0, device="cuda") -> dict:
         if b1 is not None:
             b1[e] = _normal((f,), s, seed, B1, e, device, T)
             b2[e] = _normal((d,), s, seed, B2, e, device, T)
-    out.update(w1=w1, w3=w3, w2=w2, b1=b1, b2=b2, logit_bias=None, sel_bias=None)
+    out.update(w1=w1, w3=w3, w2=w2, b1=b1, b2=b2, logit_bias=None, sel_bias=None, shared=None)
+    if c.d_ff_shared:
+        F = c.d_ff_shared
+        sh = {"s_w1": _normal((F, d), s, seed, SW1, 0, device, T),
+              "s_w3": _normal((F, d), s, seed, SW3, 0, device, T) if c.act == "swiglu" else None,
+              "s_w2": _normal((d, F), s, seed, SW2, 0, device, T),
+              "s_b1": _normal((F,), s, seed, SB1, 0, device, T) if c.has_bias else None,
+              "s_b2": _normal((d,), s, seed, SB2, 0, device, T) if c.has_bias else None}
+        out["shared"] = sh
     if w.logit_offset == "zipf1.2":
         g = _gen(seed, ZIPF, 0, "cpu")
         r = 1.0 + torch.randperm(E, generator=g).to(torch.float64)

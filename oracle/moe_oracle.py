@@ -14,7 +14,7 @@ Pages cited (by title, section / table / figure):
            §3 worked example, §4 interface and "Your graded tests" (the oracle recipe:
            a per-token loop in float64, top-k sorted with an explicit (score, id) key).
   [RB-15]  "15. Mixture of Experts" (RustingBrain tutorial): §15.2 routing and renormalised
-           gates, "Dropless", §15.3 the z-loss, §15.4 the shared expert.
+           gates, "Dropless", §15.3 the z-loss, §15.4 the shared expert (shared_output).
   [GPT2-MoE] "Extending Raschka's GPT-2: an MoE trained from scratch on an RTX 3090":
            the router walk-through (Diagram 4, all experts active; Diagrams 10-12, top-k of
            one context vector), the per-expert masked loop (Diagrams 13-19), and the
@@ -254,15 +254,28 @@ def _expert(params: Mapping[str, Any], e: int):
     return dict(w1=get("w1"), w2=get("w2"), w3=get("w3"), b1=get("b1"), b2=get("b2"))
 
 
+def shared_output(x, params: Mapping[str, Any], act: str):
+    """Shared(x) of the [L7.8] §2.1 output equation: the shared expert(s) every token passes
+    through with weight 1 ([RB-15] §15.4). S shared experts of width f are one MLP of width
+    S f ([L7.8] §2.1), so params hold a single MLP: s_w1 [S f, d], s_w3 [S f, d] (swiglu),
+    s_w2 [d, S f], s_b1 / s_b2 (gelu, optional). Returns 0 when there is no shared expert."""
+    if params.get("s_w1") is None:
+        return 0.0
+    return expert_ffn(x, act, params["s_w1"], params["s_w2"], params.get("s_w3"), params.get("s_b1"),
+                      params.get("s_b2"))
+
+
 # ----------------------------------------------------------------------------------------
-# The oracle proper: y_n = sum_{e in T_n} w_{n,e} Expert_e(x_n)  ([L7.8] §2.1 equation).
+# The oracle proper: y_n = sum_{e in T_n} w_{n,e} Expert_e(x_n) + Shared(x_n)
+# ([L7.8] §2.1 equation).
 # ----------------------------------------------------------------------------------------
 
 def forward_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_bias=None):
     """Per-token loop over the chosen experts, j ascending ([L7.8] §4 oracle recipe).
 
     params: w_g [E,d]; w1 [E,d_ff,d]; w3 [E,d_ff,d] (swiglu); w2 [E,d,d_ff];
-            b1 [E,d_ff], b2 [E,d] (optional, gelu only). Returns (y [N,d], Route).
+            b1 [E,d_ff], b2 [E,d] (optional, gelu only); the shared expert's s_w1, s_w3,
+            s_w2, s_b1, s_b2 (optional, see shared_output). Returns (y [N,d], Route).
     """
     x = np.asarray(x, f64)
     r = route(x, params["w_g"], spec, logit_bias, sel_bias)
@@ -272,6 +285,7 @@ def forward_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_
         for j in range(spec.top_k):
             e = int(r.ids[t, j])
             y[t] += r.w[t, j] * expert_ffn(x[t][None, :], spec.act, **_expert(params, e))[0]
+        y[t] += shared_output(x[t][None, :], params, spec.act)[0] if params.get("s_w1") is not None else 0.0
     return y, r
 
 
@@ -315,7 +329,7 @@ def forward_sorted(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, se
     ([L7.8] §2.2), then combine. Pinned equal to forward_loop."""
     x = np.asarray(x, f64)
     r = route(x, params["w_g"], spec, logit_bias, sel_bias)
-    y = expert_output_sorted(x, r.ids, r.w, params, spec)
+    y = expert_output_sorted(x, r.ids, r.w, params, spec) + shared_output(x, params, spec.act)
     return y, r
 
 
@@ -348,7 +362,7 @@ def forward_masked_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=Non
         mask = dense_w[:, e] > 0
         if mask.any():
             y[mask] += expert_ffn(x[mask], spec.act, **_expert(params, e)) * dense_w[mask, e][:, None]
-    return y, r
+    return y + shared_output(x, params, spec.act), r
 
 
 # ----------------------------------------------------------------------------------------

@@ -41,8 +41,11 @@ class LazyExperts:
 
 def oracle_params(inp, lazy=False):
     conv = (lambda t: None if t is None else LazyExperts(t)) if lazy else f64
-    return {"w_g": f64(inp["w_router"]), "w1": conv(inp["w1"]), "w3": conv(inp["w3"]),
-            "w2": conv(inp["w2"]), "b1": conv(inp["b1"]), "b2": conv(inp["b2"])}
+    p = {"w_g": f64(inp["w_router"]), "w1": conv(inp["w1"]), "w3": conv(inp["w3"]),
+         "w2": conv(inp["w2"]), "b1": conv(inp["b1"]), "b2": conv(inp["b2"])}
+    for name, t in (inp.get("shared") or {}).items():
+        p[name] = f64(t)
+    return p
 
 
 def tie_masks(route: O.Route):

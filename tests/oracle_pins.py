@@ -333,6 +333,58 @@ def pin_shared_weights(O):
             _close(y, want, 1e-12, f"shared weights ({router}, k={k})")
 
 
+def _with_shared(rng, params, S, d, f, act, bias=False):
+    p = dict(params)
+    p["s_w1"] = rng.normal(0, 0.3, (S * f, d))
+    p["s_w2"] = rng.normal(0, 0.3, (d, S * f))
+    if act == "swiglu":
+        p["s_w3"] = rng.normal(0, 0.3, (S * f, d))
+    if bias:
+        p["s_b1"] = rng.normal(0, 0.3, (S * f,))
+        p["s_b2"] = rng.normal(0, 0.3, (d,))
+    return p
+
+
+def pin_shared_expert_sees_every_token(O):
+    """With every routed expert's output zero (W2 = 0, no b2) the layer is the shared MLP
+    alone, for every token ([L7.8] §2.1: Shared(x_n) with weight 1; [RB-15] §15.4), and the
+    shared term is exactly additive on top of the routed sum."""
+    rng = np.random.default_rng(21)
+    N, d, f, E, k = 13, 6, 5, 4, 2
+    for act, bias in (("swiglu", False), ("gelu", True)):
+        routed = _rand_params(rng, E, d, f, act, bias)
+        params = _with_shared(rng, routed, 1, d, f, act, bias)
+        x = rng.normal(size=(N, d))
+        zero = dict(params, w2=np.zeros_like(params["w2"]))
+        if bias:
+            zero["b2"] = np.zeros_like(params["b2"])
+        y0, _ = O.forward_loop(x, zero, O.Spec(n_experts=E, top_k=k, act=act))
+        want = O.expert_ffn(x, act, params["s_w1"], params["s_w2"], params.get("s_w3"), params.get("s_b1"),
+                            params.get("s_b2"))
+        _close(y0, want, 1e-12, f"routed outputs zero: y = shared MLP ({act})")
+        y_routed, _ = O.forward_loop(x, routed, O.Spec(n_experts=E, top_k=k, act=act))
+        y_all, _ = O.forward_loop(x, params, O.Spec(n_experts=E, top_k=k, act=act))
+        _close(y_all - y_routed, want, 1e-12, f"shared term is additive ({act})")
+        y_sorted, _ = O.forward_sorted(x, params, O.Spec(n_experts=E, top_k=k, act=act))
+        y_masked, _ = O.forward_masked_loop(x, params, O.Spec(n_experts=E, top_k=k, act=act))
+        _close(y_sorted, y_all, 1e-12, f"sorted with shared ({act})")
+        _close(y_masked, y_all, 1e-12, f"masked loop with shared ({act})")
+
+
+def pin_shared_experts_concatenate(O):
+    """S shared experts of width f are one gated MLP of width S f ([L7.8] §2.1): the sum of
+    two separate shared experts equals one MLP whose hidden units are both sets."""
+    rng = np.random.default_rng(22)
+    N, d, f = 9, 7, 4
+    x = rng.normal(size=(N, d))
+    a = _with_shared(rng, {}, 1, d, f, "swiglu")
+    b = _with_shared(rng, {}, 1, d, f, "swiglu")
+    both = {"s_w1": np.concatenate([a["s_w1"], b["s_w1"]]), "s_w3": np.concatenate([a["s_w3"], b["s_w3"]]),
+            "s_w2": np.concatenate([a["s_w2"], b["s_w2"]], axis=1)}
+    _close(O.shared_output(x, both, "swiglu"),
+           O.shared_output(x, a, "swiglu") + O.shared_output(x, b, "swiglu"), 1e-12, "S = 2 shared experts")
+
+
 def pin_routed_scaling(O):
     rng = np.random.default_rng(12)
     z = rng.normal(size=(11, 6))

@@ -41,7 +41,7 @@ MIXTRAL = B.LayerConfig(8192, 4096, 8, 2, 14336)
 
 
 def test_workspace_sizes():
-    sizes = {op: B.moe_workspace_size(MIXTRAL, op) for op in B.Op}
+    sizes = {op: B.moe_workspace_size(MIXTRAL, op) for op in B.Op if op != B.Op.SHARED_FFN}
     assert all(s > 0 and s % 256 == 0 for s in sizes.values())
     A = 8192 * 2
     # forward holds x_sorted, y_sorted and h: 2 A d + A d_ff bf16 at least
@@ -78,8 +78,8 @@ def test_host_validation_codes(bad, status):
     cfg = B.LayerConfig(**kw).struct()
     lib = B.lib()
     fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
-    st = lib.moe_forward(ctypes.byref(cfg), fake, fake, None, None, fake, fake, None, fake, None, fake, fake,
-                         fake, fake, fake, fake, 1 << 40, None, None)
+    st = lib.moe_forward(ctypes.byref(cfg), fake, fake, None, None, fake, fake, None, fake, None,
+                         None, None, None, None, None, fake, fake, fake, fake, fake, fake, 1 << 40, None, None)
     assert st == status
 
 
@@ -102,8 +102,19 @@ def test_null_and_misaligned_pointers_and_small_workspace():
     assert st == B.MOE_ERR_INVALID_ARG
     # stage events must all be given when the array is
     ev = (ctypes.c_void_p * 6)(f, f, f, None, f, f)
-    st = lib.moe_forward(ctypes.byref(cfg), f, f, None, None, f, f, None, f, None, f, f, f, f, f, f, 1 << 40, ev, None)
+    st = lib.moe_forward(ctypes.byref(cfg), f, f, None, None, f, f, None, f, None, None, None, None, None, None,
+                         f, f, f, f, f, f, 1 << 40, ev, None)
     assert st == B.MOE_ERR_INVALID_ARG
+    # shared-expert weights: required iff d_ff_shared > 0 (w3 too for SwiGLU), NULL otherwise
+    scfg = B.LayerConfig(8192, 4096, 8, 2, 14336, d_ff_shared=2048).struct()
+    fwd = lambda c, *sh: lib.moe_forward(ctypes.byref(c), f, f, None, None, f, f, None, f, None, *sh,
+                                         f, f, f, f, f, f, 1 << 40, None, None)
+    assert fwd(scfg, f, None, None, f, None) == B.MOE_ERR_INVALID_ARG
+    assert fwd(cfg, f, f, None, f, None) == B.MOE_ERR_INVALID_ARG
+    bad = B.LayerConfig(8192, 4096, 8, 2, 14336, d_ff_shared=12).struct()
+    assert fwd(bad, f, f, None, f, None) == B.MOE_ERR_UNSUPPORTED
+    assert B.moe_workspace_size(B.LayerConfig(64, 64, 8, 2, 64, d_ff_shared=128), B.Op.SHARED_FFN) > 0
+    assert B.moe_workspace_size(B.LayerConfig(64, 64, 8, 2, 64), B.Op.SHARED_FFN) == 0
 
 
 def test_update_bias_host_validation():

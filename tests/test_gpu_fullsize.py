@@ -17,7 +17,8 @@ from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"tiny_f32": 256, "gpt2_small": 256, "mixtral": 192, "fine_grained": 256, "deepseek_v3": 48}
+SAMPLE = {"tiny_f32": 256, "gpt2_small": 256, "mixtral": 192, "fine_grained": 256, "deepseek_v3": 48,
+          "deepseek_v3_shared": 48}
 
 
 def say(*a):
@@ -34,7 +35,7 @@ def test_fullsize(name):
     inp = W.make_inputs(w, seed=0)
     ws = B.workspace(cfg, B.Op.FORWARD)
     out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
-                        inp["logit_bias"], inp["sel_bias"], ws=ws)
+                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"], ws=ws)
     torch.cuda.synchronize()
     E, k, N = cfg.n_experts, cfg.top_k, cfg.n_tokens
 
@@ -88,7 +89,8 @@ def test_fullsize(name):
     sample = np.array(sorted(edge | set(rng.choice(N, size=min(N, n_extra), replace=False).tolist())))
     sample = sample[agree[sample]]
     params = oracle_params(inp, lazy=True)
-    y_ref = O.expert_output_sorted(x64[sample], r.ids[sample], r.w[sample], params, spec)
+    y_ref = (O.expert_output_sorted(x64[sample], r.ids[sample], r.w[sample], params, spec)
+             + O.shared_output(x64[sample], params, cfg.act))
     y = f64(out["y"][torch.from_numpy(sample).cuda()])
     err, scale = assert_close_rel(y, y_ref, TOL[cfg.dtype], f"y ({name})")
     say(f"    output sample {sample.size} tokens: max|err| {err:.3e}, max|y| {scale:.3e}, "

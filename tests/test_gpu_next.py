@@ -86,3 +86,51 @@ def test_bias_loop_spreads_a_skewed_sigmoid_router():
         spreads.append(int(counts.max() - counts.min()))
     say(f"    max-min load per step: {spreads[:5]} ... {spreads[-5:]}")
     assert np.mean(spreads[-10:]) < 0.5 * spreads[0]
+
+
+# ---------------------------------------------------------------------------------------
+# The shared expert ([L7.8] §2.1 Shared(x_n) with weight 1; [RB-15] §15.4)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,act,bias,N,d,F", [
+    ("bf16", "swiglu", False, 777, 256, 384),
+    ("bf16", "gelu", True, 1000, 768, 1024),
+    ("f32", "gelu", True, 300, 64, 200),
+    ("f32", "swiglu", False, 129, 96, 72),
+    ("bf16", "swiglu", False, 1, 64, 64),
+])
+def test_shared_ffn(dtype, act, bias, N, d, F):
+    from gpu_helpers import TOL, assert_close_rel
+    say(f"[shared_ffn] {dtype} {act} bias={bias} N={N} d={d} F={F}")
+    cfg = B.LayerConfig(N, d, 4, 2, 64, act=act, has_bias=bias, dtype=dtype, d_ff_shared=F)
+    inp = W.make_inputs(W.Workload("shared", cfg), seed=11)
+    sh = inp["shared"]
+    y = B.moe_shared_ffn(cfg, inp["x"], sh["s_w1"], sh["s_w3"], sh["s_w2"], sh["s_b1"], sh["s_b2"])
+    torch.cuda.synchronize()
+    params = {k: f64(v) for k, v in sh.items()}
+    want = O.shared_output(f64(inp["x"]), params, act)
+    err, scale = assert_close_rel(f64(y), want, TOL[dtype], "shared expert")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
+def test_combine_adds_the_shared_term():
+    cfg = B.LayerConfig(500, 256, 8, 2, 64, dtype="bf16")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    ys = torch.randn((1000, 256), generator=g, device="cuda").to(torch.bfloat16)
+    add = torch.randn((500, 256), generator=g, device="cuda").to(torch.bfloat16)
+    inv = torch.randperm(1000, generator=g, device="cuda").to(torch.int32)
+    gw = torch.rand((500, 2), generator=g, device="cuda")
+    y = B.moe_combine(cfg, ys, gw, inv, y_add=add)
+    ys64, add64, inv_np, gw64 = f64(ys), f64(add), inv.cpu().numpy(), f64(gw)
+    want = O.combine(ys64, gw64, inv_np) + add64
+    np.testing.assert_allclose(f64(y), want, rtol=0, atol=2e-2 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("base,kw", [
+    ("deepseek_v3_shared", dict(n_tokens=600, d_model=256, n_experts=32, top_k=4, d_ff=64, d_ff_shared=128)),
+    ("gpt2_small", dict(n_tokens=400, d_model=128, d_ff=256, d_ff_shared=512)),
+    ("tiny_f32", dict(n_tokens=256, d_ff_shared=256)),
+])
+def test_forward_with_shared_expert(base, kw):
+    from test_gpu_parity import run_forward_and_check
+    run_forward_and_check(W.WORKLOADS[base].scaled(**kw))

@@ -35,7 +35,7 @@ def run_forward_and_check(w: W.Workload, seed=0, check_stats=True):
     say(f"[forward] {w.name} {cfg}")
     inp = W.make_inputs(w, seed=seed)
     out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
-                        inp["logit_bias"], inp["sel_bias"])
+                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"])
     torch.cuda.synchronize()
     params = oracle_params(inp)
     spec = spec_of(cfg)

@@ -194,6 +194,10 @@ def m_sigmoid_weights_softmax(O):
     O.gate_weights = gw
 
 
+def m_shared_skipped(O):  # pitfall: the shared expert's term left out of the output
+    O.shared_output = lambda x, params, act: np.zeros(np.shape(x))
+
+
 def m_zloss_no_square(O):
     orig = O.z_loss
     O.z_loss = lambda z: float(np.sqrt(orig(z)))
