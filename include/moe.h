@@ -93,6 +93,8 @@ typedef struct {
   float routed_scaling; /* every gate is multiplied by this after renormalisation ([L7.8] §2.1) */
   int32_t d_ff_shared;  /* hidden width S f of the shared expert(s), 0 = none ([L7.8] §2.1:
                            S shared experts of width f are one MLP of width S f; [RB-15] §15.4) */
+  float capacity_factor; /* moe_forward only: 0 = dropless; > 0 = capacity-factor dispatch
+                            (moe_dispatch_capacity) with this factor */
 } moe_config;
 
 /* Number of statistics floats moe_route / moe_forward write: f[E], P[E], L, z_loss. */
@@ -141,6 +143,29 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* top
                         int32_t* counts, int32_t* offsets, float* gate_sorted,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Expert capacity of the capacity-factor dispatch ([nanoMoE] "Computing the expert
+ * capacity"): floor(k * cf * N / E) in double precision, raised by one when odd. */
+int64_t moe_expert_capacity(int32_t top_k, float capacity_factor, int64_t n_tokens, int32_t n_experts);
+
+/* Capacity-factor (token-dropping) dispatch ([nanoMoE] "Expert Capacity"): each expert takes
+ * at most cap = moe_expert_capacity(k, capacity_factor, N, E) assignments, ranked in k-major
+ * order (every token's first choice before any second choice, tokens ascending), so top
+ * choices win; the rest are dropped (no computation, no contribution; the kept ones keep
+ * their router weight). The kept assignments of expert e form the contiguous rows
+ * [offsets[e], offsets[e+1]) in rank order: a ragged batch of at most cap rows (the padding
+ * of a fixed [E, cap] batch is never computed). moe_expert_ffn and moe_combine (inv_perm =
+ * slot) run on this layout unchanged.
+ * Out: slot [A] int32 (row of assignment a = n*k + j, or -1 if dropped); kept [E] int32;
+ *      offsets [E+1] int32 (offsets[E] = kept rows); x_kept [A,d] T (NULL: no row copy);
+ *      perm_kept [A] int32 (row -> assignment) or NULL; gate_kept [A] float32 = topk_w at
+ *      each kept row when both are given. Ids outside [0, E) are dropped and flagged as in
+ *      moe_dispatch. capacity_factor: finite, >= 0.
+ * ws: moe_workspace_size(cfg, MOE_OP_DISPATCH) bytes. */
+moe_status moe_dispatch_capacity(const moe_config* cfg, float capacity_factor, const void* x,
+                                 const int32_t* topk_ids, const float* topk_w, void* x_kept,
+                                 int32_t* perm_kept, int32_t* slot, int32_t* kept, int32_t* offsets,
+                                 float* gate_kept, void* ws, size_t ws_bytes, void* stream);
+
 /* Expert FFN over ragged per-expert slices ([L7.8] §2.2 "each expert runs once on its
  * slice"; [RB-15] "Dropless"): for every expert e and every row i in
  * [offsets[e], offsets[e+1]):  y_sorted[i] = FFN_e(x_sorted[i]) * gate_sorted[i].
@@ -182,6 +207,8 @@ moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* s_w1
  * the dispatch stage is a scatter and a row copy; results equal the separate calls'.
  * With cfg->d_ff_shared > 0 the shared expert's weights s_w1 .. s_b2 (as in moe_shared_ffn)
  * are required and Shared(x) is added in the combine; otherwise they must be NULL.
+ * With cfg->capacity_factor > 0 the dispatch is moe_dispatch_capacity's (counts and the
+ * statistics still describe the routing before any drop).
  * stage_events: NULL, or 6 hipEvent_t (as void*) recorded on `stream` at the start, after
  * routing, after dispatch, after the up projection, after the down projection (and the
  * shared expert, when there is one) and at the end.

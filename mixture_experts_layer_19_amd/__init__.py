@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     Op,
     moe_combine,
     moe_dispatch,
+    moe_dispatch_capacity,
+    moe_expert_capacity,
     moe_expert_ffn,
     moe_forward,
     moe_get_device_error,

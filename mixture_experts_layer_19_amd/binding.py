@@ -54,6 +54,7 @@ class MoeConfigStruct(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("routed_scaling", ctypes.c_float),
         ("d_ff_shared", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
     ]
 
 
@@ -73,6 +74,7 @@ class LayerConfig:
     dtype: str = "bf16"
     routed_scaling: float = 1.0
     d_ff_shared: int = 0     # width S f of the shared expert(s); 0 = none
+    capacity_factor: float = 0.0   # moe_forward: 0 = dropless, > 0 = capacity-factor dispatch
 
     def struct(self) -> MoeConfigStruct:
         if self.router not in ROUTERS or self.act not in ACTS or self.dtype not in DTYPES:
@@ -80,7 +82,7 @@ class LayerConfig:
         return MoeConfigStruct(self.n_tokens, self.d_model, self.n_experts, self.top_k, self.d_ff,
                                ROUTERS[self.router], int(self.norm_topk), ACTS[self.act],
                                int(self.has_bias), DTYPES[self.dtype], float(self.routed_scaling),
-                               int(self.d_ff_shared))
+                               int(self.d_ff_shared), float(self.capacity_factor))
 
     @property
     def torch_dtype(self):
@@ -93,7 +95,7 @@ class LayerConfig:
     def with_tokens(self, n: int) -> "LayerConfig":
         return LayerConfig(n, self.d_model, self.n_experts, self.top_k, self.d_ff, self.router,
                            self.norm_topk, self.act, self.has_bias, self.dtype, self.routed_scaling,
-                           self.d_ff_shared)
+                           self.d_ff_shared, self.capacity_factor)
 
 
 _lib = None
@@ -119,10 +121,13 @@ def lib():
     L.moe_forward.argtypes = [S] + [_P] * 20 + [ctypes.c_size_t, _P, _P]
     L.moe_get_device_error.argtypes = [_P, _P]
     L.moe_update_bias.argtypes = [S, _P, _P, ctypes.c_float, _P]
+    L.moe_dispatch_capacity.argtypes = [S, ctypes.c_float] + [_P] * 10 + [ctypes.c_size_t, _P]
+    L.moe_expert_capacity.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_int64, ctypes.c_int32]
+    L.moe_expert_capacity.restype = ctypes.c_int64
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
-                 "moe_update_bias", "moe_shared_ffn"):
+                 "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -227,6 +232,40 @@ def moe_dispatch(cfg: LayerConfig, x, topk_ids, topk_w=None, *, want_x_sorted=Tr
                             _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_dispatch")
     out["ws"] = ws
+    return out
+
+
+def moe_expert_capacity(top_k: int, capacity_factor: float, n_tokens: int, n_experts: int) -> int:
+    """floor(k * cf * N / E), raised by one when odd (the library's own computation)."""
+    return int(lib().moe_expert_capacity(int(top_k), float(capacity_factor), int(n_tokens), int(n_experts)))
+
+
+def moe_dispatch_capacity(cfg: LayerConfig, capacity_factor: float, x, topk_ids, topk_w=None, *,
+                          want_x=True, ws=None):
+    """Capacity-factor (token-dropping) dispatch. Returns a dict of device tensors: slot [A]
+    (kept row or -1), kept [E], offsets [E+1], perm_kept [A] (valid below offsets[E]), and
+    x_kept [A,d] / gate_kept [A] when requested (valid below offsets[E])."""
+    N, d, E, k = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k
+    A = N * k
+    _want(topk_ids, "topk_ids", (N, k), torch.int32)
+    _want(topk_w, "topk_w", (N, k), torch.float32, optional=True)
+    if want_x:
+        _want(x, "x", (N, d), cfg.torch_dtype)
+    dev = topk_ids.device
+    out = {
+        "slot": torch.empty((A,), dtype=torch.int32, device=dev),
+        "kept": torch.empty((E,), dtype=torch.int32, device=dev),
+        "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+        "perm_kept": torch.empty((A,), dtype=torch.int32, device=dev),
+        "x_kept": torch.empty((A, d), dtype=cfg.torch_dtype, device=dev) if want_x else None,
+        "gate_kept": torch.empty((A,), dtype=torch.float32, device=dev) if topk_w is not None else None,
+    }
+    ws = workspace(cfg, Op.DISPATCH, dev) if ws is None else ws
+    st = lib().moe_dispatch_capacity(ctypes.byref(cfg.struct()), float(capacity_factor), _ptr(x if want_x else None),
+                                     _ptr(topk_ids), _ptr(topk_w), _ptr(out["x_kept"]), _ptr(out["perm_kept"]),
+                                     _ptr(out["slot"]), _ptr(out["kept"]), _ptr(out["offsets"]), _ptr(out["gate_kept"]),
+                                     _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_dispatch_capacity")
     return out
 
 

@@ -8,14 +8,27 @@
 //                  earlier assignments of the same expert in the chunk (wave ballots), so the
 //                  order inside each expert's slice is ascending in a (stable);
 //   4. row copy:   token-major, each row of x is read once and written to its k slots.
+#include <cmath>
+
 #include "moe_internal.h"
 
 namespace moe {
 
 constexpr int kChunk = 2048;  // assignments per workgroup in the histogram / scatter passes
 
+// Expert id of the a-th assignment in the walk order: token-major (a = n k + j, the order of
+// the dropless dispatch) or k-major (a = j N + n: every token's first choice, then every
+// token's second choice, ...; the ranking order of the capacity-factor dispatch).
+template <bool KMAJOR> MOE_DEV int walk_index(int a, int n_tokens, int k) {
+  if (!KMAJOR) return a;
+  const int j = a / n_tokens;
+  return (a - j * n_tokens) * k + j;
+}
+
+template <bool KMAJOR>
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(
-    const int32_t* __restrict__ ids, int A, int E, int* __restrict__ hist, int* __restrict__ bad) {
+    const int32_t* __restrict__ ids, int A, int E, int n_tokens, int k, int* __restrict__ hist,
+    int* __restrict__ bad) {
   __shared__ int s_hist[kMaxExperts];
   __shared__ int s_bad;
   for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
@@ -25,7 +38,7 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(
   const int a1 = min(A, a0 + kChunk);
   int my_bad = 0;
   for (int a = a0 + threadIdx.x; a < a1; a += 256) {
-    const int e = ids[a];
+    const int e = ids[walk_index<KMAJOR>(a, n_tokens, k)];
     if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);  // integer counts: order-independent
     else my_bad = 1;
   }
@@ -80,10 +93,73 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
 // e in waves < w of this step) + (count of e in lower lanes of wave w). Per-wave counts are
 // published in LDS tagged with the step number, so stale entries read as zero without
 // clearing. base[blockIdx.x][e] is the first slot of this chunk's run of expert e.
+// Capacity scan: like dispatch_scan_kernel over the k-major chunks, plus kept = min(total,
+// cap) and koff = exclusive scan of kept; offsets (the kept slices) = koff with koff[E] =
+// the number of kept rows.
+__global__ __launch_bounds__(1024) void capacity_scan_kernel(
+    const int* __restrict__ hist, const int* __restrict__ bad, int n_chunks, int E, int cap,
+    int* __restrict__ base, int* __restrict__ offs_all, int* __restrict__ kept, int* __restrict__ koff,
+    int* __restrict__ offsets, int* __restrict__ err) {
+  __shared__ int s_scan[kMaxExperts];
+  __shared__ int s_kscan[kMaxExperts];
+  __shared__ int s_bad;
+  const int e = threadIdx.x;
+  if (e == 0) s_bad = 0;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < n_chunks; ++b) total += hist[(size_t)b * E + e];
+    s_scan[e] = total;
+    s_kscan[e] = min(total, cap);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < n_chunks; b += blockDim.x)
+    if (bad[b]) s_bad = 1;
+  for (int o = 1; o < E; o <<= 1) {
+    int v = 0, w = 0;
+    if (e < E && e >= o) {
+      v = s_scan[e - o];
+      w = s_kscan[e - o];
+    }
+    __syncthreads();
+    if (e < E) {
+      s_scan[e] += v;
+      s_kscan[e] += w;
+    }
+    __syncthreads();
+  }
+  if (e < E) {
+    const int start = s_scan[e] - total;
+    const int kk = min(total, cap);
+    offs_all[e] = start;
+    kept[e] = kk;
+    koff[e] = s_kscan[e] - kk;
+    offsets[e] = s_kscan[e] - kk;
+    if (e == E - 1) offsets[E] = s_kscan[e];
+    int run = start;
+    for (int b = 0; b < n_chunks; ++b) {
+      base[(size_t)b * E + e] = run;
+      run += hist[(size_t)b * E + e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && err) err[0] = s_bad ? MOE_ERR_BAD_EXPERT_ID : 0;
+}
+
+// Capacity variant (CAP): `pos` is then the assignment's place among all of its expert's
+// assignments in k-major order; rank = pos - offs_all[e]; it is kept at row koff[e] + rank
+// when rank < cap (perm / inv_perm / gate_sorted refer to the kept rows), else dropped
+// (inv_perm = -1).
+struct CapArgs {
+  int cap;
+  const int* offs_all;  // [E] exclusive scan of all assignments per expert
+  const int* koff;      // [E] exclusive scan of the kept counts
+};
+
+template <bool KMAJOR, bool CAP>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int A, int E, int id_bits, int chunk,
-    const int* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-    float* __restrict__ gate_sorted) {
+    int n_tokens, int k, const int* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    float* __restrict__ gate_sorted, CapArgs ca) {
   __shared__ int s_run[kMaxExperts];
   __shared__ int s_cnt[4][kMaxExperts];  // (step << 16) | count
   const int lane = threadIdx.x & 63;
@@ -100,7 +176,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int step = 0, as = a0; as < a1; ++step, as += nthr) {
     const int a = as + threadIdx.x;
-    const int e = (a < a1) ? ids[a] : -1;
+    const int ai = (a < a1) ? walk_index<KMAJOR>(a, n_tokens, k) : 0;  // assignment n k + j
+    const int e = (a < a1) ? ids[ai] : -1;
     const bool valid = e >= 0 && e < E;
     // lanes of this wave holding the same expert id
     uint64_t peers = __ballot(valid);
@@ -119,12 +196,18 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
         const int v = s_cnt[w][e];
         if ((v >> 16) == step) before += v & 0xffff;
       }
-      const int pos = s_run[e] + before + rank;
-      perm[pos] = a;
-      inv_perm[a] = pos;
-      if (gate_sorted) gate_sorted[pos] = topk_w[a];
+      int pos = s_run[e] + before + rank;
+      if (CAP) {
+        const int r = pos - ca.offs_all[e];
+        pos = (r < ca.cap) ? ca.koff[e] + r : -1;
+      }
+      if (pos >= 0) {
+        if (perm) perm[pos] = ai;
+        if (gate_sorted) gate_sorted[pos] = topk_w[ai];
+      }
+      inv_perm[ai] = pos;
     } else if (a < a1) {
-      inv_perm[a] = -1;
+      inv_perm[ai] = -1;
     }
     __syncthreads();
     if (leader) atomicAdd(&s_run[e], cnt);  // integer adds: the final run is order-independent
@@ -171,11 +254,45 @@ void carve_dispatch(const moe_config& c, WsCarver& w, WsLayout* L) {
   int* hist = w.take_t<int>((size_t)n_chunks * E);
   int* base = w.take_t<int>((size_t)n_chunks * E);
   int* bad = w.take_t<int>((size_t)n_chunks);
+  int* offs_all = w.take_t<int>(E);
+  int* koff = w.take_t<int>(E);
   if (L) {
     L->d_hist = hist;
     L->d_base = base;
     L->d_bad = bad;
+    L->d_offs_all = offs_all;
+    L->d_koff = koff;
   }
+}
+
+long long expert_capacity(const moe_config& c, float capacity_factor) {
+  const double v = std::floor((double)c.top_k * (double)capacity_factor * (double)c.n_tokens / (double)c.n_experts);
+  const long long cap = (long long)v;
+  return cap + (cap & 1);
+}
+
+hipError_t launch_dispatch_capacity(const moe_config& c, const WsLayout& L, float capacity_factor, const void* x,
+                                    const int32_t* topk_ids, const float* topk_w, void* x_kept, int32_t* perm_kept,
+                                    int32_t* slot, int32_t* kept, int32_t* offsets, float* gate_kept,
+                                    hipStream_t stream) {
+  const int A = (int)(c.n_tokens * c.top_k);
+  const int E = c.n_experts;
+  const int N = (int)c.n_tokens, k = c.top_k;
+  const int n_chunks = (A + kChunk - 1) / kChunk;
+  // an expert holds at most one assignment per token, so a capacity above N drops nothing
+  const int cap = (int)std::min<long long>(expert_capacity(c, capacity_factor), (long long)N);
+  if (n_chunks > 0) dispatch_hist_kernel<true><<<n_chunks, 256, 0, stream>>>(topk_ids, A, E, N, k, L.d_hist, L.d_bad);
+  capacity_scan_kernel<<<1, 1024, 0, stream>>>(L.d_hist, L.d_bad, n_chunks, E, cap, L.d_base, L.d_offs_all, kept,
+                                               L.d_koff, offsets, L.err);
+  if (n_chunks > 0) {
+    CapArgs ca{cap, L.d_offs_all, L.d_koff};
+    const bool gate = gate_kept && topk_w;
+    dispatch_scatter_kernel<true, true><<<n_chunks, 256, 0, stream>>>(
+        topk_ids, gate ? topk_w : nullptr, A, E, id_bits_of(E), kChunk, N, k, L.d_base, perm_kept, slot,
+        gate ? gate_kept : nullptr, ca);
+    launch_copy(c, x, slot, x_kept, stream);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x,
@@ -186,12 +303,13 @@ hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x
   const int E = c.n_experts;
   const int n_chunks = (A + kChunk - 1) / kChunk;
   const int id_bits = id_bits_of(E);
-  if (n_chunks > 0) dispatch_hist_kernel<<<n_chunks, 256, 0, stream>>>(topk_ids, A, E, L.d_hist, L.d_bad);
+  const int N = (int)c.n_tokens, k = c.top_k;
+  if (n_chunks > 0) dispatch_hist_kernel<false><<<n_chunks, 256, 0, stream>>>(topk_ids, A, E, N, k, L.d_hist, L.d_bad);
   dispatch_scan_kernel<<<1, 1024, 0, stream>>>(L.d_hist, L.d_bad, n_chunks, E, L.d_base, counts, offsets, L.err);
   if (n_chunks > 0) {
-    dispatch_scatter_kernel<<<n_chunks, 256, 0, stream>>>(topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr,
-                                                          A, E, id_bits, kChunk, L.d_base, perm, inv_perm,
-                                                          (gate_sorted && topk_w) ? gate_sorted : nullptr);
+    dispatch_scatter_kernel<false, false><<<n_chunks, 256, 0, stream>>>(
+        topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr, A, E, id_bits, kChunk, N, k, L.d_base, perm, inv_perm,
+        (gate_sorted && topk_w) ? gate_sorted : nullptr, CapArgs{});
     launch_copy(c, x, inv_perm, x_sorted, stream);
   }
   return hipGetLastError();
@@ -208,9 +326,9 @@ hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const
   const int chunk = route_tokens_per_block(c) * c.top_k;
   const int n_chunks = (A + chunk - 1) / chunk;
   const int threads = chunk <= 64 ? 64 : chunk <= 128 ? 128 : 256;
-  dispatch_scatter_kernel<<<n_chunks, threads, 0, stream>>>(topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr,
-                                                            A, E, id_bits_of(E), chunk, L.fbase, perm, inv_perm,
-                                                            (gate_sorted && topk_w) ? gate_sorted : nullptr);
+  dispatch_scatter_kernel<false, false><<<n_chunks, threads, 0, stream>>>(
+      topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr, A, E, id_bits_of(E), chunk, (int)c.n_tokens, c.top_k,
+      L.fbase, perm, inv_perm, (gate_sorted && topk_w) ? gate_sorted : nullptr, CapArgs{});
   launch_copy(c, x, inv_perm, x_sorted, stream);
   return hipGetLastError();
 }

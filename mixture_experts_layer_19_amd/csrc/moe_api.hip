@@ -29,6 +29,7 @@ moe_status check_config(const moe_config* c, bool needs_ff) {
   if (c->d_model < 8 || c->d_model > 65536 || c->d_model % 8) return MOE_ERR_UNSUPPORTED;
   if (needs_ff && (c->d_ff < 8 || c->d_ff > 65536 || c->d_ff % 8)) return MOE_ERR_UNSUPPORTED;
   if (c->d_ff_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->capacity_factor) || c->capacity_factor < 0.f) return MOE_ERR_INVALID_ARG;
   if (c->d_ff_shared > 0 && (c->d_ff_shared < 8 || c->d_ff_shared > 65536 || c->d_ff_shared % 8))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -80,6 +81,7 @@ void carve_forward_buffers(const moe_config& c, WsCarver& w, WsLayout* L) {
   int* inv = w.take_t<int>(A);
   int* off = w.take_t<int>((size_t)c.n_experts + 1);
   int* fbase = w.take_t<int>(route_base_ints(c));
+  int* kept = w.take_t<int>((size_t)c.n_experts);
   float* gs = w.take_t<float>(A);
   void* xs = w.take(A * row);
   void* ys = w.take(A * row);
@@ -88,6 +90,7 @@ void carve_forward_buffers(const moe_config& c, WsCarver& w, WsLayout* L) {
     L->inv_perm = inv;
     L->offsets = off;
     L->fbase = fbase;
+    L->kept = kept;
     L->gate_sorted = gs;
     L->x_sorted = xs;
     L->y_sorted = ys;
@@ -109,6 +112,7 @@ size_t layout(const moe_config& c, int op, char* base, WsLayout* L) {
     case MOE_OP_SHARED_FFN: carve_ffn(c, w, L); break;
     case MOE_OP_FORWARD:
       carve_route(c, w, L);
+      carve_dispatch(c, w, L);  // the capacity-factor dispatch's scratch
       carve_ffn(c, w, L);
       carve_forward_buffers(c, w, L);
       break;
@@ -183,6 +187,37 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* top
   MOE_TRY(check_ws(*cfg, MOE_OP_DISPATCH, ws, ws_bytes, &L));
   return hip_status(launch_dispatch(*cfg, L, x, topk_ids, topk_w, x_sorted, perm, inv_perm, counts, offsets,
                                     gate_sorted, static_cast<hipStream_t>(stream)));
+}
+
+int64_t moe_expert_capacity(int32_t top_k, float capacity_factor, int64_t n_tokens, int32_t n_experts) {
+  moe_config c{};
+  c.top_k = top_k;
+  c.n_tokens = n_tokens;
+  c.n_experts = n_experts > 0 ? n_experts : 1;
+  return expert_capacity(c, capacity_factor);
+}
+
+moe_status moe_dispatch_capacity(const moe_config* cfg, float capacity_factor, const void* x,
+                                 const int32_t* topk_ids, const float* topk_w, void* x_kept,
+                                 int32_t* perm_kept, int32_t* slot, int32_t* kept, int32_t* offsets,
+                                 float* gate_kept, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg, false));
+  if (!std::isfinite(capacity_factor) || capacity_factor < 0.f) return MOE_ERR_INVALID_ARG;
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_4(topk_ids));
+    MOE_TRY(need_4(slot));
+    MOE_TRY(opt_4(perm_kept));
+    MOE_TRY(opt_t(x_kept));
+    if (x_kept) MOE_TRY(need_t(x));
+    MOE_TRY(opt_4(topk_w));
+    MOE_TRY(opt_4(gate_kept));
+  }
+  MOE_TRY(need_4(kept));
+  MOE_TRY(need_4(offsets));
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_DISPATCH, ws, ws_bytes, &L));
+  return hip_status(launch_dispatch_capacity(*cfg, L, capacity_factor, x, topk_ids, topk_w, x_kept, perm_kept, slot,
+                                             kept, offsets, gate_kept, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int32_t* offsets,
@@ -280,10 +315,17 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   // Routing's final reduction also writes offsets, the per-block dispatch bases and the
   // m-tile table, so dispatch is a scatter and a row copy.
   MOE_TRY(hip_status(launch_route(*cfg, L, x, w_router, logit_bias, sel_bias, topk_ids, topk_w, counts, stats,
-                                  nullptr, nullptr, true, s)));
+                                  nullptr, nullptr, cfg->capacity_factor <= 0.f, s)));
   MOE_TRY(mark(1));
-  MOE_TRY(hip_status(launch_dispatch_scanned(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
-                                             L.gate_sorted, s)));
+  if (cfg->capacity_factor > 0.f) {
+    // capacity-factor dispatch: k-major ranking, drops; the tile table follows the kept slices
+    MOE_TRY(hip_status(launch_dispatch_capacity(*cfg, L, cfg->capacity_factor, x, topk_ids, topk_w, L.x_sorted,
+                                                L.perm, L.inv_perm, L.kept, L.offsets, L.gate_sorted, s)));
+    MOE_TRY(hip_status(launch_ffn_tiles(*cfg, L, L.offsets, s)));
+  } else {
+    MOE_TRY(hip_status(launch_dispatch_scanned(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
+                                               L.gate_sorted, s)));
+  }
   MOE_TRY(mark(2));
   MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s)));
   MOE_TRY(mark(3));

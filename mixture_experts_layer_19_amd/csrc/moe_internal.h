@@ -43,6 +43,8 @@ struct WsLayout {
   int* d_hist = nullptr;   // [blocks][E] per-block counts
   int* d_base = nullptr;   // [blocks][E] first sorted slot of each block's run of expert e
   int* d_bad = nullptr;    // [blocks] out-of-range id seen
+  int* d_offs_all = nullptr;  // [E] capacity dispatch: exclusive scan of all assignments
+  int* d_koff = nullptr;      // [E] capacity dispatch: exclusive scan of the kept counts
   // expert FFN
   int* tiles = nullptr;    // m-tile table (kTileHdr + kTileInts per tile ints)
   void* h = nullptr;       // [A][d_ff] T
@@ -51,6 +53,7 @@ struct WsLayout {
   int* inv_perm = nullptr;
   int* offsets = nullptr;
   int* fbase = nullptr;    // [route blocks][E] dispatch bases from the routing histograms
+  int* kept = nullptr;     // [E] kept rows per expert (capacity-factor dispatch in moe_forward)
   float* gate_sorted = nullptr;
   void* x_sorted = nullptr;
   void* y_sorted = nullptr;
@@ -170,6 +173,12 @@ hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const
                                    const int32_t* topk_ids, const float* topk_w, void* x_sorted,
                                    int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream);
 int ffn_tile_rows(const moe_config& c);
+// floor(k cf N / E) raised to the next even integer (the capacity-factor dispatch's capacity)
+long long expert_capacity(const moe_config& c, float capacity_factor);
+hipError_t launch_dispatch_capacity(const moe_config& c, const WsLayout& L, float capacity_factor, const void* x,
+                                    const int32_t* topk_ids, const float* topk_w, void* x_kept, int32_t* perm_kept,
+                                    int32_t* slot, int32_t* kept, int32_t* offsets, float* gate_kept,
+                                    hipStream_t stream);
 int ffn_max_m_tiles(const moe_config& c);
 hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x,
                            const int32_t* topk_ids, const float* topk_w, void* x_sorted,

@@ -20,7 +20,8 @@ Pages cited (by title, section / table / figure):
            one context vector), the per-expert masked loop (Diagrams 13-19), and the
            router-loss function.
   [nanoMoE] "nanoMoE: Mixture-of-Experts (MoE) LLMs from Scratch in PyTorch": the MLP and
-           MLPExperts listings (nn.GELU, optional biases), "Expert Capacity", the z-loss.
+           MLPExperts listings (nn.GELU, optional biases), "Expert Capacity" and "Computing
+           the expert capacity" (capacity_dispatch), the z-loss.
 
 Readings taken where the pages are silent or ambiguous (each also listed in the design doc):
   * selection for the softmax routers uses the logits z (softmax is monotone, so the chosen
@@ -363,6 +364,59 @@ def forward_masked_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=Non
         if mask.any():
             y[mask] += expert_ffn(x[mask], spec.act, **_expert(params, e)) * dense_w[mask, e][:, None]
     return y + shared_output(x, params, spec.act), r
+
+
+# ----------------------------------------------------------------------------------------
+# Capacity-factor (token-dropping) dispatch: [nanoMoE] "Expert Capacity", "Computing the
+# expert capacity" and the capacity router listing's ranking.
+# ----------------------------------------------------------------------------------------
+
+def expert_capacity(top_k: int, capacity_factor: float, n_tokens: int, n_experts: int) -> int:
+    """floor(k * cf * N / E), raised by one when odd so that the capacity is even."""
+    cap = math.floor(f64(top_k) * f64(capacity_factor) * f64(n_tokens) / f64(n_experts))
+    return int(cap + cap % 2)
+
+
+def capacity_dispatch(ids, n_experts: int, cap: int):
+    """Token-dropping dispatch. Within each expert the assignments are ranked in k-major order:
+    every token's first choice before any token's second choice, tokens ascending within a
+    choice level, so top choices win the capacity. Ranks >= cap are dropped (no computation,
+    no contribution). The kept assignments of expert e form one contiguous slice in rank
+    order (a ragged batch of at most cap rows; the pages pad it to cap rows).
+    Returns slot [N*k] (row of assignment a = n*k + j in the kept slices, -1 if dropped),
+    kept [E] and offsets [E+1]."""
+    ids = np.asarray(ids)
+    n, k = ids.shape
+    rank = np.zeros((n, k), np.int64)
+    seen = np.zeros(n_experts, np.int64)
+    for j in range(k):
+        for t in range(n):
+            e = int(ids[t, j])
+            rank[t, j] = seen[e]
+            seen[e] += 1
+    kept = np.minimum(seen, cap)
+    offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
+    slot = np.where(rank < cap, offsets[ids] + rank, -1).reshape(-1)
+    return slot, kept, offsets
+
+
+def forward_capacity(x, params: Mapping[str, Any], spec: Spec, capacity_factor: float, logit_bias=None,
+                     sel_bias=None):
+    """The layer with capacity-factor dispatch: dropped assignments contribute nothing, kept
+    ones keep their router weight (no renormalisation over the survivors), plus Shared(x).
+    Returns (y, Route, slot, kept)."""
+    x = np.asarray(x, f64)
+    r = route(x, params["w_g"], spec, logit_bias, sel_bias)
+    n, d = x.shape
+    cap = expert_capacity(spec.top_k, capacity_factor, n, spec.n_experts)
+    slot, kept, _ = capacity_dispatch(r.ids, spec.n_experts, cap)
+    y = np.zeros((n, d), f64)
+    for t in range(n):
+        for j in range(spec.top_k):
+            if slot[t * spec.top_k + j] >= 0:
+                e = int(r.ids[t, j])
+                y[t] += r.w[t, j] * expert_ffn(x[t][None, :], spec.act, **_expert(params, e))[0]
+    return y + shared_output(x, params, spec.act), r, slot, kept
 
 
 # ----------------------------------------------------------------------------------------

@@ -385,6 +385,52 @@ def pin_shared_experts_concatenate(O):
            O.shared_output(x, a, "swiglu") + O.shared_output(x, b, "swiglu"), 1e-12, "S = 2 shared experts")
 
 
+def pin_capacity_formula(O):
+    """[nanoMoE] "Computing the expert capacity": floor(k cf N / E), odd values raised by one."""
+    assert O.expert_capacity(2, 1.25, 8, 4) == 6       # floor(5) = 5 -> 6
+    assert O.expert_capacity(1, 1.0, 10, 4) == 2       # floor(2.5) = 2
+    assert O.expert_capacity(2, 1.0, 16, 4) == 8       # exactly 8
+    assert O.expert_capacity(8, 1.0, 100, 128) == 6    # floor(6.25) = 6
+    assert O.expert_capacity(1, 1.0, 3, 4) == 0        # floor(0.75) = 0: everything dropped
+
+
+def pin_capacity_worked_example(O):
+    """A small case ranked by hand in k-major order (all first choices, then all second
+    choices, tokens ascending), capacity 2:
+      first choices:  t0 e0 #0, t1 e0 #1, t2 e1 #0, t3 e0 #2 (dropped), t4 e2 #0
+      second choices: t0 e1 #1, t1 e2 #1, t2 e0 #3 (dropped), t3 e1 #2 (dropped), t4 e0 #4 (dropped)
+    kept = (2, 2, 2), offsets (0, 2, 4, 6); slot of a = n k + j is offsets[e] + rank."""
+    ids = np.array([[0, 1], [0, 2], [1, 0], [0, 1], [2, 0]])
+    slot, kept, offsets = O.capacity_dispatch(ids, 3, 2)
+    assert list(kept) == [2, 2, 2] and list(offsets) == [0, 2, 4, 6]
+    assert list(slot) == [0, 3, 1, 5, 2, -1, -1, -1, 4, -1]
+
+
+def pin_capacity_top_choices_win(O):
+    """Over capacity, an expert keeps all of its top-1 assignments before any top-2 one, and
+    the kept slices hold each kept assignment once; with a capacity at least every expert's
+    load, nothing is dropped and the layer equals the dropless one."""
+    rng = np.random.default_rng(23)
+    N, d, f, E, k = 40, 5, 6, 6, 3
+    params = _rand_params(rng, E, d, f, "swiglu")
+    x = rng.normal(size=(N, d))
+    spec = O.Spec(n_experts=E, top_k=k, act="swiglu")
+    r = O.route(x, params["w_g"], spec)
+    for cap in (2, 6, 10):
+        slot, kept, offsets = O.capacity_dispatch(r.ids, E, cap)
+        s2 = slot.reshape(N, k)
+        for e in range(E):
+            first_dropped = (s2[:, 0] < 0) & (r.ids[:, 0] == e)
+            later_kept = (s2[:, 1:] >= 0) & (r.ids[:, 1:] == e)
+            assert not (first_dropped.any() and later_kept.any()), (cap, e)
+        used = np.sort(slot[slot >= 0])
+        assert np.array_equal(used, np.arange(offsets[-1])) and (kept <= cap).all()
+    y_cap, _, slot, _ = O.forward_capacity(x, params, spec, capacity_factor=float(E))
+    y_ref, _ = O.forward_loop(x, params, spec)
+    assert (slot >= 0).all()
+    _close(y_cap, y_ref, 1e-12, "capacity >= load is dropless")
+
+
 def pin_routed_scaling(O):
     rng = np.random.default_rng(12)
     z = rng.normal(size=(11, 6))

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-               "moe_workspace_size", "moe_get_device_error", "moe_status_string", "moe_update_bias"):
+               "moe_workspace_size", "moe_get_device_error", "moe_status_string", "moe_update_bias",
+               "moe_shared_ffn", "moe_dispatch_capacity", "moe_expert_capacity"):
         assert fn in names
 
 
@@ -128,6 +129,15 @@ def test_update_bias_host_validation():
     assert lib.moe_update_bias(ctypes.byref(cfg), f, f, ctypes.c_float(float("inf")), None) == B.MOE_ERR_INVALID_ARG
     bad = B.LayerConfig(8192, 4096, 2048, 2, 14336).struct()
     assert lib.moe_update_bias(ctypes.byref(bad), f, f, ctypes.c_float(0.1), None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_expert_capacity_matches_the_oracle():
+    """The library's capacity formula (host code) against the oracle's, float32 factor."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    for k, cf, N, E in [(2, 1.25, 8, 4), (1, 1.0, 10, 4), (8, 1.0, 100, 128), (2, 1.1, 8192, 8),
+                        (8, 1.25, 4096, 256), (1, 1.0, 3, 4), (3, 0.7, 1001, 7), (2, 0.0, 64, 8)]:
+        assert B.moe_expert_capacity(k, cf, N, E) == O.expert_capacity(k, float(np.float32(cf)), N, E)
 
 
 def test_workload_recipes_are_seeded_and_shaped():

@@ -134,3 +134,77 @@ def test_combine_adds_the_shared_term():
 def test_forward_with_shared_expert(base, kw):
     from test_gpu_parity import run_forward_and_check
     run_forward_and_check(W.WORKLOADS[base].scaled(**kw))
+
+
+# ---------------------------------------------------------------------------------------
+# Capacity-factor (token-dropping) dispatch ([nanoMoE] "Expert Capacity")
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,E,k,zipf,cf", [
+    (1000, 8, 2, 0.0, 1.0), (1000, 8, 2, 1.2, 1.25), (3001, 64, 6, 1.3, 0.5), (4100, 256, 8, 1.1, 2.0),
+    (777, 5, 2, 0.0, 10.0), (513, 16, 1, 2.0, 1.0), (1, 4, 2, 0.0, 1.0),
+])
+def test_dispatch_capacity_bit_exact(N, E, k, zipf, cf):
+    say(f"[dispatch_capacity] N={N} E={E} k={k} zipf={zipf} cf={cf}")
+    cfg = B.LayerConfig(N, 64, E, k, 64)
+    ids = W.random_ids(N, E, k, seed=N + E, zipf=zipf)
+    gw = W.random_gates(N, k, seed=3)
+    x = W.random_rows(N, 64, torch.bfloat16, seed=4)
+    out = B.moe_dispatch_capacity(cfg, cf, x, ids, gw)
+    torch.cuda.synchronize()
+    cap = O.expert_capacity(k, float(np.float32(cf)), N, E)
+    assert B.moe_expert_capacity(k, cf, N, E) == cap
+    slot, kept, offsets = O.capacity_dispatch(ids.cpu().numpy(), E, cap)
+    assert np.array_equal(out["slot"].cpu().numpy(), slot)
+    assert np.array_equal(out["kept"].cpu().numpy(), kept)
+    assert np.array_equal(out["offsets"].cpu().numpy(), offsets)
+    n_kept = int(offsets[-1])
+    say(f"    capacity {cap}, kept {n_kept} of {N * k}")
+    keep = np.nonzero(slot >= 0)[0]
+    pk = out["perm_kept"].cpu().numpy()
+    assert np.array_equal(pk[slot[keep]], keep)
+    sl = torch.from_numpy(slot[keep]).long().cuda()
+    assert torch.equal(out["x_kept"][sl], x[torch.from_numpy(keep // k).long().cuda()])
+    assert torch.equal(out["gate_kept"][sl], gw.reshape(-1)[torch.from_numpy(keep).long().cuda()])
+
+
+@pytest.mark.parametrize("base,kw,cf", [
+    ("fine_grained", dict(n_tokens=700, d_model=256, d_ff=128), 1.0),
+    ("mixtral", dict(n_tokens=500, d_model=256, d_ff=512), 0.8),
+    ("deepseek_v3_shared", dict(n_tokens=300, d_model=128, n_experts=32, top_k=4, d_ff=64, d_ff_shared=64), 1.25),
+    ("tiny_f32", dict(n_tokens=256), 0.5),
+])
+def test_forward_with_capacity(base, kw, cf):
+    """The layer with capacity-factor dispatch against the oracle, on the device's own ids
+    (the drop set depends on every token's choice, so a near-tie flip elsewhere would move
+    it): gates from the oracle's logits at those ids, drops by the oracle's ranking."""
+    from gpu_helpers import TOL, assert_close_rel, oracle_params
+    import dataclasses
+    w = W.WORKLOADS[base].scaled(**kw)
+    w = dataclasses.replace(w, cfg=dataclasses.replace(w.cfg, capacity_factor=cf))
+    cfg = w.cfg
+    say(f"[forward capacity] {base} {cfg}")
+    inp = W.make_inputs(w, seed=9)
+    out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
+                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"])
+    torch.cuda.synchronize()
+    spec = spec_of(cfg)
+    params = oracle_params(inp)
+    x64 = f64(inp["x"])
+    r = O.route(x64, params["w_g"], spec, f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    ids = out["topk_ids"].cpu().numpy()
+    near, intra, agree = compare_ids(ids, r, cfg.top_k)
+    w_dev_ids = O.gate_weights(r.z, ids, spec)
+    cap = O.expert_capacity(cfg.top_k, float(np.float32(cf)), cfg.n_tokens, cfg.n_experts)
+    slot, kept, _ = O.capacity_dispatch(ids, cfg.n_experts, cap)
+    y_ref = np.zeros_like(x64)
+    for t in range(cfg.n_tokens):
+        for j in range(cfg.top_k):
+            if slot[t * cfg.top_k + j] >= 0:
+                e = int(ids[t, j])
+                y_ref[t] += w_dev_ids[t, j] * O.expert_ffn(x64[t][None, :], cfg.act, **O._expert(params, e))[0]
+    y_ref += O.shared_output(x64, params, cfg.act)
+    dropped = int((slot < 0).sum())
+    err, scale = assert_close_rel(f64(out["y"]), y_ref, TOL[cfg.dtype], f"y with capacity ({base})")
+    say(f"    capacity {cap}: dropped {dropped} of {slot.size}; max|err| {err:.3e} max|y| {scale:.3e}")
+    assert np.array_equal(out["counts"].cpu().numpy(), np.bincount(ids.reshape(-1), minlength=cfg.n_experts))

@@ -198,6 +198,26 @@ def m_shared_skipped(O):  # pitfall: the shared expert's term left out of the ou
     O.shared_output = lambda x, params, act: np.zeros(np.shape(x))
 
 
+def m_capacity_token_major(O):  # ranking in token order: a token's 2nd choice beats later 1st choices
+    def cd(ids, n_experts, cap):
+        ids = np.asarray(ids)
+        n, k = ids.shape
+        rank = np.zeros((n, k), np.int64)
+        seen = np.zeros(n_experts, np.int64)
+        for t in range(n):
+            for j in range(k):
+                rank[t, j] = seen[ids[t, j]]
+                seen[ids[t, j]] += 1
+        kept = np.minimum(seen, cap)
+        offsets = np.concatenate([[0], np.cumsum(kept)])
+        return np.where(rank < cap, offsets[ids] + rank, -1).reshape(-1), kept, offsets
+    O.capacity_dispatch = cd
+
+
+def m_capacity_not_even(O):
+    O.expert_capacity = lambda k, cf, n, e: int(np.floor(k * cf * n / e))
+
+
 def m_zloss_no_square(O):
     orig = O.z_loss
     O.z_loss = lambda z: float(np.sqrt(orig(z)))
