@@ -215,18 +215,34 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
 }
 
-// Token-major row copy: x_sorted[inv_perm[n*k + j]] = x[n] for j < k, 16 bytes per lane.
+// Token-major row copy: x_sorted[inv_perm[n*k + j]] = x[n] for j < k. One wave per token:
+// the k destinations are wave-uniform, the lanes stream the row in 16-byte pieces, four
+// pieces per lane in flight, each read once and written k times.
 __global__ __launch_bounds__(256) void dispatch_copy_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ inv_perm, uint4* __restrict__ x_sorted,
     long long n_tokens, int k, int vec_per_row) {
-  const long long total = n_tokens * vec_per_row;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
-    const long long n = i / vec_per_row;
-    const int c = (int)(i - n * vec_per_row);
-    const uint4 v = x[i];
-    for (int j = 0; j < k; ++j) {
-      const int dst = inv_perm[n * k + j];
-      if (dst >= 0) x_sorted[(size_t)dst * vec_per_row + c] = v;
+  const int lane = threadIdx.x & 63;
+  const long long wave0 = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long n_waves = (long long)gridDim.x * 4;
+  for (long long n = wave0; n < n_tokens; n += n_waves) {
+    const uint4* row = x + (size_t)n * vec_per_row;
+    for (int c0 = 0; c0 < vec_per_row; c0 += 4 * 64) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * 64 + lane;
+        v[u] = c < vec_per_row ? row[c] : make_uint4(0, 0, 0, 0);
+      }
+      for (int j = 0; j < k; ++j) {
+        const int dst = inv_perm[n * k + j];  // wave-uniform
+        if (dst < 0) continue;
+        uint4* out = x_sorted + (size_t)dst * vec_per_row;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < vec_per_row) out[c] = v[u];
+        }
+      }
     }
   }
 }
@@ -241,8 +257,7 @@ static void launch_copy(const moe_config& c, const void* x, const int32_t* inv_p
                         hipStream_t stream) {
   if (!x_sorted) return;
   const int vpr = (int)(c.d_model * elem_size(c) / 16);
-  const long long total = c.n_tokens * vpr;
-  const int grid = (int)std::min<long long>((total + 255) / 256, 1 << 16);
+  const int grid = (int)std::min<long long>((c.n_tokens + 3) / 4, 1 << 16);
   dispatch_copy_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(x), inv_perm,
                                                  static_cast<uint4*>(x_sorted), c.n_tokens, c.top_k, vpr);
 }
