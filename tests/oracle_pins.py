@@ -431,6 +431,51 @@ def pin_capacity_top_choices_win(O):
     _close(y_cap, y_ref, 1e-12, "capacity >= load is dropless")
 
 
+def _objective(O, x, params, spec, dy, aux, zc):
+    y, r = O.forward_loop(x, params, spec)
+    _, _, L = O.load_balance(r.p, r.ids, spec.n_experts)
+    return float(np.sum(dy * y)) + aux * L + zc * O.z_loss(r.z)
+
+
+def pin_backward_matches_finite_differences(O):
+    """Every gradient of J = <dy, y> + a L + b z_loss against central finite differences of
+    the forward oracle itself (no shared code with the backward), for every router, both
+    activations, biases and a shared expert; 8 random coordinates per tensor."""
+    rng = np.random.default_rng(24)
+    N, d, f, E, k = 6, 4, 3, 4, 2
+    eps = 1e-6
+    for router, norm, act, bias, shared, scale in (
+            ("softmax_topk", True, "swiglu", False, True, 1.0), ("softmax_topk", False, "gelu", True, False, 2.5),
+            ("topk_softmax", True, "gelu", False, True, 1.0), ("sigmoid", True, "swiglu", False, False, 2.5),
+            ("sigmoid", False, "gelu", True, True, 1.0)):
+        spec = O.Spec(n_experts=E, top_k=k, router=router, norm_topk=norm, routed_scaling=scale, act=act)
+        params = _rand_params(rng, E, d, f, act, bias)
+        if shared:
+            params = _with_shared(rng, params, 1, d, 5, act, bias)
+        x = rng.normal(size=(N, d))
+        dy = rng.normal(size=(N, d))
+        aux, zc = 0.3, 0.2
+        g = O.backward(x, params, spec, dy, aux, zc)
+        J = lambda xx, pp: _objective(O, xx, pp, spec, dy, aux, zc)
+        checks = [("x", None, "dx")] + [(nm, nm, "d" + nm) for nm in ("w1", "w3", "w2", "b1", "b2", "w_g")
+                                        if params.get(nm) is not None]
+        checks[-1] = ("w_g", "w_g", "dw_g")
+        checks += [(nm, nm, "ds_" + nm[2:]) for nm in ("s_w1", "s_w3", "s_w2", "s_b1", "s_b2") if params.get(nm) is not None]
+        for label, name, gname in checks:
+            base = x if name is None else np.asarray(params[name])
+            for _ in range(8):
+                idx = tuple(rng.integers(0, s) for s in base.shape)
+                plus, minus = base.copy(), base.copy()
+                plus[idx] += eps
+                minus[idx] -= eps
+                if name is None:
+                    num = (J(plus, params) - J(minus, params)) / (2 * eps)
+                else:
+                    num = (J(x, dict(params, **{name: plus})) - J(x, dict(params, **{name: minus}))) / (2 * eps)
+                got = g[gname][idx]
+                assert abs(got - num) <= 1e-6 * max(1.0, abs(num)), (router, norm, act, label, idx, got, num)
+
+
 def pin_routed_scaling(O):
     rng = np.random.default_rng(12)
     z = rng.normal(size=(11, 6))

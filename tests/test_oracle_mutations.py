@@ -218,6 +218,37 @@ def m_capacity_not_even(O):
     O.expert_capacity = lambda k, cf, n, e: int(np.floor(k * cf * n / e))
 
 
+def m_bw_renorm_jacobian_dropped(O):  # gradient of a renormalised gate taken as if unnormalised
+    orig = O.gate_weights_backward
+    def gwb(z_row, ids_row, dw, spec):
+        if spec.router == "softmax_topk" and spec.norm_topk:
+            wt = O.softmax(np.asarray(z_row)[ids_row][None, :])[0]
+            dz = np.zeros(len(z_row))
+            dz[ids_row] = spec.routed_scaling * wt * dw
+            return dz
+        return orig(z_row, ids_row, dw, spec)
+    O.gate_weights_backward = gwb
+
+
+def m_bw_silu_derivative(O):  # silu'(g) taken as sigmoid(g)
+    orig = O.expert_ffn_backward
+    def efb(xr, act, do, w1, w2, w3=None, b1=None, b2=None):
+        if act != "swiglu":
+            return orig(xr, act, do, w1, w2, w3, b1, b2)
+        gt, ut = xr @ np.asarray(w1).T, xr @ np.asarray(w3).T
+        sg = O.sigmoid(gt)
+        dh = do @ np.asarray(w2)
+        du, dg = dh * gt * sg, dh * ut * sg
+        return dg @ w1 + du @ w3, {"dw1": dg.T @ xr, "dw3": du.T @ xr, "dw2": do.T @ (gt * sg * ut)}
+    O.expert_ffn_backward = efb
+
+
+def m_bw_aux_ignored(O):  # the load-balancing loss contributes no router gradient
+    orig = O.backward
+    O.backward = lambda x, params, spec, dy, aux_coef=0.0, z_coef=0.0, logit_bias=None, sel_bias=None: \
+        orig(x, params, spec, dy, 0.0, z_coef, logit_bias, sel_bias)
+
+
 def m_zloss_no_square(O):
     orig = O.z_loss
     O.z_loss = lambda z: float(np.sqrt(orig(z)))
