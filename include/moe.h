@@ -1,5 +1,5 @@
 /*
- * moe.h -- C ABI of a dropless top-k mixture-of-experts FFN layer forward for AMD MI355X
+ * moe.h -- C ABI of a dropless top-k mixture-of-experts FFN layer (forward and backward) for AMD MI355X
  * (gfx950, CDNA4). Every step runs in hand-written HIP kernels; this header carries no HIP
  * or framework types, only plain pointers and sizes.
  *
@@ -76,7 +76,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Which call a workspace is sized for. */
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_COMBINE = 3, MOE_OP_FORWARD = 4,
-  MOE_OP_SHARED_FFN = 5
+  MOE_OP_SHARED_FFN = 5, MOE_OP_BACKWARD = 6
 } moe_op;
 
 typedef struct {
@@ -221,6 +221,52 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const void* s_w2, const void* s_b2,
                        void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* Gradients written by moe_backward: device pointers owned by the caller, each shaped like
+ * the tensor it is the gradient of, element type T unless stated. */
+typedef struct {
+  void* dx;         /* [N,d] */
+  void* dw_router;  /* [E,d] */
+  void* dw1;        /* [E,d_ff,d] */
+  void* dw3;        /* [E,d_ff,d] (SwiGLU) or NULL */
+  void* db1;        /* [E,d_ff] (has_bias) or NULL */
+  void* dw2;        /* [E,d,d_ff] */
+  void* db2;        /* [E,d] (has_bias) or NULL */
+  void* ds_w1;      /* shared expert (d_ff_shared > 0; NULL otherwise), shaped like s_w1 .. s_b2 */
+  void* ds_w3;
+  void* ds_b1;
+  void* ds_w2;
+  void* ds_b2;
+  float* dz;        /* [N,E] float32 dJ/dz (router logits, logit_bias included) or NULL */
+  float* dgate;     /* [N,k] float32 dJ/dw (the gates after routed_scaling) or NULL */
+} moe_grads;
+
+/* Backward of the dropless layer: the gradients of
+ *     J = <dy, y> + aux_coef * L + z_coef * z_loss
+ * (y the output of moe_forward with the same inputs and cfg->capacity_factor = 0; L and
+ * z_loss the statistics of moe_route) with respect to x and every weight, by the chain
+ * rule through [L7.8] §2.1 (output equation; routers table weights), §2.3 (L = E sum f P
+ * with f piecewise constant, so only P = mean softmax(z) carries gradient) and [RB-15]
+ * §15.3 (z-loss). The selection (top-k, sel_bias) carries none ([L7.8] §2.5). Nothing is
+ * kept from a forward call: routing, dispatch and the up projection are recomputed (their
+ * outputs topk_ids, topk_w, counts, stats are written as moe_route writes them).
+ * bfloat16 only (T = MOE_BF16; MOE_ERR_UNSUPPORTED for float32 and for
+ * capacity_factor > 0). Accumulation is float32; the pre-activations, the gate-scaled h,
+ * the activation gradients and dx_sorted are rounded to bfloat16, dz is split into two
+ * bfloat16 terms for the products with W_g and x; every gradient is rounded once.
+ * In: the forward's inputs; dy [N,d] T; aux_coef, z_coef: finite.
+ * Out: *grads (dw3 / db1 / db2 / shared gradients required exactly when the matching
+ * weight is); topk_ids, topk_w, counts, stats as in moe_route.
+ * ws: moe_workspace_size(cfg, MOE_OP_BACKWARD) bytes. */
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* logit_bias, const float* sel_bias,
+                        const void* w1, const void* w3, const void* b1,
+                        const void* w2, const void* b2,
+                        const void* s_w1, const void* s_w3, const void* s_b1,
+                        const void* s_w2, const void* s_b2,
+                        const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
+                        int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Aux-free load balancing, one update step ([L7.8] §2.5): with load_e = counts[e] and
  * mean = sum_e load_e / E,

@@ -32,6 +32,7 @@ class Op(enum.IntEnum):
     COMBINE = 3
     FORWARD = 4
     SHARED_FFN = 5
+    BACKWARD = 6
 
 
 class MoeError(RuntimeError):
@@ -102,6 +103,11 @@ _lib = None
 _P = ctypes.c_void_p
 
 
+class MoeGradsStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_router", "dw1", "dw3", "db1", "dw2", "db2", "ds_w1",
+                                               "ds_w3", "ds_b1", "ds_w2", "ds_b2", "dz", "dgate")]
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -124,10 +130,12 @@ def lib():
     L.moe_dispatch_capacity.argtypes = [S, ctypes.c_float] + [_P] * 10 + [ctypes.c_size_t, _P]
     L.moe_expert_capacity.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_int64, ctypes.c_int32]
     L.moe_expert_capacity.restype = ctypes.c_int64
+    L.moe_backward.argtypes = ([S] + [_P] * 15 + [ctypes.c_float, ctypes.c_float, ctypes.POINTER(MoeGradsStruct)]
+                               + [_P] * 5 + [ctypes.c_size_t, _P])
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
-                 "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity"):
+                 "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity", "moe_backward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -372,6 +380,56 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
                            _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]), _ptr(ws), ws.numel(),
                            ev, _stream())
     _check(st, "moe_forward")
+    return out
+
+
+GRAD_NAMES = ("dx", "dw_router", "dw1", "dw3", "db1", "dw2", "db2", "ds_w1", "ds_w3", "ds_b1", "ds_w2", "ds_b2",
+              "dz", "dgate")
+
+
+def moe_backward(cfg: LayerConfig, x, w_router, w1, w3, w2, dy, b1=None, b2=None, logit_bias=None, sel_bias=None,
+                 *, shared: Optional[dict] = None, aux_coef: float = 0.0, z_coef: float = 0.0, ws=None, out=None):
+    """Gradients of <dy, y> + aux_coef L + z_coef z_loss (bfloat16, dropless). Returns a dict
+    with dx, dw_router, dw1, dw3, db1, dw2, db2, the shared expert's ds_* (None where the
+    weight is absent), dz [N,E] and dgate [N,k] (float32), and the recomputed routing
+    (topk_ids, topk_w, counts, stats). `out` / `ws` may hold preallocated buffers."""
+    N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
+    T = cfg.torch_dtype
+    sh = shared or {}
+    s_w1, s_w3, s_w2, s_b1, s_b2 = (sh.get(n) for n in ("s_w1", "s_w3", "s_w2", "s_b1", "s_b2"))
+    swi, bias, F = cfg.act == "swiglu", cfg.has_bias, cfg.d_ff_shared
+    if out is None:
+        _want(x, "x", (N, d), T)
+        _want(dy, "dy", (N, d), T)
+        _want(w_router, "w_router", (E, d), T)
+        _want(w1, "w1", (E, f, d), T)
+        _want(w2, "w2", (E, d, f), T)
+        _want(w3, "w3", (E, f, d), T, optional=not swi)
+        _want(b1, "b1", (E, f), T, optional=not bias)
+        _want(b2, "b2", (E, d), T, optional=not bias)
+        _want(logit_bias, "logit_bias", (E,), torch.float32, optional=True)
+        _want(sel_bias, "sel_bias", (E,), torch.float32, optional=True)
+        dev = w_router.device
+        new = lambda shape, dt=T: torch.empty(shape, dtype=dt, device=dev)
+        out = {
+            "dx": new((N, d)), "dw_router": new((E, d)), "dw1": new((E, f, d)), "dw3": new((E, f, d)) if swi else None,
+            "db1": new((E, f)) if bias else None, "dw2": new((E, d, f)), "db2": new((E, d)) if bias else None,
+            "ds_w1": new((F, d)) if F else None, "ds_w3": new((F, d)) if F and swi else None,
+            "ds_b1": new((F,)) if F and bias else None, "ds_w2": new((d, F)) if F else None,
+            "ds_b2": new((d,)) if F and bias else None,
+            "dz": new((N, E), torch.float32), "dgate": new((N, k), torch.float32),
+            "topk_ids": new((N, k), torch.int32), "topk_w": new((N, k), torch.float32),
+            "counts": new((E,), torch.int32), "stats": new((2 * E + 2,), torch.float32),
+        }
+    if ws is None:
+        ws = workspace(cfg, Op.BACKWARD, w_router.device)
+    g = MoeGradsStruct(*[None if out.get(n) is None else out[n].data_ptr() for n in GRAD_NAMES])
+    st = lib().moe_backward(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(sel_bias),
+                            _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1), _ptr(s_w3), _ptr(s_b1),
+                            _ptr(s_w2), _ptr(s_b2), _ptr(dy), float(aux_coef), float(z_coef), ctypes.byref(g),
+                            _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]),
+                            _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_backward")
     return out
 
 

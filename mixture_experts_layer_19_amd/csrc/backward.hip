@@ -1,0 +1,867 @@
+// Backward of the layer (bfloat16, dropless): gradients of
+//     J = <dy, y> + aux_coef L + z_coef z_loss
+// with respect to x, the router and every expert weight, by the chain rule through the
+// forward steps ("Mixture of Experts: routing, sorted dispatch, Switch aux loss, aux-free
+// bias" (L7.8) §2.1 output equation and routers table, §2.3 load-balancing loss, §2.5: the
+// selection bias never weighs; "15. Mixture of Experts" (RustingBrain) §15.3 z-loss).
+//
+// Nothing is kept from the forward: routing, dispatch and the up projection are recomputed
+// (the up projection by the forward's GEMM with an epilogue that keeps the pre-activations).
+// Per expert e with sorted rows a (gate w_a, token t(a)), SwiGLU:
+//   dh'_a   = dy_t W2_e                       (unscaled: dgate_a = <dh'_a, h_a> = <dy_t, o_a>)
+//   dh_a    = w_a dh'_a;  dg = dh u s (1 + g (1 - s)), du = dh g s   (s = sigmoid(g))
+//   dx_s_a  = dg W1_e + du W3_e;   dW2_e = sum_a dy_t^T (w_a h_a);   dW1_e = sum_a dg^T x_t
+// GELU: da = dh gelu'(a) with a = x W1^T + b1, plus db1 / db2 column sums and the b2 term of
+// dgate. The router gradient dz follows from dgate through the routers table's weights, the
+// Switch loss through P = mean softmax(z) (f is piecewise constant) and the z-loss; then
+// dx += dz W_g and dW_g = dz^T x.
+//
+// The products run on one grouped bfloat16 MFMA kernel (bwd_gemm_kernel) whose B operand is
+// always stored with its output axis contiguous (weights [K][N] or activations [rows][N]),
+// and whose A operand is either the row operand (grouped mode: expert-sorted rows, K
+// contiguous) or, for weight gradients, a second activation with M contiguous (ragged K =
+// the expert's rows). Operands that are not K-contiguous are transposed in registers on the
+// way into LDS, so every LDS tile holds 32 consecutive k per row, as MFMA operands want.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 128, kBN = 256, kBK = 32, kThreads = 256;
+constexpr int kGM = 8, kGN = 4;          // supertile: 8 m-tiles x 4 n-tiles (m fastest)
+constexpr int kStageStride = 40;         // epilogue staging row (floats): the two half-waves,
+                                         // 4 rows apart, hit disjoint banks
+
+enum Mode { kGrouped = 0, kWgrad = 1 };
+enum Epi { kStoreT = 0, kStoreF32 = 1, kSwigluBwd = 2, kGeluBwd = 3 };
+
+struct BwdGemm {
+  // Segment s of the reduction: grouped: k in [0, klen[s]) of a[s] (rows of lda elements, K
+  // contiguous) and b[s] (k rows of ldb elements, N contiguous, + e * b_estride per
+  // expert); the segments follow each other along K (each padded to a multiple of 8).
+  // wgrad: both operands are [rows][lda | ldb] with M (resp. N) contiguous; expert e reduces
+  // over its rows [offsets[e], offsets[e+1]) (offsets null: rows [0, klen[0])), and a
+  // second segment, when a[1] is set, repeats the same rows with a[1] / b[1].
+  const uint16_t* a[2];
+  const uint16_t* b[2];
+  long long lda, ldb, b_estride;
+  int klen[2];
+  int M, N;
+  const int* tiles;
+  const int* offsets;
+  int n_experts;
+  int n_tiles_n;
+  // output: grouped rows row0 + r; wgrad rows m of expert e (m < m_split: c, else c_hi)
+  void* c;
+  void* c_hi;
+  long long ldc, c_estride;
+  int m_split;
+  const float* c_in;    // kStoreF32: added before the store (may alias c)
+  // activation backward (grouped): pre-activations, gates, row partials of <dh', h>
+  const uint16_t* pre;  // SwiGLU [rows][2 N] (gate | up), GELU [rows][N]
+  const float* gate;    // [rows] or null (1)
+  float* part;          // [rows][n_part] or null
+  int n_part;
+};
+
+// Element offset of 16-byte chunk c (8 consecutive k) of tile row r. Rows are 64 bytes. The
+// row permutation and chunk XOR are chosen so that (i) an MFMA operand read -- 16 consecutive
+// rows at one chunk per quarter-wave -- covers all 64 banks, and (ii) a transposed write --
+// rows 8 q + j for 32 values of q at one chunk -- spreads over all bank groups.
+MOE_DEV int lds_elem(int r, int c) {
+  return ((r ^ ((r >> 3) & 3)) * 4 + (c ^ (((r >> 2) ^ (r >> 5)) & 3))) * 8;
+}
+
+MOE_DEV uint32_t dword_of(const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; }
+// element j of four consecutive k rows r[0..3] (8 columns each): the column's 4 k values
+MOE_DEV uint2 column4(const uint4* r, int j) {
+  const int q = j >> 1;
+  auto pk = [&](uint32_t lo, uint32_t hi) {
+    return (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+  };
+  return make_uint2(pk(dword_of(r[0], q), dword_of(r[1], q)), pk(dword_of(r[2], q), dword_of(r[3], q)));
+}
+
+MOE_DEV void supertile(long long l, int me, int NT, int* mt, int* nt) {
+  const int band = (int)(l / ((long long)kGM * NT));
+  const int lb = (int)(l - (long long)band * kGM * NT);
+  const int bm = min(kGM, me - kGM * band);
+  const int grpn = lb / (kGN * bm);
+  const int r = lb - grpn * kGN * bm;
+  *mt = kGM * band + r % bm;
+  *nt = grpn * kGN + r / bm;
+}
+
+MOE_DEV float gelu_grad(float a) {
+  return 0.5f * (1.0f + erff(a * 0.70710678118654752440f)) + a * 0.39894228040143267794f * expf(-0.5f * a * a);
+}
+
+MOE_DEV void unpack8(const uint4& v, float* o) {
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+  o[4] = __uint_as_float(v.z << 16);
+  o[5] = __uint_as_float(v.z & 0xffff0000u);
+  o[6] = __uint_as_float(v.w << 16);
+  o[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+MOE_DEV uint4 pack8(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// ---------------------------------------------------------------------------------------
+// Grouped bfloat16 GEMM on MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulation).
+// Workgroup tile 128 x 256, four waves of 64 x 128 (2 x 4 blocks of 32 x 32). K advances 32
+// at a time through two LDS stages: the next slab's global loads are issued before the
+// current slab's multiplies and written to the other stage after them (one barrier per slab).
+// Grid: 8 * ceil(S / 8) workgroups for S tiles; workgroup b runs on XCD b mod 8 and takes
+// tile (b mod 8) * ceil(S / 8) + b / 8, so each XCD works through a contiguous run of the
+// tile order (expert-major, supertiles of 8 m-tiles x 4 n-tiles) and shares its operands in
+// its own L2.
+// ---------------------------------------------------------------------------------------
+template <int MODE, int EPI>
+__global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kBK];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int NT = g.n_tiles_n;
+
+  // ---- tile
+  long long S;
+  int MTe = 0;
+  if (MODE == kGrouped) {
+    S = (long long)g.tiles[0] * NT;
+  } else {
+    MTe = (g.M + kBM - 1) / kBM;
+    S = (long long)g.n_experts * MTe * NT;
+  }
+  const long long per = (S + 7) / 8;
+  const long long slot = blockIdx.x >> 3;
+  const long long s = (long long)(blockIdx.x & 7) * per + slot;
+  if (slot >= per || s >= S) return;
+
+  int e, mt, nt, row0 = 0, rows = 0, m0 = 0, r0 = 0, kr = 0;
+  if (MODE == kGrouped) {
+    const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
+    e = probe[0];
+    const int ts = probe[3], me = probe[4];
+    supertile(s - (long long)ts * NT, me, NT, &mt, &nt);
+    const int* tq = g.tiles + kTileHdr + kTileInts * (ts + mt);
+    row0 = tq[1];
+    rows = tq[2];
+  } else {
+    e = (int)(s / ((long long)MTe * NT));
+    supertile(s - (long long)e * MTe * NT, MTe, NT, &mt, &nt);
+    m0 = mt * kBM;
+    r0 = g.offsets ? g.offsets[e] : 0;
+    const int r1 = g.offsets ? g.offsets[e + 1] : g.klen[0];
+    kr = max(r1 - r0, 0);
+  }
+  const int n0 = nt * kBN;
+  const int M = g.M, N = g.N;
+
+  // ---- reduction length: segments padded to multiples of 8
+  int kp0, ktot;
+  if (MODE == kGrouped) {
+    kp0 = (g.klen[0] + 7) & ~7;
+    ktot = kp0 + ((g.klen[1] + 7) & ~7);
+  } else {
+    kp0 = (kr + 7) & ~7;
+    ktot = g.a[1] ? 2 * kp0 : kp0;
+  }
+  const int nk = (ktot + kBK - 1) / kBK;
+
+  // ---- load geometry
+  // A, K-contiguous (grouped): chunk q = tid + 256 i (i = 0, 1) is row q >> 2, chunk q & 3.
+  // A, M-contiguous (wgrad, waves 0 and 1): 4 k rows (4 kq ..) x 8 columns (8 mb ..).
+  // B (both modes): 4 k rows (4 kq ..) x 8 columns (8 nb ..), all four waves.
+  const int a_mb = lane & 15, a_kq = 4 * wave + (lane >> 4);
+  const int b_nb = lane & 31, b_kq = 2 * wave + (lane >> 5);
+  const uint16_t* b_exp[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) b_exp[q] = g.b[q] ? g.b[q] + (MODE == kGrouped ? (size_t)e * g.b_estride : 0) : nullptr;
+
+  uint4 ra[4], rb[4];
+  auto seg_of = [&](int kk, int* local) {
+    const int sg = kk >= kp0 ? 1 : 0;
+    *local = kk - sg * kp0;
+    return sg;
+  };
+  auto gload = [&](int kt) {
+    const int kbase = kt * kBK;
+    if (MODE == kGrouped) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = tid + 256 * i;
+        const int r = q >> 2, kk = kbase + (q & 3) * 8;
+        int local;
+        const int sg = seg_of(kk, &local);
+        const bool ok = r < rows && kk < ktot && local < g.klen[sg];
+        ra[i] = ok ? *reinterpret_cast<const uint4*>(g.a[sg] + (size_t)(row0 + r) * g.lda + local)
+                   : make_uint4(0, 0, 0, 0);
+      }
+    } else if (wave < 2) {
+      const int m = m0 + 8 * a_mb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kbase + 4 * a_kq + i;
+        int local;
+        const int sg = seg_of(kk, &local);
+        const bool ok = m < M && kk < ktot && local < kr;
+        ra[i] = ok ? *reinterpret_cast<const uint4*>(g.a[sg] + (size_t)(r0 + local) * g.lda + m)
+                   : make_uint4(0, 0, 0, 0);
+      }
+    }
+    const int n = n0 + 8 * b_nb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = kbase + 4 * b_kq + i;
+      int local;
+      const int sg = seg_of(kk, &local);
+      bool ok = n < N && kk < ktot;
+      size_t row;
+      if (MODE == kGrouped) {
+        ok = ok && local < g.klen[sg];
+        row = (size_t)local;
+      } else {
+        ok = ok && local < kr;
+        row = (size_t)(r0 + local);
+      }
+      rb[i] = ok ? *reinterpret_cast<const uint4*>(b_exp[sg] + row * g.ldb + n) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+    if (MODE == kGrouped) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = tid + 256 * i;
+        *reinterpret_cast<uint4*>(&sA[buf][lds_elem(q >> 2, q & 3)]) = ra[i];
+      }
+    } else if (wave < 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint2*>(&sA[buf][lds_elem(8 * a_mb + j, a_kq >> 1) + 4 * (a_kq & 1)]) = column4(ra, j);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint2*>(&sB[buf][lds_elem(8 * b_nb + j, b_kq >> 1) + 4 * (b_kq & 1)]) = column4(rb, j);
+  };
+
+  // MFMA operand reads: lane holds row (lane & 31) of a 32-row block at k 8 (lane >> 5) ..
+  int offa[2][2], offb[2][4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) offa[ks][i] = lds_elem(wm * 64 + 32 * i + (lane & 31), 2 * ks + (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) offb[ks][j] = lds_elem(wn * 128 + 32 * j + (lane & 31), 2 * ks + (lane >> 5));
+  }
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 fa[2], fb[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][offa[ks][i]]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][offb[ks][j]]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < nk) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: each 32 x 32 block goes through the wave's own LDS staging area (float32,
+  // padded rows), then lane l owns row l >> 1, columns 16 (l & 1) .. + 15 of the block.
+  float* st = reinterpret_cast<float*>(&sB[0][0]) + wave * 32 * kStageStride;
+  const int er = lane >> 1, ec = (lane & 1) * 16;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rl = wm * 64 + 32 * i + er;  // tile row of this lane's output row
+    bool row_ok;
+    size_t grow = 0;                       // grouped: sorted row
+    uint16_t* crow = nullptr;              // wgrad: output row
+    if (MODE == kGrouped) {
+      row_ok = rl < rows;
+      grow = (size_t)(row0 + rl);
+    } else {
+      const int m = m0 + rl;
+      row_ok = m < M;
+      if (row_ok)
+        crow = (m < g.m_split) ? static_cast<uint16_t*>(g.c) + (size_t)e * g.c_estride + (size_t)m * g.ldc
+                               : static_cast<uint16_t*>(g.c_hi) + (size_t)e * g.c_estride + (size_t)(m - g.m_split) * g.ldc;
+    }
+    float w = 1.f;
+    if ((EPI == kSwigluBwd || EPI == kGeluBwd) && row_ok && g.gate) w = g.gate[grow];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        st[((v >> 2) * 8 + 4 * (lane >> 5) + (v & 3)) * kStageStride + (lane & 31)] = acc[i][j][v];
+      __builtin_amdgcn_wave_barrier();
+      float val[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(st + er * kStageStride + ec + 4 * q);
+        val[4 * q] = f.x;
+        val[4 * q + 1] = f.y;
+        val[4 * q + 2] = f.z;
+        val[4 * q + 3] = f.w;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int col = n0 + wn * 128 + 32 * j + ec;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cc = col + 8 * h;
+        if (!row_ok || cc >= N) continue;
+        float* v8 = val + 8 * h;
+        if (EPI == kStoreT) {
+          uint16_t* dst = (MODE == kGrouped) ? static_cast<uint16_t*>(g.c) + grow * g.ldc + cc : crow + cc;
+          *reinterpret_cast<uint4*>(dst) = pack8(v8);
+        } else if (EPI == kStoreF32) {
+          float* dst = static_cast<float*>(g.c) + grow * g.ldc + cc;
+          if (g.c_in) {
+            const float* src = g.c_in + grow * g.ldc + cc;
+            const float4 p0 = *reinterpret_cast<const float4*>(src);
+            const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
+            v8[0] += p0.x; v8[1] += p0.y; v8[2] += p0.z; v8[3] += p0.w;
+            v8[4] += p1.x; v8[5] += p1.y; v8[6] += p1.z; v8[7] += p1.w;
+          }
+          *reinterpret_cast<float4*>(dst) = make_float4(v8[0], v8[1], v8[2], v8[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
+        } else if (EPI == kSwigluBwd) {
+          float gg[8], uu[8], dg[8], du[8];
+          unpack8(*reinterpret_cast<const uint4*>(g.pre + grow * 2 * (size_t)N + cc), gg);
+          unpack8(*reinterpret_cast<const uint4*>(g.pre + grow * 2 * (size_t)N + N + cc), uu);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float sg = sigmoid_f(gg[q]);
+            psum += v8[q] * (gg[q] * sg * uu[q]);
+            const float dh = w * v8[q];
+            dg[q] = dh * uu[q] * sg * (1.f + gg[q] * (1.f - sg));
+            du[q] = dh * gg[q] * sg;
+          }
+          uint16_t* dst = static_cast<uint16_t*>(g.c) + grow * g.ldc + cc;
+          *reinterpret_cast<uint4*>(dst) = pack8(dg);
+          *reinterpret_cast<uint4*>(dst + N) = pack8(du);
+        } else {  // kGeluBwd
+          float aa[8], da[8];
+          unpack8(*reinterpret_cast<const uint4*>(g.pre + grow * (size_t)N + cc), aa);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            psum += v8[q] * gelu_erf(aa[q]);
+            da[q] = w * v8[q] * gelu_grad(aa[q]);
+          }
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.c) + grow * g.ldc + cc) = pack8(da);
+        }
+      }
+    }
+    if ((EPI == kSwigluBwd || EPI == kGeluBwd) && g.part) {
+      psum += __shfl_xor(psum, 1, kWave);
+      if ((lane & 1) == 0 && row_ok) g.part[grow * g.n_part + 2 * nt + wn] = psum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Router backward, one wave per token: dJ/dw_{t,j} = <dh'_a, h_a> summed over the down
+// projection's column tiles (+ <dy_t, b2_e> with GELU biases), then dz_t through the
+// routers table's weights, plus the Switch loss term aux_coef (E/N) p (f - <p, f>) and the
+// z-loss term z_coef (2 lse / N) p. Writes dz (float32), its split dz = hi + lo into two
+// bfloat16 halves [t][0, E8) and [t][E8, 2 E8) (zero-padded) for the MFMA products with
+// the router weights and x, and dgate.
+// ---------------------------------------------------------------------------------------
+constexpr int kRQ = kMaxExperts / kWave;
+
+struct RouterBwd {
+  const float* z;
+  const int32_t* ids;
+  const int32_t* inv_perm;
+  const float* part;
+  int n_part;
+  const int32_t* counts;
+  const uint16_t* dy;
+  const uint16_t* b2;
+  int n_tokens, E, k, d, router, norm_topk, E8;
+  float sc, aux_coef, z_coef;
+  float* dz;
+  float* dgate;
+  uint16_t* dz_hl;
+};
+
+__global__ __launch_bounds__(256) void router_backward_kernel(RouterBwd a) {
+  __shared__ float s_dz[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n_tokens) return;  // whole waves; no workgroup barrier below
+  float* sd = s_dz[wave];
+  const int E = a.E, k = a.k;
+  const float* zt = a.z + (size_t)t * E;
+
+  float zv[kRQ], ex[kRQ];
+  float m = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kRQ; ++q) {
+    const int e = lane + kWave * q;
+    zv[q] = e < E ? zt[e] : -INFINITY;
+    m = fmaxf(m, zv[q]);
+  }
+  m = wave_max(m);
+  float ssum = 0.f;
+#pragma unroll
+  for (int q = 0; q < kRQ; ++q) {
+    ex[q] = (lane + kWave * q < E) ? expf(zv[q] - m) : 0.f;
+    ssum += ex[q];
+  }
+  ssum = wave_sum(ssum);
+  const float inv = 1.f / ssum;
+  const float lse = m + logf(ssum);
+  const float invN = 1.f / (float)a.n_tokens;
+
+  float spf = 0.f;
+  if (a.aux_coef != 0.f) {
+#pragma unroll
+    for (int q = 0; q < kRQ; ++q) {
+      const int e = lane + kWave * q;
+      if (e < E) spf += ex[q] * inv * ((float)a.counts[e] * invN);
+    }
+    spf = wave_sum(spf);
+  }
+
+  // the chosen experts: lane j < k holds choice j
+  int id = 0;
+  float dw = 0.f, zj = -INFINITY;
+  if (lane < k) {
+    id = a.ids[(size_t)t * k + lane];
+    const int pos = a.inv_perm[(size_t)t * k + lane];
+    const float* pp = a.part + (size_t)pos * a.n_part;
+    for (int p = 0; p < a.n_part; ++p) dw += pp[p];
+    zj = zt[id];
+  }
+  if (a.b2) {
+    const uint16_t* dyt = a.dy + (size_t)t * a.d;
+    for (int j = 0; j < k; ++j) {
+      const int idj = __shfl(id, j, kWave);
+      const uint16_t* bj = a.b2 + (size_t)idj * a.d;
+      float acc = 0.f;
+      for (int c = lane; c < a.d; c += kWave) acc += bf16_to_f32(dyt[c]) * bf16_to_f32(bj[c]);
+      acc = wave_sum(acc);
+      if (lane == j) dw += acc;
+    }
+  }
+
+  // gate term of the chosen experts (contrib, added at id) and of every expert (base)
+  float contrib = 0.f, cfull = 0.f;
+  const bool chosen = lane < k;
+  if (a.router == MOE_ROUTER_TOPK_SOFTMAX || (a.router == MOE_ROUTER_SOFTMAX_TOPK && a.norm_topk)) {
+    const float zm = wave_max(chosen ? zj : -INFINITY);
+    const float ej = chosen ? expf(zj - zm) : 0.f;
+    const float wt = ej / wave_sum(ej);
+    const float c = wave_sum(wt * dw);
+    contrib = a.sc * wt * (dw - c);
+  } else if (a.router == MOE_ROUTER_SOFTMAX_TOPK) {
+    const float pj = chosen ? expf(zj - m) * inv : 0.f;
+    cfull = wave_sum(pj * a.sc * dw);  // dz_e = p_e (gp_e - <p, gp>), gp = sc dw on the chosen
+    contrib = pj * a.sc * dw;
+  } else {
+    const float sg = chosen ? sigmoid_f(zj) : 0.f;
+    float dsg;
+    if (a.norm_topk) {
+      const float S = wave_sum(sg);
+      const float c = wave_sum((sg / S) * dw);
+      dsg = a.sc / S * (dw - c);
+    } else {
+      dsg = a.sc * dw;
+    }
+    contrib = dsg * sg * (1.f - sg);
+  }
+
+#pragma unroll
+  for (int q = 0; q < kRQ; ++q) {
+    const int e = lane + kWave * q;
+    if (e < E) {
+      const float p = ex[q] * inv;
+      float v = -p * cfull;
+      if (a.aux_coef != 0.f) v += a.aux_coef * ((float)E * invN) * p * ((float)a.counts[e] * invN - spf);
+      if (a.z_coef != 0.f) v += a.z_coef * (2.f * lse * invN) * p;
+      sd[e] = v;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (chosen) sd[id] += contrib;  // the k ids of a token are distinct
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < kRQ; ++q) {
+    const int e = lane + kWave * q;
+    if (e < a.E8) {
+      const float v = e < E ? sd[e] : 0.f;
+      if (e < E) a.dz[(size_t)t * E + e] = v;
+      const uint16_t hi = f32_to_bf16(v);
+      a.dz_hl[(size_t)t * 2 * a.E8 + e] = hi;
+      a.dz_hl[(size_t)t * 2 * a.E8 + a.E8 + e] = f32_to_bf16(v - bf16_to_f32(hi));
+    }
+  }
+  if (chosen && a.dgate) a.dgate[(size_t)t * k + lane] = dw;
+}
+
+// Clears n 16-byte words (grid-stride; used instead of a memset so the sequence can be captured).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// out[e][c] = sum over rows r of expert e (offsets, or rows [0, n_rows)) of scale[r] * M[r][c]
+// (scale null: 1), float32 in row order, rounded to bfloat16 once.
+__global__ __launch_bounds__(256) void colsum_kernel(const uint16_t* __restrict__ Mx, long long ld,
+                                                     const float* __restrict__ scale, const int* __restrict__ offsets,
+                                                     int n_rows, int C, uint16_t* __restrict__ out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int e = blockIdx.y;
+  if (c >= C) return;
+  const int lo = offsets ? offsets[e] : 0, hi = offsets ? offsets[e + 1] : n_rows;
+  float s = 0.f;
+  for (int r = lo; r < hi; ++r) {
+    const float v = bf16_to_f32(Mx[(size_t)r * ld + c]);
+    s += scale ? scale[r] * v : v;
+  }
+  out[(size_t)e * C + c] = f32_to_bf16(s);
+}
+
+// dx[t] = sum_j dx_sorted[inv_perm[t k + j]] (j ascending) + R[t] (float32), rounded once;
+// one wave per token, 8 columns per lane and step.
+__global__ __launch_bounds__(256) void bwd_combine_kernel(const uint16_t* __restrict__ dxs, const int32_t* __restrict__ inv_perm,
+                                                          const float* __restrict__ R, long long n_tokens, int k, int d,
+                                                          uint16_t* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n_tokens) return;
+  for (int c = 8 * lane; c < d; c += 8 * kWave) {
+    float acc[8], v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int row = inv_perm[t * k + j];
+      unpack8(*reinterpret_cast<const uint4*>(dxs + (size_t)row * d + c), v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    }
+    const float* rr = R + (size_t)t * d + c;
+    const float4 p0 = *reinterpret_cast<const float4*>(rr);
+    const float4 p1 = *reinterpret_cast<const float4*>(rr + 4);
+    acc[0] += p0.x; acc[1] += p0.y; acc[2] += p0.z; acc[3] += p0.w;
+    acc[4] += p1.x; acc[5] += p1.y; acc[6] += p1.z; acc[7] += p1.w;
+    *reinterpret_cast<uint4*>(dx + (size_t)t * d + c) = pack8(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Workspace of the backward (after the forward's route / ffn / forward regions).
+// ---------------------------------------------------------------------------------------
+struct BwdBufs {
+  int* tiles128;    // m-tile table of the sorted rows, 128-row tiles
+  int* tiles_d256;  // dense tables over the N token rows (shared expert, router)
+  int* tiles_d128;
+  float* z;         // [N][E] logits
+  float* dz;        // [N][E] (used when the caller passes none)
+  float* part;      // [A][n_part]
+  uint16_t* dz_hl;  // [N][2 E8]
+  uint16_t* pre;    // [A][2 F] or [A][F]
+  uint16_t* dpre;
+  uint16_t* dxs;    // [A][d]
+  float* R;         // [N][d] dz W_g (+ shared dx)
+  uint16_t* pre_s;  // shared expert: [N][2 Fs] or [N][Fs]
+  uint16_t* dpre_s;
+  uint16_t* h_s;    // [N][Fs]
+  size_t bytes;
+};
+
+int n_part_of(int F) { return 2 * ((F + kBN - 1) / kBN); }
+int e8_of(int E) { return (E + 7) & ~7; }
+
+BwdBufs bwd_bufs(const moe_config& c, char* base) {
+  WsCarver w(base);
+  const size_t N = (size_t)c.n_tokens, A = N * (size_t)c.top_k, E = (size_t)c.n_experts;
+  const size_t d = (size_t)c.d_model, F = (size_t)c.d_ff, Fs = (size_t)std::max(c.d_ff_shared, 0);
+  const size_t pf = c.act == MOE_ACT_SWIGLU ? 2 : 1;
+  BwdBufs b{};
+  b.tiles128 = w.take_t<int>(kTileHdr + kTileInts * ((A + kBM - 1) / kBM + E));
+  b.tiles_d256 = w.take_t<int>(kTileHdr + kTileInts * ((N + 255) / 256));
+  b.tiles_d128 = w.take_t<int>(kTileHdr + kTileInts * ((N + kBM - 1) / kBM));
+  b.z = w.take_t<float>(N * E);
+  b.dz = w.take_t<float>(N * E);
+  b.part = w.take_t<float>(A * (size_t)n_part_of((int)F));
+  b.dz_hl = w.take_t<uint16_t>(N * 2 * (size_t)e8_of((int)E));
+  b.pre = w.take_t<uint16_t>(A * pf * F);
+  b.dpre = w.take_t<uint16_t>(A * pf * F);
+  b.dxs = w.take_t<uint16_t>(A * d);
+  b.R = w.take_t<float>(N * d);
+  b.pre_s = w.take_t<uint16_t>(N * pf * Fs);
+  b.dpre_s = w.take_t<uint16_t>(N * pf * Fs);
+  b.h_s = w.take_t<uint16_t>(N * Fs);
+  b.bytes = w.used();
+  return b;
+}
+
+template <int MODE, int EPI>
+hipError_t run_gemm(const BwdGemm& g, long long max_tiles, hipStream_t stream) {
+  if (max_tiles <= 0) return hipGetLastError();
+  const long long grid = (max_tiles + 7) / 8 * 8;
+  if (grid > (1ll << 31) - 1) return hipErrorInvalidValue;
+  bwd_gemm_kernel<MODE, EPI><<<(unsigned)grid, kThreads, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+BwdGemm gemm_args() {
+  BwdGemm g{};
+  g.ldc = 0;
+  g.m_split = 1 << 30;
+  return g;
+}
+
+// dh' = dy_rows W2 (rows of a tile table) with the activation-backward epilogue.
+hipError_t act_backward(const moe_config& c, const int* tiles, long long max_m_tiles, const uint16_t* dy_rows,
+                        const void* w2, long long w2_estride, int F, const uint16_t* pre, const float* gate,
+                        float* part, uint16_t* dpre, hipStream_t stream) {
+  BwdGemm g = gemm_args();
+  g.a[0] = dy_rows;
+  g.lda = c.d_model;
+  g.klen[0] = c.d_model;
+  g.b[0] = static_cast<const uint16_t*>(w2);
+  g.ldb = F;
+  g.b_estride = w2_estride;
+  g.N = F;
+  g.tiles = tiles;
+  g.n_tiles_n = (F + kBN - 1) / kBN;
+  g.pre = pre;
+  g.gate = gate;
+  g.part = part;
+  g.n_part = n_part_of(F);
+  g.c = dpre;
+  const bool swi = c.act == MOE_ACT_SWIGLU;
+  g.ldc = swi ? 2 * (long long)F : F;
+  const long long S = max_m_tiles * g.n_tiles_n;
+  return swi ? run_gemm<kGrouped, kSwigluBwd>(g, S, stream) : run_gemm<kGrouped, kGeluBwd>(g, S, stream);
+}
+
+// rows of dpre times [W1; W3] (or W1) -> out (T, or float32 with optional add)
+template <int EPI>
+hipError_t dx_rows(const moe_config& c, const int* tiles, long long max_m_tiles, const uint16_t* dpre, int F,
+                   const void* w1, const void* w3, long long w_estride, void* out, const float* c_in,
+                   hipStream_t stream) {
+  BwdGemm g = gemm_args();
+  const bool swi = c.act == MOE_ACT_SWIGLU;
+  g.a[0] = dpre;
+  g.a[1] = swi ? dpre + F : nullptr;
+  g.lda = swi ? 2 * (long long)F : F;
+  g.klen[0] = F;
+  g.klen[1] = swi ? F : 0;
+  g.b[0] = static_cast<const uint16_t*>(w1);
+  g.b[1] = swi ? static_cast<const uint16_t*>(w3) : nullptr;
+  g.ldb = c.d_model;
+  g.b_estride = w_estride;
+  g.N = c.d_model;
+  g.tiles = tiles;
+  g.n_tiles_n = (c.d_model + kBN - 1) / kBN;
+  g.c = out;
+  g.ldc = c.d_model;
+  g.c_in = c_in;
+  return run_gemm<kGrouped, EPI>(g, max_m_tiles * g.n_tiles_n, stream);
+}
+
+// C_e[M][N] = sum over the expert's rows r of A[r][m] B[r][n] (+ a second segment)
+hipError_t wgrad(const uint16_t* a0, const uint16_t* a1, long long lda, const uint16_t* b0, const uint16_t* b1,
+                 long long ldb, int M, int N, const int* offsets, int n_experts, int n_rows, void* c, void* c_hi,
+                 int m_split, long long ldc, long long c_estride, hipStream_t stream) {
+  BwdGemm g = gemm_args();
+  g.a[0] = a0;
+  g.a[1] = a1;
+  g.b[0] = b0;
+  g.b[1] = b1;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.offsets = offsets;
+  g.n_experts = n_experts;
+  g.klen[0] = n_rows;
+  g.n_tiles_n = (N + kBN - 1) / kBN;
+  g.c = c;
+  g.c_hi = c_hi;
+  g.m_split = m_split;
+  g.ldc = ldc;
+  g.c_estride = c_estride;
+  const long long S = (long long)n_experts * ((M + kBM - 1) / kBM) * g.n_tiles_n;
+  return run_gemm<kWgrad, kStoreT>(g, S, stream);
+}
+
+hipError_t colsum(const uint16_t* Mx, long long ld, const float* scale, const int* offsets, int n_groups, int n_rows,
+                  int C, void* out, hipStream_t stream) {
+  dim3 grid((C + 255) / 256, n_groups);
+  colsum_kernel<<<grid, 256, 0, stream>>>(Mx, ld, scale, offsets, n_rows, C, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+#define BWD_TRY(expr)                   \
+  do {                                  \
+    const hipError_t e_ = (expr);       \
+    if (e_ != hipSuccess) return e_;    \
+  } while (0)
+
+}  // namespace
+
+void carve_backward(const moe_config& c, WsCarver& w, WsLayout* L) {
+  const size_t bytes = bwd_bufs(c, nullptr).bytes;
+  void* p = w.take(bytes);
+  if (L) L->bwd = p;
+}
+
+hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& in, const moe_grads& gr,
+                           const RouteOut& ro, hipStream_t s) {
+  const BwdBufs B = bwd_bufs(c, static_cast<char*>(L.bwd));
+  const int N = (int)c.n_tokens, E = c.n_experts, k = c.top_k, d = c.d_model, F = c.d_ff;
+  const int A = N * k, Fs = c.d_ff_shared, E8 = e8_of(E);
+  const bool swi = c.act == MOE_ACT_SWIGLU, bias = c.has_bias != 0;
+  auto T = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  int32_t* ids = ro.topk_ids;
+  float* dz = gr.dz ? gr.dz : B.dz;
+
+  // recompute: routing (logits kept), dispatch of x and dy, the up projection
+  BWD_TRY(launch_route(c, L, in.x, in.w_router, in.logit_bias, in.sel_bias, ids, ro.topk_w, ro.counts, ro.stats,
+                       B.z, nullptr, true, s));
+  if (N == 0) {
+    // no token: every gradient is zero
+    auto zero = [&](void* p, size_t bytes) {
+      if (!p) return hipSuccess;
+      zero_kernel<<<(unsigned)std::min<size_t>((bytes / 16 + 255) / 256, 4096), 256, 0, s>>>(static_cast<uint4*>(p), bytes / 16);
+      return hipGetLastError();
+    };
+    const size_t t2 = 2;
+    BWD_TRY(zero(gr.dw_router, (size_t)E * d * t2));
+    BWD_TRY(zero(gr.dw1, (size_t)E * F * d * t2));
+    BWD_TRY(zero(gr.dw3, (size_t)E * F * d * t2));
+    BWD_TRY(zero(gr.db1, (size_t)E * F * t2));
+    BWD_TRY(zero(gr.dw2, (size_t)E * d * F * t2));
+    BWD_TRY(zero(gr.db2, (size_t)E * d * t2));
+    BWD_TRY(zero(gr.ds_w1, (size_t)Fs * d * t2));
+    BWD_TRY(zero(gr.ds_w3, (size_t)Fs * d * t2));
+    BWD_TRY(zero(gr.ds_b1, (size_t)Fs * t2));
+    BWD_TRY(zero(gr.ds_w2, (size_t)d * Fs * t2));
+    BWD_TRY(zero(gr.ds_b2, (size_t)d * t2));
+    return hipGetLastError();
+  }
+  BWD_TRY(launch_dispatch_scanned(c, L, in.x, ids, ro.topk_w, L.x_sorted, L.perm, L.inv_perm, L.gate_sorted, s));
+  uint16_t* xs = static_cast<uint16_t*>(L.x_sorted);
+  uint16_t* dys = static_cast<uint16_t*>(L.y_sorted);
+  uint16_t* hw = static_cast<uint16_t*>(L.h);
+  launch_copy(c, in.dy, L.inv_perm, dys, s);
+  const long long mt128 = (A + kBM - 1) / kBM + E;
+  BWD_TRY(launch_tile_table(c, L.offsets, kBM, (int)mt128, B.tiles128, L.err, s));
+  BWD_TRY(launch_up_save(c, L.tiles, xs, in.w1, in.w3, in.b1, L.gate_sorted, F, B.pre, hw, s));
+
+  // routed experts: dh' with the activation backward, then dx_sorted and the weight gradients
+  BWD_TRY(act_backward(c, B.tiles128, mt128, dys, in.w2, (long long)d * F, F, B.pre, L.gate_sorted, B.part, B.dpre, s));
+  {
+    RouterBwd r{};
+    r.z = B.z;
+    r.ids = ids;
+    r.inv_perm = L.inv_perm;
+    r.part = B.part;
+    r.n_part = n_part_of(F);
+    r.counts = ro.counts;
+    r.dy = T(in.dy);
+    r.b2 = bias ? T(in.b2) : nullptr;
+    r.n_tokens = N;
+    r.E = E;
+    r.k = k;
+    r.d = d;
+    r.router = c.router;
+    r.norm_topk = c.norm_topk;
+    r.E8 = E8;
+    r.sc = c.routed_scaling;
+    r.aux_coef = in.aux_coef;
+    r.z_coef = in.z_coef;
+    r.dz = dz;
+    r.dgate = gr.dgate;
+    r.dz_hl = B.dz_hl;
+    router_backward_kernel<<<(N + 3) / 4, 256, 0, s>>>(r);
+    BWD_TRY(hipGetLastError());
+  }
+  BWD_TRY(dx_rows<kStoreT>(c, B.tiles128, mt128, B.dpre, F, in.w1, in.w3, (long long)F * d, B.dxs, nullptr, s));
+  BWD_TRY(wgrad(dys, nullptr, d, hw, nullptr, F, d, F, L.offsets, E, 0, gr.dw2, nullptr, d, F, (long long)d * F, s));
+  BWD_TRY(wgrad(B.dpre, nullptr, swi ? 2 * (long long)F : F, xs, nullptr, d, swi ? 2 * F : F, d, L.offsets, E, 0,
+                gr.dw1, gr.dw3, F, d, (long long)F * d, s));
+  if (bias) {
+    BWD_TRY(colsum(B.dpre, F, nullptr, L.offsets, E, 0, F, gr.db1, s));
+    BWD_TRY(colsum(dys, d, L.gate_sorted, L.offsets, E, 0, d, gr.db2, s));
+  }
+
+  // shared expert over all N rows (gate 1); its dx lands in R
+  BWD_TRY(launch_dense_tiles(N, kBM, B.tiles_d128, s));
+  const long long mtN = (N + kBM - 1) / kBM;
+  if (Fs > 0) {
+    BWD_TRY(launch_dense_tiles(N, 256, B.tiles_d256, s));
+    BWD_TRY(launch_up_save(c, B.tiles_d256, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
+    BWD_TRY(act_backward(c, B.tiles_d128, mtN, T(in.dy), in.s_w2, 0, Fs, B.pre_s, nullptr, nullptr, B.dpre_s, s));
+    BWD_TRY(dx_rows<kStoreF32>(c, B.tiles_d128, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, s));
+    BWD_TRY(wgrad(T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr, d, Fs, 0, s));
+    BWD_TRY(wgrad(B.dpre_s, nullptr, swi ? 2 * (long long)Fs : Fs, T(in.x), nullptr, d, swi ? 2 * Fs : Fs, d,
+                  nullptr, 1, N, gr.ds_w1, gr.ds_w3, Fs, d, 0, s));
+    if (bias) {
+      BWD_TRY(colsum(B.dpre_s, Fs, nullptr, nullptr, 1, N, Fs, gr.ds_b1, s));
+      BWD_TRY(colsum(T(in.dy), d, nullptr, nullptr, 1, N, d, gr.ds_b2, s));
+    }
+  }
+
+  // router: dW_g = dz^T x and R (+)= dz W_g, both with dz = hi + lo in bfloat16
+  BWD_TRY(wgrad(B.dz_hl, B.dz_hl + E8, 2 * (long long)E8, T(in.x), T(in.x), d, E, d, nullptr, 1, N, gr.dw_router,
+                nullptr, E, d, 0, s));
+  {
+    BwdGemm g = gemm_args();
+    g.a[0] = B.dz_hl;
+    g.a[1] = B.dz_hl + E8;
+    g.lda = 2 * (long long)E8;
+    g.klen[0] = E;
+    g.klen[1] = E;
+    g.b[0] = T(in.w_router);
+    g.b[1] = T(in.w_router);
+    g.ldb = d;
+    g.N = d;
+    g.tiles = B.tiles_d128;
+    g.n_tiles_n = (d + kBN - 1) / kBN;
+    g.c = B.R;
+    g.ldc = d;
+    g.c_in = Fs > 0 ? B.R : nullptr;
+    BWD_TRY((run_gemm<kGrouped, kStoreF32>(g, mtN * g.n_tiles_n, s)));
+  }
+  bwd_combine_kernel<<<(N + 3) / 4, 256, 0, s>>>(B.dxs, L.inv_perm, B.R, N, k, d, static_cast<uint16_t*>(gr.dx));
+  return hipGetLastError();
+}
+
+}  // namespace moe

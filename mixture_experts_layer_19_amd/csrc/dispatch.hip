@@ -253,8 +253,7 @@ static int id_bits_of(int E) {
   return b;
 }
 
-static void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted,
-                        hipStream_t stream) {
+void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream) {
   if (!x_sorted) return;
   const int vpr = (int)(c.d_model * elem_size(c) / 16);
   const int grid = (int)std::min<long long>((c.n_tokens + 3) / 4, 1 << 16);

@@ -16,7 +16,17 @@
 
 namespace moe {
 
-enum Epi { kEpiGelu = 0, kEpiSwiglu = 1, kEpiDown = 2 };
+enum Epi {
+  kEpiGelu = 0,
+  kEpiSwiglu = 1,
+  kEpiDown = 2,
+  // backward recompute of the up projection: also keep the pre-activations (c2) and write
+  // the gate-scaled hidden activations w_a h_a (c)
+  kEpiSwigluSave = 3,
+  kEpiGeluSave = 4,
+};
+template <int EPI> constexpr bool kSwi = EPI == kEpiSwiglu || EPI == kEpiSwigluSave;
+template <int EPI> constexpr bool kSave = EPI == kEpiSwigluSave || EPI == kEpiGeluSave;
 
 // Tile table (layout and clamping: build_tile_table) from offsets; a bad offsets array sets
 // the error word to MOE_ERR_INVALID_ARG and is otherwise clamped, so no access leaves the
@@ -41,7 +51,9 @@ struct GemmArgs {
   const void* b1;       // [E][N_b][K] T: W3 (SwiGLU up) or null
   const void* bias;     // [E][N_out] T or null
   const float* gate;    // [rows] or null (down only)
-  void* c;              // [rows][N_out] T: h (up) or y_sorted (down)
+  void* c;              // [rows][N_out] T: h (up) or y_sorted (down); save: w_a h_a
+  void* c2;             // save only: SwiGLU [rows][2 N_out] (gate | up pre-activations),
+                        // GELU [rows][N_out] (pre-activation with b1)
   const int* tiles;     // tile table
   int K, n_out;         // reduction length; output columns (= rows of each B matrix)
   int n_tiles_n;        // output column tiles
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
   const int wm = wave & 1;                                    // 128-row half of the tile
   const int wc = grp * 2 + ((wave >> 1) & 1);                 // 64-B-row block 0..3
   const int K = g.K, n_out = g.n_out, NT = g.n_tiles_n;
-  constexpr int kCols = (EPI == kEpiSwiglu) ? 128 : 256;  // output columns per tile
+  constexpr int kCols = kSwi<EPI> ? 128 : 256;  // output columns per tile
 
   const int n_mt = g.tiles[0];
   const long long S = (long long)n_mt * NT;
@@ -181,7 +193,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     // uniform bases (bytes) and 32-bit per-lane offsets of this wave's 2 A and 2 B copies
     const char* a_base = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
     const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
-    const char* b1_base = (EPI == kEpiSwiglu) ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
+    const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
     uint32_t a_off[2], b_off[2];
     const char* b_src[2];
 #pragma unroll
@@ -189,7 +201,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       const int rr = (wave * 2 + i) * 16 + lrow;  // stage row / B-row 0..255
       a_off[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
       int cl;  // B-row's output column relative to n0
-      if (EPI == kEpiSwiglu) {
+      if (kSwi<EPI>) {
         // B-rows 64 c .. 64 c + 31: gate of columns 32 c ..; the next 32: up of the same
         cl = (rr >> 6) * 32 + (rr & 31);
         b_src[i] = ((((wave * 2 + i) * 16) & 63) >= 32) ? b1_base : b0_base;  // uniform per copy
@@ -338,8 +350,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
     // (1 and 0 when absent, so the epilogue has no branches)
     if (tid < kBM) {
-      s_gate[tid] = (EPI == kEpiDown && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
-      s_bias[tid] = (EPI != kEpiSwiglu && g.bias && n0 + tid < n_out)
+      s_gate[tid] = ((EPI == kEpiDown || kSave<EPI>) && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
+      s_bias[tid] = (!kSwi<EPI> && g.bias && n0 + tid < n_out)
                         ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
     }
     __syncthreads();  // every wave is done reading the stages: reuse them for the epilogue
@@ -348,7 +360,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     // bf16 rows are staged in its own LDS buffer (rows padded by 16 bytes: the two
     // half-waves, 4 rows apart, hit disjoint banks) and written with 16-byte row stores.
     uint16_t* C = static_cast<uint16_t*>(g.c);
-    constexpr int kWCols = (EPI == kEpiSwiglu) ? 32 : 64;    // wave output columns
+    constexpr int kWCols = kSwi<EPI> ? 32 : 64;               // wave output columns
     constexpr int kStride = kWCols + 8;                       // staged row length (elements)
     constexpr int kWChunks = kWCols / 8;                      // 16-byte chunks per row
     uint16_t* stage = (wave == 0) ? sA0 : (wave == 1) ? sB0 : (wave == 2) ? sA1 : (wave == 3) ? sB1
@@ -356,24 +368,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     const int col_base = n0 + wc * kWCols;                    // first output column of the wave
     // lane's element in a 32 x 32 block: column lane & 31, rows 8 g + 4 (lane >> 5) + r
     uint16_t* st_lane = stage + ((lane >> 5) * 4) * kStride + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int prow = (v >> 2) * 8 + (v & 3);  // block row, minus 4 (lane >> 5)
-        if (EPI == kEpiSwiglu) {
-          st_lane[prow * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
-        } else {
-          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float val = acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)];
-            val = (EPI == kEpiGelu) ? gelu_erf(val) : val * gs;
-            st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
-          }
-        }
-      }
-      // each lane stores whole 16-byte chunks of the block's 32 rows
+    // each lane stores whole 16-byte chunks of the block's 32 staged rows to dst (row pitch
+    // `pitch` elements, first column col_base)
+    auto flush = [&](int i, uint16_t* dst, size_t pitch) {
 #pragma unroll
       for (int it = 0; it < 32 * kWChunks / 64; ++it) {
         const int idx = it * 64 + lane;
@@ -381,7 +378,64 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
         const int trow = wm * 128 + i * 32 + prow;
         const int col = col_base + ch * 8;
         const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
-        if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(C + (size_t)(row0 + trow) * n_out + col) = val;
+        if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + (size_t)(row0 + trow) * pitch + col) = val;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (EPI == kEpiSwigluSave) {
+        // gate pre-activation, up pre-activation, then w_a silu(g) u, one staging pass each
+        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][0][v]);
+        flush(i, C2, 2 * (size_t)n_out);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][1][v]);
+        flush(i, C2 + n_out, 2 * (size_t)n_out);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int prow = (v >> 2) * 8 + (v & 3);
+          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+          st_lane[prow * kStride] = f32_to_bf16(gs * (silu_f(acc[i][0][v]) * acc[i][1][v]));
+        }
+        flush(i, C, n_out);
+      } else if (EPI == kEpiGeluSave) {
+        // pre-activation (with b1), then w_a gelu(.)
+        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            st_lane[((v >> 2) * 8 + (v & 3)) * kStride + j * 32] =
+                f32_to_bf16(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]);
+        flush(i, C2, n_out);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int prow = (v >> 2) * 8 + (v & 3);
+          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            st_lane[prow * kStride + j * 32] =
+                f32_to_bf16(gs * gelu_erf(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]));
+        }
+        flush(i, C, n_out);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int prow = (v >> 2) * 8 + (v & 3);  // block row, minus 4 (lane >> 5)
+          if (EPI == kEpiSwiglu) {
+            st_lane[prow * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+          } else {
+            const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              float val = acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)];
+              val = (EPI == kEpiGelu) ? gelu_erf(val) : val * gs;
+              st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
+            }
+          }
+        }
+        flush(i, C, n_out);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each 32-row block's registers short-lived
     }
@@ -586,6 +640,41 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
   } else {
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const moe_config& c, const int32_t* offsets, int bm, int max_tiles, int* tiles, int* err,
+                             hipStream_t stream) {
+  const int A = (int)(c.n_tokens * c.top_k);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, bm, max_tiles, tiles, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream) {
+  dense_tiles_kernel<<<1, 256, 0, stream>>>(n, bm, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_save(const moe_config& c, const int* tiles, const void* a, const void* w1, const void* w3,
+                          const void* b1, const float* gate, int n_out, void* pre, void* hw, hipStream_t stream) {
+  GemmArgs g{};
+  g.a = a;
+  g.b0 = w1;
+  g.b1 = w3;
+  g.bias = (c.act == MOE_ACT_GELU && c.has_bias) ? b1 : nullptr;
+  g.gate = gate;
+  g.c = hw;
+  g.c2 = pre;
+  g.tiles = tiles;
+  g.K = c.d_model;
+  g.n_out = n_out;
+  if (c.act == MOE_ACT_SWIGLU) {
+    g.n_tiles_n = (n_out + 127) / 128;
+    expert_gemm_bf16_kernel<kEpiSwigluSave><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+  } else {
+    g.n_tiles_n = (n_out + 255) / 256;
+    expert_gemm_bf16_kernel<kEpiGeluSave><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
   }
   return hipGetLastError();
 }

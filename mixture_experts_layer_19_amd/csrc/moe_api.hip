@@ -67,6 +67,12 @@ moe_status check_shared(const moe_config* c, const void* s_w1, const void* s_w3,
   return MOE_OK;
 }
 
+// What the backward supports beyond check_config: bfloat16, dropless.
+moe_status check_backward_config(const moe_config* c) {
+  if (c->dtype != MOE_BF16 || c->capacity_factor != 0.f) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 #define MOE_TRY(expr)                  \
   do {                                 \
     const moe_status s_ = (expr);      \
@@ -116,6 +122,12 @@ size_t layout(const moe_config& c, int op, char* base, WsLayout* L) {
       carve_ffn(c, w, L);
       carve_forward_buffers(c, w, L);
       break;
+    case MOE_OP_BACKWARD:
+      carve_route(c, w, L);
+      carve_ffn(c, w, L);
+      carve_forward_buffers(c, w, L);
+      carve_backward(c, w, L);
+      break;
     default: return 0;
   }
   return w.used();
@@ -136,10 +148,12 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 extern "C" {
 
 size_t moe_workspace_size(const moe_config* cfg, int op) {
-  const bool needs_ff = op == MOE_OP_EXPERT_FFN || op == MOE_OP_FORWARD || op == MOE_OP_SHARED_FFN;
-  if (op < MOE_OP_ROUTE || op > MOE_OP_SHARED_FFN) return 0;
+  const bool needs_ff = op == MOE_OP_EXPERT_FFN || op == MOE_OP_FORWARD || op == MOE_OP_SHARED_FFN ||
+                        op == MOE_OP_BACKWARD;
+  if (op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD) return 0;
   if (check_config(cfg, needs_ff) != MOE_OK) return 0;
   if (op == MOE_OP_SHARED_FFN && cfg->d_ff_shared <= 0) return 0;
+  if (op == MOE_OP_BACKWARD && check_backward_config(cfg) != MOE_OK) return 0;
   return layout(*cfg, op, nullptr, nullptr);
 }
 
@@ -337,6 +351,60 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   MOE_TRY(mark(4));
   MOE_TRY(hip_status(launch_combine(*cfg, L.y_sorted, nullptr, L.inv_perm, shared ? L.x_sorted : nullptr, y, s)));
   return mark(5);
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router, const float* logit_bias,
+                        const float* sel_bias, const void* w1, const void* w3, const void* b1, const void* w2,
+                        const void* b2, const void* s_w1, const void* s_w3, const void* s_b1, const void* s_w2,
+                        const void* s_b2, const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
+                        int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, void* ws, size_t ws_bytes,
+                        void* stream) {
+  MOE_TRY(check_config(cfg, true));
+  MOE_TRY(check_backward_config(cfg));
+  MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
+  if (!grads || !std::isfinite(aux_coef) || !std::isfinite(z_coef)) return MOE_ERR_INVALID_ARG;
+  const moe_grads& g = *grads;
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_t(x));
+    MOE_TRY(need_t(dy));
+    MOE_TRY(need_t(g.dx));
+    MOE_TRY(need_4(topk_ids));
+    MOE_TRY(need_4(topk_w));
+  }
+  MOE_TRY(need_t(w_router));
+  MOE_TRY(need_t(w1));
+  MOE_TRY(need_t(w2));
+  MOE_TRY(need_t(g.dw_router));
+  MOE_TRY(need_t(g.dw1));
+  MOE_TRY(need_t(g.dw2));
+  const bool swi = cfg->act == MOE_ACT_SWIGLU;
+  if (swi) {
+    MOE_TRY(need_t(w3));
+    MOE_TRY(need_t(g.dw3));
+  } else if (g.dw3) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (cfg->has_bias) {
+    MOE_TRY(need_t(b1));
+    MOE_TRY(need_t(b2));
+    MOE_TRY(need_t(g.db1));
+    MOE_TRY(need_t(g.db2));
+  } else if (g.db1 || g.db2) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  // the shared expert's gradients follow its weights
+  MOE_TRY(check_shared(cfg, g.ds_w1, g.ds_w3, g.ds_b1, g.ds_w2, g.ds_b2));
+  MOE_TRY(need_4(counts));
+  MOE_TRY(need_4(stats));
+  MOE_TRY(opt_4(logit_bias));
+  MOE_TRY(opt_4(sel_bias));
+  MOE_TRY(opt_4(g.dz));
+  MOE_TRY(opt_4(g.dgate));
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_BACKWARD, ws, ws_bytes, &L));
+  BwdIn in{x, w_router, logit_bias, sel_bias, w1, w3, b1, w2, b2, s_w1, s_w3, s_b1, s_w2, s_b2, dy, aux_coef, z_coef};
+  RouteOut ro{topk_ids, topk_w, counts, stats};
+  return hip_status(launch_backward(*cfg, L, in, g, ro, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float* sel_bias, float rate,

@@ -57,6 +57,8 @@ struct WsLayout {
   float* gate_sorted = nullptr;
   void* x_sorted = nullptr;
   void* y_sorted = nullptr;
+  // backward (its own regions; see carve_backward)
+  void* bwd = nullptr;
 };
 
 // m-tile table of the grouped GEMMs: tiles[0] = number of m-tiles, tiles[4..7] = 16 zero
@@ -201,5 +203,31 @@ hipError_t launch_combine(const moe_config& c, const void* y_sorted, const float
 hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, const void* s_w1,
                          const void* s_w3, const void* s_b1, const void* s_w2, const void* s_b2,
                          void* y_shared, hipStream_t stream);
+
+// Tile table of one dense "expert" covering rows [0, n) in tiles of bm rows.
+hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream);
+// Backward recompute of the up projection (bfloat16): the tile table's rows of a times W1
+// (and W3), writing the pre-activations to pre (SwiGLU: [rows][2 n_out] gate | up; GELU:
+// [rows][n_out] with b1) and gate[row] * act(.) to hw [rows][n_out] (gate null: 1).
+hipError_t launch_up_save(const moe_config& c, const int* tiles, const void* a, const void* w1, const void* w3,
+                          const void* b1, const float* gate, int n_out, void* pre, void* hw, hipStream_t stream);
+// The layer's backward (bfloat16, dropless); moe_backward's launch sequence.
+struct BwdIn {
+  const void* x; const void* w_router; const float* logit_bias; const float* sel_bias;
+  const void* w1; const void* w3; const void* b1; const void* w2; const void* b2;
+  const void* s_w1; const void* s_w3; const void* s_b1; const void* s_w2; const void* s_b2;
+  const void* dy; float aux_coef, z_coef;
+};
+struct RouteOut {
+  int32_t* topk_ids; float* topk_w; int32_t* counts; float* stats;
+};
+void carve_backward(const moe_config& c, WsCarver& w, WsLayout* L);
+hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& in, const moe_grads& gr,
+                           const RouteOut& ro, hipStream_t stream);
+// m-tile table with bm-row tiles from offsets [E+1] over A = N k rows (bad offsets: *err)
+hipError_t launch_tile_table(const moe_config& c, const int32_t* offsets, int bm, int max_tiles, int* tiles, int* err,
+                             hipStream_t stream);
+// rows of x copied to their sorted slots (x_sorted[inv_perm[n k + j]] = x[n])
+void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream);
 
 }  // namespace moe
