@@ -1,12 +1,17 @@
-"""MoE layer forward benchmark on one MI355X.
+"""MoE layer benchmark on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
+                [--mode forward|backward]
 
-A step is one whole layer forward (moe_forward: route, dispatch, expert up and down
-projections, combine, statistics) over one batch of synthetic tokens already resident in
-HBM. Prints ONE JSON line: tokens/s plus the roofline of the dominant kernel (the fused
-gate/up expert projection) timed with HIP events that the library records on its own stream,
-and the CPU oracle timed on a bounded sample of the same workload.
+Forward (the default): a step is one whole layer forward (moe_forward: route, dispatch,
+expert up and down projections, combine, statistics) over one batch of synthetic tokens
+already resident in HBM. Prints ONE JSON line: tokens/s plus the roofline of the dominant
+kernel (the fused gate/up expert projection) timed with HIP events that the library records
+on its own stream, and the CPU oracle timed on a bounded sample of the same workload.
+
+Backward: a step is one moe_backward (recomputed routing, dispatch and up projection, then
+every gradient) for an upstream gradient dy of the same shape; the JSON line has the same
+form, with the roofline of the backward's slowest GEMM stage.
 """
 from __future__ import annotations
 
@@ -63,6 +68,18 @@ def traffic_for(kernel_src, workload):
     return t.get("hbm_bytes_per_launch")
 
 
+def algorithmic_backward(cfg):
+    """Algorithmic MFMA work of one backward per stage (U = 2 A d f; the up projection and the
+    products with W1 / W3 count twice for SwiGLU)."""
+    N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
+    U = 2 * N * k * d * f
+    m = 2 if cfg.act == "swiglu" else 1
+    Us = 2 * N * d * cfg.d_ff_shared
+    return {"route_dispatch": 2 * N * d * E, "up_recompute": m * U, "act_backward": U, "router_backward": 0,
+            "dx_rows": m * U, "dw2": U, "dw13": m * U, "shared": (3 * m + 2) * Us,
+            "router_dx_combine": 4 * N * d * E}
+
+
 def cpu_baseline(w, inp, n_sample=0, target_s=15.0):
     """The float64 CPU oracle, as it stands, on the first n_sample tokens of the workload
     (n_sample = 0: sized from an 8-token probe to take about target_s seconds)."""
@@ -98,6 +115,102 @@ def cpu_baseline(w, inp, n_sample=0, target_s=15.0):
                        f"before the timed region")}
 
 
+def cpu_baseline_backward(w, inp, dy, n_sample=0, target_s=15.0, aux_coef=0.0, z_coef=0.0):
+    """The float64 CPU oracle's backward, as it stands, on the first n_sample tokens (auto-sized
+    from a 4-token probe to about target_s seconds)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    f64 = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+    cfg = w.cfg
+    params = {"w_g": f64(inp["w_router"])}
+    for name in ("w1", "w3", "w2", "b1", "b2"):
+        params[name] = None if inp[name] is None else [f64(inp[name][e]) for e in range(cfg.n_experts)]
+    for name, t in (inp.get("shared") or {}).items():
+        params[name] = f64(t)
+    spec = O.Spec(n_experts=cfg.n_experts, top_k=cfg.top_k, router=cfg.router, norm_topk=cfg.norm_topk,
+                  routed_scaling=cfg.routed_scaling, act=cfg.act)
+    lb, sb = f64(inp["logit_bias"]), f64(inp["sel_bias"])
+    if not n_sample:
+        t0 = time.perf_counter()
+        O.backward(f64(inp["x"][:4]), params, spec, f64(dy[:4]), aux_coef, z_coef, lb, sb)
+        per_tok = (time.perf_counter() - t0) / 4
+        n_sample = int(min(cfg.n_tokens, max(4, target_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    O.backward(f64(inp["x"][:n_sample]), params, spec, f64(dy[:n_sample]), aux_coef, z_coef, lb, sb)
+    dt = time.perf_counter() - t0
+    return {"value": n_sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 oracle backward (routing, per-assignment expert backward, router and "
+                       f"balance-loss gradients) on the first {n_sample} of {cfg.n_tokens} tokens; "
+                       f"{dt:.1f} s; weights widened to float64 before the timed region")}
+
+
+def run_backward(args, w, inp):
+    import torch
+    from mixture_experts_layer_19_amd import binding as B
+    from mixture_experts_layer_19_amd import workload as W
+    cfg = w.cfg
+    dy = W.random_rows(cfg.n_tokens, cfg.d_model, cfg.torch_dtype, seed=0, tensor_id=30)
+    ws = B.workspace(cfg, B.Op.BACKWARD)
+    aux, zc = 0.01, 1e-3
+    call = lambda out=None, ev=None: B.moe_backward(
+        cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], dy, inp["b1"], inp["b2"],
+        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"], aux_coef=aux, z_coef=zc, ws=ws, out=out,
+        stage_events=ev)
+    out = call()
+    for _ in range(max(args.warmup - 1, 0)):
+        call(out)
+    events = [B.HipEvents(B.BWD_EVENTS) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(out, events[i].handles)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {s: 0.0 for s in B.BWD_STAGES}
+    for ev in events:
+        for j, s in enumerate(B.BWD_STAGES):
+            stage_ms[s] += ev.elapsed_ms(j, j + 1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    work = algorithmic_backward(cfg)
+    flops = sum(work.values())
+    peak = PEAK_BF16_TFLOPS
+    gemm_stages = ("up_recompute", "act_backward", "dx_rows", "dw2", "dw13")
+    rates = {s: work[s] / (stage_ms[s] * 1e-3) / 1e12 for s in gemm_stages + ("shared",) if stage_ms[s] > 0}
+    dom = max(gemm_stages, key=lambda s: stage_ms[s])
+    kernel = {"up_recompute": "expert_gemm_bf16_kernel<save epilogue>",
+              "act_backward": "bwd_gemm_kernel<grouped, activation backward>",
+              "dx_rows": "bwd_gemm_kernel<grouped, store>", "dw2": "bwd_gemm_kernel<wgrad>",
+              "dw13": "bwd_gemm_kernel<wgrad>"}[dom]
+    E = cfg.n_experts
+    res = {
+        "metric": "MoE layer bwd tokens/s (recompute + all gradients) + active TFLOP/s (% bf16 MFMA peak)",
+        "value": cfg.n_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name} backward: N={cfg.n_tokens} d={cfg.d_model} E={E} k={cfg.top_k} "
+                               f"d_ff={cfg.d_ff} {cfg.act} {cfg.router}{'+norm' if cfg.norm_topk else ''} {cfg.dtype}"
+                               f" aux_coef={aux} z_coef={zc}",
+                   "global_batch": cfg.n_tokens, "parallelism": "single GPU"},
+        "active_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "active_frac_of_peak": flops / (ms_per_step * 1e-3) / 1e12 / peak,
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "stage_tflops": {s: round(v, 1) for s, v in rates.items()},
+        "roofline": {"kernel": kernel, "stage": dom, "bound": "mfma", "achieved": rates[dom], "peak": peak,
+                     "unit": "TFLOP/s", "frac": rates[dom] / peak, "traffic": None,
+                     "flops_per_launch": work[dom], "avg_launch_ms": stage_ms[dom]},
+        "events_vs_wall": sum(stage_ms.values()) / ms_per_step,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(w, inp, dy, args.cpu_sample, aux_coef=aux, z_coef=zc)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +218,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("forward", "backward"), default="forward")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -133,6 +247,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     cfg = w.cfg
     inp = W.make_inputs(w, seed=0, device="cuda")
+    if args.mode == "backward":
+        run_backward(args, w, inp)
+        return
     ws = B.workspace(cfg, B.Op.FORWARD)
     dev = inp["x"].device
     out = {

@@ -257,7 +257,13 @@ typedef struct {
  * In: the forward's inputs; dy [N,d] T; aux_coef, z_coef: finite.
  * Out: *grads (dw3 / db1 / db2 / shared gradients required exactly when the matching
  * weight is); topk_ids, topk_w, counts, stats as in moe_route.
+ * stage_events: NULL, or MOE_BWD_EVENTS hipEvent_t (as void*) recorded on `stream` at the
+ * start, after the recomputed routing and dispatch, after the recomputed up projection, after
+ * dh' (with the activation backward), after the router backward, after dx_sorted, after dW2,
+ * after dW1 / dW3 (and the bias sums), after the shared expert's gradients and at the end
+ * (router weight gradient, dz W_g and the dx combine).
  * ws: moe_workspace_size(cfg, MOE_OP_BACKWARD) bytes. */
+#define MOE_BWD_EVENTS 10
 moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
                         const float* logit_bias, const float* sel_bias,
                         const void* w1, const void* w3, const void* b1,
@@ -266,7 +272,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const void* s_w2, const void* s_b2,
                         const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
                         int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
-                        void* ws, size_t ws_bytes, void* stream);
+                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 
 /* Aux-free load balancing, one update step ([L7.8] §2.5): with load_e = counts[e] and
  * mean = sum_e load_e / E,

@@ -131,7 +131,7 @@ def lib():
     L.moe_expert_capacity.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_int64, ctypes.c_int32]
     L.moe_expert_capacity.restype = ctypes.c_int64
     L.moe_backward.argtypes = ([S] + [_P] * 15 + [ctypes.c_float, ctypes.c_float, ctypes.POINTER(MoeGradsStruct)]
-                               + [_P] * 5 + [ctypes.c_size_t, _P])
+                               + [_P] * 5 + [ctypes.c_size_t, _P, _P])
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
@@ -383,16 +383,21 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
     return out
 
 
+BWD_EVENTS = 10
+BWD_STAGES = ("route_dispatch", "up_recompute", "act_backward", "router_backward", "dx_rows", "dw2", "dw13",
+              "shared", "router_dx_combine")
 GRAD_NAMES = ("dx", "dw_router", "dw1", "dw3", "db1", "dw2", "db2", "ds_w1", "ds_w3", "ds_b1", "ds_w2", "ds_b2",
               "dz", "dgate")
 
 
 def moe_backward(cfg: LayerConfig, x, w_router, w1, w3, w2, dy, b1=None, b2=None, logit_bias=None, sel_bias=None,
-                 *, shared: Optional[dict] = None, aux_coef: float = 0.0, z_coef: float = 0.0, ws=None, out=None):
+                 *, shared: Optional[dict] = None, aux_coef: float = 0.0, z_coef: float = 0.0, ws=None, out=None,
+                 stage_events: Optional[Sequence[int]] = None):
     """Gradients of <dy, y> + aux_coef L + z_coef z_loss (bfloat16, dropless). Returns a dict
     with dx, dw_router, dw1, dw3, db1, dw2, db2, the shared expert's ds_* (None where the
     weight is absent), dz [N,E] and dgate [N,k] (float32), and the recomputed routing
-    (topk_ids, topk_w, counts, stats). `out` / `ws` may hold preallocated buffers."""
+    (topk_ids, topk_w, counts, stats). `out` / `ws` may hold preallocated buffers;
+    stage_events: BWD_EVENTS raw hipEvent_t handles (ints) or None."""
     N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
     T = cfg.torch_dtype
     sh = shared or {}
@@ -424,11 +429,16 @@ def moe_backward(cfg: LayerConfig, x, w_router, w1, w3, w2, dy, b1=None, b2=None
     if ws is None:
         ws = workspace(cfg, Op.BACKWARD, w_router.device)
     g = MoeGradsStruct(*[None if out.get(n) is None else out[n].data_ptr() for n in GRAD_NAMES])
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != BWD_EVENTS:
+            raise ValueError(f"stage_events needs {BWD_EVENTS} events")
+        ev = (ctypes.c_void_p * BWD_EVENTS)(*[ctypes.c_void_p(int(e)) for e in stage_events])
     st = lib().moe_backward(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(sel_bias),
                             _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1), _ptr(s_w3), _ptr(s_b1),
                             _ptr(s_w2), _ptr(s_b2), _ptr(dy), float(aux_coef), float(z_coef), ctypes.byref(g),
                             _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]),
-                            _ptr(ws), ws.numel(), _stream())
+                            _ptr(ws), ws.numel(), ev, _stream())
     _check(st, "moe_backward")
     return out
 

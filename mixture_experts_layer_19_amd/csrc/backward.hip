@@ -20,8 +20,8 @@
 // always stored with its output axis contiguous (weights [K][N] or activations [rows][N]),
 // and whose A operand is either the row operand (grouped mode: expert-sorted rows, K
 // contiguous) or, for weight gradients, a second activation with M contiguous (ragged K =
-// the expert's rows). Operands that are not K-contiguous are transposed in registers on the
-// way into LDS, so every LDS tile holds 32 consecutive k per row, as MFMA operands want.
+// the expert's rows). Operands stream into LDS as stored (global_load_lds); those that are
+// not K-contiguous are turned into MFMA fragments by gfx950's LDS transpose read.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -29,7 +29,7 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 128, kBN = 256, kBK = 32, kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 512, kStages = 4;
 constexpr int kGM = 8, kGN = 4;          // supertile: 8 m-tiles x 4 n-tiles (m fastest)
 constexpr int kStageStride = 40;         // epilogue staging row (floats): the two half-waves,
                                          // 4 rows apart, hit disjoint banks
@@ -59,30 +59,17 @@ struct BwdGemm {
   long long ldc, c_estride;
   int m_split;
   const float* c_in;    // kStoreF32: added before the store (may alias c)
+  const uint16_t* zero; // 16 zero bytes (the source of masked copies)
+  // wgrad with split K: the expert's rows are cut into ksplit runs; run sp writes float32
+  // partials to kpart [ksplit][n_experts][M][N] (reduced by wgrad_reduce_kernel)
+  int ksplit;
+  float* kpart;
   // activation backward (grouped): pre-activations, gates, row partials of <dh', h>
   const uint16_t* pre;  // SwiGLU [rows][2 N] (gate | up), GELU [rows][N]
   const float* gate;    // [rows] or null (1)
   float* part;          // [rows][n_part] or null
   int n_part;
 };
-
-// Element offset of 16-byte chunk c (8 consecutive k) of tile row r. Rows are 64 bytes. The
-// row permutation and chunk XOR are chosen so that (i) an MFMA operand read -- 16 consecutive
-// rows at one chunk per quarter-wave -- covers all 64 banks, and (ii) a transposed write --
-// rows 8 q + j for 32 values of q at one chunk -- spreads over all bank groups.
-MOE_DEV int lds_elem(int r, int c) {
-  return ((r ^ ((r >> 3) & 3)) * 4 + (c ^ (((r >> 2) ^ (r >> 5)) & 3))) * 8;
-}
-
-MOE_DEV uint32_t dword_of(const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; }
-// element j of four consecutive k rows r[0..3] (8 columns each): the column's 4 k values
-MOE_DEV uint2 column4(const uint4* r, int j) {
-  const int q = j >> 1;
-  auto pk = [&](uint32_t lo, uint32_t hi) {
-    return (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-  };
-  return make_uint2(pk(dword_of(r[0], q), dword_of(r[1], q)), pk(dword_of(r[2], q), dword_of(r[3], q)));
-}
 
 MOE_DEV void supertile(long long l, int me, int NT, int* mt, int* nt) {
   const int band = (int)(l / ((long long)kGM * NT));
@@ -115,9 +102,9 @@ MOE_DEV uint4 pack8(const float* f) {
 
 // ---------------------------------------------------------------------------------------
 // Grouped bfloat16 GEMM on MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulation).
-// Workgroup tile 128 x 256, four waves of 64 x 128 (2 x 4 blocks of 32 x 32). K advances 32
-// at a time through two LDS stages: the next slab's global loads are issued before the
-// current slab's multiplies and written to the other stage after them (one barrier per slab).
+// Workgroup tile 256 x 256, eight waves (two per SIMD) of 64 x 128 (2 x 4 blocks of
+// 32 x 32), one workgroup per CU. K advances 32 at a time through four LDS stages (128 KiB),
+// three slabs in flight while one is multiplied.
 // Grid: 8 * ceil(S / 8) workgroups for S tiles; workgroup b runs on XCD b mod 8 and takes
 // tile (b mod 8) * ceil(S / 8) + b / 8, so each XCD works through a contiguous run of the
 // tile order (expert-major, supertiles of 8 m-tiles x 4 n-tiles) and shares its operands in
@@ -125,12 +112,12 @@ MOE_DEV uint4 pack8(const float* f) {
 // ---------------------------------------------------------------------------------------
 template <int MODE, int EPI>
 __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kBN * kBK];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int NT = g.n_tiles_n;
 
   // ---- tile
@@ -140,14 +127,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
     S = (long long)g.tiles[0] * NT;
   } else {
     MTe = (g.M + kBM - 1) / kBM;
-    S = (long long)g.n_experts * MTe * NT;
+    S = (long long)g.n_experts * MTe * NT * g.ksplit;
   }
   const long long per = (S + 7) / 8;
   const long long slot = blockIdx.x >> 3;
   const long long s = (long long)(blockIdx.x & 7) * per + slot;
   if (slot >= per || s >= S) return;
 
-  int e, mt, nt, row0 = 0, rows = 0, m0 = 0, r0 = 0, kr = 0;
+  int e, mt, nt, row0 = 0, rows = 0, m0 = 0, r0 = 0, kr = 0, sp = 0;
   if (MODE == kGrouped) {
     const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
     e = probe[0];
@@ -157,112 +144,133 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
     row0 = tq[1];
     rows = tq[2];
   } else {
-    e = (int)(s / ((long long)MTe * NT));
-    supertile(s - (long long)e * MTe * NT, MTe, NT, &mt, &nt);
+    // split sp of ksplit (outermost) takes the sp-th of ksplit near-equal runs of the rows
+    const long long per_split = (long long)g.n_experts * MTe * NT;
+    sp = (int)(s / per_split);
+    const long long se = s - sp * per_split;
+    e = (int)(se / ((long long)MTe * NT));
+    supertile(se - (long long)e * MTe * NT, MTe, NT, &mt, &nt);
     m0 = mt * kBM;
     r0 = g.offsets ? g.offsets[e] : 0;
     const int r1 = g.offsets ? g.offsets[e + 1] : g.klen[0];
-    kr = max(r1 - r0, 0);
+    const int all = max(r1 - r0, 0);
+    const int chunk = (all + g.ksplit - 1) / g.ksplit;
+    r0 += min(sp * chunk, all);
+    kr = max(min(chunk, all - sp * chunk), 0);
   }
   const int n0 = nt * kBN;
   const int M = g.M, N = g.N;
 
-  // ---- reduction length: segments padded to multiples of 8
-  int kp0, ktot;
+  // ---- reduction length: each segment padded to whole slabs, so a slab lies in one segment
+  int kp0, ktot, klen0, klen1;
   if (MODE == kGrouped) {
-    kp0 = (g.klen[0] + 7) & ~7;
-    ktot = kp0 + ((g.klen[1] + 7) & ~7);
+    klen0 = g.klen[0];
+    klen1 = g.klen[1];
+    kp0 = (klen0 + kBK - 1) / kBK * kBK;
+    ktot = kp0 + (klen1 + kBK - 1) / kBK * kBK;
   } else {
-    kp0 = (kr + 7) & ~7;
+    klen0 = klen1 = kr;
+    kp0 = (kr + kBK - 1) / kBK * kBK;
     ktot = g.a[1] ? 2 * kp0 : kp0;
   }
-  const int nk = (ktot + kBK - 1) / kBK;
+  const int nk = ktot / kBK;
 
-  // ---- load geometry
-  // A, K-contiguous (grouped): chunk q = tid + 256 i (i = 0, 1) is row q >> 2, chunk q & 3.
-  // A, M-contiguous (wgrad, waves 0 and 1): 4 k rows (4 kq ..) x 8 columns (8 mb ..).
-  // B (both modes): 4 k rows (4 kq ..) x 8 columns (8 nb ..), all four waves.
-  const int a_mb = lane & 15, a_kq = 4 * wave + (lane >> 4);
-  const int b_nb = lane & 31, b_kq = 2 * wave + (lane >> 5);
-  const uint16_t* b_exp[2];
+  // ---- operand stages in LDS, written by global_load_lds_dwordx4 (16 bytes per lane,
+  // 1 KiB per wave instruction); a lane whose 16 bytes lie outside the operand (rows past the
+  // tile or the expert, columns past N, k past a segment) copies zeros from g.zero instead.
+  //   A, K-contiguous (grouped): [256 rows][32 k], 64-byte rows; chunk c of row r at physical
+  //     chunk c ^ ((r >> 2) & 3); MFMA fragments by ds_read_b128.
+  //   A, M-contiguous (wgrad):   [32 k][256 m]; B: [32 k][256 n]; 512-byte rows.
+  //     Chunk c (8 columns) of k-row r at physical chunk c ^ ((r & 3) << 2); fragments by two
+  //     ds_read_b64_tr_b16 (in each 16-lane group, lane 4 q + p reads 4 columns at 4 p of
+  //     k-row q and lane i receives column i at 4 consecutive k): the four k-rows a half-wave
+  //     reads then sit in four different 64-byte bank windows.
+  // Four stages: slab kt + 3 is copied while slab kt is multiplied (one barrier per slab).
+  // Per lane and copy instruction (2 of A, 4 of B): the element address at slab-local k = 0
+  // of segment 0 (q*), the lane's k within the slab (lk*) and whether its row / column
+  // exists (ok*); per slab only a uniform offset is added. Segment 1 is segment 0's address
+  // plus a uniform distance (same row or column, other matrix).
+  const uint16_t* qa[2];
+  const uint16_t* qb[2];
+  int lka[2], lkb[2];
+  bool oka[2], okb[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) b_exp[q] = g.b[q] ? g.b[q] + (MODE == kGrouped ? (size_t)e * g.b_estride : 0) : nullptr;
-
-  uint4 ra[4], rb[4];
-  auto seg_of = [&](int kk, int* local) {
-    const int sg = kk >= kp0 ? 1 : 0;
-    *local = kk - sg * kp0;
-    return sg;
-  };
-  auto gload = [&](int kt) {
-    const int kbase = kt * kBK;
+  for (int i = 0; i < 2; ++i) {
+    const int inst = 2 * wave + i;  // 16 copy instructions per operand and slab
     if (MODE == kGrouped) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int q = tid + 256 * i;
-        const int r = q >> 2, kk = kbase + (q & 3) * 8;
-        int local;
-        const int sg = seg_of(kk, &local);
-        const bool ok = r < rows && kk < ktot && local < g.klen[sg];
-        ra[i] = ok ? *reinterpret_cast<const uint4*>(g.a[sg] + (size_t)(row0 + r) * g.lda + local)
-                   : make_uint4(0, 0, 0, 0);
-      }
-    } else if (wave < 2) {
-      const int m = m0 + 8 * a_mb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = kbase + 4 * a_kq + i;
-        int local;
-        const int sg = seg_of(kk, &local);
-        const bool ok = m < M && kk < ktot && local < kr;
-        ra[i] = ok ? *reinterpret_cast<const uint4*>(g.a[sg] + (size_t)(r0 + local) * g.lda + m)
-                   : make_uint4(0, 0, 0, 0);
-      }
+      const int r = inst * 16 + (lane >> 2);
+      lka[i] = 8 * ((lane & 3) ^ ((r >> 2) & 3));
+      oka[i] = r < rows;
+      qa[i] = g.a[0] + (size_t)(row0 + min(r, max(rows - 1, 0))) * g.lda + lka[i];
+    } else {
+      lka[i] = inst * 2 + (lane >> 5);
+      const int m = m0 + 8 * ((lane & 31) ^ ((lka[i] & 3) << 2));
+      oka[i] = m < M;
+      qa[i] = g.a[0] + (size_t)(r0 + lka[i]) * g.lda + min(m, M - 1);
     }
-    const int n = n0 + 8 * b_nb;
+    lkb[i] = inst * 2 + (lane >> 5);
+    const int n = n0 + 8 * ((lane & 31) ^ ((lkb[i] & 3) << 2));
+    okb[i] = n < N;
+    const size_t row = (MODE == kGrouped) ? (size_t)lkb[i] : (size_t)(r0 + lkb[i]);
+    const uint16_t* b0 = g.b[0] + (MODE == kGrouped ? (size_t)e * g.b_estride : 0);
+    qb[i] = b0 + row * g.ldb + min(n, N - 8);
+  }
+  // uniform distance from segment 0 to segment 1 (elements)
+  const long long da1 = g.a[1] ? (long long)(g.a[1] - g.a[0]) : 0;
+  const long long db1 = g.b[1] ? (long long)(g.b[1] - g.b[0]) : 0;
+  auto issue = [&](int slab, int buf) {
+    const int kbase = slab * kBK;
+    const int sg = kbase >= kp0 ? 1 : 0;     // uniform
+    const int kl = kbase - sg * kp0;         // slab start within the segment
+    const int klen = sg ? klen1 : klen0;
+    const long long ua = (MODE == kGrouped) ? (long long)kl + (sg ? da1 : 0)
+                                            : (long long)kl * g.lda + (sg ? da1 : 0);
+    const long long ub = (long long)kl * g.ldb + (sg ? db1 : 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = kbase + 4 * b_kq + i;
-      int local;
-      const int sg = seg_of(kk, &local);
-      bool ok = n < N && kk < ktot;
-      size_t row;
-      if (MODE == kGrouped) {
-        ok = ok && local < g.klen[sg];
-        row = (size_t)local;
-      } else {
-        ok = ok && local < kr;
-        row = (size_t)(r0 + local);
-      }
-      rb[i] = ok ? *reinterpret_cast<const uint4*>(b_exp[sg] + row * g.ldb + n) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int inst = 2 * wave + i;
+      const bool ok = oka[i] && kl + lka[i] < klen;
+      lds_dma16(ok ? qa[i] + ua : g.zero, &sA[buf][inst * 512]);   // 1 KiB = 512 elements
+      const bool okb_ = okb[i] && kl + lkb[i] < klen;
+      lds_dma16(okb_ ? qb[i] + ub : g.zero, &sB[buf][inst * 512]);
     }
-  };
-  auto lstore = [&](int buf) {
-    if (MODE == kGrouped) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int q = tid + 256 * i;
-        *reinterpret_cast<uint4*>(&sA[buf][lds_elem(q >> 2, q & 3)]) = ra[i];
-      }
-    } else if (wave < 2) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint2*>(&sA[buf][lds_elem(8 * a_mb + j, a_kq >> 1) + 4 * (a_kq & 1)]) = column4(ra, j);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint2*>(&sB[buf][lds_elem(8 * b_nb + j, b_kq >> 1) + 4 * (b_kq & 1)]) = column4(rb, j);
   };
 
-  // MFMA operand reads: lane holds row (lane & 31) of a 32-row block at k 8 (lane >> 5) ..
-  int offa[2][2], offb[2][4];
+  // fragment addresses (elements within a stage) of this lane
+  const int tg = lane >> 4, tq = (lane & 15) >> 2, tp = lane & 3;  // transpose-read roles
+  int offa[2][2][2], offb[2][4][2];  // [ks][block][read]; the K-contiguous A uses [ks][block][0]
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) offa[ks][i] = lds_elem(wm * 64 + 32 * i + (lane & 31), 2 * ks + (lane >> 5));
+    for (int rd = 0; rd < 2; ++rd) {
+      const int k = 16 * ks + 8 * (tg >> 1) + 4 * rd + tq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) offb[ks][j] = lds_elem(wn * 128 + 32 * j + (lane & 31), 2 * ks + (lane >> 5));
+      for (int i = 0; i < 2; ++i) {
+        if (MODE == kGrouped) {
+          const int r = wm * 64 + 32 * i + (lane & 31);
+          offa[ks][i][rd] = r * kBK + (((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3)) * 8);
+        } else {
+          const int m = wm * 64 + 32 * i + 16 * (tg & 1) + 4 * tp;
+          offa[ks][i][rd] = k * kBM + (((m >> 3) ^ (tq << 2)) * 8) + 4 * ((m >> 2) & 1);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = wn * 128 + 32 * j + 16 * (tg & 1) + 4 * tp;
+        offb[ks][j][rd] = k * kBN + (((n >> 3) ^ (tq << 2)) * 8) + 4 * ((n >> 2) & 1);
+      }
+    }
   }
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  auto tr_read = [](const uint16_t* base, int off) -> v4i16 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_void*)(base + off));
+  };
+  auto frag8 = [](v4i16 lo, v4i16 hi) -> bf16x8 {
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  };
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -273,28 +281,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    issue(0, 0);
+    issue(min(1, nk - 1), 1);
+    issue(min(2, nk - 1), 2);
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
+      const int buf = kt % kStages;
+      wait_vm_lds<8>();  // this wave's 4 copies of slab kt have landed (kt + 1, kt + 2 may not)
+      stage_barrier();   // every wave's have, and every wave is done with slab kt - 1
+      // slab kt + 3 into the stage slab kt - 1 used (past the end: the last slab again, into
+      // a stage that is never read, which keeps the count above exact)
+      issue(min(kt + 3, nk - 1), (kt + 3) % kStages);
+      const uint16_t* a_st = sA[buf];
+      const uint16_t* b_st = sB[buf];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 fa[2], fb[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][offa[ks][i]]);
+        for (int i = 0; i < 2; ++i) {
+          if (MODE == kGrouped) fa[i] = *reinterpret_cast<const bf16x8*>(a_st + offa[ks][i][0]);
+          else fa[i] = frag8(tr_read(a_st, offa[ks][i][0]), tr_read(a_st, offa[ks][i][1]));
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][offb[ks][j]]);
+        for (int j = 0; j < 4; ++j) fb[j] = frag8(tr_read(b_st, offb[ks][j][0]), tr_read(b_st, offb[ks][j][1]));
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) lstore(buf ^ 1);
-      __syncthreads();
     }
+    wait_vm_lds<0>();  // the copies past the end land before the stages are reused
   }
+  __syncthreads();
 
   // ---- epilogue: each 32 x 32 block goes through the wave's own LDS staging area (float32,
   // padded rows), then lane l owns row l >> 1, columns 16 (l & 1) .. + 15 of the block.
@@ -306,13 +323,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
     bool row_ok;
     size_t grow = 0;                       // grouped: sorted row
     uint16_t* crow = nullptr;              // wgrad: output row
+    float* prow = nullptr;                 // wgrad with split K: this split's float32 partial row
     if (MODE == kGrouped) {
       row_ok = rl < rows;
       grow = (size_t)(row0 + rl);
     } else {
       const int m = m0 + rl;
       row_ok = m < M;
-      if (row_ok)
+      if (row_ok && g.kpart)
+        prow = g.kpart + (((size_t)sp * g.n_experts + e) * M + m) * (size_t)N;
+      else if (row_ok)
         crow = (m < g.m_split) ? static_cast<uint16_t*>(g.c) + (size_t)e * g.c_estride + (size_t)m * g.ldc
                                : static_cast<uint16_t*>(g.c_hi) + (size_t)e * g.c_estride + (size_t)(m - g.m_split) * g.ldc;
     }
@@ -341,7 +361,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
         const int cc = col + 8 * h;
         if (!row_ok || cc >= N) continue;
         float* v8 = val + 8 * h;
-        if (EPI == kStoreT) {
+        if (EPI == kStoreT && MODE == kWgrad && prow) {
+          *reinterpret_cast<float4*>(prow + cc) = make_float4(v8[0], v8[1], v8[2], v8[3]);
+          *reinterpret_cast<float4*>(prow + cc + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
+        } else if (EPI == kStoreT) {
           uint16_t* dst = (MODE == kGrouped) ? static_cast<uint16_t*>(g.c) + grow * g.ldc + cc : crow + cc;
           *reinterpret_cast<uint4*>(dst) = pack8(v8);
         } else if (EPI == kStoreF32) {
@@ -538,20 +561,61 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, size_t
 }
 
 // out[e][c] = sum over rows r of expert e (offsets, or rows [0, n_rows)) of scale[r] * M[r][c]
-// (scale null: 1), float32 in row order, rounded to bfloat16 once.
+// (scale null: 1), rounded to bfloat16 once. A workgroup owns 64 columns of one expert: its
+// 32 row phases each sum every 32nd row (8 columns per thread, 16-byte loads), then the 32
+// partials of a column are added in phase order.
 __global__ __launch_bounds__(256) void colsum_kernel(const uint16_t* __restrict__ Mx, long long ld,
                                                      const float* __restrict__ scale, const int* __restrict__ offsets,
                                                      int n_rows, int C, uint16_t* __restrict__ out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int e = blockIdx.y;
-  if (c >= C) return;
+  __shared__ float s_part[32][65];
+  const int t = threadIdx.x, e = blockIdx.y;
+  const int cg = t & 7, ph = t >> 3;
+  const int c0 = blockIdx.x * 64 + 8 * cg;
   const int lo = offsets ? offsets[e] : 0, hi = offsets ? offsets[e + 1] : n_rows;
-  float s = 0.f;
-  for (int r = lo; r < hi; ++r) {
-    const float v = bf16_to_f32(Mx[(size_t)r * ld + c]);
-    s += scale ? scale[r] * v : v;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < C) {
+    for (int r = lo + ph; r < hi; r += 32) {
+      float v[8];
+      unpack8(*reinterpret_cast<const uint4*>(Mx + (size_t)r * ld + c0), v);
+      const float sc = scale ? scale[r] : 1.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += sc * v[q];
+    }
   }
-  out[(size_t)e * C + c] = f32_to_bf16(s);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s_part[ph][8 * cg + q] = acc[q];
+  __syncthreads();
+  if (t < 64 && blockIdx.x * 64 + t < C) {
+    float sum = 0.f;
+    for (int p = 0; p < 32; ++p) sum += s_part[p][t];
+    out[(size_t)e * C + blockIdx.x * 64 + t] = f32_to_bf16(sum);
+  }
+}
+
+// Split-K weight gradients: out = bfloat16(sum over the ksplit partials, in split order), rows
+// m < m_split of expert e to c, the others to c_hi (as the wgrad epilogue stores them).
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ kpart, int ksplit, int n_experts,
+                                                           int M, int N, uint16_t* c, uint16_t* c_hi, int m_split,
+                                                           long long ldc, long long c_estride) {
+  const long long per_e = (long long)M * (N / 8);
+  const long long total = per_e * n_experts;
+  const size_t plane = (size_t)n_experts * M * N;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    const int e = (int)(i / per_e);
+    const long long r = i - e * per_e;
+    const int m = (int)(r / (N / 8)), n = (int)(r - (long long)m * (N / 8)) * 8;
+    const float* src = kpart + ((size_t)e * M + m) * N + n;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < ksplit; ++sp) {
+      const float4 p0 = *reinterpret_cast<const float4*>(src + sp * plane);
+      const float4 p1 = *reinterpret_cast<const float4*>(src + sp * plane + 4);
+      acc[0] += p0.x; acc[1] += p0.y; acc[2] += p0.z; acc[3] += p0.w;
+      acc[4] += p1.x; acc[5] += p1.y; acc[6] += p1.z; acc[7] += p1.w;
+    }
+    uint16_t* dst = (m < m_split) ? c + (size_t)e * c_estride + (size_t)m * ldc + n
+                                  : c_hi + (size_t)e * c_estride + (size_t)(m - m_split) * ldc + n;
+    *reinterpret_cast<uint4*>(dst) = pack8(acc);
+  }
 }
 
 // dx[t] = sum_j dx_sorted[inv_perm[t k + j]] (j ascending) + R[t] (float32), rounded once;
@@ -585,9 +649,8 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(const uint16_t* __rest
 // Workspace of the backward (after the forward's route / ffn / forward regions).
 // ---------------------------------------------------------------------------------------
 struct BwdBufs {
-  int* tiles128;    // m-tile table of the sorted rows, 128-row tiles
-  int* tiles_d256;  // dense tables over the N token rows (shared expert, router)
-  int* tiles_d128;
+  uint16_t* zero;   // 256 zero bytes (cleared by every call)
+  int* tiles_dense; // m-tile table of one dense "expert" over the N token rows (shared, router)
   float* z;         // [N][E] logits
   float* dz;        // [N][E] (used when the caller passes none)
   float* part;      // [A][n_part]
@@ -599,10 +662,25 @@ struct BwdBufs {
   uint16_t* pre_s;  // shared expert: [N][2 Fs] or [N][Fs]
   uint16_t* dpre_s;
   uint16_t* h_s;    // [N][Fs]
+  float* kpart;     // split-K partials of the weight gradients that split
   size_t bytes;
 };
 
 int n_part_of(int F) { return 2 * ((F + kBN - 1) / kBN); }
+
+// K splits of a weight gradient: enough workgroups for the chip (about 1024) when the
+// output has few tiles, with at least about 512 rows per split, at most 16 splits.
+int wgrad_split(int M, int N, int n_experts, long long rows_total) {
+  const long long tiles = (long long)n_experts * ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  if (tiles <= 0 || tiles >= 1024) return 1;
+  const long long want = (1024 + tiles - 1) / tiles;
+  const long long by_rows = std::max<long long>(1, rows_total / std::max(n_experts, 1) / 512);
+  return (int)std::min<long long>(std::min(want, by_rows), 16);
+}
+size_t wgrad_part_floats(int M, int N, int n_experts, long long rows_total) {
+  const int k = wgrad_split(M, N, n_experts, rows_total);
+  return k > 1 ? (size_t)k * n_experts * M * N : 0;
+}
 int e8_of(int E) { return (E + 7) & ~7; }
 
 BwdBufs bwd_bufs(const moe_config& c, char* base) {
@@ -611,9 +689,8 @@ BwdBufs bwd_bufs(const moe_config& c, char* base) {
   const size_t d = (size_t)c.d_model, F = (size_t)c.d_ff, Fs = (size_t)std::max(c.d_ff_shared, 0);
   const size_t pf = c.act == MOE_ACT_SWIGLU ? 2 : 1;
   BwdBufs b{};
-  b.tiles128 = w.take_t<int>(kTileHdr + kTileInts * ((A + kBM - 1) / kBM + E));
-  b.tiles_d256 = w.take_t<int>(kTileHdr + kTileInts * ((N + 255) / 256));
-  b.tiles_d128 = w.take_t<int>(kTileHdr + kTileInts * ((N + kBM - 1) / kBM));
+  b.zero = w.take_t<uint16_t>(128);
+  b.tiles_dense = w.take_t<int>(kTileHdr + kTileInts * ((N + kBM - 1) / kBM));
   b.z = w.take_t<float>(N * E);
   b.dz = w.take_t<float>(N * E);
   b.part = w.take_t<float>(A * (size_t)n_part_of((int)F));
@@ -625,6 +702,16 @@ BwdBufs bwd_bufs(const moe_config& c, char* base) {
   b.pre_s = w.take_t<uint16_t>(N * pf * Fs);
   b.dpre_s = w.take_t<uint16_t>(N * pf * Fs);
   b.h_s = w.take_t<uint16_t>(N * Fs);
+  const int m = c.act == MOE_ACT_SWIGLU ? 2 : 1;
+  size_t kp = 0;
+  kp = std::max(kp, wgrad_part_floats((int)d, (int)F, (int)E, (long long)A));
+  kp = std::max(kp, wgrad_part_floats(m * (int)F, (int)d, (int)E, (long long)A));
+  if (Fs) {
+    kp = std::max(kp, wgrad_part_floats((int)d, (int)Fs, 1, (long long)N));
+    kp = std::max(kp, wgrad_part_floats(m * (int)Fs, (int)d, 1, (long long)N));
+  }
+  kp = std::max(kp, wgrad_part_floats((int)E, (int)d, 1, (long long)N));
+  b.kpart = w.take_t<float>(kp);
   b.bytes = w.used();
   return b;
 }
@@ -638,18 +725,20 @@ hipError_t run_gemm(const BwdGemm& g, long long max_tiles, hipStream_t stream) {
   return hipGetLastError();
 }
 
-BwdGemm gemm_args() {
+BwdGemm gemm_args(const uint16_t* zero) {
   BwdGemm g{};
+  g.zero = zero;
+  g.ksplit = 1;
   g.ldc = 0;
   g.m_split = 1 << 30;
   return g;
 }
 
 // dh' = dy_rows W2 (rows of a tile table) with the activation-backward epilogue.
-hipError_t act_backward(const moe_config& c, const int* tiles, long long max_m_tiles, const uint16_t* dy_rows,
+hipError_t act_backward(const moe_config& c, const uint16_t* zero, const int* tiles, long long max_m_tiles, const uint16_t* dy_rows,
                         const void* w2, long long w2_estride, int F, const uint16_t* pre, const float* gate,
                         float* part, uint16_t* dpre, hipStream_t stream) {
-  BwdGemm g = gemm_args();
+  BwdGemm g = gemm_args(zero);
   g.a[0] = dy_rows;
   g.lda = c.d_model;
   g.klen[0] = c.d_model;
@@ -672,10 +761,10 @@ hipError_t act_backward(const moe_config& c, const int* tiles, long long max_m_t
 
 // rows of dpre times [W1; W3] (or W1) -> out (T, or float32 with optional add)
 template <int EPI>
-hipError_t dx_rows(const moe_config& c, const int* tiles, long long max_m_tiles, const uint16_t* dpre, int F,
+hipError_t dx_rows(const moe_config& c, const uint16_t* zero, const int* tiles, long long max_m_tiles, const uint16_t* dpre, int F,
                    const void* w1, const void* w3, long long w_estride, void* out, const float* c_in,
                    hipStream_t stream) {
-  BwdGemm g = gemm_args();
+  BwdGemm g = gemm_args(zero);
   const bool swi = c.act == MOE_ACT_SWIGLU;
   g.a[0] = dpre;
   g.a[1] = swi ? dpre + F : nullptr;
@@ -696,10 +785,13 @@ hipError_t dx_rows(const moe_config& c, const int* tiles, long long max_m_tiles,
 }
 
 // C_e[M][N] = sum over the expert's rows r of A[r][m] B[r][n] (+ a second segment)
-hipError_t wgrad(const uint16_t* a0, const uint16_t* a1, long long lda, const uint16_t* b0, const uint16_t* b1,
-                 long long ldb, int M, int N, const int* offsets, int n_experts, int n_rows, void* c, void* c_hi,
-                 int m_split, long long ldc, long long c_estride, hipStream_t stream) {
-  BwdGemm g = gemm_args();
+hipError_t wgrad(const uint16_t* zero, float* kpart, long long rows_total, const uint16_t* a0, const uint16_t* a1,
+                 long long lda, const uint16_t* b0, const uint16_t* b1, long long ldb, int M, int N, const int* offsets,
+                 int n_experts, int n_rows, void* c, void* c_hi, int m_split, long long ldc, long long c_estride,
+                 hipStream_t stream) {
+  BwdGemm g = gemm_args(zero);
+  g.ksplit = wgrad_split(M, N, n_experts, rows_total);
+  g.kpart = g.ksplit > 1 ? kpart : nullptr;
   g.a[0] = a0;
   g.a[1] = a1;
   g.b[0] = b0;
@@ -717,13 +809,18 @@ hipError_t wgrad(const uint16_t* a0, const uint16_t* a1, long long lda, const ui
   g.m_split = m_split;
   g.ldc = ldc;
   g.c_estride = c_estride;
-  const long long S = (long long)n_experts * ((M + kBM - 1) / kBM) * g.n_tiles_n;
-  return run_gemm<kWgrad, kStoreT>(g, S, stream);
+  const long long S = (long long)n_experts * ((M + kBM - 1) / kBM) * g.n_tiles_n * g.ksplit;
+  const hipError_t err = run_gemm<kWgrad, kStoreT>(g, S, stream);
+  if (err != hipSuccess || g.ksplit == 1) return err;
+  const long long total = (long long)n_experts * M * (N / 8);
+  wgrad_reduce_kernel<<<(unsigned)std::min<long long>((total + 255) / 256, 8192), 256, 0, stream>>>(
+      kpart, g.ksplit, n_experts, M, N, static_cast<uint16_t*>(c), static_cast<uint16_t*>(c_hi), m_split, ldc, c_estride);
+  return hipGetLastError();
 }
 
 hipError_t colsum(const uint16_t* Mx, long long ld, const float* scale, const int* offsets, int n_groups, int n_rows,
                   int C, void* out, hipStream_t stream) {
-  dim3 grid((C + 255) / 256, n_groups);
+  dim3 grid((C + 63) / 64, n_groups);
   colsum_kernel<<<grid, 256, 0, stream>>>(Mx, ld, scale, offsets, n_rows, C, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
@@ -743,8 +840,19 @@ void carve_backward(const moe_config& c, WsCarver& w, WsLayout* L) {
 }
 
 hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& in, const moe_grads& gr,
-                           const RouteOut& ro, hipStream_t s) {
+                           const RouteOut& ro, void* const* events, hipStream_t s) {
   const BwdBufs B = bwd_bufs(c, static_cast<char*>(L.bwd));
+  int next_event = 0;
+  auto mark = [&](int upto) -> hipError_t {  // record every event up to index `upto`
+    for (; events && next_event <= upto; ++next_event) {
+      const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[next_event]), s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  BWD_TRY(mark(0));
+  zero_kernel<<<1, 256, 0, s>>>(reinterpret_cast<uint4*>(B.zero), 16);
+  BWD_TRY(hipGetLastError());
   const int N = (int)c.n_tokens, E = c.n_experts, k = c.top_k, d = c.d_model, F = c.d_ff;
   const int A = N * k, Fs = c.d_ff_shared, E8 = e8_of(E);
   const bool swi = c.act == MOE_ACT_SWIGLU, bias = c.has_bias != 0;
@@ -774,19 +882,24 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     BWD_TRY(zero(gr.ds_b1, (size_t)Fs * t2));
     BWD_TRY(zero(gr.ds_w2, (size_t)d * Fs * t2));
     BWD_TRY(zero(gr.ds_b2, (size_t)d * t2));
-    return hipGetLastError();
+    BWD_TRY(hipGetLastError());
+    return mark(MOE_BWD_EVENTS - 1);
   }
   BWD_TRY(launch_dispatch_scanned(c, L, in.x, ids, ro.topk_w, L.x_sorted, L.perm, L.inv_perm, L.gate_sorted, s));
   uint16_t* xs = static_cast<uint16_t*>(L.x_sorted);
   uint16_t* dys = static_cast<uint16_t*>(L.y_sorted);
   uint16_t* hw = static_cast<uint16_t*>(L.h);
   launch_copy(c, in.dy, L.inv_perm, dys, s);
-  const long long mt128 = (A + kBM - 1) / kBM + E;
-  BWD_TRY(launch_tile_table(c, L.offsets, kBM, (int)mt128, B.tiles128, L.err, s));
+  // the routed m-tile table is the forward's (routing's final reduction wrote it)
+  if (ffn_tile_rows(c) != kBM) return hipErrorInvalidValue;
+  const long long mtA = ffn_max_m_tiles(c);
+  BWD_TRY(mark(1));
   BWD_TRY(launch_up_save(c, L.tiles, xs, in.w1, in.w3, in.b1, L.gate_sorted, F, B.pre, hw, s));
+  BWD_TRY(mark(2));
 
   // routed experts: dh' with the activation backward, then dx_sorted and the weight gradients
-  BWD_TRY(act_backward(c, B.tiles128, mt128, dys, in.w2, (long long)d * F, F, B.pre, L.gate_sorted, B.part, B.dpre, s));
+  BWD_TRY(act_backward(c, B.zero, L.tiles, mtA, dys, in.w2, (long long)d * F, F, B.pre, L.gate_sorted, B.part, B.dpre, s));
+  BWD_TRY(mark(3));
   {
     RouterBwd r{};
     r.z = B.z;
@@ -813,37 +926,43 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     router_backward_kernel<<<(N + 3) / 4, 256, 0, s>>>(r);
     BWD_TRY(hipGetLastError());
   }
-  BWD_TRY(dx_rows<kStoreT>(c, B.tiles128, mt128, B.dpre, F, in.w1, in.w3, (long long)F * d, B.dxs, nullptr, s));
-  BWD_TRY(wgrad(dys, nullptr, d, hw, nullptr, F, d, F, L.offsets, E, 0, gr.dw2, nullptr, d, F, (long long)d * F, s));
-  BWD_TRY(wgrad(B.dpre, nullptr, swi ? 2 * (long long)F : F, xs, nullptr, d, swi ? 2 * F : F, d, L.offsets, E, 0,
+  BWD_TRY(mark(4));
+  BWD_TRY(dx_rows<kStoreT>(c, B.zero, L.tiles, mtA, B.dpre, F, in.w1, in.w3, (long long)F * d, B.dxs, nullptr, s));
+  BWD_TRY(mark(5));
+  BWD_TRY(wgrad(B.zero, B.kpart, A, dys, nullptr, d, hw, nullptr, F, d, F, L.offsets, E, 0, gr.dw2, nullptr, d, F,
+                (long long)d * F, s));
+  BWD_TRY(mark(6));
+  BWD_TRY(wgrad(B.zero, B.kpart, A, B.dpre, nullptr, swi ? 2 * (long long)F : F, xs, nullptr, d, swi ? 2 * F : F, d, L.offsets, E, 0,
                 gr.dw1, gr.dw3, F, d, (long long)F * d, s));
   if (bias) {
     BWD_TRY(colsum(B.dpre, F, nullptr, L.offsets, E, 0, F, gr.db1, s));
     BWD_TRY(colsum(dys, d, L.gate_sorted, L.offsets, E, 0, d, gr.db2, s));
   }
+  BWD_TRY(mark(7));
 
   // shared expert over all N rows (gate 1); its dx lands in R
-  BWD_TRY(launch_dense_tiles(N, kBM, B.tiles_d128, s));
+  BWD_TRY(launch_dense_tiles(N, kBM, B.tiles_dense, s));
   const long long mtN = (N + kBM - 1) / kBM;
   if (Fs > 0) {
-    BWD_TRY(launch_dense_tiles(N, 256, B.tiles_d256, s));
-    BWD_TRY(launch_up_save(c, B.tiles_d256, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
-    BWD_TRY(act_backward(c, B.tiles_d128, mtN, T(in.dy), in.s_w2, 0, Fs, B.pre_s, nullptr, nullptr, B.dpre_s, s));
-    BWD_TRY(dx_rows<kStoreF32>(c, B.tiles_d128, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, s));
-    BWD_TRY(wgrad(T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr, d, Fs, 0, s));
-    BWD_TRY(wgrad(B.dpre_s, nullptr, swi ? 2 * (long long)Fs : Fs, T(in.x), nullptr, d, swi ? 2 * Fs : Fs, d,
+    BWD_TRY(launch_up_save(c, B.tiles_dense, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
+    BWD_TRY(act_backward(c, B.zero, B.tiles_dense, mtN, T(in.dy), in.s_w2, 0, Fs, B.pre_s, nullptr, nullptr, B.dpre_s, s));
+    BWD_TRY(dx_rows<kStoreF32>(c, B.zero, B.tiles_dense, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, s));
+    BWD_TRY(wgrad(B.zero, B.kpart, N, T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr,
+                  d, Fs, 0, s));
+    BWD_TRY(wgrad(B.zero, B.kpart, N, B.dpre_s, nullptr, swi ? 2 * (long long)Fs : Fs, T(in.x), nullptr, d, swi ? 2 * Fs : Fs, d,
                   nullptr, 1, N, gr.ds_w1, gr.ds_w3, Fs, d, 0, s));
     if (bias) {
       BWD_TRY(colsum(B.dpre_s, Fs, nullptr, nullptr, 1, N, Fs, gr.ds_b1, s));
       BWD_TRY(colsum(T(in.dy), d, nullptr, nullptr, 1, N, d, gr.ds_b2, s));
     }
   }
+  BWD_TRY(mark(8));
 
   // router: dW_g = dz^T x and R (+)= dz W_g, both with dz = hi + lo in bfloat16
-  BWD_TRY(wgrad(B.dz_hl, B.dz_hl + E8, 2 * (long long)E8, T(in.x), T(in.x), d, E, d, nullptr, 1, N, gr.dw_router,
+  BWD_TRY(wgrad(B.zero, B.kpart, N, B.dz_hl, B.dz_hl + E8, 2 * (long long)E8, T(in.x), T(in.x), d, E, d, nullptr, 1, N, gr.dw_router,
                 nullptr, E, d, 0, s));
   {
-    BwdGemm g = gemm_args();
+    BwdGemm g = gemm_args(B.zero);
     g.a[0] = B.dz_hl;
     g.a[1] = B.dz_hl + E8;
     g.lda = 2 * (long long)E8;
@@ -853,7 +972,7 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     g.b[1] = T(in.w_router);
     g.ldb = d;
     g.N = d;
-    g.tiles = B.tiles_d128;
+    g.tiles = B.tiles_dense;
     g.n_tiles_n = (d + kBN - 1) / kBN;
     g.c = B.R;
     g.ldc = d;
@@ -861,7 +980,8 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     BWD_TRY((run_gemm<kGrouped, kStoreF32>(g, mtN * g.n_tiles_n, s)));
   }
   bwd_combine_kernel<<<(N + 3) / 4, 256, 0, s>>>(B.dxs, L.inv_perm, B.R, N, k, d, static_cast<uint16_t*>(gr.dx));
-  return hipGetLastError();
+  BWD_TRY(hipGetLastError());
+  return mark(MOE_BWD_EVENTS - 1);
 }
 
 }  // namespace moe

@@ -99,27 +99,7 @@ constexpr int kGM = 8, kGN = 4;
 constexpr int kStageElems = kBM * kBK;  // bf16 elements of one operand stage (16 KiB)
 constexpr int kGemmThreads = 512;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
-// (global_load_lds_dwordx4; M0 holds the wave-uniform LDS base). Written as asm so the
-// compiler's wait insertion, which cannot tell the four stage buffers apart once more than a
-// few copies are in flight, does not stall every LDS read on every copy: the kernel waits
-// for each stage explicitly. The instruction has no register outputs.
-MOE_DEV void lds_dma16(const void* src, uint16_t* lds_base) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-}
-// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's loads older than its last N have landed in LDS
-// and its own LDS accesses are done.
-template <int N> MOE_DEV void wait_vm_lds() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
-}
-// Workgroup barrier without a memory fence: __syncthreads() would also wait for every load
-// in flight (the stages still being prefetched). The waits each phase needs are explicit;
-// the clobber keeps the compiler from moving memory accesses across it.
-MOE_DEV void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// lds_dma16, wait_vm_lds and stage_barrier: moe_common.h
 
 template <int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
@@ -641,13 +621,6 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_tile_table(const moe_config& c, const int32_t* offsets, int bm, int max_tiles, int* tiles, int* err,
-                             hipStream_t stream) {
-  const int A = (int)(c.n_tokens * c.top_k);
-  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, bm, max_tiles, tiles, err);
   return hipGetLastError();
 }
 

@@ -358,7 +358,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const void* b2, const void* s_w1, const void* s_w3, const void* s_b1, const void* s_w2,
                         const void* s_b2, const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
                         int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        void* const* stage_events, void* stream) {
   MOE_TRY(check_config(cfg, true));
   MOE_TRY(check_backward_config(cfg));
   MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
@@ -400,11 +400,14 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_TRY(opt_4(sel_bias));
   MOE_TRY(opt_4(g.dz));
   MOE_TRY(opt_4(g.dgate));
+  if (stage_events)
+    for (int i = 0; i < MOE_BWD_EVENTS; ++i)
+      if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
   WsLayout L{};
   MOE_TRY(check_ws(*cfg, MOE_OP_BACKWARD, ws, ws_bytes, &L));
   BwdIn in{x, w_router, logit_bias, sel_bias, w1, w3, b1, w2, b2, s_w1, s_w3, s_b1, s_w2, s_b2, dy, aux_coef, z_coef};
   RouteOut ro{topk_ids, topk_w, counts, stats};
-  return hip_status(launch_backward(*cfg, L, in, g, ro, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_backward(*cfg, L, in, g, ro, stage_events, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float* sel_bias, float rate,

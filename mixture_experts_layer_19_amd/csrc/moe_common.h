@@ -87,4 +87,29 @@ MOE_DEV float wave_max(float v) {
   return v;
 }
 
+
+// ---- streaming operands into LDS (the grouped GEMMs)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; M0 holds the wave-uniform LDS base). Written as asm so the
+// compiler's wait insertion, which cannot tell the four stage buffers apart once more than a
+// few copies are in flight, does not stall every LDS read on every copy: the kernel waits
+// for each stage explicitly. The instruction has no register outputs.
+MOE_DEV void lds_dma16(const void* src, uint16_t* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wave's loads older than its last N have landed in LDS
+// and its own LDS accesses are done.
+template <int N> MOE_DEV void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+// Workgroup barrier without a memory fence: __syncthreads() would also wait for every load
+// in flight (the stages still being prefetched). The waits each phase needs are explicit;
+// the clobber keeps the compiler from moving memory accesses across it.
+MOE_DEV void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace moe

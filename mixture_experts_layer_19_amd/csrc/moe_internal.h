@@ -222,11 +222,9 @@ struct RouteOut {
   int32_t* topk_ids; float* topk_w; int32_t* counts; float* stats;
 };
 void carve_backward(const moe_config& c, WsCarver& w, WsLayout* L);
+// events: null or MOE_BWD_EVENTS events recorded at the stage boundaries (moe.h)
 hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& in, const moe_grads& gr,
-                           const RouteOut& ro, hipStream_t stream);
-// m-tile table with bm-row tiles from offsets [E+1] over A = N k rows (bad offsets: *err)
-hipError_t launch_tile_table(const moe_config& c, const int32_t* offsets, int bm, int max_tiles, int* tiles, int* err,
-                             hipStream_t stream);
+                           const RouteOut& ro, void* const* events, hipStream_t stream);
 // rows of x copied to their sorted slots (x_sorted[inv_perm[n k + j]] = x[n])
 void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream);
 

@@ -157,3 +157,38 @@ def test_workload_recipes_are_seeded_and_shaped():
 def torch_equal(x, y):
     import torch
     return torch.equal(x, y)
+
+
+def test_backward_host_validation():
+    """moe_backward rejects unsupported or incomplete calls before any HIP call."""
+    lib = B.lib()
+    f = 0x10000
+    fp = ctypes.c_void_p(f)
+
+    def grads(**o):
+        names = B.GRAD_NAMES
+        full = dict(dx=f, dw_router=f, dw1=f, dw3=f, dw2=f)
+        full.update(o)
+        return B.MoeGradsStruct(*[full.get(n) for n in names])
+
+    def call(cfg, g, ev=None, shared=(None,) * 5, ws_bytes=1 << 40):
+        return lib.moe_backward(ctypes.byref(cfg.struct()), fp, fp, None, None, fp, fp, None, fp, None, *shared,
+                                fp, ctypes.c_float(0.0), ctypes.c_float(0.0), ctypes.byref(g) if g else None,
+                                fp, fp, fp, fp, fp, ws_bytes, ev, None)
+
+    assert call(MIXTRAL.with_tokens(64), None) == B.MOE_ERR_INVALID_ARG
+    f32 = B.LayerConfig(64, 64, 8, 2, 64, dtype="f32")
+    assert call(f32, grads()) == B.MOE_ERR_UNSUPPORTED
+    cap = B.LayerConfig(64, 64, 8, 2, 64, capacity_factor=1.0)
+    assert call(cap, grads()) == B.MOE_ERR_UNSUPPORTED
+    assert B.moe_workspace_size(f32, B.Op.BACKWARD) == 0 and B.moe_workspace_size(cap, B.Op.BACKWARD) == 0
+    ok = B.LayerConfig(64, 64, 8, 2, 64)
+    assert call(ok, grads(dw3=None)) == B.MOE_ERR_INVALID_ARG         # SwiGLU needs dw3
+    assert call(ok, grads(db1=f)) == B.MOE_ERR_INVALID_ARG            # no bias: no bias gradients
+    assert call(ok, grads(dx=0x10008)) == B.MOE_ERR_UNSUPPORTED       # misaligned
+    ev = (ctypes.c_void_p * B.BWD_EVENTS)(*([f] * (B.BWD_EVENTS - 1) + [None]))
+    assert call(ok, grads(), ev) == B.MOE_ERR_INVALID_ARG
+    assert call(ok, grads(), ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    sh = B.LayerConfig(64, 64, 8, 2, 64, d_ff_shared=64)
+    assert call(sh, grads(), shared=(f, f, None, f, None)) == B.MOE_ERR_INVALID_ARG   # shared grads missing
+    assert B.moe_workspace_size(ok, B.Op.BACKWARD) > B.moe_workspace_size(ok, B.Op.FORWARD) > 0

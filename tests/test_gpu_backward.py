@@ -116,6 +116,10 @@ CASES = {
     "sigmoid_raw_gelu_shared": (W.WORKLOADS["gpt2_small"].scaled(n_tokens=64, d_model=64, n_experts=8, top_k=3,
                                                                  d_ff=96, router="sigmoid", norm_topk=False,
                                                                  routed_scaling=1.7, d_ff_shared=64), 0.0, 0.0),
+    # long ragged K over few output tiles: the weight gradients (routed, shared and router)
+    # split K into runs reduced in a fixed order
+    "split_k": (W.WORKLOADS["mixtral"].scaled(n_tokens=4096, d_model=64, n_experts=4, top_k=1, d_ff=64,
+                                              d_ff_shared=64), 0.01, 1e-3),
     # one expert for all (k = E = 1): every token in one ragged K of the weight gradients
     "single_expert": (W.WORKLOADS["mixtral"].scaled(n_tokens=70, d_model=64, n_experts=1, top_k=1, d_ff=64), 0.1, 0.1),
 }
