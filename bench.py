@@ -55,9 +55,9 @@ def file_sha(path):
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def traffic_for(kernel_src, workload):
+def traffic_for(kernel_src, workload, kernel=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
-    current source of the kernel; else None."""
+    current source of the kernel; else None. `kernel`: the entry of a per-kernel file."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -65,6 +65,8 @@ def traffic_for(kernel_src, workload):
         t = json.load(fh)
     if t.get("source_sha") != file_sha(kernel_src):
         return None
+    if kernel is not None:
+        return (t.get("kernels", {}).get(kernel) or {}).get("hbm_bytes_per_launch")
     return t.get("hbm_bytes_per_launch")
 
 
@@ -182,10 +184,17 @@ def run_backward(args, w, inp):
     gemm_stages = ("up_recompute", "act_backward", "dx_rows", "dw2", "dw13")
     rates = {s: work[s] / (stage_ms[s] * 1e-3) / 1e12 for s in gemm_stages + ("shared",) if stage_ms[s] > 0}
     dom = max(gemm_stages, key=lambda s: stage_ms[s])
-    kernel = {"up_recompute": "expert_gemm_bf16_kernel<save epilogue>",
-              "act_backward": "bwd_gemm_kernel<grouped, activation backward>",
-              "dx_rows": "bwd_gemm_kernel<grouped, store>", "dw2": "bwd_gemm_kernel<wgrad>",
-              "dw13": "bwd_gemm_kernel<wgrad>"}[dom]
+    swi = cfg.act == "swiglu"
+    kernel = {"up_recompute": "expert_gemm_bf16_kernel<3>" if swi else "expert_gemm_bf16_kernel<4>",
+              "act_backward": "bwd_gemm_kernel<0, 2>" if swi else "bwd_gemm_kernel<0, 3>",
+              "dx_rows": "bwd_gemm_kernel<0, 0>", "dw2": "bwd_gemm_kernel<1, 0>", "dw13": "bwd_gemm_kernel<1, 0>"}[dom]
+    csrc = os.path.join(ROOT, "mixture_experts_layer_19_amd", "csrc")
+    # the weight-gradient kernel serves several launches per call, so its averaged counters
+    # do not describe one stage
+    traffic = None
+    if dom not in ("dw2", "dw13"):
+        src = "expert_ffn.hip" if dom == "up_recompute" else "backward.hip"
+        traffic = traffic_for(os.path.join(csrc, src), f"{w.name}_backward", kernel)
     E = cfg.n_experts
     res = {
         "metric": "MoE layer bwd tokens/s (recompute + all gradients) + active TFLOP/s (% bf16 MFMA peak)",
@@ -202,7 +211,7 @@ def run_backward(args, w, inp):
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "stage_tflops": {s: round(v, 1) for s, v in rates.items()},
         "roofline": {"kernel": kernel, "stage": dom, "bound": "mfma", "achieved": rates[dom], "peak": peak,
-                     "unit": "TFLOP/s", "frac": rates[dom] / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": rates[dom] / peak, "traffic": traffic,
                      "flops_per_launch": work[dom], "avg_launch_ms": stage_ms[dom]},
         "events_vs_wall": sum(stage_ms.values()) / ms_per_step,
     }
