@@ -430,35 +430,36 @@ def _phi(u):
     return np.exp(-0.5 * u * u) / math.sqrt(2.0 * math.pi)
 
 
-def expert_ffn_backward(xr, act: str, do, w1, w2, w3=None, b1=None, b2=None):
+def expert_ffn_backward(xr, act: str, do, w1, w2, w3=None, b1=None, b2=None, weights: bool = True):
     """One expert on rows xr [m, d] with upstream do [m, d_out]: returns (dx, grads) where
-    grads holds dw1, dw2 (and dw3 for swiglu, db1 / db2 when the biases are given)."""
+    grads holds dw1, dw2 (and dw3 for swiglu, db1 / db2 when the biases are given);
+    weights=False skips the weight gradients (grads is then empty)."""
     xr, do = np.asarray(xr, f64), np.asarray(do, f64)
     w1, w2 = np.asarray(w1, f64), np.asarray(w2, f64)
     g = {}
     if act == "gelu":
         a = xr @ w1.T + (0.0 if b1 is None else np.asarray(b1, f64)[None, :])
-        h = gelu_erf(a)
         dh = do @ w2
-        g["dw2"] = do.T @ h
-        if b2 is not None:
-            g["db2"] = do.sum(axis=0)
         da = dh * (0.5 * (1.0 + _erf(a / math.sqrt(2.0))) + a * _phi(a))
-        g["dw1"] = da.T @ xr
-        if b1 is not None:
-            g["db1"] = da.sum(axis=0)
+        if weights:
+            g["dw2"] = do.T @ gelu_erf(a)
+            if b2 is not None:
+                g["db2"] = do.sum(axis=0)
+            g["dw1"] = da.T @ xr
+            if b1 is not None:
+                g["db1"] = da.sum(axis=0)
         return da @ w1, g
     w3 = np.asarray(w3, f64)
     gt = xr @ w1.T
     ut = xr @ w3.T
     sg = sigmoid(gt)
-    h = gt * sg * ut
     dh = do @ w2
-    g["dw2"] = do.T @ h
     du = dh * gt * sg
     dg = dh * ut * sg * (1.0 + gt * (1.0 - sg))
-    g["dw1"] = dg.T @ xr
-    g["dw3"] = du.T @ xr
+    if weights:
+        g["dw2"] = do.T @ (gt * sg * ut)
+        g["dw1"] = dg.T @ xr
+        g["dw3"] = du.T @ xr
     return dg @ w1 + du @ w3, g
 
 
@@ -490,48 +491,61 @@ def gate_weights_backward(z_row, ids_row, dw, spec: Spec) -> np.ndarray:
 
 
 def backward(x, params: Mapping[str, Any], spec: Spec, dy, aux_coef: float = 0.0, z_coef: float = 0.0,
-             logit_bias=None, sel_bias=None):
+             logit_bias=None, sel_bias=None, tokens=None):
     """Gradients of J = <dy, y> + aux_coef L + z_coef z_loss, y and L as in forward_loop /
     load_balance, z_loss as in z_loss. Returns a dict: dx, dw_g, dw1 / dw3 / dw2 / db1 / db2
     (per expert, like params; zero for idle experts), the shared expert's ds_w1 ... when
-    present, dgate [N, k] (dJ/dw) and dz [N, E]."""
+    present, dgate [N, k] (dJ/dw) and dz [N, E].
+
+    tokens: None, or a list of token indices: then only dx, dz and dgate of those tokens are
+    returned (rows in the list's order); routing, f, P and the z-loss still cover all N
+    tokens, so the rows equal the full result's."""
     x, dy = np.asarray(x, f64), np.asarray(dy, f64)
     r = route(x, params["w_g"], spec, logit_bias, sel_bias)
     n, d = x.shape
     E, k = spec.n_experts, spec.top_k
-    out = {"dx": np.zeros_like(x), "dz": np.zeros((n, E), f64), "dgate": np.zeros((n, k), f64)}
-    for name in ("w1", "w3", "w2", "b1", "b2"):
-        if params.get(name) is not None:
-            out["d" + name] = np.zeros((E,) + np.shape(params[name][0]), f64)
-    for t in range(n):
+    rows = list(range(n)) if tokens is None else [int(t) for t in tokens]
+    full = tokens is None
+    m = len(rows)
+    out = {"dx": np.zeros((m, d), f64), "dz": np.zeros((m, E), f64), "dgate": np.zeros((m, k), f64)}
+    if full:
+        for name in ("w1", "w3", "w2", "b1", "b2"):
+            if params.get(name) is not None:
+                out["d" + name] = np.zeros((E,) + np.shape(params[name][0]), f64)
+    for i, t in enumerate(rows):
         for j in range(k):
             e = int(r.ids[t, j])
             pe = _expert(params, e)
             o = expert_ffn(x[t][None, :], spec.act, **pe)[0]
-            out["dgate"][t, j] = np.dot(dy[t], o)
-            dxt, g = expert_ffn_backward(x[t][None, :], spec.act, r.w[t, j] * dy[t][None, :], **pe)
-            out["dx"][t] += dxt[0]
-            for name, v in g.items():
-                out[name][e] += v
-        out["dz"][t] = gate_weights_backward(r.z[t], r.ids[t], out["dgate"][t], spec)
+            out["dgate"][i, j] = np.dot(dy[t], o)
+            dxt, g = expert_ffn_backward(x[t][None, :], spec.act, r.w[t, j] * dy[t][None, :], **pe, weights=full)
+            out["dx"][i] += dxt[0]
+            if full:
+                for name, v in g.items():
+                    out[name][e] += v
+        out["dz"][i] = gate_weights_backward(r.z[t], r.ids[t], out["dgate"][i], spec)
     if params.get("s_w1") is not None:
-        dxs, g = expert_ffn_backward(x, spec.act, dy, params["s_w1"], params["s_w2"], params.get("s_w3"),
-                                     params.get("s_b1"), params.get("s_b2"))
+        dxs, g = expert_ffn_backward(x[rows], spec.act, dy[rows], params["s_w1"], params["s_w2"], params.get("s_w3"),
+                                     params.get("s_b1"), params.get("s_b2"), weights=full)
         out["dx"] += dxs
-        for name, v in g.items():
-            out["ds_" + name[1:]] = v
+        if full:
+            for name, v in g.items():
+                out["ds_" + name[1:]] = v
     # aux losses through p = softmax(z): L = E sum_e f_e P_e with f constant, and z_loss
     f, _, _ = load_balance(r.p, r.ids, E)
+    p = r.p[rows]
     if aux_coef:
         gp = (E / n) * f[None, :]
-        out["dz"] += f64(aux_coef) * r.p * (gp - (r.p * gp).sum(axis=1, keepdims=True))
+        out["dz"] += f64(aux_coef) * p * (gp - (p * gp).sum(axis=1, keepdims=True))
     if z_coef:
-        m = r.z.max(axis=1)
-        lse = m + np.log(np.exp(r.z - m[:, None]).sum(axis=1))
-        out["dz"] += f64(z_coef) * (2.0 * lse / n)[:, None] * r.p
+        z = r.z[rows]
+        mx = z.max(axis=1)
+        lse = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))
+        out["dz"] += f64(z_coef) * (2.0 * lse / n)[:, None] * p
     w_g = np.asarray(params["w_g"], f64)
     out["dx"] += out["dz"] @ w_g
-    out["dw_g"] = out["dz"].T @ x
+    if full:
+        out["dw_g"] = out["dz"].T @ x
     return out
 
 

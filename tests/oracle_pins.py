@@ -571,4 +571,24 @@ def pin_validation(O):
         O.dispatch(np.array([[-1, 0]]), 4)
 
 
+def pin_backward_token_subset_equals_full(O):
+    """backward(tokens=...) returns exactly the full result's rows (routing, f, P and the
+    z-loss over all tokens)."""
+    rng = np.random.default_rng(11)
+    n, d, E, k, f = 12, 6, 5, 2, 7
+    x = rng.standard_normal((n, d))
+    params = {"w_g": rng.standard_normal((E, d)),
+              "w1": rng.standard_normal((E, f, d)) * 0.3, "w3": rng.standard_normal((E, f, d)) * 0.3,
+              "w2": rng.standard_normal((E, d, f)) * 0.3}
+    spec = O.Spec(n_experts=E, top_k=k, router="softmax_topk", norm_topk=True, act="swiglu")
+    dy = rng.standard_normal((n, d))
+    full = O.backward(x, params, spec, dy, 0.3, 0.2)
+    sub = [7, 2, 11]
+    part = O.backward(x, params, spec, dy, 0.3, 0.2, tokens=sub)
+    assert set(part) == {"dx", "dz", "dgate"}
+    for key in ("dx", "dz", "dgate"):
+        np.testing.assert_allclose(part[key], full[key][sub], rtol=1e-13, atol=1e-13)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+

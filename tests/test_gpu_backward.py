@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import f64, oracle_params, spec_of
+from gpu_helpers import compare_ids, f64, oracle_params, spec_of
 from mixture_experts_layer_19_amd import binding as B
 from mixture_experts_layer_19_amd import workload as W
 from oracle import moe_oracle as O
@@ -180,3 +180,65 @@ def test_backward_is_deterministic():
     for k in a:
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
+
+
+def test_backward_fullsize_sampled():
+    """The Mixtral-shaped backward in the configuration bench.py --mode backward times (full
+    N = 8192, d = 4096, d_ff = 14336, preallocated workspace, aux 0.01, z-loss 1e-3, the
+    bench's inputs). Routing is checked on every token; dx, dz and dgate on a sample of tokens
+    whose two experts are the two sampled experts (so the oracle widens only their weights),
+    including tokens at the edges of their slices; dW1, dW3 and dW2 on 6 hidden units of each
+    sampled expert, which the oracle's per-expert backward gives exactly from those units'
+    weights alone (hidden units do not interact in these gradients)."""
+    w = W.WORKLOADS["mixtral"]
+    cfg = w.cfg
+    N, d, E, k, F = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
+    aux, zc = 0.01, 1e-3
+    say(f"[backward fullsize] {cfg} aux={aux} z={zc}")
+    inp = W.make_inputs(w, seed=0)
+    dy = W.random_rows(N, d, cfg.torch_dtype, seed=0, tensor_id=DY)
+    ws = B.workspace(cfg, B.Op.BACKWARD)
+    out = B.moe_backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], dy, ws=ws,
+                         aux_coef=aux, z_coef=zc)
+    torch.cuda.synchronize()
+    spec = spec_of(cfg)
+    x64, dy64 = f64(inp["x"]), f64(dy)
+    wg = f64(inp["w_router"])
+    r = O.route(x64, wg, spec)
+    ids = out["topk_ids"].cpu().numpy()
+    near, intra, agree = compare_ids(ids, r, k)
+    say(f"    tokens routed differently {int((~agree).sum())}, near ties {int(near.sum())}")
+    counts = np.bincount(r.ids.reshape(-1), minlength=E)
+    # the two sampled experts: the fullest and the emptiest
+    e_hi, e_lo = int(np.argmax(counts)), int(np.argmin(counts))
+    pair = {e_hi, e_lo}
+    touched = set(ids[~agree].reshape(-1).tolist()) | set(r.ids[~agree].reshape(-1).tolist())
+    cand = np.nonzero(agree & np.isin(r.ids, list(pair)).all(axis=1))[0]
+    perm, _, _, off = O.dispatch(r.ids, E)
+    edge = [int(perm[off[e]] // k) for e in pair] + [int(perm[off[e + 1] - 1] // k) for e in pair]
+    rng = np.random.default_rng(5)
+    sample = sorted(set([t for t in edge if t in set(cand.tolist())]) |
+                    set(rng.choice(cand, size=min(16, cand.size), replace=False).tolist()))
+    say(f"    experts {sorted(pair)} rows {[int(counts[e]) for e in sorted(pair)]}, sampled tokens {len(sample)}")
+    params = {"w_g": wg, "w1": {}, "w3": {}, "w2": {}}
+    for e in pair:
+        params["w1"][e], params["w3"][e], params["w2"][e] = f64(inp["w1"][e]), f64(inp["w3"][e]), f64(inp["w2"][e])
+    ref = O.backward(x64, params, spec, dy64, aux, zc, tokens=sample)
+    st = torch.from_numpy(np.array(sample)).cuda()
+    close("dx[sample]", f64(out["dx"][st]), ref["dx"])
+    close("dz[sample]", f64(out["dz"][st]), ref["dz"])
+    close("dgate[sample]", f64(out["dgate"][st]), ref["dgate"])
+    for e in sorted(pair):
+        if e in touched:
+            say(f"    expert {e}: a differently routed token touches it, weight slices skipped")
+            continue
+        units = sorted({0, F - 1} | set(np.random.default_rng(e).choice(F, size=4, replace=False).tolist()))
+        tok, jj = np.nonzero(r.ids == e)
+        xr = x64[tok]
+        do = r.w[tok, jj][:, None] * dy64[tok]
+        _, g = O.expert_ffn_backward(xr, "swiglu", do, params["w1"][e][units], params["w2"][e][:, units],
+                                     params["w3"][e][units])
+        u = torch.tensor(units).cuda()
+        close(f"dw1[{e}]", f64(out["dw1"][e][u]), g["dw1"])
+        close(f"dw3[{e}]", f64(out["dw3"][e][u]), g["dw3"])
+        close(f"dw2[{e}]", f64(out["dw2"][e][:, u]), g["dw2"])
