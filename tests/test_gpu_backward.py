@@ -120,6 +120,12 @@ CASES = {
     # split K into runs reduced in a fixed order
     "split_k": (W.WORKLOADS["mixtral"].scaled(n_tokens=4096, d_model=64, n_experts=4, top_k=1, d_ff=64,
                                               d_ff_shared=64), 0.01, 1e-3),
+    # the largest router: E = 1024, k = 32 (16 experts per lane in the router backward)
+    "e1024_k32": (W.WORKLOADS["mixtral"].scaled(n_tokens=24, d_model=64, n_experts=1024, top_k=32, d_ff=32),
+                  0.02, 1e-3),
+    # GELU with biases and top-1 routing
+    "gelu_bias_top1": (W.WORKLOADS["gpt2_small"].scaled(n_tokens=333, d_model=72, n_experts=5, top_k=1, d_ff=40,
+                                                        router="topk_softmax"), 0.01, 1e-3),
     # one expert for all (k = E = 1): every token in one ragged K of the weight gradients
     "single_expert": (W.WORKLOADS["mixtral"].scaled(n_tokens=70, d_model=64, n_experts=1, top_k=1, d_ff=64), 0.1, 0.1),
 }
