@@ -55,8 +55,10 @@ struct GemmArgs {
   void* c2;             // save only: SwiGLU [rows][2 N_out] (gate | up pre-activations),
                         // GELU [rows][N_out] (pre-activation with b1)
   const int* tiles;     // tile table
+  float* partial;       // down projection's tail: [kMaxTailItems][256][256] float32 partials
   int K, n_out;         // reduction length; output columns (= rows of each B matrix)
   int n_tiles_n;        // output column tiles
+  int grid;             // tail_reduce_kernel: the GEMM launches' grid
 };
 
 // ---------------------------------------------------------------------------------------
@@ -101,7 +103,38 @@ constexpr int kGemmThreads = 512;
 
 // lds_dma16, wait_vm_lds and stage_barrier: moe_common.h
 
-template <int EPI>
+// Tile s of a grouped GEMM: expert-major, then supertiles of kGM m-tiles x kGN n-tiles (m
+// fastest), so tiles that run together share operand panels.
+MOE_DEV void decode_tile(const int* tiles, long long s, int NT, int* e, int* row0, int* rows, int* nt) {
+  const int* probe = tiles + kTileHdr + kTileInts * (int)(s / NT);
+  const int ts = probe[3], me = probe[4];
+  *e = probe[0];
+  const long long l = s - (long long)ts * NT;
+  const int band = (int)(l / ((long long)kGM * NT));
+  const int lb = (int)(l - (long long)band * kGM * NT);
+  const int bm = min(kGM, me - kGM * band);
+  const int grpn = lb / (kGN * bm);
+  const int r = lb - grpn * kGN * bm;
+  const int* tq = tiles + kTileHdr + kTileInts * (ts + kGM * band + r % bm);
+  *row0 = tq[1];
+  *rows = tq[2];
+  *nt = grpn * kGN + r / bm;
+}
+
+// K pieces of each tail tile: enough (tile, piece) pairs to fill the grid, at least 4 slabs
+// per piece, at most kMaxTailItems pairs (the partial buffer's size).
+constexpr int kMaxTailItems = 256;
+MOE_DEV int tail_pieces(long long s_tail, int nk_all, int grid) {
+  if (s_tail <= 0) return 1;
+  const long long q = min((long long)grid / s_tail, (long long)kMaxTailItems / s_tail);
+  return (int)max(1ll, min(q, (long long)(nk_all / 4)));
+}
+
+// PART: 0 = every tile; 1 = only the whole rounds (the first floor(S / G) * G tiles of the
+// S = m-tiles * NT, G = gridDim.x); 2 = the remaining S mod G tiles, each cut along K into q
+// pieces (q = tail_pieces), one piece per workgroup, writing float32 partials when q > 1
+// (tail_reduce_kernel sums them and applies the epilogue).
+template <int EPI, int PART = 0>
 __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t sB0[kStageElems];
@@ -126,17 +159,30 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
   constexpr int kCols = kSwi<EPI> ? 128 : 256;  // output columns per tile
 
   const int n_mt = g.tiles[0];
-  const long long S = (long long)n_mt * NT;
+  const long long S_all = (long long)n_mt * NT;
+  const int nk_all = (K + kBK - 1) / kBK;
+  const long long S_main = (PART == 0) ? S_all : S_all / gridDim.x * gridDim.x;
+  const int q = (PART == 2) ? tail_pieces(S_all - S_main, nk_all, gridDim.x) : 1;
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
-  const long long chunk = (S + 7) / 8;
-  const long long s_begin = (long long)xcd * chunk;
-  const long long s_end = min(S, s_begin + chunk);
-  const int nk = (K + kBK - 1) / kBK;
+  const long long chunk = (S_main + 7) / 8;
+  // work items: tiles of [0, S_main) in per-XCD runs, or the tail's (tile, piece) pairs
+  const long long w_begin = (PART == 2) ? (long long)blockIdx.x : (long long)xcd * chunk + slot;
+  const long long w_end = (PART == 2) ? (S_all - S_main) * q : min(S_main, (long long)xcd * chunk + chunk);
+  const int w_step = (PART == 2) ? (int)gridDim.x : per_xcd;
   const bool k_tail = (K % kBK) != 0;
 
-  for (long long s = s_begin + slot; s < s_end; s += per_xcd) {
+  for (long long w = w_begin; w < w_end; w += w_step) {
+    long long s = w;       // tile
+    int kso = 0;           // first slab of this item
+    int nk = nk_all;       // slabs of this item
+    if (PART == 2) {
+      s = S_main + w / q;
+      const int piece = (int)(w % q);
+      kso = piece * nk_all / q;
+      nk = (piece + 1) * nk_all / q - kso;
+    }
     // The lane index is made opaque per tile: otherwise the compiler hoists every
     // lane-dependent address out of the tile loop and spills them across it.
     int lane = tid & 63;
@@ -155,19 +201,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     const int b_rd = wc * 64 * kBK;
 
 
-    // ---- tile decode: expert-major, then supertiles of kGM m-tiles x kGN n-tiles
-    const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
-    const int e = probe[0], ts = probe[3], me = probe[4];
-    const long long l = s - (long long)ts * NT;
-    const int band = (int)(l / ((long long)kGM * NT));
-    const int lb = (int)(l - (long long)band * kGM * NT);
-    const int bm = min(kGM, me - kGM * band);
-    const int grpn = lb / (kGN * bm);
-    const int r = lb - grpn * kGN * bm;
-    const int mt = ts + kGM * band + r % bm;
-    const int nt = grpn * kGN + r / bm;
-    const int* tq = g.tiles + kTileHdr + kTileInts * mt;
-    const int row0 = tq[1], rows = tq[2];
+    int e, row0, rows, nt;
+    decode_tile(g.tiles, s, NT, &e, &row0, &rows, &nt);
     const int n0 = nt * kCols;
 
     // uniform bases (bytes) and 32-bit per-lane offsets of this wave's 2 A and 2 B copies
@@ -195,7 +230,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       return (k_tail && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
     };
     auto refill = [&](uint16_t* sa, uint16_t* sb, int slab) {
-      const uint32_t ka = dma_k(slab * kBK);
+      const uint32_t ka = dma_k((kso + slab) * kBK);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         lds_dma16(a_base + a_off[i] + ka, sa + (wave * 2 + i) * 16 * kBK);
@@ -204,7 +239,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     };
     // zero this wave's copied chunks of the last slab that lie past K (after they landed)
     auto zero_tail = [&](uint16_t* sa, uint16_t* sb, int slab) {
-      if (!k_tail || slab != nk - 1 || slab * kBK + lchunk < K) return;
+      if (!k_tail || kso + slab != nk_all - 1 || (kso + slab) * kBK + lchunk < K) return;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int off = (wave * 2 + i) * 16 * kBK + lane * 8;
@@ -259,7 +294,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     // A stage is refilled only when both groups are done with its previous slab.
     // multiply slab k while refilling stage (fa, fb) with `slab`: one copy after every 4 MFMAs
     auto multiply_refill = [&](uint16_t* fa_, uint16_t* fb_, int slab) {
-      const uint32_t ka = dma_k(slab * kBK);
+      const uint32_t ka = dma_k((kso + slab) * kBK);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -326,6 +361,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       if (rem > 3) g1_step(sA3, sB3, sA4, sB4, kt + 3);
     }
     wait_vm_lds<0>();  // copies past the end land before the stages are reused
+    if (PART == 2 && q > 1) {
+      // a K piece of a tail tile: raw float32 accumulators to this item's partial tile
+      // [256 rows][256 columns] (the sum and the epilogue follow in tail_reduce_kernel)
+      float* pt = g.partial + (size_t)w * (kBM * kBNB);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * 128 + i * 32 + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
+            const int col = wc * 64 + j * 32 + (lane & 31);
+            pt[row * kBNB + col] = acc[i][j][v];
+          }
+      __syncthreads();
+      continue;
+    }
 
     // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
     // (1 and 0 when absent, so the epilogue has no branches)
@@ -421,6 +473,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     }
     __syncthreads();  // the staging area is the next tile's first stage
   }
+}
+
+// The down projection's tail tiles (PART 2 with q > 1): y_s = (sum of the q partials, in piece
+// order, + b2) * gate, rounded once. Workgroup (t, rg) covers rows 4 rg .. 4 rg + 3 of tail
+// tile t, a thread per 4 columns.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
+  const int NT = g.n_tiles_n, K = g.K, n_out = g.n_out;
+  const long long S_all = (long long)g.tiles[0] * NT;
+  const int G = g.grid;
+  const long long S_main = S_all / G * G;
+  const long long S_tail = S_all - S_main;
+  const int q = tail_pieces(S_tail, (K + kBK - 1) / kBK, G);
+  if (q <= 1 || blockIdx.x >= S_tail) return;
+  int e, row0, rows, nt;
+  decode_tile(g.tiles, S_main + blockIdx.x, NT, &e, &row0, &rows, &nt);
+  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c4 = (threadIdx.x & 63) * 4;
+  const int col = nt * kBNB + c4;
+  if (r >= rows || col >= n_out) return;
+  const float* pt = g.partial + (size_t)blockIdx.x * q * (kBM * kBNB) + r * kBNB + c4;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < q; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(pt + (size_t)p * (kBM * kBNB));
+    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+  }
+  const float gs = g.gate ? g.gate[row0 + r] : 1.f;
+  const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
+  float o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (v[i] + (bias ? bf16_to_f32(bias[(size_t)e * n_out + col + i]) : 0.f)) * gs;
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + (size_t)(row0 + r) * n_out + col) =
+      make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -558,9 +642,18 @@ void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   const size_t h_elems = std::max(A * (size_t)c.d_ff, (size_t)c.n_tokens * (size_t)std::max(c.d_ff_shared, 0));
   int* tiles = w.take_t<int>(kTileHdr + kTileInts * tiles_n);
   void* h = w.take(h_elems * elem_size(c));
+  // the down projection's tail partials (bfloat16 path, when its K allows several pieces)
+  size_t part = 0;
+  const long long nk_down = (c.d_ff + kBK - 1) / kBK;
+  if (c.dtype == MOE_BF16 && nk_down / 4 >= 2) {
+    const long long s_max = (long long)ffn_max_m_tiles(c) * ((c.d_model + kBNB - 1) / kBNB);
+    part = (size_t)std::min<long long>(kMaxTailItems, s_max * (nk_down / 4)) * kBM * kBNB;
+  }
+  float* tail = w.take_t<float>(part);
   if (L) {
     L->tiles = tiles;
     L->h = h;
+    L->tail_part = part ? tail : nullptr;
   }
 }
 
@@ -616,7 +709,18 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
   const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_model + 255) / 256;
-    expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+    const int grid = persistent_grid();
+    if (!L.tail_part) {
+      expert_gemm_bf16_kernel<kEpiDown><<<grid, kGemmThreads, 0, stream>>>(g);
+    } else {
+      // whole rounds of tiles, then the last partial round cut along K so that it fills the
+      // chip, then the fixed-order sum of the pieces with the epilogue
+      g.partial = L.tail_part;
+      g.grid = grid;
+      expert_gemm_bf16_kernel<kEpiDown, 1><<<grid, kGemmThreads, 0, stream>>>(g);
+      expert_gemm_bf16_kernel<kEpiDown, 2><<<grid, kGemmThreads, 0, stream>>>(g);
+      tail_reduce_kernel<<<dim3(grid, kBM / 4), 256, 0, stream>>>(g);
+    }
   } else {
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);

@@ -48,6 +48,7 @@ struct WsLayout {
   // expert FFN
   int* tiles = nullptr;    // m-tile table (kTileHdr + kTileInts per tile ints)
   void* h = nullptr;       // [A][d_ff] T
+  float* tail_part = nullptr;  // down projection's tail: K-piece partials (or null: no split)
   // forward intermediates
   int* perm = nullptr;
   int* inv_perm = nullptr;
