@@ -152,6 +152,10 @@ def cpu_baseline_backward(w, inp, dy, n_sample=0, target_s=15.0, aux_coef=0.0, z
 
 
 def run_backward(args, w, inp):
+    """--mode backward: moe_backward from the state one moe_forward_train left (the training
+    path), or with --recompute the self-contained backward that recomputes routing, dispatch
+    and the up projection. --mode train: a whole training step, moe_forward_train then
+    moe_backward(saved)."""
     import torch
     from mixture_experts_layer_19_amd import binding as B
     from mixture_experts_layer_19_amd import workload as W
@@ -159,10 +163,20 @@ def run_backward(args, w, inp):
     dy = W.random_rows(cfg.n_tokens, cfg.d_model, cfg.torch_dtype, seed=0, tensor_id=30)
     ws = B.workspace(cfg, B.Op.BACKWARD)
     aux, zc = 0.01, 1e-3
-    call = lambda out=None, ev=None: B.moe_backward(
-        cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], dy, inp["b1"], inp["b2"],
-        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"], aux_coef=aux, z_coef=zc, ws=ws, out=out,
-        stage_events=ev)
+    fkw = dict(b1=inp["b1"], b2=inp["b2"], logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], shared=inp["shared"])
+    saved = None if args.recompute else B.moe_forward_train(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"],
+                                                            inp["w2"], ws=ws, **fkw)
+    train = args.mode == "train"
+    fwd_ev = B.HipEvents(2) if train else None
+
+    def call(out=None, ev=None):
+        if train:
+            fwd_ev.record(0)
+            B.moe_forward_train(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], ws=ws,
+                                out=saved, **fkw)
+            fwd_ev.record(1)
+        return B.moe_backward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], dy, aux_coef=aux,
+                              z_coef=zc, ws=ws, out=out, stage_events=ev, saved=saved, **fkw)
     out = call()
     for _ in range(max(args.warmup - 1, 0)):
         call(out)
@@ -179,11 +193,21 @@ def run_backward(args, w, inp):
             stage_ms[s] += ev.elapsed_ms(j, j + 1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     work = algorithmic_backward(cfg)
+    if saved is not None:
+        # nothing recomputed: the routing and up-projection work belongs to the forward
+        work["route_dispatch"] = 0
+        work["up_recompute"] = 0
     flops = sum(work.values())
+    fwd_flops = 0
+    if train:
+        f = algorithmic(cfg)
+        fwd_flops = f["router_flops"] + f["up_flops"] + f["down_flops"] + f["shared_flops"]
+        flops += fwd_flops
     peak = PEAK_BF16_TFLOPS
     gemm_stages = ("up_recompute", "act_backward", "dx_rows", "dw2", "dw13")
-    rates = {s: work[s] / (stage_ms[s] * 1e-3) / 1e12 for s in gemm_stages + ("shared",) if stage_ms[s] > 0}
-    dom = max(gemm_stages, key=lambda s: stage_ms[s])
+    rates = {s: work[s] / (stage_ms[s] * 1e-3) / 1e12 for s in gemm_stages + ("shared",)
+             if stage_ms[s] > 0 and work[s] > 0}
+    dom = max((s for s in gemm_stages if work[s] > 0), key=lambda s: stage_ms[s])
     swi = cfg.act == "swiglu"
     kernel = {"up_recompute": "expert_gemm_bf16_kernel<3>" if swi else "expert_gemm_bf16_kernel<4>",
               "act_backward": "bwd_gemm_kernel<0, 2>" if swi else "bwd_gemm_kernel<0, 3>",
@@ -196,13 +220,16 @@ def run_backward(args, w, inp):
         src = "expert_ffn.hip" if dom == "up_recompute" else "backward.hip"
         traffic = traffic_for(os.path.join(csrc, src), f"{w.name}_backward", kernel)
     E = cfg.n_experts
+    what = ("train step (moe_forward_train + moe_backward from its saved state)" if train else
+            "bwd tokens/s (recompute + all gradients)" if saved is None else
+            "bwd tokens/s (all gradients, from moe_forward_train's saved state)")
     res = {
-        "metric": "MoE layer bwd tokens/s (recompute + all gradients) + active TFLOP/s (% bf16 MFMA peak)",
+        "metric": f"MoE layer {what} + active TFLOP/s (% bf16 MFMA peak)",
         "value": cfg.n_tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name} backward: N={cfg.n_tokens} d={cfg.d_model} E={E} k={cfg.top_k} "
+        "config": {"workload": f"{w.name} {args.mode}{' (recompute)' if saved is None else ''}: N={cfg.n_tokens} d={cfg.d_model} E={E} k={cfg.top_k} "
                                f"d_ff={cfg.d_ff} {cfg.act} {cfg.router}{'+norm' if cfg.norm_topk else ''} {cfg.dtype}"
                                f" aux_coef={aux} z_coef={zc}",
                    "global_batch": cfg.n_tokens, "parallelism": "single GPU"},
@@ -215,6 +242,8 @@ def run_backward(args, w, inp):
                      "flops_per_launch": work[dom], "avg_launch_ms": stage_ms[dom]},
         "events_vs_wall": sum(stage_ms.values()) / ms_per_step,
     }
+    if train:
+        res["forward_train_ms"] = fwd_ev.elapsed_ms(0, 1)  # the last step's
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_backward(w, inp, dy, args.cpu_sample, aux_coef=aux, z_coef=zc)
     print(json.dumps(res), flush=True)
@@ -227,7 +256,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("forward", "backward"), default="forward")
+    ap.add_argument("--mode", choices=("forward", "backward", "train"), default="forward")
+    ap.add_argument("--recompute", action="store_true",
+                    help="backward: recompute routing, dispatch and the up projection instead of a saved forward")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -256,7 +287,7 @@ def main():
     w = W.WORKLOADS[args.workload]
     cfg = w.cfg
     inp = W.make_inputs(w, seed=0, device="cuda")
-    if args.mode == "backward":
+    if args.mode in ("backward", "train"):
         run_backward(args, w, inp)
         return
     ws = B.workspace(cfg, B.Op.FORWARD)

@@ -257,6 +257,11 @@ typedef struct {
  * In: the forward's inputs; dy [N,d] T; aux_coef, z_coef: finite.
  * Out: *grads (dw3 / db1 / db2 / shared gradients required exactly when the matching
  * weight is); topk_ids, topk_w, counts, stats as in moe_route.
+ * saved: 0 = recompute as above. 1 = `ws` holds the state a moe_forward_train call left with
+ * the same cfg and inputs, and topk_ids, topk_w, counts and stats hold that call's outputs:
+ * they are then read, not written, and routing, dispatch and the up projections are not
+ * recomputed. The gradients are the same bits as with saved = 0. The saved state survives
+ * this call, so several backward calls may follow one moe_forward_train.
  * stage_events: NULL, or MOE_BWD_EVENTS hipEvent_t (as void*) recorded on `stream` at the
  * start, after the recomputed routing and dispatch, after the recomputed up projection, after
  * dh' (with the activation backward), after the router backward, after dx_sorted, after dW2,
@@ -271,8 +276,24 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const void* s_w1, const void* s_w3, const void* s_b1,
                         const void* s_w2, const void* s_b2,
                         const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
-                        int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                        int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, int saved,
                         void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
+
+/* The forward for training: the layer's output y and routing outputs as moe_forward's
+ * (bfloat16, dropless only, like moe_backward), run so that its intermediates stay in the
+ * workspace (moe_workspace_size(cfg, MOE_OP_BACKWARD) bytes) for moe_backward(saved = 1):
+ * the logits, x_sorted, the up projection's pre-activations and the gate-scaled hidden
+ * activations w_a h_a, from which the down projection computes y_sorted = (w_a h_a) W2^T +
+ * w_a b2. y equals moe_forward's within the bfloat16 tolerance (h is rounded after the gate
+ * is applied instead of before); ids, gates, counts and statistics are the same bits. */
+moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w_router,
+                             const float* logit_bias, const float* sel_bias,
+                             const void* w1, const void* w3, const void* b1,
+                             const void* w2, const void* b2,
+                             const void* s_w1, const void* s_w3, const void* s_b1,
+                             const void* s_w2, const void* s_b2,
+                             void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Aux-free load balancing, one update step ([L7.8] §2.5): with load_e = counts[e] and
  * mean = sum_e load_e / E,

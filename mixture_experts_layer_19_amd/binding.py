@@ -131,11 +131,13 @@ def lib():
     L.moe_expert_capacity.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_int64, ctypes.c_int32]
     L.moe_expert_capacity.restype = ctypes.c_int64
     L.moe_backward.argtypes = ([S] + [_P] * 15 + [ctypes.c_float, ctypes.c_float, ctypes.POINTER(MoeGradsStruct)]
-                               + [_P] * 5 + [ctypes.c_size_t, _P, _P])
+                               + [_P] * 4 + [ctypes.c_int, _P, ctypes.c_size_t, _P, _P])
+    L.moe_forward_train.argtypes = [S] + [_P] * 20 + [ctypes.c_size_t, _P]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
-                 "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity", "moe_backward"):
+                 "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity", "moe_backward",
+                 "moe_forward_train"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -392,12 +394,14 @@ GRAD_NAMES = ("dx", "dw_router", "dw1", "dw3", "db1", "dw2", "db2", "ds_w1", "ds
 
 def moe_backward(cfg: LayerConfig, x, w_router, w1, w3, w2, dy, b1=None, b2=None, logit_bias=None, sel_bias=None,
                  *, shared: Optional[dict] = None, aux_coef: float = 0.0, z_coef: float = 0.0, ws=None, out=None,
-                 stage_events: Optional[Sequence[int]] = None):
+                 stage_events: Optional[Sequence[int]] = None, saved: Optional[dict] = None):
     """Gradients of <dy, y> + aux_coef L + z_coef z_loss (bfloat16, dropless). Returns a dict
     with dx, dw_router, dw1, dw3, db1, dw2, db2, the shared expert's ds_* (None where the
     weight is absent), dz [N,E] and dgate [N,k] (float32), and the recomputed routing
     (topk_ids, topk_w, counts, stats). `out` / `ws` may hold preallocated buffers;
-    stage_events: BWD_EVENTS raw hipEvent_t handles (ints) or None."""
+    stage_events: BWD_EVENTS raw hipEvent_t handles (ints) or None. saved: the dict a
+    moe_forward_train call with the same inputs returned (its workspace and routing outputs
+    are reused instead of recomputing routing, dispatch and the up projection)."""
     N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
     T = cfg.torch_dtype
     sh = shared or {}
@@ -426,6 +430,10 @@ def moe_backward(cfg: LayerConfig, x, w_router, w1, w3, w2, dy, b1=None, b2=None
             "topk_ids": new((N, k), torch.int32), "topk_w": new((N, k), torch.float32),
             "counts": new((E,), torch.int32), "stats": new((2 * E + 2,), torch.float32),
         }
+    if saved is not None:
+        ws = saved["ws"]
+        for name in ("topk_ids", "topk_w", "counts", "stats"):
+            out[name] = saved[name]
     if ws is None:
         ws = workspace(cfg, Op.BACKWARD, w_router.device)
     g = MoeGradsStruct(*[None if out.get(n) is None else out[n].data_ptr() for n in GRAD_NAMES])
@@ -438,8 +446,36 @@ def moe_backward(cfg: LayerConfig, x, w_router, w1, w3, w2, dy, b1=None, b2=None
                             _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1), _ptr(s_w3), _ptr(s_b1),
                             _ptr(s_w2), _ptr(s_b2), _ptr(dy), float(aux_coef), float(z_coef), ctypes.byref(g),
                             _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]),
-                            _ptr(ws), ws.numel(), ev, _stream())
+                            1 if saved is not None else 0, _ptr(ws), ws.numel(), ev, _stream())
     _check(st, "moe_backward")
+    return out
+
+
+def moe_forward_train(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, logit_bias=None, sel_bias=None,
+                      *, shared: Optional[dict] = None, ws=None, out=None):
+    """The forward for training: returns moe_forward's dict (y, topk_ids, topk_w, counts,
+    stats) plus "ws", the backward workspace holding what moe_backward(saved=...) reuses."""
+    N, d, E, k = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k
+    sh = shared or {}
+    s_w1, s_w3, s_w2, s_b1, s_b2 = (sh.get(n) for n in ("s_w1", "s_w3", "s_w2", "s_b1", "s_b2"))
+    if out is None:
+        _want(x, "x", (N, d), cfg.torch_dtype)
+        _want(w_router, "w_router", (E, d), cfg.torch_dtype)
+        dev = w_router.device
+        out = {"y": torch.empty((N, d), dtype=cfg.torch_dtype, device=dev),
+               "topk_ids": torch.empty((N, k), dtype=torch.int32, device=dev),
+               "topk_w": torch.empty((N, k), dtype=torch.float32, device=dev),
+               "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+               "stats": torch.empty((2 * E + 2,), dtype=torch.float32, device=dev)}
+    if ws is None:
+        ws = workspace(cfg, Op.BACKWARD, w_router.device)
+    out["ws"] = ws
+    st = lib().moe_forward_train(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                 _ptr(sel_bias), _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1),
+                                 _ptr(s_w3), _ptr(s_b1), _ptr(s_w2), _ptr(s_b2), _ptr(out["y"]),
+                                 _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["counts"]),
+                                 _ptr(out["stats"]), _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_forward_train")
     return out
 
 
@@ -478,6 +514,7 @@ def _hiprt():
         _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
         _hip.hipEventSynchronize.argtypes = [_P]
         _hip.hipEventDestroy.argtypes = [_P]
+        _hip.hipEventRecord.argtypes = [_P, _P]
     return _hip
 
 
@@ -492,6 +529,11 @@ class HipEvents:
             if h.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.handles.append(e.value)
+
+    def record(self, i: int):
+        """Records event i on torch's current stream."""
+        if _hiprt().hipEventRecord(ctypes.c_void_p(self.handles[i]), _stream()) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i: int, j: int) -> float:
         h = _hiprt()

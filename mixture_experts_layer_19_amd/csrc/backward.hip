@@ -840,7 +840,7 @@ void carve_backward(const moe_config& c, WsCarver& w, WsLayout* L) {
 }
 
 hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& in, const moe_grads& gr,
-                           const RouteOut& ro, void* const* events, hipStream_t s) {
+                           const RouteOut& ro, bool saved, void* const* events, hipStream_t s) {
   const BwdBufs B = bwd_bufs(c, static_cast<char*>(L.bwd));
   int next_event = 0;
   auto mark = [&](int upto) -> hipError_t {  // record every event up to index `upto`
@@ -860,9 +860,11 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   int32_t* ids = ro.topk_ids;
   float* dz = gr.dz ? gr.dz : B.dz;
 
-  // recompute: routing (logits kept), dispatch of x and dy, the up projection
-  BWD_TRY(launch_route(c, L, in.x, in.w_router, in.logit_bias, in.sel_bias, ids, ro.topk_w, ro.counts, ro.stats,
-                       B.z, nullptr, true, s));
+  // recompute (unless a moe_forward_train left them in the workspace): routing with its
+  // logits, the dispatch of x, the up projection's pre-activations and gate-scaled h
+  if (!saved)
+    BWD_TRY(launch_route(c, L, in.x, in.w_router, in.logit_bias, in.sel_bias, ids, ro.topk_w, ro.counts, ro.stats,
+                         B.z, nullptr, true, s));
   if (N == 0) {
     // no token: every gradient is zero
     auto zero = [&](void* p, size_t bytes) {
@@ -885,7 +887,8 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     BWD_TRY(hipGetLastError());
     return mark(MOE_BWD_EVENTS - 1);
   }
-  BWD_TRY(launch_dispatch_scanned(c, L, in.x, ids, ro.topk_w, L.x_sorted, L.perm, L.inv_perm, L.gate_sorted, s));
+  if (!saved)
+    BWD_TRY(launch_dispatch_scanned(c, L, in.x, ids, ro.topk_w, L.x_sorted, L.perm, L.inv_perm, L.gate_sorted, s));
   uint16_t* xs = static_cast<uint16_t*>(L.x_sorted);
   uint16_t* dys = static_cast<uint16_t*>(L.y_sorted);
   uint16_t* hw = static_cast<uint16_t*>(L.h);
@@ -894,7 +897,7 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   if (ffn_tile_rows(c) != kBM) return hipErrorInvalidValue;
   const long long mtA = ffn_max_m_tiles(c);
   BWD_TRY(mark(1));
-  BWD_TRY(launch_up_save(c, L.tiles, xs, in.w1, in.w3, in.b1, L.gate_sorted, F, B.pre, hw, s));
+  if (!saved) BWD_TRY(launch_up_save(c, L.tiles, xs, in.w1, in.w3, in.b1, L.gate_sorted, F, B.pre, hw, s));
   BWD_TRY(mark(2));
 
   // routed experts: dh' with the activation backward, then dx_sorted and the weight gradients
@@ -944,7 +947,7 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   BWD_TRY(launch_dense_tiles(N, kBM, B.tiles_dense, s));
   const long long mtN = (N + kBM - 1) / kBM;
   if (Fs > 0) {
-    BWD_TRY(launch_up_save(c, B.tiles_dense, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
+    if (!saved) BWD_TRY(launch_up_save(c, B.tiles_dense, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
     BWD_TRY(act_backward(c, B.zero, B.tiles_dense, mtN, T(in.dy), in.s_w2, 0, Fs, B.pre_s, nullptr, nullptr, B.dpre_s, s));
     BWD_TRY(dx_rows<kStoreF32>(c, B.zero, B.tiles_dense, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, s));
     BWD_TRY(wgrad(B.zero, B.kpart, N, T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr,
@@ -982,6 +985,33 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   bwd_combine_kernel<<<(N + 3) / 4, 256, 0, s>>>(B.dxs, L.inv_perm, B.R, N, k, d, static_cast<uint16_t*>(gr.dx));
   BWD_TRY(hipGetLastError());
   return mark(MOE_BWD_EVENTS - 1);
+}
+
+hipError_t launch_forward_train(const moe_config& c, const WsLayout& L, const BwdIn& in, void* y, const RouteOut& ro,
+                                hipStream_t s) {
+  const BwdBufs B = bwd_bufs(c, static_cast<char*>(L.bwd));
+  const int N = (int)c.n_tokens, A = N * c.top_k, F = c.d_ff, Fs = c.d_ff_shared;
+  BWD_TRY(launch_route(c, L, in.x, in.w_router, in.logit_bias, in.sel_bias, ro.topk_ids, ro.topk_w, ro.counts, ro.stats,
+                       B.z, nullptr, true, s));
+  if (N == 0) return hipGetLastError();
+  if (ffn_tile_rows(c) != kBM) return hipErrorInvalidValue;
+  BWD_TRY(launch_dispatch_scanned(c, L, in.x, ro.topk_ids, ro.topk_w, L.x_sorted, L.perm, L.inv_perm, L.gate_sorted,
+                                  s));
+  // up projection keeping the pre-activations; the down projection then reads w_a h_a
+  BWD_TRY(launch_up_save(c, L.tiles, L.x_sorted, in.w1, in.w3, in.b1, L.gate_sorted, F, B.pre, L.h, s));
+  BWD_TRY(launch_down(c, L.tiles, ffn_max_m_tiles(c), L.h, F, in.w2, in.b2, L.gate_sorted, true, L.y_sorted,
+                      L.tail_part, s));
+  // the shared expert the same way, its output in dx_sorted's buffer (A >= N rows; free until
+  // the backward)
+  const bool shared = Fs > 0;
+  if (shared) {
+    BWD_TRY(launch_dense_tiles(N, kBM, B.tiles_dense, s));
+    BWD_TRY(launch_up_save(c, B.tiles_dense, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
+    BWD_TRY(launch_down(c, B.tiles_dense, (N + kBM - 1) / kBM, B.h_s, Fs, in.s_w2, in.s_b2, nullptr, false, B.dxs,
+                        nullptr, s));
+  }
+  (void)A;
+  return launch_combine(c, L.y_sorted, nullptr, L.inv_perm, shared ? B.dxs : nullptr, y, s);
 }
 
 }  // namespace moe

@@ -59,6 +59,7 @@ struct GemmArgs {
   int K, n_out;         // reduction length; output columns (= rows of each B matrix)
   int n_tiles_n;        // output column tiles
   int grid;             // tail_reduce_kernel: the GEMM launches' grid
+  int pre_gated;        // down: a = gate * h already, so y = a W2^T + gate * b2
 };
 
 // ---------------------------------------------------------------------------------------
@@ -461,8 +462,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
             const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-              float val = acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)];
-              val = (EPI == kEpiGelu) ? gelu_erf(val) : val * gs;
+              const float bj = s_bias[wc * kWCols + j * 32 + (lane & 31)];
+              float val;
+              if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
+              else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
               st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
             }
           }
@@ -502,7 +505,10 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
   const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
   float o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (v[i] + (bias ? bf16_to_f32(bias[(size_t)e * n_out + col + i]) : 0.f)) * gs;
+  for (int i = 0; i < 4; ++i) {
+    const float b = bias ? bf16_to_f32(bias[(size_t)e * n_out + col + i]) : 0.f;
+    o[i] = g.pre_gated ? v[i] + b * gs : (v[i] + b) * gs;
+  }
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + (size_t)(row0 + r) * n_out + col) =
       make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
 }
@@ -692,40 +698,46 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t* offsets,
-                           const void* w2, const void* b2, const float* gate_sorted,
-                           void* y_sorted, hipStream_t stream) {
-  const int A = (int)(c.n_tokens * c.top_k);
-  if (A == 0) return hipGetLastError();
+hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
+                       const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
+                       hipStream_t stream) {
   GemmArgs g{};
-  g.a = L.h;
+  g.a = h;
   g.b0 = w2;
   g.bias = (c.act == MOE_ACT_GELU && c.has_bias) ? b2 : nullptr;
-  g.gate = gate_sorted;
-  g.c = y_sorted;
-  g.tiles = L.tiles;
-  g.K = c.d_ff;
+  g.gate = gate;
+  g.pre_gated = pre_gated ? 1 : 0;
+  g.c = y;
+  g.tiles = tiles;
+  g.K = K;
   g.n_out = c.d_model;
-  const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_model + 255) / 256;
     const int grid = persistent_grid();
-    if (!L.tail_part) {
+    if (!tail_part) {
       expert_gemm_bf16_kernel<kEpiDown><<<grid, kGemmThreads, 0, stream>>>(g);
     } else {
       // whole rounds of tiles, then the last partial round cut along K so that it fills the
       // chip, then the fixed-order sum of the pieces with the epilogue
-      g.partial = L.tail_part;
+      g.partial = tail_part;
       g.grid = grid;
       expert_gemm_bf16_kernel<kEpiDown, 1><<<grid, kGemmThreads, 0, stream>>>(g);
       expert_gemm_bf16_kernel<kEpiDown, 2><<<grid, kGemmThreads, 0, stream>>>(g);
       tail_reduce_kernel<<<dim3(grid, kBM / 4), 256, 0, stream>>>(g);
     }
   } else {
-    dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
+    dim3 grid(max_m_tiles, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(g);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t* offsets,
+                           const void* w2, const void* b2, const float* gate_sorted,
+                           void* y_sorted, hipStream_t stream) {
+  if (c.n_tokens * c.top_k == 0) return hipGetLastError();
+  return launch_down(c, L.tiles, ffn_max_m_tiles(c), L.h, c.d_ff, w2, b2, gate_sorted, false, y_sorted, L.tail_part,
+                     stream);
 }
 
 hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream) {

@@ -357,12 +357,13 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                         const float* sel_bias, const void* w1, const void* w3, const void* b1, const void* w2,
                         const void* b2, const void* s_w1, const void* s_w3, const void* s_b1, const void* s_w2,
                         const void* s_b2, const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
-                        int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, void* ws, size_t ws_bytes,
-                        void* const* stage_events, void* stream) {
+                        int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats, int saved, void* ws,
+                        size_t ws_bytes, void* const* stage_events, void* stream) {
   MOE_TRY(check_config(cfg, true));
   MOE_TRY(check_backward_config(cfg));
   MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
   if (!grads || !std::isfinite(aux_coef) || !std::isfinite(z_coef)) return MOE_ERR_INVALID_ARG;
+  if (saved != 0 && saved != 1) return MOE_ERR_INVALID_ARG;
   const moe_grads& g = *grads;
   if (cfg->n_tokens > 0) {
     MOE_TRY(need_t(x));
@@ -407,7 +408,40 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_TRY(check_ws(*cfg, MOE_OP_BACKWARD, ws, ws_bytes, &L));
   BwdIn in{x, w_router, logit_bias, sel_bias, w1, w3, b1, w2, b2, s_w1, s_w3, s_b1, s_w2, s_b2, dy, aux_coef, z_coef};
   RouteOut ro{topk_ids, topk_w, counts, stats};
-  return hip_status(launch_backward(*cfg, L, in, g, ro, stage_events, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_backward(*cfg, L, in, g, ro, saved == 1, stage_events, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w_router, const float* logit_bias,
+                             const float* sel_bias, const void* w1, const void* w3, const void* b1, const void* w2,
+                             const void* b2, const void* s_w1, const void* s_w3, const void* s_b1, const void* s_w2,
+                             const void* s_b2, void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                             void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_config(cfg, true));
+  MOE_TRY(check_backward_config(cfg));
+  MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
+  if (cfg->n_tokens > 0) {
+    MOE_TRY(need_t(x));
+    MOE_TRY(need_t(y));
+    MOE_TRY(need_4(topk_ids));
+    MOE_TRY(need_4(topk_w));
+  }
+  MOE_TRY(need_t(w_router));
+  MOE_TRY(need_t(w1));
+  MOE_TRY(need_t(w2));
+  if (cfg->act == MOE_ACT_SWIGLU) MOE_TRY(need_t(w3));
+  if (cfg->has_bias) {
+    MOE_TRY(need_t(b1));
+    MOE_TRY(need_t(b2));
+  }
+  MOE_TRY(need_4(counts));
+  MOE_TRY(need_4(stats));
+  MOE_TRY(opt_4(logit_bias));
+  MOE_TRY(opt_4(sel_bias));
+  WsLayout L{};
+  MOE_TRY(check_ws(*cfg, MOE_OP_BACKWARD, ws, ws_bytes, &L));
+  BwdIn in{x, w_router, logit_bias, sel_bias, w1, w3, b1, w2, b2, s_w1, s_w3, s_b1, s_w2, s_b2, nullptr, 0.f, 0.f};
+  RouteOut ro{topk_ids, topk_w, counts, stats};
+  return hip_status(launch_forward_train(*cfg, L, in, y, ro, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float* sel_bias, float rate,

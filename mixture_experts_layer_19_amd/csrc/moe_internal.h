@@ -205,6 +205,12 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
                          const void* s_w3, const void* s_b1, const void* s_w2, const void* s_b2,
                          void* y_shared, hipStream_t stream);
 
+// Down projection y = h W2^T (+ b2) times gate over a tile table's rows, K = the hidden width:
+// (acc + b2) * gate, or with pre_gated (h already scaled by its row's gate) acc + gate * b2.
+// tail_part: the K-split tail's partials (bfloat16; null: one persistent launch).
+hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
+                       const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
+                       hipStream_t stream);
 // Tile table of one dense "expert" covering rows [0, n) in tiles of bm rows.
 hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream);
 // Backward recompute of the up projection (bfloat16): the tile table's rows of a times W1
@@ -225,7 +231,11 @@ struct RouteOut {
 void carve_backward(const moe_config& c, WsCarver& w, WsLayout* L);
 // events: null or MOE_BWD_EVENTS events recorded at the stage boundaries (moe.h)
 hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& in, const moe_grads& gr,
-                           const RouteOut& ro, void* const* events, hipStream_t stream);
+                           const RouteOut& ro, bool saved, void* const* events, hipStream_t stream);
+// The forward for training (moe_forward_train): the layer's output, leaving in the backward
+// workspace what launch_backward(saved = true) reads instead of recomputing.
+hipError_t launch_forward_train(const moe_config& c, const WsLayout& L, const BwdIn& in, void* y, const RouteOut& ro,
+                                hipStream_t stream);
 // rows of x copied to their sorted slots (x_sorted[inv_perm[n k + j]] = x[n])
 void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream);
 

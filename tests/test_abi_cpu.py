@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
                "moe_workspace_size", "moe_get_device_error", "moe_status_string", "moe_update_bias",
-               "moe_shared_ffn", "moe_dispatch_capacity", "moe_expert_capacity"):
+               "moe_shared_ffn", "moe_dispatch_capacity", "moe_expert_capacity", "moe_backward",
+               "moe_forward_train"):
         assert fn in names
 
 
@@ -171,10 +172,10 @@ def test_backward_host_validation():
         full.update(o)
         return B.MoeGradsStruct(*[full.get(n) for n in names])
 
-    def call(cfg, g, ev=None, shared=(None,) * 5, ws_bytes=1 << 40):
+    def call(cfg, g, ev=None, shared=(None,) * 5, ws_bytes=1 << 40, saved=0):
         return lib.moe_backward(ctypes.byref(cfg.struct()), fp, fp, None, None, fp, fp, None, fp, None, *shared,
                                 fp, ctypes.c_float(0.0), ctypes.c_float(0.0), ctypes.byref(g) if g else None,
-                                fp, fp, fp, fp, fp, ws_bytes, ev, None)
+                                fp, fp, fp, fp, saved, fp, ws_bytes, ev, None)
 
     assert call(MIXTRAL.with_tokens(64), None) == B.MOE_ERR_INVALID_ARG
     f32 = B.LayerConfig(64, 64, 8, 2, 64, dtype="f32")
@@ -192,3 +193,22 @@ def test_backward_host_validation():
     sh = B.LayerConfig(64, 64, 8, 2, 64, d_ff_shared=64)
     assert call(sh, grads(), shared=(f, f, None, f, None)) == B.MOE_ERR_INVALID_ARG   # shared grads missing
     assert B.moe_workspace_size(ok, B.Op.BACKWARD) > B.moe_workspace_size(ok, B.Op.FORWARD) > 0
+    assert call(ok, grads(), saved=2) == B.MOE_ERR_INVALID_ARG
+
+
+def test_forward_train_host_validation():
+    """moe_forward_train takes moe_forward's arguments, bf16 and dropless only, and the
+    backward's workspace."""
+    lib = B.lib()
+    fp = ctypes.c_void_p(0x10000)
+
+    def call(cfg, ws_bytes=1 << 40, x=fp):
+        return lib.moe_forward_train(ctypes.byref(cfg.struct()), x, fp, None, None, fp, fp, None, fp, None,
+                                     None, None, None, None, None, fp, fp, fp, fp, fp, fp, ws_bytes, None)
+
+    assert call(B.LayerConfig(64, 64, 8, 2, 64, dtype="f32")) == B.MOE_ERR_UNSUPPORTED
+    assert call(B.LayerConfig(64, 64, 8, 2, 64, capacity_factor=1.0)) == B.MOE_ERR_UNSUPPORTED
+    ok = B.LayerConfig(64, 64, 8, 2, 64)
+    assert call(ok, x=None) == B.MOE_ERR_INVALID_ARG
+    need = B.moe_workspace_size(ok, B.Op.BACKWARD)
+    assert call(ok, ws_bytes=need - 256) == B.MOE_ERR_WORKSPACE

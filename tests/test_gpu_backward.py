@@ -248,3 +248,42 @@ def test_backward_fullsize_sampled():
         close(f"dw1[{e}]", f64(out["dw1"][e][u]), g["dw1"])
         close(f"dw3[{e}]", f64(out["dw3"][e][u]), g["dw3"])
         close(f"dw2[{e}]", f64(out["dw2"][e][:, u]), g["dw2"])
+
+
+SAVED_CASES = ["mixtral", "gpt2_bias", "deepseek_shared", "sigmoid_raw_gelu_shared"]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES)
+def test_forward_train_and_saved_backward(case):
+    """moe_forward_train: routing outputs are moe_forward's bits and y agrees with the oracle
+    to the forward's bf16 bound (its h is rounded after the gate). moe_backward(saved) then
+    gives exactly the recomputing backward's bits, twice in a row from one forward."""
+    w, aux, z = CASES[case]
+    cfg = w.cfg
+    inp = W.make_inputs(w, seed=0)
+    dy = W.random_rows(cfg.n_tokens, cfg.d_model, torch.bfloat16, seed=0, tensor_id=DY)
+    args = (cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"])
+    kw = dict(b1=inp["b1"], b2=inp["b2"], logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"], shared=inp["shared"])
+    fwd = B.moe_forward(*args, **kw)
+    ft = B.moe_forward_train(*args, **kw)
+    torch.cuda.synchronize()
+    for k in ("topk_ids", "topk_w", "counts", "stats"):
+        assert torch.equal(fwd[k], ft[k]), k
+    params = oracle_params(inp)
+    y_ref, r = O.forward_loop(f64(inp["x"]), params, spec_of(cfg), f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    agree = (ft["topk_ids"].cpu().numpy() == r.ids).all(axis=1)
+    y = f64(ft["y"])
+    err, scale = np.abs(y[agree] - y_ref[agree]).max(), np.abs(y_ref[agree]).max()
+    say(f"[forward_train] {case}: max|err| {err:.3e} of {scale:.3e}, tokens compared {int(agree.sum())}")
+    assert err <= 2e-2 * scale
+    bkw = dict(b1=inp["b1"], b2=inp["b2"], logit_bias=inp["logit_bias"], sel_bias=inp["sel_bias"],
+               shared=inp["shared"], aux_coef=aux, z_coef=z)
+    ref = B.moe_backward(*args, dy, **bkw)
+    s1 = B.moe_backward(*args, dy, saved=ft, **bkw)
+    s2 = B.moe_backward(*args, dy, saved=ft, **bkw)
+    torch.cuda.synchronize()
+    for name in B.GRAD_NAMES:
+        if ref.get(name) is None:
+            continue
+        assert torch.equal(ref[name], s1[name]), f"saved backward differs in {name}"
+        assert torch.equal(ref[name], s2[name]), f"second saved backward differs in {name}"
