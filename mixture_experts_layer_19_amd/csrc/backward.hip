@@ -31,8 +31,8 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 512, kStages = 4;
 constexpr int kGM = 8, kGN = 4;          // supertile: 8 m-tiles x 4 n-tiles (m fastest)
-constexpr int kStageStride = 40;         // epilogue staging row (floats): the two half-waves,
-                                         // 4 rows apart, hit disjoint banks
+constexpr int kStageStride = 72;         // epilogue staging row (floats, 64 columns + 8): the
+                                         // two half-waves, 4 rows apart, hit disjoint banks
 
 enum Mode { kGrouped = 0, kWgrad = 1 };
 enum Epi { kStoreT = 0, kStoreF32 = 1, kSwigluBwd = 2, kGeluBwd = 3 };
@@ -313,54 +313,53 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
   }
   __syncthreads();
 
-  // ---- epilogue: each 32 x 32 block goes through the wave's own LDS staging area (float32,
-  // padded rows), then lane l owns row l >> 1, columns 16 (l & 1) .. + 15 of the block.
-  float* st = reinterpret_cast<float*>(&sB[0][0]) + wave * 32 * kStageStride;
-  const int er = lane >> 1, ec = (lane & 1) * 16;
+  // ---- epilogue: per 32-row block i and column pair jp (64 columns), the wave stages its
+  // float32 accumulators in its own LDS area (rows padded to kStageStride floats, so the
+  // half-waves, 4 rows apart, hit disjoint banks); then lane l takes row 8 it + (l >> 3)
+  // (it = 0..3), columns 8 (l & 7) .. + 7, so one store instruction covers 8 rows x 64
+  // columns (128 contiguous bytes per row in bfloat16).
+  float* st = reinterpret_cast<float*>(wave < 4 ? &sA[0][0] : &sB[0][0]) + (wave & 3) * 32 * kStageStride;
+  const int lr = lane >> 3, lc = 8 * (lane & 7);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int rl = wm * 64 + 32 * i + er;  // tile row of this lane's output row
-    bool row_ok;
-    size_t grow = 0;                       // grouped: sorted row
-    uint16_t* crow = nullptr;              // wgrad: output row
-    float* prow = nullptr;                 // wgrad with split K: this split's float32 partial row
-    if (MODE == kGrouped) {
-      row_ok = rl < rows;
-      grow = (size_t)(row0 + rl);
-    } else {
-      const int m = m0 + rl;
-      row_ok = m < M;
-      if (row_ok && g.kpart)
-        prow = g.kpart + (((size_t)sp * g.n_experts + e) * M + m) * (size_t)N;
-      else if (row_ok)
-        crow = (m < g.m_split) ? static_cast<uint16_t*>(g.c) + (size_t)e * g.c_estride + (size_t)m * g.ldc
-                               : static_cast<uint16_t*>(g.c_hi) + (size_t)e * g.c_estride + (size_t)(m - g.m_split) * g.ldc;
-    }
-    float w = 1.f;
-    if ((EPI == kSwigluBwd || EPI == kGeluBwd) && row_ok && g.gate) w = g.gate[grow];
-    float psum = 0.f;
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int jp = 0; jp < 2; ++jp) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        st[((v >> 2) * 8 + 4 * (lane >> 5) + (v & 3)) * kStageStride + (lane & 31)] = acc[i][j][v];
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          st[((v >> 2) * 8 + 4 * (lane >> 5) + (v & 3)) * kStageStride + 32 * jj + (lane & 31)] = acc[i][2 * jp + jj][v];
       __builtin_amdgcn_wave_barrier();
-      float val[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(st + er * kStageStride + ec + 4 * q);
-        val[4 * q] = f.x;
-        val[4 * q + 1] = f.y;
-        val[4 * q + 2] = f.z;
-        val[4 * q + 3] = f.w;
-      }
-      __builtin_amdgcn_wave_barrier();
-      const int col = n0 + wn * 128 + 32 * j + ec;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int cc = col + 8 * h;
+      for (int it = 0; it < 4; ++it) {
+        const int er = 8 * it + lr;
+        const int rl = wm * 64 + 32 * i + er;  // tile row of this lane's output row
+        float v8[8];
+        {
+          const float4 f0 = *reinterpret_cast<const float4*>(st + er * kStageStride + lc);
+          const float4 f1 = *reinterpret_cast<const float4*>(st + er * kStageStride + lc + 4);
+          v8[0] = f0.x; v8[1] = f0.y; v8[2] = f0.z; v8[3] = f0.w;
+          v8[4] = f1.x; v8[5] = f1.y; v8[6] = f1.z; v8[7] = f1.w;
+        }
+        const int cc = n0 + wn * 128 + 64 * jp + lc;
+        bool row_ok;
+        size_t grow = 0;                       // grouped: sorted row
+        uint16_t* crow = nullptr;              // wgrad: output row
+        float* prow = nullptr;                 // wgrad with split K: this split's float32 partial row
+        if (MODE == kGrouped) {
+          row_ok = rl < rows;
+          grow = (size_t)(row0 + rl);
+        } else {
+          const int m = m0 + rl;
+          row_ok = m < M;
+          if (row_ok && g.kpart)
+            prow = g.kpart + (((size_t)sp * g.n_experts + e) * M + m) * (size_t)N;
+          else if (row_ok)
+            crow = (m < g.m_split) ? static_cast<uint16_t*>(g.c) + (size_t)e * g.c_estride + (size_t)m * g.ldc
+                                   : static_cast<uint16_t*>(g.c_hi) + (size_t)e * g.c_estride + (size_t)(m - g.m_split) * g.ldc;
+        }
         if (!row_ok || cc >= N) continue;
-        float* v8 = val + 8 * h;
         if (EPI == kStoreT && MODE == kWgrad && prow) {
           *reinterpret_cast<float4*>(prow + cc) = make_float4(v8[0], v8[1], v8[2], v8[3]);
           *reinterpret_cast<float4*>(prow + cc + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
@@ -379,13 +378,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
           *reinterpret_cast<float4*>(dst) = make_float4(v8[0], v8[1], v8[2], v8[3]);
           *reinterpret_cast<float4*>(dst + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
         } else if (EPI == kSwigluBwd) {
+          const float w = g.gate ? g.gate[grow] : 1.f;
           float gg[8], uu[8], dg[8], du[8];
           unpack8(*reinterpret_cast<const uint4*>(g.pre + grow * 2 * (size_t)N + cc), gg);
           unpack8(*reinterpret_cast<const uint4*>(g.pre + grow * 2 * (size_t)N + N + cc), uu);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const float sg = sigmoid_f(gg[q]);
-            psum += v8[q] * (gg[q] * sg * uu[q]);
+            psum[it] += v8[q] * (gg[q] * sg * uu[q]);
             const float dh = w * v8[q];
             dg[q] = dh * uu[q] * sg * (1.f + gg[q] * (1.f - sg));
             du[q] = dh * gg[q] * sg;
@@ -394,20 +394,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
           *reinterpret_cast<uint4*>(dst) = pack8(dg);
           *reinterpret_cast<uint4*>(dst + N) = pack8(du);
         } else {  // kGeluBwd
+          const float w = g.gate ? g.gate[grow] : 1.f;
           float aa[8], da[8];
           unpack8(*reinterpret_cast<const uint4*>(g.pre + grow * (size_t)N + cc), aa);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            psum += v8[q] * gelu_erf(aa[q]);
+            psum[it] += v8[q] * gelu_erf(aa[q]);
             da[q] = w * v8[q] * gelu_grad(aa[q]);
           }
           *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.c) + grow * g.ldc + cc) = pack8(da);
         }
       }
+      __builtin_amdgcn_wave_barrier();  // the next pair overwrites the staging area
     }
     if ((EPI == kSwigluBwd || EPI == kGeluBwd) && g.part) {
-      psum += __shfl_xor(psum, 1, kWave);
-      if ((lane & 1) == 0 && row_ok) g.part[grow * g.n_part + 2 * nt + wn] = psum;
+      // a row's 8 lanes hold its partial over this wave's 128 columns: fixed butterfly
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        float p = psum[it];
+        p += __shfl_xor(p, 1, kWave);
+        p += __shfl_xor(p, 2, kWave);
+        p += __shfl_xor(p, 4, kWave);
+        const int rl = wm * 64 + 32 * i + 8 * it + lr;
+        if ((lane & 7) == 0 && rl < rows) g.part[(size_t)(row0 + rl) * g.n_part + 2 * nt + wn] = p;
+      }
     }
   }
 }
