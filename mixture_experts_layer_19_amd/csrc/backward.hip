@@ -64,6 +64,9 @@ struct BwdGemm {
   // partials to kpart [ksplit][n_experts][M][N] (reduced by wgrad_reduce_kernel)
   int ksplit;
   float* kpart;
+  // weight gradients, balanced schedule (or null): cost prefix [E+1], per-XCD counters [8]
+  const long long* sched;
+  int* sched_cnt;
   // activation backward (grouped): pre-activations, gates, row partials of <dh', h>
   const uint16_t* pre;  // SwiGLU [rows][2 N] (gate | up), GELU [rows][N]
   const float* gate;    // [rows] or null (1)
@@ -129,10 +132,48 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
     MTe = (g.M + kBM - 1) / kBM;
     S = (long long)g.n_experts * MTe * NT * g.ksplit;
   }
-  const long long per = (S + 7) / 8;
-  const long long slot = blockIdx.x >> 3;
-  const long long s = (long long)(blockIdx.x & 7) * per + slot;
-  if (slot >= per || s >= S) return;
+  // Static mapping: one tile per workgroup. Weight gradients with a schedule (g.sched): the
+  // tile order is cut into 8 runs of equal cost (a tile costs its expert's slabs plus a fixed
+  // overhead), one per XCD, and the XCD's persistent workgroups take the run's tiles in order
+  // from an atomic counter, so a large expert's long tiles spread over the whole run.
+  const bool dyn = MODE == kWgrad && g.sched != nullptr;
+  const int xcd = blockIdx.x & 7;
+  long long run_lo = 0, run_hi = 0, s = 0;
+  if (dyn) {
+    const long long tpe = (long long)MTe * NT;
+    auto run_start = [&](int x) -> long long {
+      const long long total = g.sched[g.n_experts];
+      const long long target = total / 8 * x + (total % 8) * x / 8;
+      int lo = 0, hi = g.n_experts;  // the last expert whose prefix is <= target
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.sched[mid] <= target) lo = mid;
+        else hi = mid - 1;
+      }
+      if (lo >= g.n_experts) return (long long)g.n_experts * tpe;
+      const long long per_tile = (g.sched[lo + 1] - g.sched[lo]) / tpe;
+      return (long long)lo * tpe + min(tpe, (target - g.sched[lo]) / max(per_tile, 1ll));
+    };
+    run_lo = run_start(xcd);
+    run_hi = xcd == 7 ? (long long)g.n_experts * tpe : run_start(xcd + 1);
+  } else {
+    const long long per = (S + 7) / 8;
+    const long long slot = blockIdx.x >> 3;
+    s = (long long)xcd * per + slot;
+    if (slot >= per || s >= S) return;
+  }
+  __shared__ int s_fetch;
+
+  for (int iter = 0;; ++iter) {
+  if (dyn) {
+    if (tid == 0) s_fetch = atomicAdd(g.sched_cnt + xcd, 1);
+    __syncthreads();
+    s = run_lo + s_fetch;
+    __syncthreads();
+    if (s >= run_hi) break;
+  } else if (iter > 0) {
+    break;
+  }
 
   int e, mt, nt, row0 = 0, rows = 0, m0 = 0, r0 = 0, kr = 0, sp = 0;
   if (MODE == kGrouped) {
@@ -420,6 +461,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
       }
     }
   }
+  __syncthreads();  // the next tile's copies reuse the stages
+  }
+}
+
+// Cost prefix of the weight-gradient schedule: sched[e] = sum over experts e' < e of
+// tiles_per_expert * (slabs(rows of e') + kTileCost), and the 8 per-XCD counters cleared.
+constexpr int kTileCost = 4;  // a tile's fixed cost (prologue, epilogue) in slabs
+__global__ __launch_bounds__(1024) void wgrad_sched_kernel(const int* __restrict__ offsets, int E, long long tpe,
+                                                           long long* __restrict__ sched, int* __restrict__ cnt) {
+  __shared__ long long s_scan[kMaxExperts];
+  const int e = threadIdx.x;
+  long long c = 0;
+  if (e < E) c = tpe * ((max(offsets[e + 1] - offsets[e], 0) + kBK - 1) / kBK + kTileCost);
+  if (e < kMaxExperts) s_scan[e] = c;
+  __syncthreads();
+  for (int o = 1; o < E; o <<= 1) {
+    long long v = 0;
+    if (e < E && e >= o) v = s_scan[e - o];
+    __syncthreads();
+    if (e < E) s_scan[e] += v;
+    __syncthreads();
+  }
+  if (e < E) sched[e + 1] = s_scan[e];
+  if (e == 0) sched[0] = 0;
+  if (e < 8) cnt[e] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -673,6 +739,8 @@ struct BwdBufs {
   uint16_t* dpre_s;
   uint16_t* h_s;    // [N][Fs]
   float* kpart;     // split-K partials of the weight gradients that split
+  long long* sched; // weight-gradient schedule: cost prefix [E+1]
+  int* sched_cnt;   // and its 8 per-XCD counters
   size_t bytes;
 };
 
@@ -722,6 +790,8 @@ BwdBufs bwd_bufs(const moe_config& c, char* base) {
   }
   kp = std::max(kp, wgrad_part_floats((int)E, (int)d, 1, (long long)N));
   b.kpart = w.take_t<float>(kp);
+  b.sched = w.take_t<long long>(E + 1);
+  b.sched_cnt = w.take_t<int>(8);
   b.bytes = w.used();
   return b;
 }
@@ -795,11 +865,12 @@ hipError_t dx_rows(const moe_config& c, const uint16_t* zero, const int* tiles, 
 }
 
 // C_e[M][N] = sum over the expert's rows r of A[r][m] B[r][n] (+ a second segment)
-hipError_t wgrad(const uint16_t* zero, float* kpart, long long rows_total, const uint16_t* a0, const uint16_t* a1,
+hipError_t wgrad(const BwdBufs& B, long long rows_total, const uint16_t* a0, const uint16_t* a1,
                  long long lda, const uint16_t* b0, const uint16_t* b1, long long ldb, int M, int N, const int* offsets,
                  int n_experts, int n_rows, void* c, void* c_hi, int m_split, long long ldc, long long c_estride,
                  hipStream_t stream) {
-  BwdGemm g = gemm_args(zero);
+  float* kpart = B.kpart;
+  BwdGemm g = gemm_args(B.zero);
   g.ksplit = wgrad_split(M, N, n_experts, rows_total);
   g.kpart = g.ksplit > 1 ? kpart : nullptr;
   g.a[0] = a0;
@@ -819,8 +890,19 @@ hipError_t wgrad(const uint16_t* zero, float* kpart, long long rows_total, const
   g.m_split = m_split;
   g.ldc = ldc;
   g.c_estride = c_estride;
-  const long long S = (long long)n_experts * ((M + kBM - 1) / kBM) * g.n_tiles_n * g.ksplit;
-  const hipError_t err = run_gemm<kWgrad, kStoreT>(g, S, stream);
+  const long long tpe = (long long)((M + kBM - 1) / kBM) * g.n_tiles_n;
+  const long long S = n_experts * tpe * g.ksplit;
+  hipError_t err;
+  if (offsets && n_experts > 1 && g.ksplit == 1) {
+    // routed experts of uneven sizes: the balanced persistent schedule
+    wgrad_sched_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, tpe, B.sched, B.sched_cnt);
+    g.sched = B.sched;
+    g.sched_cnt = B.sched_cnt;
+    bwd_gemm_kernel<kWgrad, kStoreT><<<persistent_grid(), kThreads, 0, stream>>>(g);
+    err = hipGetLastError();
+  } else {
+    err = run_gemm<kWgrad, kStoreT>(g, S, stream);
+  }
   if (err != hipSuccess || g.ksplit == 1) return err;
   const long long total = (long long)n_experts * M * (N / 8);
   wgrad_reduce_kernel<<<(unsigned)std::min<long long>((total + 255) / 256, 8192), 256, 0, stream>>>(
@@ -942,10 +1024,10 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   BWD_TRY(mark(4));
   BWD_TRY(dx_rows<kStoreT>(c, B.zero, L.tiles, mtA, B.dpre, F, in.w1, in.w3, (long long)F * d, B.dxs, nullptr, s));
   BWD_TRY(mark(5));
-  BWD_TRY(wgrad(B.zero, B.kpart, A, dys, nullptr, d, hw, nullptr, F, d, F, L.offsets, E, 0, gr.dw2, nullptr, d, F,
+  BWD_TRY(wgrad(B, A, dys, nullptr, d, hw, nullptr, F, d, F, L.offsets, E, 0, gr.dw2, nullptr, d, F,
                 (long long)d * F, s));
   BWD_TRY(mark(6));
-  BWD_TRY(wgrad(B.zero, B.kpart, A, B.dpre, nullptr, swi ? 2 * (long long)F : F, xs, nullptr, d, swi ? 2 * F : F, d, L.offsets, E, 0,
+  BWD_TRY(wgrad(B, A, B.dpre, nullptr, swi ? 2 * (long long)F : F, xs, nullptr, d, swi ? 2 * F : F, d, L.offsets, E, 0,
                 gr.dw1, gr.dw3, F, d, (long long)F * d, s));
   if (bias) {
     BWD_TRY(colsum(B.dpre, F, nullptr, L.offsets, E, 0, F, gr.db1, s));
@@ -960,9 +1042,9 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     if (!saved) BWD_TRY(launch_up_save(c, B.tiles_dense, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
     BWD_TRY(act_backward(c, B.zero, B.tiles_dense, mtN, T(in.dy), in.s_w2, 0, Fs, B.pre_s, nullptr, nullptr, B.dpre_s, s));
     BWD_TRY(dx_rows<kStoreF32>(c, B.zero, B.tiles_dense, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, s));
-    BWD_TRY(wgrad(B.zero, B.kpart, N, T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr,
+    BWD_TRY(wgrad(B, N, T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr,
                   d, Fs, 0, s));
-    BWD_TRY(wgrad(B.zero, B.kpart, N, B.dpre_s, nullptr, swi ? 2 * (long long)Fs : Fs, T(in.x), nullptr, d, swi ? 2 * Fs : Fs, d,
+    BWD_TRY(wgrad(B, N, B.dpre_s, nullptr, swi ? 2 * (long long)Fs : Fs, T(in.x), nullptr, d, swi ? 2 * Fs : Fs, d,
                   nullptr, 1, N, gr.ds_w1, gr.ds_w3, Fs, d, 0, s));
     if (bias) {
       BWD_TRY(colsum(B.dpre_s, Fs, nullptr, nullptr, 1, N, Fs, gr.ds_b1, s));
@@ -972,7 +1054,7 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   BWD_TRY(mark(8));
 
   // router: dW_g = dz^T x and R (+)= dz W_g, both with dz = hi + lo in bfloat16
-  BWD_TRY(wgrad(B.zero, B.kpart, N, B.dz_hl, B.dz_hl + E8, 2 * (long long)E8, T(in.x), T(in.x), d, E, d, nullptr, 1, N, gr.dw_router,
+  BWD_TRY(wgrad(B, N, B.dz_hl, B.dz_hl + E8, 2 * (long long)E8, T(in.x), T(in.x), d, E, d, nullptr, 1, N, gr.dw_router,
                 nullptr, E, d, 0, s));
   {
     BwdGemm g = gemm_args(B.zero);

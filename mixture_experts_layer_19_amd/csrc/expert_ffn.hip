@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(GemmArgs g) {
 int ffn_tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM; }
 
 // One persistent workgroup per CU (a multiple of 8, so every XCD gets the same count).
-static int persistent_grid() {
+int persistent_grid() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

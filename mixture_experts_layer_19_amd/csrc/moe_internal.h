@@ -211,6 +211,8 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
 hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
                        const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
                        hipStream_t stream);
+// One persistent workgroup per CU: the CU count rounded up to a multiple of 8 (the XCDs).
+int persistent_grid();
 // Tile table of one dense "expert" covering rows [0, n) in tiles of bm rows.
 hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream);
 // Backward recompute of the up projection (bfloat16): the tile table's rows of a times W1
