@@ -67,6 +67,11 @@ struct BwdGemm {
   // weight gradients, balanced schedule (or null): cost prefix [E+1], per-XCD counters [8]
   const long long* sched;
   int* sched_cnt;
+  // grouped, split tail (or null): workgroups [0, grid_static) take the first
+  // floor(S / cu_grid) * cu_grid tiles, the later ones the K pieces of the rest, writing float32
+  // partials [kMaxTailItems][256][256] (summed by bwd_tail_reduce_kernel)
+  float* tpart;
+  int grid_static, cu_grid;
   // activation backward (grouped): pre-activations, gates, row partials of <dh', h>
   const uint16_t* pre;  // SwiGLU [rows][2 N] (gate | up), GELU [rows][N]
   const float* gate;    // [rows] or null (1)
@@ -103,6 +108,11 @@ MOE_DEV uint4 pack8(const float* f) {
                     pack_bf16x2(f[6], f[7]));
 }
 
+// slabs of a grouped product's reduction (each segment padded to whole slabs)
+MOE_DEV int grouped_slabs(const BwdGemm& g) {
+  return (g.klen[0] + kBK - 1) / kBK + (g.klen[1] + kBK - 1) / kBK;
+}
+
 // ---------------------------------------------------------------------------------------
 // Grouped bfloat16 GEMM on MFMA (v_mfma_f32_32x32x16_bf16, float32 accumulation).
 // Workgroup tile 256 x 256, eight waves (two per SIMD) of 64 x 128 (2 x 4 blocks of
@@ -137,6 +147,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
   // overhead), one per XCD, and the XCD's persistent workgroups take the run's tiles in order
   // from an atomic counter, so a large expert's long tiles spread over the whole run.
   const bool dyn = MODE == kWgrad && g.sched != nullptr;
+  int tail_w = -1, tail_q = 1;  // split-tail item (grouped) and the tail's pieces per tile
   const int xcd = blockIdx.x & 7;
   long long run_lo = 0, run_hi = 0, s = 0;
   if (dyn) {
@@ -156,6 +167,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
     };
     run_lo = run_start(xcd);
     run_hi = xcd == 7 ? (long long)g.n_experts * tpe : run_start(xcd + 1);
+  } else if (MODE == kGrouped && g.tpart) {
+    const long long S_main = S / g.cu_grid * g.cu_grid;
+    if ((int)blockIdx.x >= g.grid_static) {
+      const int q = tail_pieces(S - S_main, grouped_slabs(g), g.cu_grid);
+      tail_w = (int)blockIdx.x - g.grid_static;
+      if (tail_w >= (S - S_main) * q) return;
+      s = S_main + tail_w / q;
+      tail_q = q;
+    } else {
+      const long long per = (S_main + 7) / 8;
+      const long long slot = blockIdx.x >> 3;
+      s = (long long)xcd * per + slot;
+      if (slot >= per || s >= S_main) return;
+    }
   } else {
     const long long per = (S + 7) / 8;
     const long long slot = blockIdx.x >> 3;
@@ -214,7 +239,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
     kp0 = (kr + kBK - 1) / kBK * kBK;
     ktot = g.a[1] ? 2 * kp0 : kp0;
   }
-  const int nk = ktot / kBK;
+  int nk = ktot / kBK;
+  int kso = 0;  // first slab (a split-tail piece covers slabs [kso, kso + nk))
+  if (tail_w >= 0) {
+    const int piece = tail_w % tail_q;
+    kso = piece * nk / tail_q;
+    nk = (piece + 1) * nk / tail_q - kso;
+  }
 
   // ---- operand stages in LDS, written by global_load_lds_dwordx4 (16 bytes per lane,
   // 1 KiB per wave instruction); a lane whose 16 bytes lie outside the operand (rows past the
@@ -260,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
   const long long da1 = g.a[1] ? (long long)(g.a[1] - g.a[0]) : 0;
   const long long db1 = g.b[1] ? (long long)(g.b[1] - g.b[0]) : 0;
   auto issue = [&](int slab, int buf) {
-    const int kbase = slab * kBK;
+    const int kbase = (kso + slab) * kBK;
     const int sg = kbase >= kp0 ? 1 : 0;     // uniform
     const int kl = kbase - sg * kp0;         // slab start within the segment
     const int klen = sg ? klen1 : klen0;
@@ -401,7 +432,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
                                    : static_cast<uint16_t*>(g.c_hi) + (size_t)e * g.c_estride + (size_t)(m - g.m_split) * g.ldc;
         }
         if (!row_ok || cc >= N) continue;
-        if (EPI == kStoreT && MODE == kWgrad && prow) {
+        if (MODE == kGrouped && tail_q > 1) {
+          // a K piece of a split-tail tile: float32 partial of the tile, [256 rows][256 cols]
+          float* tp = g.tpart + (size_t)tail_w * (kBM * kBN) + (size_t)rl * kBN + (cc - n0);
+          *reinterpret_cast<float4*>(tp) = make_float4(v8[0], v8[1], v8[2], v8[3]);
+          *reinterpret_cast<float4*>(tp + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
+        } else if (EPI == kStoreT && MODE == kWgrad && prow) {
           *reinterpret_cast<float4*>(prow + cc) = make_float4(v8[0], v8[1], v8[2], v8[3]);
           *reinterpret_cast<float4*>(prow + cc + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
         } else if (EPI == kStoreT) {
@@ -463,6 +499,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
   }
   __syncthreads();  // the next tile's copies reuse the stages
   }
+}
+
+// The split tail of a grouped bf16 product: out = bf16(sum of the tail tile's pieces, in
+// piece order). Workgroup (t, rg): rows 4 rg .. 4 rg + 3 of tail tile t, a thread per 4
+// columns.
+__global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdGemm g) {
+  const int NT = g.n_tiles_n;
+  const long long S = (long long)g.tiles[0] * NT;
+  const long long S_main = S / g.cu_grid * g.cu_grid;
+  const int q = tail_pieces(S - S_main, grouped_slabs(g), g.cu_grid);
+  if (q <= 1 || blockIdx.x >= S - S_main) return;
+  const long long s = S_main + blockIdx.x;
+  const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
+  const int ts = probe[3], me = probe[4];
+  int mt, nt;
+  supertile(s - (long long)ts * NT, me, NT, &mt, &nt);
+  const int* tq = g.tiles + kTileHdr + kTileInts * (ts + mt);
+  const int row0 = tq[1], rows = tq[2];
+  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c4 = (threadIdx.x & 63) * 4;
+  const int col = nt * kBN + c4;
+  if (r >= rows || col >= g.N) return;
+  const float* pt = g.tpart + (size_t)blockIdx.x * q * (kBM * kBN) + (size_t)r * kBN + c4;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < q; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(pt + (size_t)p * (kBM * kBN));
+    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+  }
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + (size_t)(row0 + r) * g.ldc + col) =
+      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // Cost prefix of the weight-gradient schedule: sched[e] = sum over experts e' < e of
@@ -739,6 +805,7 @@ struct BwdBufs {
   uint16_t* dpre_s;
   uint16_t* h_s;    // [N][Fs]
   float* kpart;     // split-K partials of the weight gradients that split
+  float* tpart;     // split tail of dx_sorted: [kMaxTailItems][256][256]
   long long* sched; // weight-gradient schedule: cost prefix [E+1]
   int* sched_cnt;   // and its 8 per-XCD counters
   size_t bytes;
@@ -790,6 +857,7 @@ BwdBufs bwd_bufs(const moe_config& c, char* base) {
   }
   kp = std::max(kp, wgrad_part_floats((int)E, (int)d, 1, (long long)N));
   b.kpart = w.take_t<float>(kp);
+  b.tpart = w.take_t<float>((size_t)kMaxTailItems * kBM * kBN);
   b.sched = w.take_t<long long>(E + 1);
   b.sched_cnt = w.take_t<int>(8);
   b.bytes = w.used();
@@ -843,7 +911,7 @@ hipError_t act_backward(const moe_config& c, const uint16_t* zero, const int* ti
 template <int EPI>
 hipError_t dx_rows(const moe_config& c, const uint16_t* zero, const int* tiles, long long max_m_tiles, const uint16_t* dpre, int F,
                    const void* w1, const void* w3, long long w_estride, void* out, const float* c_in,
-                   hipStream_t stream) {
+                   float* tpart, hipStream_t stream) {
   BwdGemm g = gemm_args(zero);
   const bool swi = c.act == MOE_ACT_SWIGLU;
   g.a[0] = dpre;
@@ -861,7 +929,16 @@ hipError_t dx_rows(const moe_config& c, const uint16_t* zero, const int* tiles, 
   g.c = out;
   g.ldc = c.d_model;
   g.c_in = c_in;
-  return run_gemm<kGrouped, EPI>(g, max_m_tiles * g.n_tiles_n, stream);
+  const long long S_max = max_m_tiles * g.n_tiles_n;
+  if (EPI != kStoreT || !tpart) return run_gemm<kGrouped, EPI>(g, S_max, stream);
+  // whole rounds, then the last round's tiles in K pieces, then their fixed-order sum
+  g.tpart = tpart;
+  g.cu_grid = persistent_grid();
+  g.grid_static = (int)((S_max + 7) / 8 * 8);
+  bwd_gemm_kernel<kGrouped, EPI><<<(unsigned)(g.grid_static + kMaxTailItems), kThreads, 0, stream>>>(g);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  bwd_tail_reduce_kernel<<<dim3(g.cu_grid, kBM / 4), 256, 0, stream>>>(g);
+  return hipGetLastError();
 }
 
 // C_e[M][N] = sum over the expert's rows r of A[r][m] B[r][n] (+ a second segment)
@@ -1022,7 +1099,7 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
     BWD_TRY(hipGetLastError());
   }
   BWD_TRY(mark(4));
-  BWD_TRY(dx_rows<kStoreT>(c, B.zero, L.tiles, mtA, B.dpre, F, in.w1, in.w3, (long long)F * d, B.dxs, nullptr, s));
+  BWD_TRY(dx_rows<kStoreT>(c, B.zero, L.tiles, mtA, B.dpre, F, in.w1, in.w3, (long long)F * d, B.dxs, nullptr, B.tpart, s));
   BWD_TRY(mark(5));
   BWD_TRY(wgrad(B, A, dys, nullptr, d, hw, nullptr, F, d, F, L.offsets, E, 0, gr.dw2, nullptr, d, F,
                 (long long)d * F, s));
@@ -1041,7 +1118,7 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
   if (Fs > 0) {
     if (!saved) BWD_TRY(launch_up_save(c, B.tiles_dense, in.x, in.s_w1, in.s_w3, in.s_b1, nullptr, Fs, B.pre_s, B.h_s, s));
     BWD_TRY(act_backward(c, B.zero, B.tiles_dense, mtN, T(in.dy), in.s_w2, 0, Fs, B.pre_s, nullptr, nullptr, B.dpre_s, s));
-    BWD_TRY(dx_rows<kStoreF32>(c, B.zero, B.tiles_dense, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, s));
+    BWD_TRY(dx_rows<kStoreF32>(c, B.zero, B.tiles_dense, mtN, B.dpre_s, Fs, in.s_w1, in.s_w3, 0, B.R, nullptr, nullptr, s));
     BWD_TRY(wgrad(B, N, T(in.dy), nullptr, d, B.h_s, nullptr, Fs, d, Fs, nullptr, 1, N, gr.ds_w2, nullptr,
                   d, Fs, 0, s));
     BWD_TRY(wgrad(B, N, B.dpre_s, nullptr, swi ? 2 * (long long)Fs : Fs, T(in.x), nullptr, d, swi ? 2 * Fs : Fs, d,

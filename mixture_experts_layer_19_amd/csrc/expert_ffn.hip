@@ -122,15 +122,6 @@ MOE_DEV void decode_tile(const int* tiles, long long s, int NT, int* e, int* row
   *nt = grpn * kGN + r / bm;
 }
 
-// K pieces of each tail tile: enough (tile, piece) pairs to fill the grid, at least 4 slabs
-// per piece, at most kMaxTailItems pairs (the partial buffer's size).
-constexpr int kMaxTailItems = 256;
-MOE_DEV int tail_pieces(long long s_tail, int nk_all, int grid) {
-  if (s_tail <= 0) return 1;
-  const long long q = min((long long)grid / s_tail, (long long)kMaxTailItems / s_tail);
-  return (int)max(1ll, min(q, (long long)(nk_all / 4)));
-}
-
 // PART: 0 = every tile; 1 = only the whole rounds (the first floor(S / G) * G tiles of the
 // S = m-tiles * NT, G = gridDim.x); 2 = the remaining S mod G tiles, each cut along K into q
 // pieces (q = tail_pieces), one piece per workgroup, writing float32 partials when q > 1

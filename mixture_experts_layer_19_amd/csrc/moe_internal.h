@@ -67,6 +67,15 @@ struct WsLayout {
 // tile, the expert's first m-tile, the expert's m-tile count).
 constexpr int kTileHdr = 8, kTileInts = 8;
 
+// K pieces of each tail tile: enough (tile, piece) pairs to fill the grid, at least 4 slabs
+// per piece, at most kMaxTailItems pairs (the partial buffer's size).
+constexpr int kMaxTailItems = 256;
+MOE_DEV int tail_pieces(long long s_tail, int nk_all, int grid) {
+  if (s_tail <= 0) return 1;
+  const long long q = min((long long)grid / s_tail, (long long)kMaxTailItems / s_tail);
+  return (int)max(1ll, min(q, (long long)(nk_all / 4)));
+}
+
 // Builds the tile table with one workgroup of at least E threads (thread e owns expert e).
 // lo_e / hi_e are expert e's row range; ranges outside [0, rows] or decreasing are clamped,
 // the list is capped at max_tiles (so no access leaves the buffers) and *bad is set.
