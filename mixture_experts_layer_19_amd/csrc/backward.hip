@@ -835,7 +835,7 @@ BwdBufs bwd_bufs(const moe_config& c, char* base) {
   const size_t pf = c.act == MOE_ACT_SWIGLU ? 2 : 1;
   BwdBufs b{};
   b.zero = w.take_t<uint16_t>(128);
-  b.tiles_dense = w.take_t<int>(kTileHdr + kTileInts * ((N + kBM - 1) / kBM));
+  b.tiles_dense = w.take_t<int>((size_t)tile_table_ints((N + kBM - 1) / kBM));
   b.z = w.take_t<float>(N * E);
   b.dz = w.take_t<float>(N * E);
   b.part = w.take_t<float>(A * (size_t)n_part_of((int)F));

@@ -32,7 +32,7 @@ template <int EPI> constexpr bool kSave = EPI == kEpiSwigluSave || EPI == kEpiGe
 // the error word to MOE_ERR_INVALID_ARG and is otherwise clamped, so no access leaves the
 // buffers.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict__ offsets, int E, int rows,
-                                                          int bm, int max_tiles, int* __restrict__ tiles,
+                                                          int bm, int narrow, int max_tiles, int* __restrict__ tiles,
                                                           int* __restrict__ err) {
   __shared__ int s_scan[kMaxExperts];
   __shared__ int s_bad;
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int* __restrict_
   __syncthreads();
   const int lo = e < E ? offsets[e] : 0;
   const int hi = e < E ? offsets[e + 1] : 0;
-  build_tile_table(lo, hi, E, rows, bm, max_tiles, tiles, s_scan, &s_bad);
+  build_tile_table(lo, hi, E, rows, bm, narrow, max_tiles, tiles, s_scan, &s_bad);
   if (e == 0 && s_bad && err) err[0] = MOE_ERR_INVALID_ARG;
 }
 
@@ -65,108 +65,478 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------------------
 // bfloat16 grouped GEMM on MFMA (v_mfma_f32_32x32x16_bf16), float32 accumulation.
 //
-// Workgroup tile: 256 rows x 256 B-rows, 8 waves = 2 per SIMD, each wave 128 rows x 64
-// B-rows (4 x 2 blocks of 32 x 32, 128 accumulators per lane). GELU / down: 256 output
-// columns per tile. SwiGLU: each wave's 64 B-rows are 32 gate rows then the 32 up rows of
-// the same columns, so the gate and up value of an output land in the same lane and the
-// activation is applied in registers (128 output columns per tile).
+// Two tile shapes, both 8 waves = 2 per SIMD with 128 rows x 64 B-rows per wave (4 x 2
+// blocks of 32 x 32, 128 accumulators per lane):
+//   full:   256 rows x 256 B-rows (waves 2 x 4), for m-tiles of more than 128 rows;
+//   narrow: 128 rows x 512 B-rows (waves 1 x 8), for an expert's last m-tile of at most 128
+//           rows, which a full tile would compute with half or more of its rows empty.
+// GELU / down: one output column per B-row. SwiGLU: each wave's 64 B-rows are 32 gate rows
+// then the 32 up rows of the same columns, so the gate and up value of an output land in the
+// same lane and the activation is applied in registers (half as many output columns).
 //
-// Operands stream through five LDS stages of 32 reduction elements (A 16 KiB + B 16 KiB, all
-// 160 KiB of the CU's LDS) written by global_load_lds_dwordx4 (memory straight to LDS, no
-// VGPR staging), four or five slabs ahead. The four 16-byte chunks of a 64-byte LDS row are
-// XOR-swizzled by (row >> 2) mod 4, so the 16 rows one 256-byte LDS cycle of a 16-byte
-// operand read serves (rows r .. r+15 at one logical chunk) fall in 16 distinct bank slots.
+// Operands stream through LDS stages of 32 reduction elements written by
+// global_load_lds_dwordx4 (memory straight to LDS, no VGPR staging): five stages of
+// A 16 KiB + B 16 KiB (full) or four of A 8 KiB + B 32 KiB (narrow), all 160 KiB of the CU's
+// LDS. The four 16-byte chunks of a 64-byte LDS row are XOR-swizzled by (row >> 2) mod 4, so
+// the 16 rows one 256-byte LDS cycle of a 16-byte operand read serves (rows r .. r+15 at one
+// logical chunk) fall in 16 distinct bank slots.
 //
 // Ping-pong: the waves form two groups offset by half a step. In every phase one group's
-// wave on a SIMD issues its 16 multiplies (with one LDS refill copy after every 4) while the
-// other group's wave reads the next slab's operands from LDS, then a barrier swaps the
-// roles; so the MFMA pipe is fed by one wave while the other's LDS latency is hidden, and
-// the copies are issued from the wave whose MFMAs keep the pipe busy meanwhile.
-//   phase 2k:   group 0 multiplies slab k, refills slab k+4   group 1 reads slab k
-//   phase 2k+1: group 0 reads slab k+1          group 1 multiplies slab k, refills slab k+5
-// Each wave issues 4 of the 32 copies of a slab per refill and keeps three refills in
-// flight, so at every phase boundary `vmcnt(12)` guarantees that the next slab to be read
-// has landed for every wave. Refills past the last slab copy the last slab again into a
-// stage that is never read, which keeps that count exact.
+// wave on a SIMD issues its 16 multiplies (with the LDS refill copies spread between them)
+// while the other group's wave reads the next slab's operands from LDS, then a barrier swaps
+// the roles; so the MFMA pipe is fed by one wave while the other's LDS latency is hidden, and
+// the copies are issued from the wave whose MFMAs keep the pipe busy meanwhile. With S
+// stages:
+//   phase 2k:   group 0 multiplies slab k, refills slab k+S-1   group 1 reads slab k
+//   phase 2k+1: group 0 reads slab k+1          group 1 multiplies slab k, refills slab k+S
+// Each wave issues C copies per refill (full 2 + 2, narrow 1 + 4 of A + B) and keeps S - 2
+// refills in flight, so at every phase boundary `vmcnt((S - 2) C)` guarantees that the next
+// slab to be read has landed for every wave. Refills past the last slab copy the last slab
+// again into a stage that is never read, which keeps that count exact.
 //
-// Scheduling: a persistent grid of one workgroup per CU. The tile sequence is split into 8
+// Scheduling: a persistent grid of one workgroup per CU. The work sequence is split into 8
 // contiguous chunks, one per XCD (workgroup i runs on XCD i mod 8), so tiles that share
-// operands share an L2. Within an expert, tiles are ordered in supertiles of 8 m-tiles x 4
-// n-tiles (m fastest), so the ~32 tiles an XCD runs at once reuse 8 A and 4 B slices.
+// operands share an L2. Within an expert, full tiles are ordered in supertiles of 8 m-tiles x
+// 4 n-tiles (m fastest), so the ~32 tiles an XCD runs at once reuse 8 A and 4 B slices. A
+// narrow tile reads its expert's whole B on its own, so the narrow items are spread evenly
+// through the sequence (decode_tile): every XCD runs its share of them, interleaved in time
+// with full tiles, and their weight reads overlap the full tiles' compute.
 // Rows past an expert's slice and columns past N are clamped to a valid row (their results
 // are never stored); reduction chunks past K are loaded from inside the row and zeroed in
 // LDS once they have landed.
 // ---------------------------------------------------------------------------------------
 constexpr int kBM = 256, kBNB = 256, kBK = 32;
 constexpr int kGM = 8, kGN = 4;
-constexpr int kStageElems = kBM * kBK;  // bf16 elements of one operand stage (16 KiB)
+constexpr int kStageElems = kBM * kBK;  // bf16 elements of one 16 KiB LDS array
 constexpr int kGemmThreads = 512;
 
 // lds_dma16, wait_vm_lds and stage_barrier: moe_common.h
 
-// Tile s of a grouped GEMM: expert-major, then supertiles of kGM m-tiles x kGN n-tiles (m
-// fastest), so tiles that run together share operand panels.
-MOE_DEV void decode_tile(const int* tiles, long long s, int NT, int* e, int* row0, int* rows, int* nt) {
-  const int* probe = tiles + kTileHdr + kTileInts * (int)(s / NT);
-  const int ts = probe[3], me = probe[4];
-  *e = probe[0];
-  const long long l = s - (long long)ts * NT;
+// Whether a launch runs narrow tiles. A narrow tile reads twice the B rows per item of a
+// full one, and its expert's B on its own; a launch that splits its tail (the down
+// projection, PART 1 / 2) runs all of its tail at once, so it uses them only when they are at
+// least a quarter of the m-tiles (then most tiles stream their weights anyway and the halved
+// MFMA work wins). Otherwise every m-tile runs with the full shape, in table order.
+MOE_DEV bool use_narrow(const int* tiles, bool split) {
+  const int n_nar = tiles[0] - tiles[1];
+  return n_nar > 0 && (!split || 4 * n_nar >= tiles[0]);
+}
+
+// Work items of a grouped GEMM with NT n-tiles per full m-tile: NT per m-tile, or with narrow
+// tiles NT per full m-tile and ceil(NT / 2) per narrow one.
+MOE_DEV long long gemm_items(const int* tiles, int NT, bool nar) {
+  return nar ? (long long)tiles[1] * NT + (long long)(tiles[0] - tiles[1]) * ((NT + 1) >> 1)
+             : (long long)tiles[0] * NT;
+}
+
+// Narrow items a launch of `grid` persistent workgroups that splits the tail (PART 1 / 2)
+// places last: as many as the tail (the last S mod grid items) holds, so that the whole
+// rounds are made of full items where possible (every workgroup then runs the same work) and
+// the narrow items' K pieces are balanced like any tail item's.
+MOE_DEV long long narrow_tail(const int* tiles, int NT, bool nar, int grid) {
+  if (!nar) return 0;
+  const long long S = gemm_items(tiles, NT, true);
+  const long long S_nar = (long long)(tiles[0] - tiles[1]) * ((NT + 1) >> 1);
+  return min(S_nar, S - S / grid * grid);
+}
+
+// Supertile order over a group of `me` m-tiles starting at index ts: local item l -> (m-tile
+// index within the group, n-tile); kGM m-tiles x kGN n-tiles, m fastest.
+MOE_DEV void ffn_supertile(long long l, int me, int NT, int* m, int* nt) {
   const int band = (int)(l / ((long long)kGM * NT));
   const int lb = (int)(l - (long long)band * kGM * NT);
   const int bm = min(kGM, me - kGM * band);
   const int grpn = lb / (kGN * bm);
   const int r = lb - grpn * kGN * bm;
-  const int* tq = tiles + kTileHdr + kTileInts * (ts + kGM * band + r % bm);
-  *row0 = tq[1];
-  *rows = tq[2];
+  *m = kGM * band + r % bm;
   *nt = grpn * kGN + r / bm;
 }
 
-// PART: 0 = every tile; 1 = only the whole rounds (the first floor(S / G) * G tiles of the
-// S = m-tiles * NT, G = gridDim.x); 2 = the remaining S mod G tiles, each cut along K into q
+// Work item u (0 <= u < gemm_items): its m-tile (expert, first row, rows) and n-tile; returns
+// whether it is narrow. Without narrow tiles the items are expert-major, then in supertiles
+// of the expert's m-tiles. With them, the full m-tiles (fmap) are ordered that way; the last
+// n_tail items are narrow ones, and the other narrow items are spread evenly through the rest
+// (item u is the narrow item floor(u Sn / S) when that count steps at u), so that every XCD's
+// run and every round holds its share of them.
+MOE_DEV bool decode_tile(const int* tiles, long long u, int NT, bool use_nar, long long n_tail, int* e, int* row0,
+                         int* rows, int* nt) {
+  const int* T = tiles + kTileHdr;
+  int t, m;
+  if (!use_nar) {
+    const int* probe = T + kTileInts * (int)(u / NT);
+    const int ts = probe[3];
+    ffn_supertile(u - (long long)ts * NT, probe[4], NT, &m, nt);
+    t = ts + m;
+  } else {
+    const int NT2 = (NT + 1) >> 1;
+    const long long s_full = (long long)tiles[1] * NT;
+    const long long S_nar = (long long)(tiles[0] - tiles[1]) * NT2 - n_tail;  // interleaved ones
+    const long long S = s_full + S_nar;
+    long long nb;  // narrow items before u
+    bool nar;
+    if (u >= S) {
+      nb = S_nar + (u - S);
+      nar = true;
+    } else {
+      nb = u * S_nar / S;
+      nar = (u + 1) * S_nar / S > nb;
+    }
+    if (nar) {
+      const long long j = nb / NT2;
+      t = tiles[tiles[3] + (int)j];
+      *nt = (int)(nb - j * NT2);
+    } else {
+      const int* fmap = tiles + tiles[2];
+      const long long s = u - nb;  // full item
+      const int* probe = T + kTileInts * fmap[(int)(s / NT)];
+      const int fs = probe[5];
+      ffn_supertile(s - (long long)fs * NT, probe[6], NT, &m, nt);
+      t = fmap[fs + m];
+    }
+    const int* q = T + kTileInts * t;
+    *e = q[0];
+    *row0 = q[1];
+    *rows = q[2];
+    return nar;
+  }
+  const int* q = T + kTileInts * t;
+  *e = q[0];
+  *row0 = q[1];
+  *rows = q[2];
+  return false;
+}
+
+// One work item: tile (e, row0, rows, nt) over slabs [kso, kso + nk) of nk_all; NAR picks the
+// narrow shape. PART 2 with q > 1 writes this item's float32 partial tile (item w).
+template <int EPI, int PART, int NAR>
+MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int e, int row0, int rows, int nt,
+                       int kso, int nk, int nk_all, long long w, int q) {
+  constexpr int TBM = NAR ? 128 : 256;            // tile rows
+  constexpr int TBN = NAR ? 512 : 256;            // tile B-rows
+  constexpr int NST = NAR ? 4 : 5;                // LDS stages
+  constexpr int CA = TBM / 128, CB = TBN / 128;   // copies of A / B per wave and slab (16 rows each)
+  constexpr int CPR = CA + CB;                    // copies per refill
+  constexpr int kVm = (NST - 2) * CPR;            // copies a wave may leave in flight at a boundary
+  constexpr int kCols = kSwi<EPI> ? TBN / 2 : TBN;  // output columns per tile
+  const int K = g.K, n_out = g.n_out;
+  const int grp = wave >> 2;                                        // ping-pong group
+  const int wm = NAR ? 0 : (wave & 1);                              // 128-row block of the tile
+  const int wc = NAR ? wave : grp * 2 + ((wave >> 1) & 1);          // 64-B-row block
+  const bool k_tail = (K % kBK) != 0;
+  // stage j: A at sa(j), B at sb(j)
+  auto sa = [&](int j) -> uint16_t* { return NAR ? smem + 8 * kStageElems + j * (kStageElems / 2) : smem + 2 * j * kStageElems; };
+  auto sb = [&](int j) -> uint16_t* { return NAR ? smem + 2 * j * kStageElems : smem + (2 * j + 1) * kStageElems; };
+  // epilogue only: this tile's per-row gates (down projection) and per-column biases
+  float* s_gate = reinterpret_cast<float*>(smem + 8 * kStageElems);
+  float* s_bias = s_gate + kBM;
+
+  // The lane index is made opaque per tile: otherwise the compiler hoists every
+  // lane-dependent address out of the tile loop and spills them across it.
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  // Load geometry: copy instruction i of this wave fills 16 LDS rows of a stage; lane l
+  // writes row (l >> 2) of them at physical chunk l & 3, which holds the logical chunk
+  // (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
+  const int lrow = lane >> 2;
+  const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  // MFMA operand reads: row (lane & 31) of a 32-row block, logical chunk 2 ks + (lane >> 5),
+  // physical chunk = logical ^ ((row >> 2) & 3); element offsets for ks = 0, 1.
+  int rdk[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) rdk[ks] = (lane & 31) * kBK + (((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3)) * 8);
+  const int a_rd = wm * 128 * kBK;
+  const int b_rd = wc * 64 * kBK;
+  const int n0 = nt * kCols;
+
+  // uniform bases (bytes) and 32-bit per-lane offsets of this wave's A and B copies
+  const char* a_base = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
+  const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
+  const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
+  uint32_t a_off[CA], b_off[CB];
+  const char* b_src[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
+    a_off[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int rr = (wave * CB + i) * 16 + lrow;  // B-row 0 .. TBN-1
+    int cl;  // B-row's output column relative to n0
+    if (kSwi<EPI>) {
+      // B-rows 64 c .. 64 c + 31: gate of columns 32 c ..; the next 32: up of the same
+      cl = (rr >> 6) * 32 + (rr & 31);
+      b_src[i] = ((((wave * CB + i) * 16) & 63) >= 32) ? b1_base : b0_base;  // uniform per copy
+    } else {
+      cl = rr;
+      b_src[i] = b0_base;
+    }
+    b_off[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
+  }
+  auto dma_k = [&](int k0) -> uint32_t {  // lanes past K read inside the row (zeroed later)
+    return (k_tail && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
+  };
+  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) of slab-offset ka into stage j
+  auto copy = [&](int c, int j, uint32_t ka) {
+    const bool is_a = NAR ? c == 0 : (c & 1) == 0;
+    const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
+    if (is_a) lds_dma16(a_base + a_off[i] + ka, sa(j) + (wave * CA + i) * 16 * kBK);
+    else lds_dma16(b_src[i] + b_off[i] + ka, sb(j) + (wave * CB + i) * 16 * kBK);
+  };
+  auto refill = [&](int j, int slab) {
+    const uint32_t ka = dma_k((kso + slab) * kBK);
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) copy(c, j, ka);
+  };
+  // zero this wave's copied chunks of the last slab that lie past K (after they landed)
+  auto zero_tail = [&](int j, int slab) {
+    if (!k_tail || kso + slab != nk_all - 1 || (kso + slab) * kBK + lchunk < K) return;
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      *reinterpret_cast<uint4*>(sa(j) + (wave * CA + i) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<uint4*>(sb(j) + (wave * CB + i) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  bf16x8 fa[2][4], fb[2][2];  // operands of one slab: [ks][block]
+  auto read_slab = [&](int j) {
+    const uint16_t* a_st = sa(j);
+    const uint16_t* b_st = sb(j);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        fa[ks][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a_st + a_rd + t * 32 * kBK + rdk[ks]));
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        fb[ks][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(b_st + b_rd + t * 32 * kBK + rdk[ks]));
+    }
+  };
+  // phase boundary; `next` = the slab group 0 reads in the coming phase, in stage j (its K
+  // tail is zeroed here, once every wave's copies of it have landed), or -1: none
+  auto boundary = [&](int j, int next) {
+    __builtin_amdgcn_sched_barrier(0);  // the phase's multiplies / reads stay in the phase
+    wait_vm_lds<kVm>();
+    if (next >= 0) zero_tail(j, next);
+    wait_vm_lds<63>();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // multiply the slab in registers while refilling stage j with `slab`: copy c after MFMA
+  // number floor((c + 1) 16 / CPR) - 1, so the copies spread over the phase
+  auto multiply_refill = [&](int j, int slab) {
+    const uint32_t ka = dma_k((kso + slab) * kBK);
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm) {
+      const int ks = mm >> 3, i = (mm >> 1) & 3, jj = mm & 1;
+      acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][jj], acc[i][jj], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < CPR; ++c)
+        if (mm == (c + 1) * 16 / CPR - 1) {
+          copy(c, j, ka);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  };
+  // Slab k lives in stage k mod NST. Each group runs its own straight-line loop; both pass
+  // the same sequence of barriers (two per slab plus one before the first):
+  //   group 0: [read 0] | mult 0 | read 1 | mult 1 | read 2 | ...      (reads in odd phases)
+  //   group 1: [ idle ] | read 0 | mult 0 | read 1 | mult 1 | ...      (reads in even phases)
+  // A stage is refilled only when both groups are done with its previous slab.
+  // group 0, slab k in stage j: multiply k and refill slab k+NST-1; then read k+1 (which
+  // exists unless `last` may be the final slab)
+  auto g0_step = [&](int j, int k, bool last) {
+    multiply_refill((j + NST - 1) % NST, min(k + NST - 1, nk - 1));
+    boundary((j + 1) % NST, k + 1);
+    if (!last || k + 1 < nk) read_slab((j + 1) % NST);
+    boundary((j + 1) % NST, -1);
+  };
+  // group 1, slab k in stage j: read k; then multiply k and refill its stage with slab k+NST
+  auto g1_step = [&](int j, int k) {
+    read_slab(j);
+    boundary((j + 1) % NST, k + 1);
+    multiply_refill(j, min(k + NST, nk - 1));
+    boundary((j + 1) % NST, -1);
+  };
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) refill(j, min(j, nk - 1));
+  boundary(0, 0);
+  int kt = 0;
+  if (grp == 0) {
+    read_slab(0);
+    boundary(0, -1);
+    for (; kt + NST <= nk; kt += NST) {
+#pragma unroll
+      for (int j = 0; j < NST; ++j) g0_step(j, kt + j, j == NST - 1);
+    }
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+      if (kt + j < nk) g0_step(j, kt + j, true);
+  } else {
+    refill(NST - 1, min(NST - 1, nk - 1));
+    boundary(0, -1);
+    for (; kt + NST <= nk; kt += NST) {
+#pragma unroll
+      for (int j = 0; j < NST; ++j) g1_step(j, kt + j);
+    }
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+      if (kt + j < nk) g1_step(j, kt + j);
+  }
+  // every wave's copies (those past the end included) have landed and every wave is done
+  // reading the stages: the LDS is free for the epilogue (or the next tile). The explicit
+  // wait is needed: the barrier's fence does not wait for LDS-DMA copies in flight.
+  wait_vm_lds<0>();
+  __syncthreads();
+  if (PART == 2 && q > 1) {
+    // a K piece of a tail tile: raw float32 accumulators to this item's partial tile
+    // [TBM rows][TBN columns] (the sum and the epilogue follow in tail_reduce_kernel)
+    float* pt = g.partial + (size_t)w * (kBM * kBNB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 128 + i * 32 + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
+          const int col = wc * 64 + j * 32 + (lane & 31);
+          pt[row * TBN + col] = acc[i][j][v];
+        }
+    return;
+  }
+
+  // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
+  // (1 and 0 when absent, so the epilogue has no branches)
+  if (tid < TBM)
+    s_gate[tid] = ((EPI == kEpiDown || kSave<EPI>) && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
+  if (tid < kCols)
+    s_bias[tid] = (!kSwi<EPI> && g.bias && n0 + tid < n_out)
+                      ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
+  __syncthreads();
+
+  // ---- epilogue: activation / bias / gate in registers, then per 32-row block the wave's
+  // bf16 rows are staged in its own LDS buffer (rows padded by 16 bytes: the two
+  // half-waves, 4 rows apart, hit disjoint banks) and written with 16-byte row stores.
+  uint16_t* C = static_cast<uint16_t*>(g.c);
+  constexpr int kWCols = kSwi<EPI> ? 32 : 64;               // wave output columns
+  constexpr int kStride = kWCols + 8;                       // staged row length (elements)
+  constexpr int kWChunks = kWCols / 8;                      // 16-byte chunks per row
+  uint16_t* stage = smem + wave * kStageElems;              // LDS arrays 0..7, one per wave
+  const int col_base = n0 + wc * kWCols;                    // first output column of the wave
+  // lane's element in a 32 x 32 block: column lane & 31, rows 8 g + 4 (lane >> 5) + r
+  uint16_t* st_lane = stage + ((lane >> 5) * 4) * kStride + (lane & 31);
+  // each lane stores whole 16-byte chunks of the block's 32 staged rows to dst (row pitch
+  // `pitch` elements, first column col_base)
+  auto flush = [&](int i, uint16_t* dst, size_t pitch) {
+#pragma unroll
+    for (int it = 0; it < 32 * kWChunks / 64; ++it) {
+      const int idx = it * 64 + lane;
+      const int prow = idx / kWChunks, ch = idx % kWChunks;
+      const int trow = wm * 128 + i * 32 + prow;
+      const int col = col_base + ch * 8;
+      const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
+      if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + (size_t)(row0 + trow) * pitch + col) = val;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (EPI == kEpiSwigluSave) {
+      // gate pre-activation, up pre-activation, then w_a silu(g) u, one staging pass each
+      uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][0][v]);
+      flush(i, C2, 2 * (size_t)n_out);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][1][v]);
+      flush(i, C2 + n_out, 2 * (size_t)n_out);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int prow = (v >> 2) * 8 + (v & 3);
+        const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+        st_lane[prow * kStride] = f32_to_bf16(gs * (silu_f(acc[i][0][v]) * acc[i][1][v]));
+      }
+      flush(i, C, n_out);
+    } else if (EPI == kEpiGeluSave) {
+      // pre-activation (with b1), then w_a gelu(.)
+      uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          st_lane[((v >> 2) * 8 + (v & 3)) * kStride + j * 32] =
+              f32_to_bf16(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]);
+      flush(i, C2, n_out);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int prow = (v >> 2) * 8 + (v & 3);
+        const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          st_lane[prow * kStride + j * 32] =
+              f32_to_bf16(gs * gelu_erf(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]));
+      }
+      flush(i, C, n_out);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int prow = (v >> 2) * 8 + (v & 3);  // block row, minus 4 (lane >> 5)
+        if (EPI == kEpiSwiglu) {
+          st_lane[prow * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+        } else {
+          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float bj = s_bias[wc * kWCols + j * 32 + (lane & 31)];
+            float val;
+            if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
+            else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
+            st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
+          }
+        }
+      }
+      flush(i, C, n_out);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each 32-row block's registers short-lived
+  }
+  __syncthreads();  // the staging area is the next tile's first stage
+}
+
+// PART: 0 = every work item; 1 = only the whole rounds (the first floor(S / G) * G items of
+// S = gemm_items, G = gridDim.x); 2 = the remaining S mod G items, each cut along K into q
 // pieces (q = tail_pieces), one piece per workgroup, writing float32 partials when q > 1
 // (tail_reduce_kernel sums them and applies the epilogue).
 template <int EPI, int PART = 0>
 __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA0[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sB0[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sA1[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sB1[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sA2[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sB2[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sA3[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sB3[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sA4[kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sB4[kStageElems];
-  // epilogue only: this tile's per-row gates (down projection) and per-column biases
-  float* s_gate = reinterpret_cast<float*>(sA4);
-  float* s_bias = reinterpret_cast<float*>(sA4) + kBM;
-
+  __shared__ __attribute__((aligned(16))) uint16_t smem[10 * kStageElems];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-  const int grp = wave >> 2;                                  // ping-pong group
-  const int wm = wave & 1;                                    // 128-row half of the tile
-  const int wc = grp * 2 + ((wave >> 1) & 1);                 // 64-B-row block 0..3
-  const int K = g.K, n_out = g.n_out, NT = g.n_tiles_n;
-  constexpr int kCols = kSwi<EPI> ? 128 : 256;  // output columns per tile
-
-  const int n_mt = g.tiles[0];
-  const long long S_all = (long long)n_mt * NT;
-  const int nk_all = (K + kBK - 1) / kBK;
+  const int NT = g.n_tiles_n;
+  const bool nar = use_narrow(g.tiles, PART != 0);
+  const long long S_all = gemm_items(g.tiles, NT, nar);
+  const int nk_all = (g.K + kBK - 1) / kBK;
   const long long S_main = (PART == 0) ? S_all : S_all / gridDim.x * gridDim.x;
   const int q = (PART == 2) ? tail_pieces(S_all - S_main, nk_all, gridDim.x) : 1;
+  const long long n_tail = (PART == 0) ? 0 : narrow_tail(g.tiles, NT, nar, gridDim.x);
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   const long long chunk = (S_main + 7) / 8;
-  // work items: tiles of [0, S_main) in per-XCD runs, or the tail's (tile, piece) pairs
+  // work items: [0, S_main) in per-XCD runs, or the tail's (item, piece) pairs
   const long long w_begin = (PART == 2) ? (long long)blockIdx.x : (long long)xcd * chunk + slot;
   const long long w_end = (PART == 2) ? (S_all - S_main) * q : min(S_main, (long long)xcd * chunk + chunk);
   const int w_step = (PART == 2) ? (int)gridDim.x : per_xcd;
-  const bool k_tail = (K % kBK) != 0;
 
   for (long long w = w_begin; w < w_end; w += w_step) {
-    long long s = w;       // tile
+    long long s = w;       // work item (position in the sequence)
     int kso = 0;           // first slab of this item
     int nk = nk_all;       // slabs of this item
     if (PART == 2) {
@@ -175,318 +545,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       kso = piece * nk_all / q;
       nk = (piece + 1) * nk_all / q - kso;
     }
-    // The lane index is made opaque per tile: otherwise the compiler hoists every
-    // lane-dependent address out of the tile loop and spills them across it.
-    int lane = tid & 63;
-    asm volatile("" : "+v"(lane));
-    // Load geometry: copy instruction i (0, 1) of this wave fills the 16 LDS rows
-    // (2 wave + i) * 16 .. +15 of a stage; lane l writes row (l >> 2) of them at physical
-    // chunk l & 3, which holds the logical chunk (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
-    const int lrow = lane >> 2;
-    const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
-    // MFMA operand reads: row (lane & 31) of a 32-row block, logical chunk 2 ks + (lane >> 5),
-    // physical chunk = logical ^ ((row >> 2) & 3); element offsets for ks = 0, 1.
-    int rdk[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) rdk[ks] = (lane & 31) * kBK + (((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 2) & 3)) * 8);
-    const int a_rd = wm * 128 * kBK;
-    const int b_rd = wc * 64 * kBK;
-
-
+    // Rebuilt / made opaque per item, so that what the two tile shapes derive from them is
+    // computed per tile instead of being held (and spilled to memory) across the whole loop;
+    // the thread index comes from the wave index and the lane's position in the wave.
+    int wave_i = wave, NT_i = NT;
+    asm volatile("" : "+s"(wave_i), "+s"(NT_i));
+    const int tid_i = wave_i * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     int e, row0, rows, nt;
-    decode_tile(g.tiles, s, NT, &e, &row0, &rows, &nt);
-    const int n0 = nt * kCols;
-
-    // uniform bases (bytes) and 32-bit per-lane offsets of this wave's 2 A and 2 B copies
-    const char* a_base = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
-    const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
-    const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
-    uint32_t a_off[2], b_off[2];
-    const char* b_src[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rr = (wave * 2 + i) * 16 + lrow;  // stage row / B-row 0..255
-      a_off[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
-      int cl;  // B-row's output column relative to n0
-      if (kSwi<EPI>) {
-        // B-rows 64 c .. 64 c + 31: gate of columns 32 c ..; the next 32: up of the same
-        cl = (rr >> 6) * 32 + (rr & 31);
-        b_src[i] = ((((wave * 2 + i) * 16) & 63) >= 32) ? b1_base : b0_base;  // uniform per copy
-      } else {
-        cl = rr;
-        b_src[i] = b0_base;
-      }
-      b_off[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
-    }
-    auto dma_k = [&](int k0) -> uint32_t {  // lanes past K read inside the row (zeroed later)
-      return (k_tail && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
-    };
-    auto refill = [&](uint16_t* sa, uint16_t* sb, int slab) {
-      const uint32_t ka = dma_k((kso + slab) * kBK);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        lds_dma16(a_base + a_off[i] + ka, sa + (wave * 2 + i) * 16 * kBK);
-        lds_dma16(b_src[i] + b_off[i] + ka, sb + (wave * 2 + i) * 16 * kBK);
-      }
-    };
-    // zero this wave's copied chunks of the last slab that lie past K (after they landed)
-    auto zero_tail = [&](uint16_t* sa, uint16_t* sb, int slab) {
-      if (!k_tail || kso + slab != nk_all - 1 || (kso + slab) * kBK + lchunk < K) return;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int off = (wave * 2 + i) * 16 * kBK + lane * 8;
-        *reinterpret_cast<uint4*>(sa + off) = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(sb + off) = make_uint4(0, 0, 0, 0);
-      }
-    };
-
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    bf16x8 fa[2][4], fb[2][2];  // operands of one slab: [ks][block]
-    auto read_slab = [&](const uint16_t* sa, const uint16_t* sb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          fa[ks][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sa + a_rd + t * 32 * kBK + rdk[ks]));
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          fb[ks][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sb + b_rd + t * 32 * kBK + rdk[ks]));
-      }
-    };
-    auto multiply = [&]() {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
-    };
-    // phase boundary; `next` = the slab group 0 reads in the coming phase (its K tail is
-    // zeroed here, once every wave's copies of it have landed)
-    auto boundary = [&](uint16_t* na, uint16_t* nb, int next) {
-      __builtin_amdgcn_sched_barrier(0);  // the phase's multiplies / reads stay in the phase
-      wait_vm_lds<12>();
-      zero_tail(na, nb, next);
-      wait_vm_lds<63>();
-      stage_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // Slab k lives in stage k mod 5. Each group runs its own straight-line loop; both pass
-    // the same sequence of barriers (two per slab plus one before the first):
-    //   group 0: [read 0] | mult 0 | read 1 | mult 1 | read 2 | ...      (reads in odd phases)
-    //   group 1: [ idle ] | read 0 | mult 0 | read 1 | mult 1 | ...      (reads in even phases)
-    // A stage is refilled only when both groups are done with its previous slab.
-    // multiply slab k while refilling stage (fa, fb) with `slab`: one copy after every 4 MFMAs
-    auto multiply_refill = [&](uint16_t* fa_, uint16_t* fb_, int slab) {
-      const uint32_t ka = dma_k((kso + slab) * kBK);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int mm = q * 4 + m, ks = mm >> 3, i = (mm >> 1) & 3, j = mm & 1;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
-        }
-        const int ii = q >> 1;
-        if ((q & 1) == 0) lds_dma16(a_base + a_off[ii] + ka, fa_ + (wave * 2 + ii) * 16 * kBK);
-        else lds_dma16(b_src[ii] + b_off[ii] + ka, fb_ + (wave * 2 + ii) * 16 * kBK);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    // group 0: phase 2k multiplies k and refills stage (k+4)%5 with slab k+4; phase 2k+1 reads k+1
-    auto g0_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1,
-                       uint16_t* a_k4, uint16_t* b_k4, int k) {
-      multiply_refill(a_k4, b_k4, min(k + 4, nk - 1));
-      boundary(a_k1, b_k1, k + 1);
-      if (k + 1 < nk) read_slab(a_k1, b_k1);
-      boundary(a_k1, b_k1, -1);
-    };
-    // group 1: phase 2k reads k; phase 2k+1 multiplies k and refills stage k%5 with slab k+5
-    auto g1_step = [&](uint16_t* a_k, uint16_t* b_k, uint16_t* a_k1, uint16_t* b_k1, int k) {
-      read_slab(a_k, b_k);
-      boundary(a_k1, b_k1, k + 1);
-      multiply_refill(a_k, b_k, min(k + 5, nk - 1));
-      boundary(a_k1, b_k1, -1);
-    };
-    refill(sA0, sB0, 0);
-    refill(sA1, sB1, min(1, nk - 1));
-    refill(sA2, sB2, min(2, nk - 1));
-    refill(sA3, sB3, min(3, nk - 1));
-    boundary(sA0, sB0, 0);
-    int kt = 0;
-    if (grp == 0) {
-      read_slab(sA0, sB0);
-      boundary(sA0, sB0, -1);
-      for (; kt + 5 <= nk; kt += 5) {
-        g0_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
-        g0_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-        g0_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-        g0_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
-        g0_step(sA4, sB4, sA0, sB0, sA3, sB3, kt + 4);
-      }
-      const int rem = nk - kt;
-      if (rem > 0) g0_step(sA0, sB0, sA1, sB1, sA4, sB4, kt);
-      if (rem > 1) g0_step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-      if (rem > 2) g0_step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-      if (rem > 3) g0_step(sA3, sB3, sA4, sB4, sA2, sB2, kt + 3);
-    } else {
-      refill(sA4, sB4, min(4, nk - 1));
-      boundary(sA0, sB0, -1);
-      for (; kt + 5 <= nk; kt += 5) {
-        g1_step(sA0, sB0, sA1, sB1, kt);
-        g1_step(sA1, sB1, sA2, sB2, kt + 1);
-        g1_step(sA2, sB2, sA3, sB3, kt + 2);
-        g1_step(sA3, sB3, sA4, sB4, kt + 3);
-        g1_step(sA4, sB4, sA0, sB0, kt + 4);
-      }
-      const int rem = nk - kt;
-      if (rem > 0) g1_step(sA0, sB0, sA1, sB1, kt);
-      if (rem > 1) g1_step(sA1, sB1, sA2, sB2, kt + 1);
-      if (rem > 2) g1_step(sA2, sB2, sA3, sB3, kt + 2);
-      if (rem > 3) g1_step(sA3, sB3, sA4, sB4, kt + 3);
-    }
-    wait_vm_lds<0>();  // copies past the end land before the stages are reused
-    if (PART == 2 && q > 1) {
-      // a K piece of a tail tile: raw float32 accumulators to this item's partial tile
-      // [256 rows][256 columns] (the sum and the epilogue follow in tail_reduce_kernel)
-      float* pt = g.partial + (size_t)w * (kBM * kBNB);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = wm * 128 + i * 32 + (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
-            const int col = wc * 64 + j * 32 + (lane & 31);
-            pt[row * kBNB + col] = acc[i][j][v];
-          }
-      __syncthreads();
-      continue;
-    }
-
-    // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
-    // (1 and 0 when absent, so the epilogue has no branches)
-    if (tid < kBM) {
-      s_gate[tid] = ((EPI == kEpiDown || kSave<EPI>) && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
-      s_bias[tid] = (!kSwi<EPI> && g.bias && n0 + tid < n_out)
-                        ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
-    }
-    __syncthreads();  // every wave is done reading the stages: reuse them for the epilogue
-
-    // ---- epilogue: activation / bias / gate in registers, then per 32-row block the wave's
-    // bf16 rows are staged in its own LDS buffer (rows padded by 16 bytes: the two
-    // half-waves, 4 rows apart, hit disjoint banks) and written with 16-byte row stores.
-    uint16_t* C = static_cast<uint16_t*>(g.c);
-    constexpr int kWCols = kSwi<EPI> ? 32 : 64;               // wave output columns
-    constexpr int kStride = kWCols + 8;                       // staged row length (elements)
-    constexpr int kWChunks = kWCols / 8;                      // 16-byte chunks per row
-    uint16_t* stage = (wave == 0) ? sA0 : (wave == 1) ? sB0 : (wave == 2) ? sA1 : (wave == 3) ? sB1
-                    : (wave == 4) ? sA2 : (wave == 5) ? sB2 : (wave == 6) ? sA3 : sB3;
-    const int col_base = n0 + wc * kWCols;                    // first output column of the wave
-    // lane's element in a 32 x 32 block: column lane & 31, rows 8 g + 4 (lane >> 5) + r
-    uint16_t* st_lane = stage + ((lane >> 5) * 4) * kStride + (lane & 31);
-    // each lane stores whole 16-byte chunks of the block's 32 staged rows to dst (row pitch
-    // `pitch` elements, first column col_base)
-    auto flush = [&](int i, uint16_t* dst, size_t pitch) {
-#pragma unroll
-      for (int it = 0; it < 32 * kWChunks / 64; ++it) {
-        const int idx = it * 64 + lane;
-        const int prow = idx / kWChunks, ch = idx % kWChunks;
-        const int trow = wm * 128 + i * 32 + prow;
-        const int col = col_base + ch * 8;
-        const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
-        if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + (size_t)(row0 + trow) * pitch + col) = val;
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (EPI == kEpiSwigluSave) {
-        // gate pre-activation, up pre-activation, then w_a silu(g) u, one staging pass each
-        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][0][v]);
-        flush(i, C2, 2 * (size_t)n_out);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][1][v]);
-        flush(i, C2 + n_out, 2 * (size_t)n_out);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int prow = (v >> 2) * 8 + (v & 3);
-          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
-          st_lane[prow * kStride] = f32_to_bf16(gs * (silu_f(acc[i][0][v]) * acc[i][1][v]));
-        }
-        flush(i, C, n_out);
-      } else if (EPI == kEpiGeluSave) {
-        // pre-activation (with b1), then w_a gelu(.)
-        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            st_lane[((v >> 2) * 8 + (v & 3)) * kStride + j * 32] =
-                f32_to_bf16(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]);
-        flush(i, C2, n_out);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int prow = (v >> 2) * 8 + (v & 3);
-          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            st_lane[prow * kStride + j * 32] =
-                f32_to_bf16(gs * gelu_erf(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]));
-        }
-        flush(i, C, n_out);
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int prow = (v >> 2) * 8 + (v & 3);  // block row, minus 4 (lane >> 5)
-          if (EPI == kEpiSwiglu) {
-            st_lane[prow * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
-          } else {
-            const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const float bj = s_bias[wc * kWCols + j * 32 + (lane & 31)];
-              float val;
-              if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
-              else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
-              st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
-            }
-          }
-        }
-        flush(i, C, n_out);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep each 32-row block's registers short-lived
-    }
-    __syncthreads();  // the staging area is the next tile's first stage
+    if (decode_tile(g.tiles, s, NT_i, nar, n_tail, &e, &row0, &rows, &nt))
+      gemm_tile<EPI, PART, 1>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
+    else
+      gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
   }
 }
 
-// The down projection's tail tiles (PART 2 with q > 1): y_s = (sum of the q partials, in piece
-// order, + b2) * gate, rounded once. Workgroup (t, rg) covers rows 4 rg .. 4 rg + 3 of tail
-// tile t, a thread per 4 columns.
+// The down projection's tail items (PART 2 with q > 1): y_s = (sum of the q partials, in
+// piece order, + b2) * gate, rounded once. Workgroup (t, rg) covers 1 / 64 of tail item t's
+// rows (4 of a full tile's 256, 2 of a narrow tile's 128), a thread per 4 columns.
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
   const int NT = g.n_tiles_n, K = g.K, n_out = g.n_out;
-  const long long S_all = (long long)g.tiles[0] * NT;
+  const bool use_nar = use_narrow(g.tiles, true);
+  const long long S_all = gemm_items(g.tiles, NT, use_nar);
   const int G = g.grid;
   const long long S_main = S_all / G * G;
   const long long S_tail = S_all - S_main;
   const int q = tail_pieces(S_tail, (K + kBK - 1) / kBK, G);
   if (q <= 1 || blockIdx.x >= S_tail) return;
   int e, row0, rows, nt;
-  decode_tile(g.tiles, S_main + blockIdx.x, NT, &e, &row0, &rows, &nt);
-  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int c4 = (threadIdx.x & 63) * 4;
-  const int col = nt * kBNB + c4;
+  const bool nar = decode_tile(g.tiles, S_main + blockIdx.x, NT, use_nar, narrow_tail(g.tiles, NT, use_nar, G), &e,
+                               &row0, &rows, &nt);
+  const int tbn = nar ? 512 : 256;  // the partial tile's columns
+  const int r = nar ? blockIdx.y * 2 + (threadIdx.x >> 7) : blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c4 = nar ? (threadIdx.x & 127) * 4 : (threadIdx.x & 63) * 4;
+  const int col = nt * tbn + c4;
   if (r >= rows || col >= n_out) return;
-  const float* pt = g.partial + (size_t)blockIdx.x * q * (kBM * kBNB) + r * kBNB + c4;
+  const float* pt = g.partial + (size_t)blockIdx.x * q * (kBM * kBNB) + r * tbn + c4;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < q; ++p) {
     const float4 x = *reinterpret_cast<const float4*>(pt + (size_t)p * (kBM * kBNB));
@@ -593,6 +686,7 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(GemmArgs g) {
 // Host side
 // ---------------------------------------------------------------------------------------
 int ffn_tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM; }
+int ffn_narrow_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM / 2 : 0; }
 
 // One persistent workgroup per CU (a multiple of 8, so every XCD gets the same count).
 int persistent_grid() {
@@ -611,7 +705,14 @@ int persistent_grid() {
 __global__ __launch_bounds__(256) void dense_tiles_kernel(int n, int bm, int* __restrict__ tiles) {
   const int nt = (n + bm - 1) / bm;
   if (threadIdx.x < 4) tiles[4 + threadIdx.x] = 0;
-  if (threadIdx.x == 0) tiles[0] = nt;
+  // all full; fmap (the identity) right after the entries, no nmap
+  const int fmap = kTileHdr + kTileInts * nt;
+  if (threadIdx.x == 0) {
+    tiles[0] = nt;
+    tiles[1] = nt;
+    tiles[2] = fmap;
+    tiles[3] = fmap + nt;
+  }
   for (int t = threadIdx.x; t < nt; t += blockDim.x) {
     int* q = tiles + kTileHdr + kTileInts * t;
     q[0] = 0;
@@ -619,6 +720,9 @@ __global__ __launch_bounds__(256) void dense_tiles_kernel(int n, int bm, int* __
     q[2] = min(bm, n - t * bm);
     q[3] = 0;
     q[4] = nt;
+    q[5] = 0;
+    q[6] = nt;
+    tiles[fmap + t] = t;
   }
 }
 
@@ -637,7 +741,7 @@ void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   // the shared expert (run after the routed experts) reuses the tile table and h
   const size_t tiles_n = (size_t)std::max(ffn_max_m_tiles(c), shared_m_tiles(c));
   const size_t h_elems = std::max(A * (size_t)c.d_ff, (size_t)c.n_tokens * (size_t)std::max(c.d_ff_shared, 0));
-  int* tiles = w.take_t<int>(kTileHdr + kTileInts * tiles_n);
+  int* tiles = w.take_t<int>((size_t)tile_table_ints((long long)tiles_n));
   void* h = w.take(h_elems * elem_size(c));
   // the down projection's tail partials (bfloat16 path, when its K allows several pieces)
   size_t part = 0;
@@ -657,7 +761,8 @@ void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
 hipError_t launch_ffn_tiles(const moe_config& c, const WsLayout& L, const int32_t* offsets, hipStream_t stream) {
   const int A = (int)(c.n_tokens * c.top_k);
   if (A == 0) return hipGetLastError();
-  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, ffn_tile_rows(c), ffn_max_m_tiles(c), L.tiles, L.err);
+  tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, c.n_experts, A, ffn_tile_rows(c), ffn_narrow_rows(c),
+                                            ffn_max_m_tiles(c), L.tiles, L.err);
   return hipGetLastError();
 }
 

@@ -62,10 +62,16 @@ struct WsLayout {
   void* bwd = nullptr;
 };
 
-// m-tile table of the grouped GEMMs: tiles[0] = number of m-tiles, tiles[4..7] = 16 zero
-// bytes, and m-tile t is tiles[kTileHdr + kTileInts t ..] = (expert, first row, rows in the
-// tile, the expert's first m-tile, the expert's m-tile count).
+// m-tile table of the grouped GEMMs. Header: tiles[0] = m-tiles, tiles[1] = full m-tiles,
+// tiles[2] / tiles[3] = offsets (in ints, from tiles) of fmap / nmap, tiles[4..7] = 16 zero
+// bytes. m-tile t (experts in order, each expert's rows in order) is
+// tiles[kTileHdr + kTileInts t ..] = (expert, first row, rows in the tile, the expert's first
+// m-tile, the expert's m-tile count, the expert's first full m-tile in fmap, the expert's
+// full m-tiles). An expert's last m-tile is narrow when it has at most `narrow` rows;
+// fmap[i] is the table index of the i-th full m-tile and nmap[j] that of the j-th narrow one.
 constexpr int kTileHdr = 8, kTileInts = 8;
+// ints of a tile table for at most cap m-tiles
+constexpr long long tile_table_ints(long long cap) { return kTileHdr + (kTileInts + 2) * cap; }
 
 // K pieces of each tail tile: enough (tile, piece) pairs to fill the grid, at least 4 slabs
 // per piece, at most kMaxTailItems pairs (the partial buffer's size).
@@ -79,29 +85,44 @@ MOE_DEV int tail_pieces(long long s_tail, int nk_all, int grid) {
 // Builds the tile table with one workgroup of at least E threads (thread e owns expert e).
 // lo_e / hi_e are expert e's row range; ranges outside [0, rows] or decreasing are clamped,
 // the list is capped at max_tiles (so no access leaves the buffers) and *bad is set.
-// s_scan: kMaxExperts ints of LDS. Every thread of the block must call it.
-MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int max_tiles, int* tiles,
+// An expert's rows are cut into m-tiles of bm rows; a last tile of at most `narrow` rows
+// (0: none) is narrow. s_scan: kMaxExperts ints of LDS. Every thread of the block must call it.
+MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narrow, int max_tiles, int* tiles,
                               int* s_scan, int* bad) {
   const int e = threadIdx.x;
   if (e < 4) tiles[4 + e] = 0;
-  int n = 0;
+  int n = 0, n_nar = 0;
   if (e < E) {
     if (lo < 0 || hi > rows || hi < lo || (e == 0 && lo != 0)) *bad = 1;
     lo = min(max(lo, 0), rows);
     hi = min(max(hi, lo), rows);
     n = (hi - lo + bm - 1) / bm;
-    s_scan[e] = n;
+    n_nar = (n > 0 && hi - lo - (n - 1) * bm <= narrow) ? 1 : 0;
   }
-  __syncthreads();
-  for (int o = 1; o < E; o <<= 1) {
-    int v = 0;
-    if (e < E && e >= o) v = s_scan[e - o];
+  // exclusive prefix over experts of v (through s_scan); *total = the sum
+  auto scan = [&](int v, int* total) -> int {
+    if (e < E) s_scan[e] = v;
     __syncthreads();
-    if (e < E) s_scan[e] += v;
+    for (int o = 1; o < E; o <<= 1) {
+      int u = 0;
+      if (e < E && e >= o) u = s_scan[e - o];
+      __syncthreads();
+      if (e < E) s_scan[e] += u;
+      __syncthreads();
+    }
+    const int ex = e < E ? s_scan[e] - v : 0;
+    *total = s_scan[E - 1];
     __syncthreads();
-  }
+    return ex;
+  };
+  int total, total_full, total_nar;
+  const int start = scan(n, &total);
+  const int fstart = scan(n - n_nar, &total_full);
+  const int nstart = scan(n_nar, &total_nar);
+  int* fmap = tiles + kTileHdr + kTileInts * max_tiles;
+  int* nmap = fmap + max_tiles;
   if (e < E) {
-    const int start = s_scan[e] - n;
+    const int n_full = n - n_nar;
     for (int t = 0; t < n && start + t < max_tiles; ++t) {
       const int r0 = lo + t * bm;
       int* q = tiles + kTileHdr + kTileInts * (start + t);
@@ -110,10 +131,19 @@ MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int max_t
       q[2] = min(bm, hi - r0);
       q[3] = start;
       q[4] = min(n, max_tiles - start);
+      q[5] = fstart;
+      q[6] = max(0, min(n_full, max_tiles - fstart));
+      if (t < n_full && fstart + t < max_tiles) fmap[fstart + t] = start + t;
     }
+    if (n_nar && nstart < max_tiles && start + n - 1 < max_tiles) nmap[nstart] = start + n - 1;
     if (e == E - 1) {
-      if (s_scan[e] > max_tiles) *bad = 1;
-      tiles[0] = min(s_scan[e], max_tiles);
+      if (total > max_tiles) *bad = 1;
+      // with a clamped list every kept m-tile is counted full (their narrow entries may be gone)
+      const bool ok = total <= max_tiles;
+      tiles[0] = min(total, max_tiles);
+      tiles[1] = ok ? total_full : min(total, max_tiles);
+      tiles[2] = kTileHdr + kTileInts * max_tiles;
+      tiles[3] = kTileHdr + (kTileInts + 1) * max_tiles;
     }
   }
   __syncthreads();
@@ -143,7 +173,7 @@ struct FinalizeArgs {
   int* base;      // [n_blocks][E] first sorted slot of each block's run of each expert
   int* err;       // device error word (written 0: routed ids are always valid)
   int* tiles;     // tile table or null
-  int tile_bm, max_tiles;
+  int tile_bm, tile_narrow, max_tiles;
 };
 
 struct RouteArgs {
@@ -185,6 +215,8 @@ hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const
                                    const int32_t* topk_ids, const float* topk_w, void* x_sorted,
                                    int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream);
 int ffn_tile_rows(const moe_config& c);
+// rows at or below which an expert's last m-tile is narrow (0: no narrow tiles)
+int ffn_narrow_rows(const moe_config& c);
 // floor(k cf N / E) raised to the next even integer (the capacity-factor dispatch's capacity)
 long long expert_capacity(const moe_config& c, float capacity_factor);
 hipError_t launch_dispatch_capacity(const moe_config& c, const WsLayout& L, float capacity_factor, const void* x,

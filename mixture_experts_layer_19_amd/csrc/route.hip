@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
   if (a.tiles) {
     const int lo = tid < E ? s_off[tid] : 0;
     const int hi = tid < E ? s_off[tid + 1] : 0;
-    build_tile_table(lo, hi, E, s_off[E], a.tile_bm, a.max_tiles, a.tiles, s_scan, &s_bad);
+    build_tile_table(lo, hi, E, s_off[E], a.tile_bm, a.tile_narrow, a.max_tiles, a.tiles, s_scan, &s_bad);
   }
   __syncthreads();
   if (tid == 0 && a.err) a.err[0] = s_bad ? MOE_ERR_INVALID_ARG : 0;
@@ -662,6 +662,7 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
     fa.err = L.err;
     fa.tiles = L.tiles;
     fa.tile_bm = ffn_tile_rows(c);
+    fa.tile_narrow = ffn_narrow_rows(c);
     fa.max_tiles = ffn_max_m_tiles(c);
   }
   route_finalize_kernel<<<1, kFinThreads, 0, stream>>>(fa);

@@ -167,6 +167,40 @@ def test_expert_ffn(dtype, act, bias, rows, E, d, f, empty):
     say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
 
 
+BOUNDARY_COUNTS = [0, 1, 127, 128, 129, 255, 256, 257, 384, 385, 640]   # 6 of 15 m-tiles narrow
+FEW_NARROW_COUNTS = [1000, 700, 513, 100, 0, 900]                       # 2 of 15
+
+
+@pytest.mark.parametrize("act,bias,d,f,counts", [("swiglu", False, 200, 600, BOUNDARY_COUNTS),
+                                                 ("gelu", True, 264, 712, BOUNDARY_COUNTS),
+                                                 ("swiglu", False, 136, 520, FEW_NARROW_COUNTS)])
+def test_expert_ffn_tile_boundaries(act, bias, d, f, counts):
+    """Per-expert row counts on both sides of the 128-row (narrow tile) and 256-row (full
+    tile) boundaries; widths off both tile grids and K not a multiple of 32. The down
+    projection's rounds are all tail, so its K pieces of narrow tiles are summed too; with
+    few narrow m-tiles it runs them with the full shape instead."""
+    counts = np.array(counts)
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[ffn tiles] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act=act, has_bias=bias, dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_tiles", cfg, weight_std=0.1), seed=6)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=6)
+    gate = W.random_gates(rows, 1, seed=6).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    xs64, g64 = f64(xs), f64(gate)
+    p = oracle_params(inp)
+    ref = np.zeros((rows, d))
+    off = offsets.cpu().numpy()
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            ex = {n: (None if p[n] is None else p[n][e]) for n in ("w1", "w2", "w3", "b1", "b2")}
+            ref[lo:hi] = O.expert_ffn(xs64[lo:hi], act, **ex) * g64[lo:hi, None]
+    err, scale = assert_close_rel(f64(ys), ref, TOL["bf16"], "y_sorted")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
 @pytest.mark.parametrize("dtype,N,k,d", [("bf16", 1000, 2, 256), ("bf16", 77, 8, 7168), ("f32", 300, 3, 64)])
 def test_combine(dtype, N, k, d):
     cfg = B.LayerConfig(N, d, max(k, 8), k, 64, dtype=dtype)
