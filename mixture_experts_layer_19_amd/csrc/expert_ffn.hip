@@ -514,13 +514,15 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
 // S = gemm_items, G = gridDim.x); 2 = the remaining S mod G items, each cut along K into q
 // pieces (q = tail_pieces), one piece per workgroup, writing float32 partials when q > 1
 // (tail_reduce_kernel sums them and applies the epilogue).
-template <int EPI, int PART = 0>
+// NAR: whether the launch may run narrow tiles; without them the narrow shape is not
+// compiled in, and the kernel keeps the registers of the full shape alone.
+template <int EPI, int PART = 0, bool NAR = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[10 * kStageElems];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
   const int NT = g.n_tiles_n;
-  const bool nar = use_narrow(g.tiles, PART != 0);
+  const bool nar = NAR && use_narrow(g.tiles, PART != 0);
   const long long S_all = gemm_items(g.tiles, NT, nar);
   const int nk_all = (g.K + kBK - 1) / kBK;
   const long long S_main = (PART == 0) ? S_all : S_all / gridDim.x * gridDim.x;
@@ -552,10 +554,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     asm volatile("" : "+s"(wave_i), "+s"(NT_i));
     const int tid_i = wave_i * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     int e, row0, rows, nt;
-    if (decode_tile(g.tiles, s, NT_i, nar, n_tail, &e, &row0, &rows, &nt))
-      gemm_tile<EPI, PART, 1>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
-    else
+    const bool is_nar = decode_tile(g.tiles, s, NT_i, nar, n_tail, &e, &row0, &rows, &nt);
+    if constexpr (NAR) {
+      if (is_nar) gemm_tile<EPI, PART, 1>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
+      else gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
+    } else {
+      (void)is_nar;
       gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
+    }
   }
 }
 
@@ -686,7 +692,19 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(GemmArgs g) {
 // Host side
 // ---------------------------------------------------------------------------------------
 int ffn_tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM; }
-int ffn_narrow_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM / 2 : 0; }
+// Narrow tiles pay where an expert's last m-tile is a large share of its work: experts of at
+// most two full m-tiles on average (A / E <= 512 rows). With more rows per expert they save
+// little, and the narrow shape's registers slow the full tiles of the same kernel.
+int ffn_narrow_rows(const moe_config& c) {
+  return (c.dtype == MOE_BF16 && c.n_tokens * c.top_k <= 512LL * c.n_experts) ? kBM / 2 : 0;
+}
+
+// A bf16 grouped GEMM launch: the instantiation with narrow tiles when the table may hold them.
+template <int EPI, int PART = 0>
+void launch_bf16_gemm(bool narrow, int grid, const GemmArgs& g, hipStream_t stream) {
+  if (narrow) expert_gemm_bf16_kernel<EPI, PART, true><<<grid, kGemmThreads, 0, stream>>>(g);
+  else expert_gemm_bf16_kernel<EPI, PART, false><<<grid, kGemmThreads, 0, stream>>>(g);
+}
 
 // One persistent workgroup per CU (a multiple of 8, so every XCD gets the same count).
 int persistent_grid() {
@@ -784,8 +802,9 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
     const int grid = persistent_grid();
-    if (c.act == MOE_ACT_SWIGLU) expert_gemm_bf16_kernel<kEpiSwiglu><<<grid, kGemmThreads, 0, stream>>>(g);
-    else expert_gemm_bf16_kernel<kEpiGelu><<<grid, kGemmThreads, 0, stream>>>(g);
+    const bool nar = ffn_narrow_rows(c) > 0;
+    if (c.act == MOE_ACT_SWIGLU) launch_bf16_gemm<kEpiSwiglu>(nar, grid, g, stream);
+    else launch_bf16_gemm<kEpiGelu>(nar, grid, g, stream);
   } else {
     dim3 grid(mt, (c.d_ff + kFBN - 1) / kFBN);
     if (c.act == MOE_ACT_SWIGLU) expert_gemm_f32_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
@@ -811,14 +830,14 @@ hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, c
     g.n_tiles_n = (c.d_model + 255) / 256;
     const int grid = persistent_grid();
     if (!tail_part) {
-      expert_gemm_bf16_kernel<kEpiDown><<<grid, kGemmThreads, 0, stream>>>(g);
+      launch_bf16_gemm<kEpiDown>(ffn_narrow_rows(c) > 0, grid, g, stream);
     } else {
       // whole rounds of tiles, then the last partial round cut along K so that it fills the
       // chip, then the fixed-order sum of the pieces with the epilogue
       g.partial = tail_part;
       g.grid = grid;
-      expert_gemm_bf16_kernel<kEpiDown, 1><<<grid, kGemmThreads, 0, stream>>>(g);
-      expert_gemm_bf16_kernel<kEpiDown, 2><<<grid, kGemmThreads, 0, stream>>>(g);
+      launch_bf16_gemm<kEpiDown, 1>(ffn_narrow_rows(c) > 0, grid, g, stream);
+      launch_bf16_gemm<kEpiDown, 2>(ffn_narrow_rows(c) > 0, grid, g, stream);
       tail_reduce_kernel<<<dim3(grid, kBM / 4), 256, 0, stream>>>(g);
     }
   } else {
@@ -856,10 +875,10 @@ hipError_t launch_up_save(const moe_config& c, const int* tiles, const void* a, 
   g.n_out = n_out;
   if (c.act == MOE_ACT_SWIGLU) {
     g.n_tiles_n = (n_out + 127) / 128;
-    expert_gemm_bf16_kernel<kEpiSwigluSave><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+    launch_bf16_gemm<kEpiSwigluSave>(ffn_narrow_rows(c) > 0, persistent_grid(), g, stream);
   } else {
     g.n_tiles_n = (n_out + 255) / 256;
-    expert_gemm_bf16_kernel<kEpiGeluSave><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+    launch_bf16_gemm<kEpiGeluSave>(ffn_narrow_rows(c) > 0, persistent_grid(), g, stream);
   }
   return hipGetLastError();
 }

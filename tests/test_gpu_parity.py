@@ -139,6 +139,7 @@ def test_dispatch_flags_bad_ids():
     ("bf16", "gelu", True, 1000, 6, 256, 392, 2),
     ("bf16", "gelu", False, 389, 3, 72, 136, 0),
     ("bf16", "swiglu", False, 1300, 16, 128, 96, 9),
+    ("bf16", "swiglu", False, 3000, 4, 136, 264, 0),   # > 512 rows per expert: no narrow tiles
     ("f32", "gelu", True, 500, 4, 64, 256, 1),
     ("f32", "swiglu", False, 333, 7, 40, 72, 3),
 ])
@@ -168,7 +169,7 @@ def test_expert_ffn(dtype, act, bias, rows, E, d, f, empty):
 
 
 BOUNDARY_COUNTS = [0, 1, 127, 128, 129, 255, 256, 257, 384, 385, 640]   # 6 of 15 m-tiles narrow
-FEW_NARROW_COUNTS = [1000, 700, 513, 100, 0, 900]                       # 2 of 15
+FEW_NARROW_COUNTS = [1000, 700, 513, 100, 0, 900, 0, 0]                 # 2 of 15
 
 
 @pytest.mark.parametrize("act,bias,d,f,counts", [("swiglu", False, 200, 600, BOUNDARY_COUNTS),
@@ -176,9 +177,10 @@ FEW_NARROW_COUNTS = [1000, 700, 513, 100, 0, 900]                       # 2 of 1
                                                  ("swiglu", False, 136, 520, FEW_NARROW_COUNTS)])
 def test_expert_ffn_tile_boundaries(act, bias, d, f, counts):
     """Per-expert row counts on both sides of the 128-row (narrow tile) and 256-row (full
-    tile) boundaries; widths off both tile grids and K not a multiple of 32. The down
-    projection's rounds are all tail, so its K pieces of narrow tiles are summed too; with
-    few narrow m-tiles it runs them with the full shape instead."""
+    tile) boundaries; widths off both tile grids and K not a multiple of 32 (at most 512 rows
+    per expert on average, so narrow tiles are in use). The down projection's rounds are all
+    tail, so its K pieces of narrow tiles are summed too; with few narrow m-tiles it runs them
+    with the full shape instead."""
     counts = np.array(counts)
     rows, E = int(counts.sum()), len(counts)
     say(f"[ffn tiles] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
