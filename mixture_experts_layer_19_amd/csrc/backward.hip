@@ -30,7 +30,6 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 512, kStages = 4;
-constexpr int kGM = 8, kGN = 4;          // supertile: 8 m-tiles x 4 n-tiles (m fastest)
 constexpr int kStageStride = 72;         // epilogue staging row (floats, 64 columns + 8): the
                                          // two half-waves, 4 rows apart, hit disjoint banks
 
@@ -78,16 +77,6 @@ struct BwdGemm {
   float* part;          // [rows][n_part] or null
   int n_part;
 };
-
-MOE_DEV void supertile(long long l, int me, int NT, int* mt, int* nt) {
-  const int band = (int)(l / ((long long)kGM * NT));
-  const int lb = (int)(l - (long long)band * kGM * NT);
-  const int bm = min(kGM, me - kGM * band);
-  const int grpn = lb / (kGN * bm);
-  const int r = lb - grpn * kGN * bm;
-  *mt = kGM * band + r % bm;
-  *nt = grpn * kGN + r / bm;
-}
 
 MOE_DEV float gelu_grad(float a) {
   return 0.5f * (1.0f + erff(a * 0.70710678118654752440f)) + a * 0.39894228040143267794f * expf(-0.5f * a * a);

@@ -106,7 +106,6 @@ struct GemmArgs {
 // LDS once they have landed.
 // ---------------------------------------------------------------------------------------
 constexpr int kBM = 256, kBNB = 256, kBK = 32;
-constexpr int kGM = 8, kGN = 4;
 constexpr int kStageElems = kBM * kBK;  // bf16 elements of one 16 KiB LDS array
 constexpr int kGemmThreads = 512;
 
@@ -140,18 +139,6 @@ MOE_DEV long long narrow_tail(const int* tiles, int NT, bool nar, int grid) {
   return min(S_nar, S - S / grid * grid);
 }
 
-// Supertile order over a group of `me` m-tiles starting at index ts: local item l -> (m-tile
-// index within the group, n-tile); kGM m-tiles x kGN n-tiles, m fastest.
-MOE_DEV void ffn_supertile(long long l, int me, int NT, int* m, int* nt) {
-  const int band = (int)(l / ((long long)kGM * NT));
-  const int lb = (int)(l - (long long)band * kGM * NT);
-  const int bm = min(kGM, me - kGM * band);
-  const int grpn = lb / (kGN * bm);
-  const int r = lb - grpn * kGN * bm;
-  *m = kGM * band + r % bm;
-  *nt = grpn * kGN + r / bm;
-}
-
 // Work item u (0 <= u < gemm_items): its m-tile (expert, first row, rows) and n-tile; returns
 // whether it is narrow. Without narrow tiles the items are expert-major, then in supertiles
 // of the expert's m-tiles. With them, the full m-tiles (fmap) are ordered that way; the last
@@ -165,7 +152,7 @@ MOE_DEV bool decode_tile(const int* tiles, long long u, int NT, bool use_nar, lo
   if (!use_nar) {
     const int* probe = T + kTileInts * (int)(u / NT);
     const int ts = probe[3];
-    ffn_supertile(u - (long long)ts * NT, probe[4], NT, &m, nt);
+    supertile(u - (long long)ts * NT, probe[4], NT, &m, nt);
     t = ts + m;
   } else {
     const int NT2 = (NT + 1) >> 1;
@@ -190,7 +177,7 @@ MOE_DEV bool decode_tile(const int* tiles, long long u, int NT, bool use_nar, lo
       const long long s = u - nb;  // full item
       const int* probe = T + kTileInts * fmap[(int)(s / NT)];
       const int fs = probe[5];
-      ffn_supertile(s - (long long)fs * NT, probe[6], NT, &m, nt);
+      supertile(s - (long long)fs * NT, probe[6], NT, &m, nt);
       t = fmap[fs + m];
     }
     const int* q = T + kTileInts * t;

@@ -82,6 +82,20 @@ MOE_DEV int tail_pieces(long long s_tail, int nk_all, int grid) {
   return (int)max(1ll, min(q, (long long)(nk_all / 4)));
 }
 
+// Supertile order of a group of `me` m-tiles with NT n-tiles each: bands of kGM m-tiles, each
+// walked in groups of kGN n-tiles with the m-tile fastest, so the tiles that run at the same
+// time share A and B panels in L2. Local item l -> (m-tile within the group, n-tile).
+constexpr int kGM = 8, kGN = 4;
+MOE_DEV void supertile(long long l, int me, int NT, int* mt, int* nt) {
+  const int band = (int)(l / ((long long)kGM * NT));
+  const int lb = (int)(l - (long long)band * kGM * NT);
+  const int bm = min(kGM, me - kGM * band);
+  const int grpn = lb / (kGN * bm);
+  const int r = lb - grpn * kGN * bm;
+  *mt = kGM * band + r % bm;
+  *nt = grpn * kGN + r / bm;
+}
+
 // Builds the tile table with one workgroup of at least E threads (thread e owns expert e).
 // lo_e / hi_e are expert e's row range; ranges outside [0, rows] or decreasing are clamped,
 // the list is capped at max_tiles (so no access leaves the buffers) and *bad is set.
