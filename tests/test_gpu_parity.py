@@ -203,6 +203,36 @@ def test_expert_ffn_tile_boundaries(act, bias, d, f, counts):
     say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
 
 
+@pytest.mark.parametrize("offs", [[0, 700, 300, 1000, 1000],        # a decreasing range
+                                  [0, 400, 1200, 1000, 1000],       # a range past the rows
+                                  [0, 1000, 0, 1000, 0, 1000, 0]])  # overlapping ranges: table overflows
+def test_expert_ffn_bad_offsets(offs):
+    """Malformed offsets are clamped on the device (no access leaves the buffers) and reported
+    as MOE_ERR_INVALID_ARG; a valid call afterwards on the same workspace is exact again."""
+    rows, E, d, f = 1000, len(offs) - 1, 64, 128
+    say(f"[ffn bad offsets] {offs}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act="swiglu", dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_bad", cfg, weight_std=0.1), seed=7)
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=7)
+    ws = B.workspace(cfg, B.Op.EXPERT_FFN)
+    bad = torch.tensor(offs, dtype=torch.int32).cuda()
+    B.moe_expert_ffn(cfg, xs, bad, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], ws=ws)
+    assert B.moe_get_device_error(ws) == B.MOE_ERR_INVALID_ARG
+    counts = W.random_counts(rows, E, seed=7)
+    good = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    ys = B.moe_expert_ffn(cfg, xs, good, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], ws=ws)
+    assert B.moe_get_device_error(ws) == B.MOE_OK
+    p = oracle_params(inp)
+    x64, off = f64(xs), good.cpu().numpy()
+    ref = np.zeros((rows, d))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            ex = {n: (None if p[n] is None else p[n][e]) for n in ("w1", "w2", "w3", "b1", "b2")}
+            ref[lo:hi] = O.expert_ffn(x64[lo:hi], "swiglu", **ex)
+    assert_close_rel(f64(ys), ref, TOL["bf16"], "y_sorted after bad offsets")
+
+
 @pytest.mark.parametrize("dtype,N,k,d", [("bf16", 1000, 2, 256), ("bf16", 77, 8, 7168), ("f32", 300, 3, 64)])
 def test_combine(dtype, N, k, d):
     cfg = B.LayerConfig(N, d, max(k, 8), k, 64, dtype=dtype)
