@@ -193,39 +193,129 @@ MOE_DEV bool decode_tile(const int* tiles, long long u, int NT, bool use_nar, lo
   return false;
 }
 
+// A wave's share of a tile's operand copies into the LDS stages (full or narrow shape):
+// stage j holds A at sa(j) and B at sb(j); copy instruction i of the wave fills 16 rows of a
+// stage, lane l writing row (l >> 2) of them at physical chunk l & 3, which holds the logical
+// chunk (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
+template <int EPI, int NAR>
+struct TileLoads {
+  static constexpr int TBM = NAR ? 128 : 256;           // tile rows
+  static constexpr int TBN = NAR ? 512 : 256;           // tile B-rows
+  static constexpr int CA = TBM / 128, CB = TBN / 128;  // copies of A / B per wave and slab
+  static constexpr int CPR = CA + CB;                   // copies per refill
+  static constexpr int kCols = kSwi<EPI> ? TBN / 2 : TBN;  // output columns per tile
+  // uniform bases (bytes) and 32-bit per-lane offsets of the wave's A and B copies of a tile
+  struct Src {
+    const char* a;
+    const char* b[CB];
+    uint32_t ao[CA], bo[CB];
+  };
+  const GemmArgs& g;
+  uint16_t* smem;
+  int wave, lrow, lchunk;
+  MOE_DEV TileLoads(const GemmArgs& g_, uint16_t* smem_, int wave_, int lane)
+      : g(g_), smem(smem_), wave(wave_), lrow(lane >> 2), lchunk(((lane & 3) ^ ((lane >> 4) & 3)) * 8) {}
+  MOE_DEV uint16_t* sa(int j) const {
+    return NAR ? smem + 8 * kStageElems + j * (kStageElems / 2) : smem + 2 * j * kStageElems;
+  }
+  MOE_DEV uint16_t* sb(int j) const { return NAR ? smem + 2 * j * kStageElems : smem + (2 * j + 1) * kStageElems; }
+  MOE_DEV Src src(int e, int row0, int rows, int nt) const {
+    const int K = g.K, n_out = g.n_out, n0 = nt * kCols;
+    Src r;
+    r.a = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
+    const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
+    const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
+      r.ao[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int rr = (wave * CB + i) * 16 + lrow;  // B-row 0 .. TBN-1
+      int cl;  // B-row's output column relative to n0
+      if (kSwi<EPI>) {
+        // B-rows 64 c .. 64 c + 31: gate of columns 32 c ..; the next 32: up of the same
+        cl = (rr >> 6) * 32 + (rr & 31);
+        r.b[i] = ((((wave * CB + i) * 16) & 63) >= 32) ? b1_base : b0_base;  // uniform per copy
+      } else {
+        cl = rr;
+        r.b[i] = b0_base;
+      }
+      r.bo[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
+    }
+    return r;
+  }
+  // byte offset of reduction index k0 for this lane; lanes past K read inside the row (their
+  // chunks are zeroed once they have landed)
+  MOE_DEV uint32_t dma_k(int k0) const {
+    const int K = g.K;
+    return ((K % kBK) != 0 && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
+  }
+  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) at byte offset ka into stage j
+  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka) const {
+    const bool is_a = NAR ? c == 0 : (c & 1) == 0;
+    const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
+    if (is_a) lds_dma16(sr.a + sr.ao[i] + ka, sa(j) + (wave * CA + i) * 16 * kBK);
+    else lds_dma16(sr.b[i] + sr.bo[i] + ka, sb(j) + (wave * CB + i) * 16 * kBK);
+  }
+  // every copy of slab k (from the start of K) into stage j
+  MOE_DEV void refill(const Src& sr, int j, int k) const {
+    const uint32_t ka = dma_k(k * kBK);
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) copy(sr, c, j, ka);
+  }
+};
+
+// Global store instructions each wave issues in the epilogue of a tile whose rows and columns
+// are all in range: 4 row blocks x 2 halves x the flushes of a half (one per output array:
+// SwiGLU saving keeps gate and up pre-activations and the result, GELU saving the
+// pre-activation and the result) x 16-byte chunks per lane (a 64-column half: 2, 32: 1).
+template <int EPI> constexpr int kStores =
+    8 * (EPI == kEpiSwigluSave ? 3 : EPI == kEpiGeluSave ? 2 : 1) * (kSwi<EPI> ? 1 : 2);
+
 // One work item: tile (e, row0, rows, nt) over slabs [kso, kso + nk) of nk_all; NAR picks the
 // narrow shape. PART 2 with q > 1 writes this item's float32 partial tile (item w).
-template <int EPI, int PART, int NAR>
-MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int e, int row0, int rows, int nt,
-                       int kso, int nk, int nk_all, long long w, int q) {
-  constexpr int TBM = NAR ? 128 : 256;            // tile rows
-  constexpr int TBN = NAR ? 512 : 256;            // tile B-rows
+//
+// DEFER (full shape, whole-K items): the next item of the workgroup, s_next (-1: none), is
+// decoded once this item's slabs are done (returned in *ne, *nrow0, *nrows, *nnt). When this
+// tile's rows and columns are all in range (and nk >= NST), the next item's first NST - 1
+// stages are issued before this item's epilogue stores, so that those stores drain while
+// the next item starts instead of before it; the next item then runs with RLX: its first
+// stages were issued by the previous item, followed by exactly kStores<EPI> stores that may
+// still be in flight. Without RLX an item issues its own first stages. Returns for the next
+// item: 2 = RLX, 1 = not.
+template <int EPI, int PART, int NAR, bool DEFER = false, bool RLX = false>
+MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int e, int row0, int rows, int nt,
+                      int kso, int nk, int nk_all, long long w, int q, long long s_next = -1, int NT = 0,
+                      int* ne = nullptr, int* nrow0 = nullptr, int* nrows = nullptr, int* nnt = nullptr) {
+  using TL = TileLoads<EPI, NAR>;
+  constexpr int TBM = TL::TBM, TBN = TL::TBN;
   constexpr int NST = NAR ? 4 : 5;                // LDS stages
-  constexpr int CA = TBM / 128, CB = TBN / 128;   // copies of A / B per wave and slab (16 rows each)
-  constexpr int CPR = CA + CB;                    // copies per refill
+  constexpr int CA = TL::CA, CB = TL::CB, CPR = TL::CPR;
   constexpr int kVm = (NST - 2) * CPR;            // copies a wave may leave in flight at a boundary
-  constexpr int kCols = kSwi<EPI> ? TBN / 2 : TBN;  // output columns per tile
+  constexpr int kCols = TL::kCols;                // output columns per tile
   const int K = g.K, n_out = g.n_out;
   const int grp = wave >> 2;                                        // ping-pong group
   const int wm = NAR ? 0 : (wave & 1);                              // 128-row block of the tile
   const int wc = NAR ? wave : grp * 2 + ((wave >> 1) & 1);          // 64-B-row block
   const bool k_tail = (K % kBK) != 0;
-  // stage j: A at sa(j), B at sb(j)
-  auto sa = [&](int j) -> uint16_t* { return NAR ? smem + 8 * kStageElems + j * (kStageElems / 2) : smem + 2 * j * kStageElems; };
-  auto sb = [&](int j) -> uint16_t* { return NAR ? smem + 2 * j * kStageElems : smem + (2 * j + 1) * kStageElems; };
-  // epilogue only: this tile's per-row gates (down projection) and per-column biases
-  float* s_gate = reinterpret_cast<float*>(smem + 8 * kStageElems);
+  static_assert(!DEFER || (!NAR && PART != 2), "deferred stores: full shape, whole-K items");
+  static_assert(DEFER || !RLX, "relaxed waits follow deferred stores");
+  // Epilogue LDS (arrays 8 and 9, the last full stage, not refilled before the next item's
+  // first barrier): each wave's 16-row staging buffer, then this tile's per-row gates (down
+  // projection) and per-column biases.
+  constexpr int kStageBuf = 16 * 72;  // elements of a wave's staging buffer (16 padded rows)
+  float* s_gate = reinterpret_cast<float*>(smem + 8 * kStageElems + 8 * kStageBuf);
   float* s_bias = s_gate + kBM;
 
   // The lane index is made opaque per tile: otherwise the compiler hoists every
   // lane-dependent address out of the tile loop and spills them across it.
   int lane = tid & 63;
   asm volatile("" : "+v"(lane));
-  // Load geometry: copy instruction i of this wave fills 16 LDS rows of a stage; lane l
-  // writes row (l >> 2) of them at physical chunk l & 3, which holds the logical chunk
-  // (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
-  const int lrow = lane >> 2;
-  const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  const TL L(g, smem, wave, lane);
+  auto sa = [&](int j) { return L.sa(j); };
+  auto sb = [&](int j) { return L.sb(j); };
   // MFMA operand reads: row (lane & 31) of a 32-row block, logical chunk 2 ks + (lane >> 5),
   // physical chunk = logical ^ ((row >> 2) & 3); element offsets for ks = 0, 1.
   int rdk[2];
@@ -235,49 +325,22 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
   const int b_rd = wc * 64 * kBK;
   const int n0 = nt * kCols;
 
-  // uniform bases (bytes) and 32-bit per-lane offsets of this wave's A and B copies
-  const char* a_base = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
-  const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
-  const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
-  uint32_t a_off[CA], b_off[CB];
-  const char* b_src[CB];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
-    a_off[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
-  }
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int rr = (wave * CB + i) * 16 + lrow;  // B-row 0 .. TBN-1
-    int cl;  // B-row's output column relative to n0
-    if (kSwi<EPI>) {
-      // B-rows 64 c .. 64 c + 31: gate of columns 32 c ..; the next 32: up of the same
-      cl = (rr >> 6) * 32 + (rr & 31);
-      b_src[i] = ((((wave * CB + i) * 16) & 63) >= 32) ? b1_base : b0_base;  // uniform per copy
-    } else {
-      cl = rr;
-      b_src[i] = b0_base;
-    }
-    b_off[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
-  }
-  auto dma_k = [&](int k0) -> uint32_t {  // lanes past K read inside the row (zeroed later)
-    return (k_tail && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
-  };
-  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) of slab-offset ka into stage j
-  auto copy = [&](int c, int j, uint32_t ka) {
-    const bool is_a = NAR ? c == 0 : (c & 1) == 0;
-    const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
-    if (is_a) lds_dma16(a_base + a_off[i] + ka, sa(j) + (wave * CA + i) * 16 * kBK);
-    else lds_dma16(b_src[i] + b_off[i] + ka, sb(j) + (wave * CB + i) * 16 * kBK);
-  };
+  // Refills issued since the previous item's epilogue stores, while fewer than 3 (RLX): a
+  // boundary then leaves those stores in flight (kVm + kStores<EPI>). That wait still covers
+  // what the plain kVm covers, every copy but the last three refills, as the stores were
+  // issued after all but those refills; with 3 refills after them it needs them done. The
+  // count is a compile-time constant at every boundary (the first NST slabs are peeled).
+  int relax = RLX ? 3 : 0;
+  const typename TL::Src cur = L.src(e, row0, rows, nt);
+  auto copy = [&](int c, int j, uint32_t ka) { L.copy(cur, c, j, ka); };
+  auto dma_k = [&](int k0) { return L.dma_k(k0); };
   auto refill = [&](int j, int slab) {
-    const uint32_t ka = dma_k((kso + slab) * kBK);
-#pragma unroll
-    for (int c = 0; c < CPR; ++c) copy(c, j, ka);
+    L.refill(cur, j, kso + slab);
+    relax -= relax > 0;
   };
   // zero this wave's copied chunks of the last slab that lie past K (after they landed)
   auto zero_tail = [&](int j, int slab) {
-    if (!k_tail || kso + slab != nk_all - 1 || (kso + slab) * kBK + lchunk < K) return;
+    if (!k_tail || kso + slab != nk_all - 1 || (kso + slab) * kBK + L.lchunk < K) return;
 #pragma unroll
     for (int i = 0; i < CA; ++i)
       *reinterpret_cast<uint4*>(sa(j) + (wave * CA + i) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);
@@ -312,7 +375,8 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
   // tail is zeroed here, once every wave's copies of it have landed), or -1: none
   auto boundary = [&](int j, int next) {
     __builtin_amdgcn_sched_barrier(0);  // the phase's multiplies / reads stay in the phase
-    wait_vm_lds<kVm>();
+    if (relax > 0) wait_vm_lds<kVm + kStores<EPI>>();
+    else wait_vm_lds<kVm>();
     if (next >= 0) zero_tail(j, next);
     wait_vm_lds<63>();
     stage_barrier();
@@ -333,6 +397,7 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
           __builtin_amdgcn_sched_barrier(0);
         }
     }
+    relax -= relax > 0;
   };
   // Slab k lives in stage k mod NST. Each group runs its own straight-line loop; both pass
   // the same sequence of barriers (two per slab plus one before the first):
@@ -354,13 +419,20 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
     multiply_refill(j, min(k + NST, nk - 1));
     boundary((j + 1) % NST, -1);
   };
+  if (!RLX) {
 #pragma unroll
-  for (int j = 0; j < NST - 1; ++j) refill(j, min(j, nk - 1));
+    for (int j = 0; j < NST - 1; ++j) refill(j, min(j, nk - 1));
+  }
   boundary(0, 0);
   int kt = 0;
   if (grp == 0) {
     read_slab(0);
     boundary(0, -1);
+    if (RLX) {
+#pragma unroll
+      for (int j = 0; j < NST; ++j) g0_step(j, j, j == NST - 1);
+      kt = NST;
+    }
     for (; kt + NST <= nk; kt += NST) {
 #pragma unroll
       for (int j = 0; j < NST; ++j) g0_step(j, kt + j, j == NST - 1);
@@ -371,6 +443,11 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
   } else {
     refill(NST - 1, min(NST - 1, nk - 1));
     boundary(0, -1);
+    if (RLX) {
+#pragma unroll
+      for (int j = 0; j < NST; ++j) g1_step(j, j);
+      kt = NST;
+    }
     for (; kt + NST <= nk; kt += NST) {
 #pragma unroll
       for (int j = 0; j < NST; ++j) g1_step(j, kt + j);
@@ -398,8 +475,14 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
           const int col = wc * 64 + j * 32 + (lane & 31);
           pt[row * TBN + col] = acc[i][j][v];
         }
-    return;
+    return 0;
   }
+  // the next item (its tile table entry is read with nothing else in flight), and whether
+  // its first stages go ahead of this tile's stores (every store then has live lanes, so
+  // each wave issues exactly kStores<EPI> of them)
+  const bool has_next = DEFER && s_next >= 0;
+  if (has_next) decode_tile(g.tiles, s_next, NT, false, 0, ne, nrow0, nrows, nnt);
+  const bool pre_issue = has_next && rows == TBM && n0 + kCols <= n_out && nk_all >= NST;
 
   // per-row gate and per-column bias of the tile, staged once in LDS for the epilogue
   // (1 and 0 when absent, so the epilogue has no branches)
@@ -408,27 +491,36 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
   if (tid < kCols)
     s_bias[tid] = (!kSwi<EPI> && g.bias && n0 + tid < n_out)
                       ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
+  // the next item's first stages (arrays 0..7), behind the loads above and ahead of the stores
+  if (pre_issue) {
+    const typename TL::Src nx = L.src(*ne, *nrow0, *nrows, *nnt);
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j) L.refill(nx, j, min(j, nk_all - 1));
+  }
   __syncthreads();
 
-  // ---- epilogue: activation / bias / gate in registers, then per 32-row block the wave's
-  // bf16 rows are staged in its own LDS buffer (rows padded by 16 bytes: the two
-  // half-waves, 4 rows apart, hit disjoint banks) and written with 16-byte row stores.
+  // ---- epilogue: activation / bias / gate in registers, then per 16-row half of a 32-row
+  // block the wave's bf16 rows are staged in its own LDS buffer (rows padded by 16 bytes: the
+  // two half-waves, 4 rows apart, hit disjoint banks) and written with 16-byte row stores.
   uint16_t* C = static_cast<uint16_t*>(g.c);
   constexpr int kWCols = kSwi<EPI> ? 32 : 64;               // wave output columns
   constexpr int kStride = kWCols + 8;                       // staged row length (elements)
   constexpr int kWChunks = kWCols / 8;                      // 16-byte chunks per row
-  uint16_t* stage = smem + wave * kStageElems;              // LDS arrays 0..7, one per wave
+  static_assert(16 * kStride <= kStageBuf, "staging buffer");
+  uint16_t* stage = smem + 8 * kStageElems + wave * kStageBuf;
   const int col_base = n0 + wc * kWCols;                    // first output column of the wave
-  // lane's element in a 32 x 32 block: column lane & 31, rows 8 g + 4 (lane >> 5) + r
+  // lane's element v (8 h <= v < 8 h + 8) of a 32 x 32 block, in half h: column lane & 31,
+  // staged row 8 ((v >> 2) & 1) + 4 (lane >> 5) + (v & 3)
   uint16_t* st_lane = stage + ((lane >> 5) * 4) * kStride + (lane & 31);
-  // each lane stores whole 16-byte chunks of the block's 32 staged rows to dst (row pitch
+  auto srow = [](int v) { return ((v >> 2) & 1) * 8 + (v & 3); };
+  // each lane stores whole 16-byte chunks of the half's 16 staged rows to dst (row pitch
   // `pitch` elements, first column col_base)
-  auto flush = [&](int i, uint16_t* dst, size_t pitch) {
+  auto flush = [&](int i, int h, uint16_t* dst, size_t pitch) {
 #pragma unroll
-    for (int it = 0; it < 32 * kWChunks / 64; ++it) {
+    for (int it = 0; it < 16 * kWChunks / 64; ++it) {
       const int idx = it * 64 + lane;
       const int prow = idx / kWChunks, ch = idx % kWChunks;
-      const int trow = wm * 128 + i * 32 + prow;
+      const int trow = wm * 128 + i * 32 + h * 16 + prow;
       const int col = col_base + ch * 8;
       const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
       if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + (size_t)(row0 + trow) * pitch + col) = val;
@@ -436,65 +528,71 @@ MOE_DEV void gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int
   };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (EPI == kEpiSwigluSave) {
-      // gate pre-activation, up pre-activation, then w_a silu(g) u, one staging pass each
-      uint16_t* C2 = static_cast<uint16_t*>(g.c2);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][0][v]);
-      flush(i, C2, 2 * (size_t)n_out);
+    for (int h = 0; h < 2; ++h) {
+      // the gate of the lane's row of element v
+      auto gate_of = [&](int v) { return s_gate[wm * 128 + i * 32 + h * 16 + srow(v) + (lane >> 5) * 4]; };
+      if (EPI == kEpiSwigluSave) {
+        // gate pre-activation, up pre-activation, then w_a silu(g) u, one staging pass each
+        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) st_lane[((v >> 2) * 8 + (v & 3)) * kStride] = f32_to_bf16(acc[i][1][v]);
-      flush(i, C2 + n_out, 2 * (size_t)n_out);
+        for (int v = 8 * h; v < 8 * h + 8; ++v) st_lane[srow(v) * kStride] = f32_to_bf16(acc[i][0][v]);
+        flush(i, h, C2, 2 * (size_t)n_out);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int prow = (v >> 2) * 8 + (v & 3);
-        const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
-        st_lane[prow * kStride] = f32_to_bf16(gs * (silu_f(acc[i][0][v]) * acc[i][1][v]));
-      }
-      flush(i, C, n_out);
-    } else if (EPI == kEpiGeluSave) {
-      // pre-activation (with b1), then w_a gelu(.)
-      uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+        for (int v = 8 * h; v < 8 * h + 8; ++v) st_lane[srow(v) * kStride] = f32_to_bf16(acc[i][1][v]);
+        flush(i, h, C2 + n_out, 2 * (size_t)n_out);
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
+        for (int v = 8 * h; v < 8 * h + 8; ++v)
+          st_lane[srow(v) * kStride] = f32_to_bf16(gate_of(v) * (silu_f(acc[i][0][v]) * acc[i][1][v]));
+        flush(i, h, C, n_out);
+      } else if (EPI == kEpiGeluSave) {
+        // pre-activation (with b1), then w_a gelu(.)
+        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          st_lane[((v >> 2) * 8 + (v & 3)) * kStride + j * 32] =
-              f32_to_bf16(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]);
-      flush(i, C2, n_out);
+        for (int v = 8 * h; v < 8 * h + 8; ++v)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int prow = (v >> 2) * 8 + (v & 3);
-        const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+          for (int j = 0; j < 2; ++j)
+            st_lane[srow(v) * kStride + j * 32] =
+                f32_to_bf16(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]);
+        flush(i, h, C2, n_out);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          st_lane[prow * kStride + j * 32] =
-              f32_to_bf16(gs * gelu_erf(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]));
-      }
-      flush(i, C, n_out);
-    } else {
+        for (int v = 8 * h; v < 8 * h + 8; ++v) {
+          const float gs = gate_of(v);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int prow = (v >> 2) * 8 + (v & 3);  // block row, minus 4 (lane >> 5)
-        if (EPI == kEpiSwiglu) {
-          st_lane[prow * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
-        } else {
-          const float gs = s_gate[wm * 128 + i * 32 + prow + (lane >> 5) * 4];
+          for (int j = 0; j < 2; ++j)
+            st_lane[srow(v) * kStride + j * 32] =
+                f32_to_bf16(gs * gelu_erf(acc[i][j][v] + s_bias[wc * kWCols + j * 32 + (lane & 31)]));
+        }
+        flush(i, h, C, n_out);
+      } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float bj = s_bias[wc * kWCols + j * 32 + (lane & 31)];
-            float val;
-            if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
-            else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
-            st_lane[prow * kStride + j * 32] = f32_to_bf16(val);
+        for (int v = 8 * h; v < 8 * h + 8; ++v) {
+          if (EPI == kEpiSwiglu) {
+            st_lane[srow(v) * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+          } else {
+            const float gs = gate_of(v);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const float bj = s_bias[wc * kWCols + j * 32 + (lane & 31)];
+              float val;
+              if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
+              else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
+              st_lane[srow(v) * kStride + j * 32] = f32_to_bf16(val);
+            }
           }
         }
+        flush(i, h, C, n_out);
       }
-      flush(i, C, n_out);
+      __builtin_amdgcn_sched_barrier(0);  // keep each half block's registers short-lived
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep each 32-row block's registers short-lived
   }
-  __syncthreads();  // the staging area is the next tile's first stage
+  if (!DEFER) {
+    // the staging area and the gates may be a narrow tile's first stages
+    __syncthreads();
+    return 0;
+  }
+  // the next item's first barrier comes before anything refills arrays 8 and 9
+  return pre_issue ? 2 : 1;
 }
 
 // PART: 0 = every work item; 1 = only the whole rounds (the first floor(S / G) * G items of
@@ -524,6 +622,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
   const long long w_end = (PART == 2) ? (S_all - S_main) * q : min(S_main, (long long)xcd * chunk + chunk);
   const int w_step = (PART == 2) ? (int)gridDim.x : per_xcd;
 
+  if constexpr (!NAR && PART != 2) {
+    // full-shape, whole-K items: each item issues the next one's first stages before its
+    // epilogue stores (gemm_tile, DEFER)
+    if (w_begin >= w_end) return;
+    int e, row0, rows, nt;
+    decode_tile(g.tiles, w_begin, NT, false, 0, &e, &row0, &rows, &nt);
+    int pre = 1;
+    for (long long w = w_begin;; w += w_step) {
+      int wave_i = wave, NT_i = NT;
+      asm volatile("" : "+s"(wave_i), "+s"(NT_i));
+      const int tid_i = wave_i * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const long long w2 = w + w_step;
+      const long long sn = w2 < w_end ? w2 : -1;
+      int ne = 0, nrow0 = 0, nrows = 0, nnt = 0;
+      if (pre == 2)
+        pre = gemm_tile<EPI, PART, 0, true, true>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w, 1,
+                                                  sn, NT_i, &ne, &nrow0, &nrows, &nnt);
+      else
+        pre = gemm_tile<EPI, PART, 0, true, false>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w,
+                                                   1, sn, NT_i, &ne, &nrow0, &nrows, &nnt);
+      if (w2 >= w_end) break;
+      e = ne;
+      row0 = nrow0;
+      rows = nrows;
+      nt = nnt;
+    }
+  } else {
   for (long long w = w_begin; w < w_end; w += w_step) {
     long long s = w;       // work item (position in the sequence)
     int kso = 0;           // first slab of this item
@@ -549,6 +674,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       (void)is_nar;
       gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
     }
+  }
   }
 }
 

@@ -203,6 +203,43 @@ def test_expert_ffn_tile_boundaries(act, bias, d, f, counts):
     say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
 
 
+@pytest.mark.parametrize("act,bias,d,f,counts", [("swiglu", False, 1984, 1000, [6000, 5120, 7000, 6500]),
+                                                 ("gelu", True, 1000, 1984, [6000, 5120, 7000, 6500])])
+def test_expert_ffn_items_per_workgroup(act, bias, d, f, counts):
+    """Several work items per persistent workgroup in both projections (an item issues the
+    next one's first stages ahead of its own output stores), with experts ending in partial
+    m-tiles, partial last n-tiles and, for SwiGLU, a reduction length off the 32 grid. The
+    oracle computes the first, the last and one random row of every m-tile, all columns, so
+    every output tile is checked."""
+    counts = np.array(counts)
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[ffn items] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act=act, has_bias=bias, dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_items", cfg, weight_std=0.05), seed=8)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=8)
+    gate = W.random_gates(rows, 1, seed=8).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    rng = np.random.default_rng(8)
+    p = oracle_params(inp, lazy=True)
+    xs64, g64 = f64(xs), f64(gate)
+    got, want = [], []
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        sel = set()
+        for t0 in range(lo, hi, 256):
+            t1 = min(hi, t0 + 256)
+            sel |= {t0, t1 - 1, int(rng.integers(t0, t1))}
+        sel = np.array(sorted(sel))
+        ex = {n: (None if p[n] is None else p[n][e]) for n in ("w1", "w2", "w3", "b1", "b2")}
+        want.append(O.expert_ffn(xs64[sel], act, **ex) * g64[sel, None])
+        got.append(f64(ys[torch.from_numpy(sel).cuda()]))
+    err, scale = assert_close_rel(np.concatenate(got), np.concatenate(want), TOL["bf16"], "y_sorted")
+    say(f"    {sum(g.shape[0] for g in got)} rows: max|err| {err:.3e} max|y| {scale:.3e}")
+
+
 @pytest.mark.parametrize("offs", [[0, 700, 300, 1000, 1000],        # a decreasing range
                                   [0, 400, 1200, 1000, 1000],       # a range past the rows
                                   [0, 1000, 0, 1000, 0, 1000, 0]])  # overlapping ranges: table overflows
