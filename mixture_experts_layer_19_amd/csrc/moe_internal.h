@@ -163,9 +163,10 @@ MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narro
   __syncthreads();
 }
 
-// Routing launch shape. A token is handled by a group of lpt lanes (lpt = E rounded up to a
-// power of two, at most 64), each lane holding epl experts, so a wave routes 64/lpt tokens at
-// once; tokens_per_wave is a multiple of 64/lpt.
+// Routing launch shape. A token is handled by a group of lpt lanes (a power of two: E rounded
+// up to one for E <= 64; else 8 to 64, chosen by plan_route from E, k and the token count),
+// each lane holding epl experts, so a wave routes 64/lpt tokens at once; tokens_per_wave is a
+// multiple of 64/lpt.
 struct RoutePlan {
   int lpt, epl;
   int tokens_per_wave, tokens_per_block, n_blocks;

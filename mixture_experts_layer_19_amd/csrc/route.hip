@@ -529,8 +529,21 @@ RoutePlan plan_route(const moe_config& c) {
   RoutePlan p{};
   const long long N = c.n_tokens;
   const int E = c.n_experts;
+  // Lanes per token (a power of two). Each of a token's k choices is an arg-max reduction
+  // over its lanes, so fewer lanes per token mean shorter cross-lane chains and more tokens
+  // side by side in a wave. Up to 64 experts a lane holds one. Beyond that a lane holds up
+  // to 16 experts, and the lanes per token shrink as long as the token groups (N lpt / 64,
+  // one wave pass each) stay at least 4096, about 16 per CU. Fewer groups leave too few
+  // waves to hide the reductions' latency: on 128 experts x 16384 tokens and 256 x 4096
+  // tokens, 4096 groups timed best of 1024 to 16384. Lane j < k of a group keeps the
+  // token's j-th choice, so a group has at least k lanes (k <= kMaxTopK <= 64).
+  const int k = c.top_k;
   p.lpt = 1;
-  while (p.lpt < E && p.lpt < kWave) p.lpt <<= 1;
+  if (E <= kWave) {
+    while (p.lpt < E) p.lpt <<= 1;
+  } else {
+    while (p.lpt < kWave && (p.lpt * 16 < E || p.lpt < k || N * p.lpt < 64ll * 4096)) p.lpt <<= 1;
+  }
   p.epl = 1;
   while (p.lpt * p.epl < E) p.epl <<= 1;
   // Tokens per wave: enough that the per-block partial arrays ([blocks][E]) stay within
@@ -641,6 +654,12 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
       case 1601: launch_tokens<16, 1>(p, ra, stream); break;
       case 3201: launch_tokens<32, 1>(p, ra, stream); break;
       case 6401: launch_tokens<64, 1>(p, ra, stream); break;
+      case 816: launch_tokens<8, 16>(p, ra, stream); break;
+      case 1608: launch_tokens<16, 8>(p, ra, stream); break;
+      case 1616: launch_tokens<16, 16>(p, ra, stream); break;
+      case 3204: launch_tokens<32, 4>(p, ra, stream); break;
+      case 3208: launch_tokens<32, 8>(p, ra, stream); break;
+      case 3216: launch_tokens<32, 16>(p, ra, stream); break;
       case 6402: launch_tokens<64, 2>(p, ra, stream); break;
       case 6404: launch_tokens<64, 4>(p, ra, stream); break;
       case 6408: launch_tokens<64, 8>(p, ra, stream); break;

@@ -296,7 +296,23 @@ def test_combine(dtype, N, k, d):
     ("softmax_topk", True, 1.0, 1000, 32, "bf16"), ("topk_softmax", True, 1.0, 5, 5, "f32"),
 ])
 def test_route(router, norm, scale, E, k, dtype):
-    N, d = 1500, 384
+    check_route(router, norm, scale, E, k, dtype, 1500, 384)
+
+
+# Token counts that give each lane layout of the routing kernel above 64 experts (lanes per
+# token x experts per lane, chosen from E, k and N): 128 experts at 8 x 16, 16 x 8 and 32 x 4,
+# 16 x 8 again with k = 16 (a group holds at least k lanes), 256 at 16 x 16 and 32 x 8, 512 at
+# 32 x 16.
+@pytest.mark.parametrize("router,E,k,N", [
+    ("softmax_topk", 128, 8, 32768), ("softmax_topk", 128, 8, 16384), ("topk_softmax", 128, 8, 8192),
+    ("softmax_topk", 128, 16, 32768), ("sigmoid", 256, 8, 16384), ("sigmoid", 256, 8, 8192),
+    ("softmax_topk", 512, 8, 8192),
+])
+def test_route_lane_layouts(router, E, k, N):
+    check_route(router, True, 1.0, E, k, "bf16", N, 128)
+
+
+def check_route(router, norm, scale, E, k, dtype, N, d):
     cfg = B.LayerConfig(N, d, E, k, 64, router=router, norm_topk=norm, routed_scaling=scale, dtype=dtype)
     wl = W.Workload("route", cfg, logit_offset="zipf1.2" if E == 128 else None,
                     sel_bias="uniform0.1" if router == "sigmoid" else None)
