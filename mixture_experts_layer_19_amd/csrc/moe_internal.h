@@ -101,6 +101,54 @@ MOE_DEV void supertile(long long l, int me, int NT, int* mt, int* nt) {
 // the list is capped at max_tiles (so no access leaves the buffers) and *bad is set.
 // An expert's rows are cut into m-tiles of bm rows; a last tile of at most `narrow` rows
 // (0: none) is narrow. s_scan: kMaxExperts ints of LDS. Every thread of the block must call it.
+// Exclusive prefix sum of v over the threads of the block in thread order (threads without
+// a value pass 0), and the block's total in *total. Every thread of the block calls it; the
+// block size is a multiple of 64. An inclusive scan within each wave by shuffles, then each
+// thread adds the totals of the waves before its own: two barriers at any block size.
+// s_tmp: one int per wave.
+MOE_DEV int block_excl_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = s_tmp[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// The same over the first E threads (v = 0 beyond), with E <= blockDim.x: up to 64 experts
+// a step-doubling scan through s_tmp (E ints; log2 E steps of two barriers, cheaper than the
+// shuffles there), beyond them block_excl_scan (s_tmp: one int per wave). Every thread of the
+// block calls it and receives *total.
+MOE_DEV int expert_excl_scan(int v, int E, int* s_tmp, int* total) {
+  if (E > 64) return block_excl_scan(v, s_tmp, total);
+  const int e = threadIdx.x;
+  if (e < E) s_tmp[e] = v;
+  __syncthreads();
+  for (int o = 1; o < E; o <<= 1) {
+    int u = 0;
+    if (e < E && e >= o) u = s_tmp[e - o];
+    __syncthreads();
+    if (e < E) s_tmp[e] += u;
+    __syncthreads();
+  }
+  const int ex = e < E ? s_tmp[e] - v : 0;
+  *total = s_tmp[E - 1];
+  __syncthreads();
+  return ex;
+}
+
 MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narrow, int max_tiles, int* tiles,
                               int* s_scan, int* bad) {
   const int e = threadIdx.x;
@@ -114,21 +162,7 @@ MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narro
     n_nar = (n > 0 && hi - lo - (n - 1) * bm <= narrow) ? 1 : 0;
   }
   // exclusive prefix over experts of v (through s_scan); *total = the sum
-  auto scan = [&](int v, int* total) -> int {
-    if (e < E) s_scan[e] = v;
-    __syncthreads();
-    for (int o = 1; o < E; o <<= 1) {
-      int u = 0;
-      if (e < E && e >= o) u = s_scan[e - o];
-      __syncthreads();
-      if (e < E) s_scan[e] += u;
-      __syncthreads();
-    }
-    const int ex = e < E ? s_scan[e] - v : 0;
-    *total = s_scan[E - 1];
-    __syncthreads();
-    return ex;
-  };
+  auto scan = [&](int v, int* total) -> int { return expert_excl_scan(e < E ? v : 0, E, s_scan, total); };
   int total, total_full, total_nar;
   const int start = scan(n, &total);
   const int fstart = scan(n - n_nar, &total_full);

@@ -63,20 +63,26 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
 
 // Router projection for E > 64 experts, bfloat16 inputs: workgroup tile 64 tokens x 64 WE
 // experts, one wave per 64 experts (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), K walked in
-// slabs of 32 that are double-buffered in LDS with the next slab prefetched in registers.
-// Sharing each x slab across the workgroup's waves and each W_g slab across its 64 tokens
-// keeps the L2 traffic near one read of x plus one read of W_g per 64 tokens. grid.z splits
-// the reduction axis as in router_gemm_bf16_kernel.
+// slabs of 128 or 64 held in LDS, with the next slab loaded into registers while this one
+// is multiplied (wider slabs than 32 took the 128-expert projection of 16384 tokens from 44
+// to 42 us and the whole routing stage from 94 to 89 us). Sharing each
+// x slab across the workgroup's waves and each W_g slab across its 64 tokens keeps the L2
+// traffic near one read of x plus one read of W_g per 64 tokens. grid.z splits the
+// reduction axis as in router_gemm_bf16_kernel.
 template <int WE>
 __global__ __launch_bounds__(64 * WE) void router_gemm_tiled_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, float* __restrict__ zpart,
     int n_tokens, int d, int n_experts, int k_chunk) {
-  constexpr int kBMr = 64, kBEr = 64 * WE, kBKr = 32, kLd = kBKr + 8;  // LDS rows of 80 bytes
+  // Slabs of 128 (64 for 256 experts, whose 87 KiB of LDS at 128 would leave one workgroup
+  // per CU). LDS rows of kBKr + 8 elements (68 or 36 dwords): 16 lanes reading 16 bytes of 16
+  // consecutive rows cover all 64 banks once.
+  constexpr int kBMr = 64, kBEr = 64 * WE, kBKr = WE == 2 ? 128 : 64, kLd = kBKr + 8;
   constexpr int kThreads = 64 * WE;
-  constexpr int kAPer = kBMr * 4 / kThreads;  // 16-byte chunks per thread per slab
-  constexpr int kBPer = kBEr * 4 / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBMr * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBEr * kLd];
+  constexpr int kCh = kBKr / 8;                // 16-byte chunks per row of a slab
+  constexpr int kAPer = kBMr * kCh / kThreads;  // 16-byte chunks per thread per slab
+  constexpr int kBPer = kBEr * kCh / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kBMr * kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kBEr * kLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kBMr, e0 = blockIdx.y * kBEr;
   const int kb = blockIdx.z * k_chunk;
@@ -88,29 +94,29 @@ __global__ __launch_bounds__(64 * WE) void router_gemm_tiled_kernel(
   auto gload = [&](int k) {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
-      const int idx = tid + i * kThreads, row = idx >> 2, kk = k + (idx & 3) * 8;
+      const int idx = tid + i * kThreads, row = idx / kCh, kk = k + (idx % kCh) * 8;
       const int t = t0 + row;
       ra[i] = (t < n_tokens && kk < ke) ? *reinterpret_cast<const uint4*>(xs + (size_t)t * d + kk)
                                         : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
-      const int idx = tid + i * kThreads, row = idx >> 2, kk = k + (idx & 3) * 8;
+      const int idx = tid + i * kThreads, row = idx / kCh, kk = k + (idx % kCh) * 8;
       const int e = e0 + row;
       rb[i] = (e < n_experts && kk < ke) ? *reinterpret_cast<const uint4*>(ws + (size_t)e * d + kk)
                                          : make_uint4(0, 0, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&]() {
 #pragma unroll
     for (int i = 0; i < kAPer; ++i) {
       const int idx = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(&sA[buf][(idx >> 2) * kLd + (idx & 3) * 8]) = ra[i];
+      *reinterpret_cast<uint4*>(&sA[(idx / kCh) * kLd + (idx % kCh) * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
       const int idx = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(&sB[buf][(idx >> 2) * kLd + (idx & 3) * 8]) = rb[i];
+      *reinterpret_cast<uint4*>(&sB[(idx / kCh) * kLd + (idx % kCh) * 8]) = rb[i];
     }
   };
 
@@ -124,32 +130,33 @@ __global__ __launch_bounds__(64 * WE) void router_gemm_tiled_kernel(
 
   if (kb < ke) {
     gload(kb);
-    lstore(0);
+    lstore();
   }
   __syncthreads();
-  int buf = 0;
   for (int k = kb; k < ke; k += kBKr) {
     const bool more = k + kBKr < ke;
     if (more) gload(k + kBKr);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kBKr / 16; ++ks) {
       bf16x8 fa[2], fb[2];
       const int kq = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(i * 32 + (lane & 31)) * kLd + kq]);
+        fa[i] = *reinterpret_cast<const bf16x8*>(&sA[(i * 32 + (lane & 31)) * kLd + kq]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wave * 64 + j * 32 + (lane & 31)) * kLd + kq]);
+        fb[j] = *reinterpret_cast<const bf16x8*>(&sB[(wave * 64 + j * 32 + (lane & 31)) * kLd + kq]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    __syncthreads();  // every wave is done reading the slab
+    if (more) {
+      lstore();
+      __syncthreads();
+    }
   }
   // lane's element v of a 32 x 32 block: column lane & 31, row 8 (v >> 2) + 4 (lane >> 5) + (v & 3)
   float* zp = zpart + (size_t)blockIdx.z * n_tokens * n_experts;
@@ -455,21 +462,15 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
   if (!a.offsets) return;  // uniform over the block
 
   // offsets: exclusive scan of the counts over the experts
-  if (tid < E) s_scan[tid] = total;
-  __syncthreads();
-  for (int o = 1; o < E; o <<= 1) {
-    const int v = (tid < E && tid >= o) ? s_scan[tid - o] : 0;
-    __syncthreads();
-    if (tid < E) s_scan[tid] += v;
-    __syncthreads();
-  }
+  int all;
+  const int ex = expert_excl_scan(tid < E ? total : 0, E, s_scan, &all);
   if (tid < E) {
-    s_off[tid] = s_scan[tid] - total;
-    a.offsets[tid] = s_scan[tid] - total;
-    if (tid == E - 1) {
-      s_off[E] = s_scan[tid];
-      a.offsets[E] = s_scan[tid];
-    }
+    s_off[tid] = ex;
+    a.offsets[tid] = ex;
+  }
+  if (tid == 0) {
+    s_off[E] = all;
+    a.offsets[E] = all;
   }
   __syncthreads();
   // per-block bases: this thread's block range continues after the earlier groups' rows
