@@ -50,6 +50,17 @@ def algorithmic(cfg):
     }
 
 
+def up_bytes(cfg, n_active):
+    """Algorithmic HBM bytes of the up projection: the weights (W1, and W3 for SwiGLU, with
+    b1) of the n_active experts that received rows, each read once, x_sorted read once and
+    the hidden activations written once."""
+    A = cfg.n_tokens * cfg.top_k
+    b = 2 if cfg.dtype == "bf16" else 4
+    m_up = 2 if cfg.act == "swiglu" else 1
+    weights = n_active * (m_up * cfg.d_ff * cfg.d_model + (cfg.d_ff if cfg.has_bias else 0)) * b
+    return weights + A * cfg.d_model * b + A * cfg.d_ff * b
+
+
 def file_sha(path):
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
@@ -326,7 +337,25 @@ def main():
     E = cfg.n_experts
     counts = out["counts"].cpu().numpy()
 
+    # The up projection's bound: its arithmetic intensity against the ridge point (peak flop
+    # rate / HBM bandwidth). Below it the kernel streams its weights (few rows per expert, as
+    # in the DeepSeek-V3 shape) and its roofline is HBM bandwidth.
+    ub = up_bytes(cfg, int((counts > 0).sum()))
+    intensity = work["up_flops"] / ub
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    up_s = stage_ms["expert_up"] * 1e-3
+    kname = "expert_gemm_bf16_kernel<SwiGLU up>" if cfg.act == "swiglu" else "expert_gemm up"
     src = os.path.join(ROOT, "mixture_experts_layer_19_amd", "csrc", "expert_ffn.hip")
+    if intensity >= ridge:
+        roof = {"kernel": kname, "bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": up_tflops / peak}
+    else:
+        gbs = ub / up_s / 1e9
+        roof = {"kernel": kname, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "tflops": up_tflops}
+    roof.update({"traffic": traffic_for(src, w.name), "flops_per_launch": work["up_flops"],
+                 "bytes_per_launch": ub, "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+                 "avg_launch_ms": stage_ms["expert_up"]})
     res = {
         "metric": "MoE layer fwd tokens/s + active TFLOP/s (% bf16 MFMA peak), 8\u00d7top-2 SwiGLU",
         "value": cfg.n_tokens / (ms_per_step * 1e-3),
@@ -353,12 +382,7 @@ def main():
             "dispatch_gbs": work["dispatch_bytes"] / (stage_ms["dispatch"] * 1e-3) / 1e9,
             "combine_gbs": work["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9,
         },
-        "roofline": {
-            "kernel": "expert_gemm_bf16_kernel<SwiGLU up>" if cfg.act == "swiglu" else "expert_gemm up",
-            "bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": up_tflops / peak, "traffic": traffic_for(src, w.name),
-            "flops_per_launch": work["up_flops"], "avg_launch_ms": stage_ms["expert_up"],
-        },
+        "roofline": roof,
         "switch_loss": float(stats[2 * E]),
         "z_loss": float(stats[2 * E + 1]),
         "expert_rows": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
