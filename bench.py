@@ -1,13 +1,15 @@
 """MoE layer benchmark on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
-                [--mode forward|backward]
+                [--mode forward|backward] [--weights tiled|rowmajor]
 
 Forward (the default): a step is one whole layer forward (moe_forward: route, dispatch,
 expert up and down projections, combine, statistics) over one batch of synthetic tokens
 already resident in HBM. Prints ONE JSON line: tokens/s plus the roofline of the dominant
 kernel (the fused gate/up expert projection) timed with HIP events that the library records
-on its own stream, and the CPU oracle timed on a bounded sample of the same workload.
+on its own stream, and the CPU oracle timed on a bounded sample of the same workload. The
+routed experts' bf16 weights are re-laid out once, before the timed region, into the grouped
+GEMM's tiled layout (moe_pack_weights); --weights rowmajor times them as given instead.
 
 Backward: a step is one moe_backward (recomputed routing, dispatch and up projection, then
 every gradient) for an upstream gradient dy of the same shape; the JSON line has the same
@@ -16,6 +18,7 @@ form, with the roofline of the backward's slowest GEMM stage.
 from __future__ import annotations
 
 import argparse
+from dataclasses import replace
 import hashlib
 import json
 import os
@@ -266,6 +269,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--weights", choices=("tiled", "rowmajor"), default="tiled",
+                    help="forward: routed experts' weights re-laid out once into the tiled layout "
+                         "(moe_pack_weights, outside the timed region) or row-major as given")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("forward", "backward", "train"), default="forward")
     ap.add_argument("--recompute", action="store_true",
@@ -310,25 +316,39 @@ def main():
         "counts": torch.empty((cfg.n_experts,), dtype=torch.int32, device=dev),
         "stats": torch.empty((2 * cfg.n_experts + 2,), dtype=torch.float32, device=dev),
     }
-    call = lambda ev=None: B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"],
-                                         inp["b1"], inp["b2"], inp["logit_bias"], inp["sel_bias"],
-                                         shared=inp["shared"], ws=ws, out=out, stage_events=ev)
-    for _ in range(args.warmup):
-        call()
-    events = [B.HipEvents(6) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(events[i].handles)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def time_forward(c, w1, w3, w2):
+        call = lambda ev=None: B.moe_forward(c, inp["x"], inp["w_router"], w1, w3, w2, inp["b1"], inp["b2"],
+                                             inp["logit_bias"], inp["sel_bias"], shared=inp["shared"], ws=ws,
+                                             out=out, stage_events=ev)
+        for _ in range(args.warmup):
+            call()
+        events = [B.HipEvents(6) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            call(events[i].handles)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        sm = {s: 0.0 for s in STAGES}
+        for ev in events:
+            for j, s in enumerate(STAGES):
+                sm[s] += ev.elapsed_ms(j, j + 1) / args.steps
+        return sm, wall * 1e3 / args.steps
 
-    stage_ms = {s: 0.0 for s in STAGES}
-    for ev in events:
-        for j, s in enumerate(STAGES):
-            stage_ms[s] += ev.elapsed_ms(j, j + 1) / args.steps
+    # bf16: the weights re-laid out once into the GEMM's tiled layout (moe_pack_weights, before
+    # the timed region, as an engine does when it loads weights), unless --weights rowmajor
+    # asks for the row-major weights as given. One layout per run, so that a kernel trace of
+    # this command times the launches the roofline reports.
+    layout = "tiled" if cfg.dtype == "bf16" and args.weights == "tiled" else "rowmajor"
+    if layout == "tiled":
+        tcfg = replace(cfg, weight_layout="tiled")
+        tw = {n: None if inp[n] is None else B.moe_pack_weights(cfg, 1 if n == "w2" else 0, inp[n])
+              for n in ("w1", "w3", "w2")}
+        torch.cuda.synchronize()
+        stage_ms, ms_per_step = time_forward(tcfg, tw["w1"], tw["w3"], tw["w2"])
+    else:
+        stage_ms, ms_per_step = time_forward(cfg, inp["w1"], inp["w3"], inp["w2"])
     fwd_ms_events = sum(stage_ms.values())
-    ms_per_step = wall * 1e3 / args.steps
     work = algorithmic(cfg)
     flops = work["router_flops"] + work["up_flops"] + work["down_flops"] + work["shared_flops"]
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -371,7 +391,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: N={cfg.n_tokens} d={cfg.d_model} E={E} k={cfg.top_k} "
                                f"d_ff={cfg.d_ff} {cfg.act} {cfg.router}{'+norm' if cfg.norm_topk else ''} {cfg.dtype}",
-                   "global_batch": cfg.n_tokens, "parallelism": "single GPU"},
+                   "global_batch": cfg.n_tokens, "parallelism": "single GPU", "weight_layout": layout},
         "active_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "active_frac_of_peak": flops / (ms_per_step * 1e-3) / 1e12 / peak,
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},

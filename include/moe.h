@@ -73,6 +73,17 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Layout of the routed experts' weights W1, W3 and W2 in moe_expert_ffn and moe_forward.
+ * ROWMAJOR: [E,N,K] as each call states (N output features, K reduction).
+ * TILED: written once by moe_pack_weights (bf16 only). Per expert, the N rows are taken in
+ * blocks of 128, and each block is stored K-slab by K-slab, 32 reduction elements at a time:
+ * element (e, n, k) sits at
+ *   e*Np*Kp + (n/128)*128*Kp + (k/32)*128*32 + (n%128)*32 + k%32,
+ * with Np = N rounded up to 128 and Kp = K rounded up to 32; the padding is zero. Each
+ * 32-wide reduction slab of a 128-row block is then one contiguous 8 KiB run, which is how
+ * the grouped GEMM reads it (same results as ROWMAJOR, bit for bit). */
+typedef enum { MOE_WEIGHTS_ROWMAJOR = 0, MOE_WEIGHTS_TILED = 1 } moe_weight_layout;
+
 /* Which call a workspace is sized for. */
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2, MOE_OP_COMBINE = 3, MOE_OP_FORWARD = 4,
@@ -95,6 +106,9 @@ typedef struct {
                            S shared experts of width f are one MLP of width S f; [RB-15] §15.4) */
   float capacity_factor; /* moe_forward only: 0 = dropless; > 0 = capacity-factor dispatch
                             (moe_dispatch_capacity) with this factor */
+  int32_t weight_layout; /* moe_weight_layout of w1, w3 and w2 (moe_expert_ffn, moe_forward);
+                            MOE_WEIGHTS_TILED needs dtype MOE_BF16, and moe_backward /
+                            moe_forward_train return MOE_ERR_UNSUPPORTED with it */
 } moe_config;
 
 /* Number of statistics floats moe_route / moe_forward write: f[E], P[E], L, z_loss. */
@@ -175,11 +189,25 @@ moe_status moe_dispatch_capacity(const moe_config* cfg, float capacity_factor, c
  *      b1 [E,d_ff] T and b2 [E,d] T (has_bias only); w2 [E,d,d_ff] T;
  *      gate_sorted [A] float32 or NULL (NULL: no scaling).
  * Out: y_sorted [A,d] T (rows at or past offsets[E] are not written).
+ * With cfg->weight_layout = MOE_WEIGHTS_TILED, w1, w3 and w2 are moe_pack_weights copies
+ * (which = 0, 0, 1); the results are the same.
  * ws: moe_workspace_size(cfg, MOE_OP_EXPERT_FFN) bytes (holds h [A,d_ff] T). */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x_sorted, const int32_t* offsets,
                           const void* w1, const void* w3, const void* b1,
                           const void* w2, const void* b2, const float* gate_sorted,
                           void* y_sorted, void* ws, size_t ws_bytes, void* stream);
+
+/* Tiled weights (MOE_WEIGHTS_TILED, layout above), for the bf16 grouped GEMMs: a once-only
+ * re-layout of static weights, done before moe_expert_ffn / moe_forward calls that read them.
+ * which = 0: W1 or W3, [E,d_ff,d] (N = d_ff, K = d); which = 1: W2, [E,d,d_ff] (N = d,
+ * K = d_ff).
+ * moe_packed_weight_size: bytes of the tiled copy, E * Np * Kp * 2; 0 when the configuration
+ * is invalid, not bf16, or which is neither 0 nor 1.
+ * moe_pack_weights: w (row-major, device, 16-byte aligned) -> w_tiled (device, 16-byte
+ * aligned, moe_packed_weight_size bytes, not overlapping w), on `stream`, padding zeroed.
+ * The caller owns both buffers. MOE_ERR_UNSUPPORTED for dtype f32. */
+size_t moe_packed_weight_size(const moe_config* cfg, int which);
+moe_status moe_pack_weights(const moe_config* cfg, int which, const void* w, void* w_tiled, void* stream);
 
 /* Combine ([L7.8] §2.2, §3): y[n] = sum_{j<k} g_{n,j} y_sorted[inv_perm[n*k+j]] (+ y_add[n]),
  * summed in float32 with j ascending, then y_add, and rounded to T once; g = topk_w [N,k]
@@ -209,6 +237,8 @@ moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* s_w1
  * are required and Shared(x) is added in the combine; otherwise they must be NULL.
  * With cfg->capacity_factor > 0 the dispatch is moe_dispatch_capacity's (counts and the
  * statistics still describe the routing before any drop).
+ * With cfg->weight_layout = MOE_WEIGHTS_TILED, w1, w3 and w2 are moe_pack_weights copies (the
+ * shared expert's weights stay row-major); the results are the same.
  * stage_events: NULL, or 6 hipEvent_t (as void*) recorded on `stream` at the start, after
  * routing, after dispatch, after the up projection, after the down projection (and the
  * shared expert, when there is one) and at the end.

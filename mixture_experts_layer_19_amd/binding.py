@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 import enum
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional, Sequence
 
 import torch
@@ -19,6 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_BAD_EXPERT_ID, MOE_ERR_HIP = range(6)
+LAYOUTS = {"rowmajor": 0, "tiled": 1}
 ROUTERS = {"softmax_topk": 0, "topk_softmax": 1, "sigmoid": 2}
 ACTS = {"gelu": 0, "swiglu": 1}
 DTYPES = {"f32": 0, "bf16": 1}
@@ -56,6 +57,7 @@ class MoeConfigStruct(ctypes.Structure):
         ("routed_scaling", ctypes.c_float),
         ("d_ff_shared", ctypes.c_int32),
         ("capacity_factor", ctypes.c_float),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -76,14 +78,16 @@ class LayerConfig:
     routed_scaling: float = 1.0
     d_ff_shared: int = 0     # width S f of the shared expert(s); 0 = none
     capacity_factor: float = 0.0   # moe_forward: 0 = dropless, > 0 = capacity-factor dispatch
+    weight_layout: str = "rowmajor"  # w1 / w3 / w2: "rowmajor" [E,N,K], or "tiled" (moe_pack_weights)
 
     def struct(self) -> MoeConfigStruct:
-        if self.router not in ROUTERS or self.act not in ACTS or self.dtype not in DTYPES:
-            raise ValueError(f"unknown router/act/dtype in {self}")
+        if self.router not in ROUTERS or self.act not in ACTS or self.dtype not in DTYPES \
+                or self.weight_layout not in LAYOUTS:
+            raise ValueError(f"unknown router/act/dtype/weight_layout in {self}")
         return MoeConfigStruct(self.n_tokens, self.d_model, self.n_experts, self.top_k, self.d_ff,
                                ROUTERS[self.router], int(self.norm_topk), ACTS[self.act],
                                int(self.has_bias), DTYPES[self.dtype], float(self.routed_scaling),
-                               int(self.d_ff_shared), float(self.capacity_factor))
+                               int(self.d_ff_shared), float(self.capacity_factor), LAYOUTS[self.weight_layout])
 
     @property
     def torch_dtype(self):
@@ -96,7 +100,7 @@ class LayerConfig:
     def with_tokens(self, n: int) -> "LayerConfig":
         return LayerConfig(n, self.d_model, self.n_experts, self.top_k, self.d_ff, self.router,
                            self.norm_topk, self.act, self.has_bias, self.dtype, self.routed_scaling,
-                           self.d_ff_shared, self.capacity_factor)
+                           self.d_ff_shared, self.capacity_factor, self.weight_layout)
 
 
 _lib = None
@@ -133,11 +137,14 @@ def lib():
     L.moe_backward.argtypes = ([S] + [_P] * 15 + [ctypes.c_float, ctypes.c_float, ctypes.POINTER(MoeGradsStruct)]
                                + [_P] * 4 + [ctypes.c_int, _P, ctypes.c_size_t, _P, _P])
     L.moe_forward_train.argtypes = [S] + [_P] * 20 + [ctypes.c_size_t, _P]
+    L.moe_packed_weight_size.argtypes = [S, ctypes.c_int]
+    L.moe_packed_weight_size.restype = ctypes.c_size_t
+    L.moe_pack_weights.argtypes = [S, ctypes.c_int, _P, _P, _P]
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
                  "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity", "moe_backward",
-                 "moe_forward_train"):
+                 "moe_forward_train", "moe_pack_weights"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -286,9 +293,9 @@ def moe_expert_ffn(cfg: LayerConfig, x_sorted, offsets, w1, w3, b1, w2, b2, gate
     T = cfg.torch_dtype
     _want(x_sorted, "x_sorted", (A, d), T)
     _want(offsets, "offsets", (E + 1,), torch.int32)
-    _want(w1, "w1", (E, f, d), T)
-    _want(w2, "w2", (E, d, f), T)
-    _want(w3, "w3", (E, f, d), T, optional=cfg.act != "swiglu")
+    _want(w1, "w1", weight_shape(cfg, 0), T)
+    _want(w2, "w2", weight_shape(cfg, 1), T)
+    _want(w3, "w3", weight_shape(cfg, 0), T, optional=cfg.act != "swiglu")
     _want(b1, "b1", (E, f), T, optional=not cfg.has_bias)
     _want(b2, "b2", (E, d), T, optional=not cfg.has_bias)
     _want(gate_sorted, "gate_sorted", (A,), torch.float32, optional=True)
@@ -299,6 +306,39 @@ def moe_expert_ffn(cfg: LayerConfig, x_sorted, offsets, w1, w3, b1, w2, b2, gate
                               _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_expert_ffn")
     return y_sorted
+
+
+TILED_ROWS, TILED_K = 128, 32
+
+
+def weight_shape(cfg: LayerConfig, which: int):
+    """Shape of W1 / W3 (which = 0) or W2 (which = 1) as the calls take them: row-major
+    [E,N,K], or for cfg.weight_layout == "tiled" the padded [E,Np,Kp] of moe_pack_weights."""
+    N, K = (cfg.d_ff, cfg.d_model) if which == 0 else (cfg.d_model, cfg.d_ff)
+    if cfg.weight_layout == "tiled":
+        N = -(-N // TILED_ROWS) * TILED_ROWS
+        K = -(-K // TILED_K) * TILED_K
+    return (cfg.n_experts, N, K)
+
+
+def moe_packed_weight_size(cfg: LayerConfig, which: int) -> int:
+    return int(lib().moe_packed_weight_size(ctypes.byref(cfg.struct()), int(which)))
+
+
+def moe_pack_weights(cfg: LayerConfig, which: int, w):
+    """Tiled copy ([E,Np,Kp] storage in the MOE_WEIGHTS_TILED layout) of the row-major
+    weight w: W1 or W3 (which = 0, [E,d_ff,d]) or W2 (which = 1, [E,d,d_ff])."""
+    tcfg = replace(cfg, weight_layout="tiled")
+    rcfg = replace(cfg, weight_layout="rowmajor")
+    _want(w, "w", weight_shape(rcfg, which), cfg.torch_dtype)
+    size = moe_packed_weight_size(rcfg, which)
+    if size == 0:
+        raise ValueError(f"no tiled layout for weight {which} of {cfg} (bf16, valid sizes only)")
+    out = torch.empty(weight_shape(tcfg, which), dtype=cfg.torch_dtype, device=w.device)
+    assert out.numel() * out.element_size() == size
+    st = lib().moe_pack_weights(ctypes.byref(rcfg.struct()), int(which), _ptr(w), _ptr(out), _stream())
+    _check(st, "moe_pack_weights")
+    return out
 
 
 def moe_combine(cfg: LayerConfig, y_sorted, topk_w, inv_perm, y_add=None):
@@ -347,9 +387,9 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
     if out is None:
         _want(x, "x", (N, d), T)
         _want(w_router, "w_router", (E, d), T)
-        _want(w1, "w1", (E, f, d), T)
-        _want(w2, "w2", (E, d, f), T)
-        _want(w3, "w3", (E, f, d), T, optional=cfg.act != "swiglu")
+        _want(w1, "w1", weight_shape(cfg, 0), T)
+        _want(w2, "w2", weight_shape(cfg, 1), T)
+        _want(w3, "w3", weight_shape(cfg, 0), T, optional=cfg.act != "swiglu")
         _want(b1, "b1", (E, f), T, optional=not cfg.has_bias)
         _want(b2, "b2", (E, d), T, optional=not cfg.has_bias)
         _want(logit_bias, "logit_bias", (E,), torch.float32, optional=True)

@@ -60,6 +60,7 @@ struct GemmArgs {
   int n_tiles_n;        // output column tiles
   int grid;             // tail_reduce_kernel: the GEMM launches' grid
   int pre_gated;        // down: a = gate * h already, so y = a W2^T + gate * b2
+  int b_kp, b_np;       // B tiled (MOE_WEIGHTS_TILED): padded K and rows per expert; 0: row-major
 };
 
 // ---------------------------------------------------------------------------------------
@@ -221,10 +222,15 @@ struct TileLoads {
   MOE_DEV uint16_t* sb(int j) const { return NAR ? smem + 2 * j * kStageElems : smem + (2 * j + 1) * kStageElems; }
   MOE_DEV Src src(int e, int row0, int rows, int nt) const {
     const int K = g.K, n_out = g.n_out, n0 = nt * kCols;
+    // B row pitch (row-major: K; tiled: the padded K) and rows per expert; n0 is a multiple
+    // of 128, so a tile's B rows start a tiled block
+    const bool tiled = g.b_kp > 0;
+    const int Kb = tiled ? g.b_kp : K;
+    const size_t b_off = ((size_t)e * (tiled ? g.b_np : n_out) + n0) * Kb * 2;
     Src r;
     r.a = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
-    const char* b0_base = static_cast<const char*>(g.b0) + ((size_t)e * n_out + n0) * K * 2;
-    const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + ((size_t)e * n_out + n0) * K * 2 : b0_base;
+    const char* b0_base = static_cast<const char*>(g.b0) + b_off;
+    const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + b_off : b0_base;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
@@ -242,28 +248,36 @@ struct TileLoads {
         cl = rr;
         r.b[i] = b0_base;
       }
-      r.bo[i] = (uint32_t)(min(cl, n_out - 1 - n0) * K + lchunk) * 2u;
+      cl = min(cl, n_out - 1 - n0);
+      // tiled: block cl / 128, row cl % 128 of its 32-element slab rows (the slab offset
+      // is added per copy)
+      r.bo[i] = tiled ? (uint32_t)((cl & ~(kTiledRows - 1)) * Kb + (cl & (kTiledRows - 1)) * kTiledK + lchunk) * 2u
+                      : (uint32_t)(cl * K + lchunk) * 2u;
     }
     return r;
   }
+  // byte offset of reduction index k0 (a multiple of 32) in B: row-major as for A; tiled,
+  // slab k0 / 32 of a block (128 x 32 elements each), where lanes past K read the padding
+  MOE_DEV uint32_t dma_kb(int k0, uint32_t ka) const { return g.b_kp > 0 ? (uint32_t)k0 * (kTiledRows * 2u) : ka; }
   // byte offset of reduction index k0 for this lane; lanes past K read inside the row (their
   // chunks are zeroed once they have landed)
   MOE_DEV uint32_t dma_k(int k0) const {
     const int K = g.K;
     return ((K % kBK) != 0 && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
   }
-  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) at byte offset ka into stage j
-  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka) const {
+  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) at byte offsets ka (A) and
+  // kb (B) into stage j
+  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kb) const {
     const bool is_a = NAR ? c == 0 : (c & 1) == 0;
     const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
     if (is_a) lds_dma16(sr.a + sr.ao[i] + ka, sa(j) + (wave * CA + i) * 16 * kBK);
-    else lds_dma16(sr.b[i] + sr.bo[i] + ka, sb(j) + (wave * CB + i) * 16 * kBK);
+    else lds_dma16(sr.b[i] + sr.bo[i] + kb, sb(j) + (wave * CB + i) * 16 * kBK);
   }
   // every copy of slab k (from the start of K) into stage j
   MOE_DEV void refill(const Src& sr, int j, int k) const {
-    const uint32_t ka = dma_k(k * kBK);
+    const uint32_t ka = dma_k(k * kBK), kb = dma_kb(k * kBK, ka);
 #pragma unroll
-    for (int c = 0; c < CPR; ++c) copy(sr, c, j, ka);
+    for (int c = 0; c < CPR; ++c) copy(sr, c, j, ka, kb);
   }
 };
 
@@ -332,7 +346,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   // count is a compile-time constant at every boundary (the first NST slabs are peeled).
   int relax = RLX ? 3 : 0;
   const typename TL::Src cur = L.src(e, row0, rows, nt);
-  auto copy = [&](int c, int j, uint32_t ka) { L.copy(cur, c, j, ka); };
+  auto copy = [&](int c, int j, uint32_t ka, uint32_t kb) { L.copy(cur, c, j, ka, kb); };
   auto dma_k = [&](int k0) { return L.dma_k(k0); };
   auto refill = [&](int j, int slab) {
     L.refill(cur, j, kso + slab);
@@ -385,7 +399,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   // multiply the slab in registers while refilling stage j with `slab`: copy c after MFMA
   // number floor((c + 1) 16 / CPR) - 1, so the copies spread over the phase
   auto multiply_refill = [&](int j, int slab) {
-    const uint32_t ka = dma_k((kso + slab) * kBK);
+    const uint32_t ka = dma_k((kso + slab) * kBK), kb = L.dma_kb((kso + slab) * kBK, ka);
 #pragma unroll
     for (int mm = 0; mm < 16; ++mm) {
       const int ks = mm >> 3, i = (mm >> 1) & 3, jj = mm & 1;
@@ -393,7 +407,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
 #pragma unroll
       for (int c = 0; c < CPR; ++c)
         if (mm == (c + 1) * 16 / CPR - 1) {
-          copy(c, j, ka);
+          copy(c, j, ka, kb);
           __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -911,6 +925,10 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
   g.tiles = L.tiles;
   g.K = c.d_model;
   g.n_out = c.d_ff;
+  if (c.weight_layout == MOE_WEIGHTS_TILED) {
+    g.b_kp = tiled_k(c, 0);
+    g.b_np = tiled_n(c, 0);
+  }
   const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
@@ -928,10 +946,14 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
 
 hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
                        const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool w2_tiled) {
   GemmArgs g{};
   g.a = h;
   g.b0 = w2;
+  if (w2_tiled) {
+    g.b_kp = tiled_k(c, 1);
+    g.b_np = tiled_n(c, 1);
+  }
   g.bias = (c.act == MOE_ACT_GELU && c.has_bias) ? b2 : nullptr;
   g.gate = gate;
   g.pre_gated = pre_gated ? 1 : 0;
@@ -965,7 +987,7 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
                            void* y_sorted, hipStream_t stream) {
   if (c.n_tokens * c.top_k == 0) return hipGetLastError();
   return launch_down(c, L.tiles, ffn_max_m_tiles(c), L.h, c.d_ff, w2, b2, gate_sorted, false, y_sorted, L.tail_part,
-                     stream);
+                     stream, c.weight_layout == MOE_WEIGHTS_TILED);
 }
 
 hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream) {
@@ -1039,6 +1061,38 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(d);
   }
+  return hipGetLastError();
+}
+
+// Tiled weights (MOE_WEIGHTS_TILED, layout in moe.h): one thread per 16-byte chunk of the
+// tiled copy, which is written in order; each chunk is 8 consecutive reduction elements of
+// one row, read from the row-major source or zero in the padding (K is a multiple of 8, so a
+// chunk is wholly inside or outside the row).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ w, uint4* __restrict__ out,
+                                                           long long n_chunks, int N, int K, int Np, int Kp) {
+  const long long per_expert = (long long)Np * Kp / 8;
+  const int kc = K / 8;
+  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < n_chunks;
+       q += (long long)gridDim.x * blockDim.x) {
+    const long long e = q / per_expert;
+    const long long r = q - e * per_expert;      // chunk within the expert
+    const long long blk = r / (kTiledRows * Kp / 8);  // 128-row block
+    const int rr = (int)(r - blk * (kTiledRows * Kp / 8));
+    const int slab = rr / (kTiledRows * kTiledK / 8);
+    const int within = rr - slab * (kTiledRows * kTiledK / 8);
+    const int row = (int)blk * kTiledRows + within / (kTiledK / 8);
+    const int k8 = slab * (kTiledK / 8) + within % (kTiledK / 8);  // chunk index along K
+    out[q] = (row < N && k8 < kc) ? w[(e * N + row) * (long long)kc + k8] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+hipError_t launch_pack_weights(const moe_config& c, int which, const void* w, void* w_tiled, hipStream_t stream) {
+  const int N = which ? c.d_model : c.d_ff, K = which ? c.d_ff : c.d_model;
+  const long long n_chunks = (long long)packed_weight_elems(c, which) / 8;
+  if (n_chunks == 0) return hipGetLastError();
+  const int grid = (int)std::min<long long>((n_chunks + 255) / 256, 65536);
+  pack_weights_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(w), static_cast<uint4*>(w_tiled),
+                                                n_chunks, N, K, tiled_n(c, which), tiled_k(c, which));
   return hipGetLastError();
 }
 

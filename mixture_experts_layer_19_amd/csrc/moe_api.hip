@@ -32,6 +32,8 @@ moe_status check_config(const moe_config* c, bool needs_ff) {
   if (!std::isfinite(c->capacity_factor) || c->capacity_factor < 0.f) return MOE_ERR_INVALID_ARG;
   if (c->d_ff_shared > 0 && (c->d_ff_shared < 8 || c->d_ff_shared > 65536 || c->d_ff_shared % 8))
     return MOE_ERR_UNSUPPORTED;
+  if (c->weight_layout != MOE_WEIGHTS_ROWMAJOR && c->weight_layout != MOE_WEIGHTS_TILED) return MOE_ERR_INVALID_ARG;
+  if (c->weight_layout == MOE_WEIGHTS_TILED && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -70,6 +72,7 @@ moe_status check_shared(const moe_config* c, const void* s_w1, const void* s_w3,
 // What the backward supports beyond check_config: bfloat16, dropless.
 moe_status check_backward_config(const moe_config* c) {
   if (c->dtype != MOE_BF16 || c->capacity_factor != 0.f) return MOE_ERR_UNSUPPORTED;
+  if (c->weight_layout != MOE_WEIGHTS_ROWMAJOR) return MOE_ERR_UNSUPPORTED;  // row-major weights only
   return MOE_OK;
 }
 
@@ -442,6 +445,24 @@ moe_status moe_forward_train(const moe_config* cfg, const void* x, const void* w
   BwdIn in{x, w_router, logit_bias, sel_bias, w1, w3, b1, w2, b2, s_w1, s_w3, s_b1, s_w2, s_b2, nullptr, 0.f, 0.f};
   RouteOut ro{topk_ids, topk_w, counts, stats};
   return hip_status(launch_forward_train(*cfg, L, in, y, ro, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_packed_weight_size(const moe_config* cfg, int which) {
+  if (check_config(cfg, true) != MOE_OK || cfg->dtype != MOE_BF16 || (which != 0 && which != 1)) return 0;
+  return packed_weight_elems(*cfg, which) * 2;
+}
+
+moe_status moe_pack_weights(const moe_config* cfg, int which, const void* w, void* w_tiled, void* stream) {
+  MOE_TRY(check_config(cfg, true));
+  if (which != 0 && which != 1) return MOE_ERR_INVALID_ARG;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(need_t(w));
+  MOE_TRY(need_t(w_tiled));
+  const size_t src_bytes = (size_t)cfg->n_experts * cfg->d_ff * cfg->d_model * 2;
+  const size_t dst_bytes = packed_weight_elems(*cfg, which) * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_tiled);
+  if (a < b + dst_bytes && b < a + src_bytes) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  return hip_status(launch_pack_weights(*cfg, which, w, w_tiled, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float* sel_bias, float rate,

@@ -266,6 +266,16 @@ hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const
 int ffn_tile_rows(const moe_config& c);
 // rows at or below which an expert's last m-tile is narrow (0: no narrow tiles)
 int ffn_narrow_rows(const moe_config& c);
+// Tiled weights (MOE_WEIGHTS_TILED): rows per block and reduction elements per slab, the
+// padded sizes of weight `which` (0: W1 / W3, N = d_ff, K = d; 1: W2, N = d, K = d_ff), its
+// element count, and the re-layout kernel.
+constexpr int kTiledRows = 128, kTiledK = 32;
+inline int tiled_n(const moe_config& c, int which) { return ((which ? c.d_model : c.d_ff) + kTiledRows - 1) / kTiledRows * kTiledRows; }
+inline int tiled_k(const moe_config& c, int which) { return ((which ? c.d_ff : c.d_model) + kTiledK - 1) / kTiledK * kTiledK; }
+inline size_t packed_weight_elems(const moe_config& c, int which) {
+  return (size_t)c.n_experts * (size_t)tiled_n(c, which) * (size_t)tiled_k(c, which);
+}
+hipError_t launch_pack_weights(const moe_config& c, int which, const void* w, void* w_tiled, hipStream_t stream);
 // floor(k cf N / E) raised to the next even integer (the capacity-factor dispatch's capacity)
 long long expert_capacity(const moe_config& c, float capacity_factor);
 hipError_t launch_dispatch_capacity(const moe_config& c, const WsLayout& L, float capacity_factor, const void* x,
@@ -298,9 +308,10 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
 // Down projection y = h W2^T (+ b2) times gate over a tile table's rows, K = the hidden width:
 // (acc + b2) * gate, or with pre_gated (h already scaled by its row's gate) acc + gate * b2.
 // tail_part: the K-split tail's partials (bfloat16; null: one persistent launch).
+// w2_tiled: w2 is a moe_pack_weights copy (which = 1).
 hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
                        const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
-                       hipStream_t stream);
+                       hipStream_t stream, bool w2_tiled = false);
 // One persistent workgroup per CU: the CU count rounded up to a multiple of 8 (the XCDs).
 int persistent_grid();
 // Tile table of one dense "expert" covering rows [0, n) in tiles of bm rows.

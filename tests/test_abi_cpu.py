@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
                "moe_workspace_size", "moe_get_device_error", "moe_status_string", "moe_update_bias",
                "moe_shared_ffn", "moe_dispatch_capacity", "moe_expert_capacity", "moe_backward",
-               "moe_forward_train"):
+               "moe_forward_train", "moe_packed_weight_size", "moe_pack_weights"):
         assert fn in names
 
 
@@ -212,3 +212,35 @@ def test_forward_train_host_validation():
     assert call(ok, x=None) == B.MOE_ERR_INVALID_ARG
     need = B.moe_workspace_size(ok, B.Op.BACKWARD)
     assert call(ok, ws_bytes=need - 256) == B.MOE_ERR_WORKSPACE
+
+
+def test_tiled_weight_sizes_and_rejections():
+    """moe_packed_weight_size is E * Np * Kp * 2 (rows rounded up to 128, reduction to 32);
+    the tiled layout is bf16-only, and the training calls reject it on the host."""
+    lib = B.lib()
+    f = ctypes.c_void_p(0x10000)
+    for (d, ff) in ((4096, 14336), (200, 600), (7168, 2048), (136, 520)):
+        cfg = B.LayerConfig(1000, d, 8, 2, ff)
+        np_ = lambda n: -(-n // 128) * 128
+        kp_ = lambda k: -(-k // 32) * 32
+        assert B.moe_packed_weight_size(cfg, 0) == 8 * np_(ff) * kp_(d) * 2
+        assert B.moe_packed_weight_size(cfg, 1) == 8 * np_(d) * kp_(ff) * 2
+        assert B.weight_shape(B.LayerConfig(1000, d, 8, 2, ff, weight_layout="tiled"), 1) == (8, np_(d), kp_(ff))
+    assert B.moe_packed_weight_size(B.LayerConfig(1000, 64, 8, 2, 64, dtype="f32"), 0) == 0
+    assert B.moe_packed_weight_size(B.LayerConfig(1000, 64, 8, 2, 64), 2) == 0
+    f32 = B.LayerConfig(1000, 64, 8, 2, 64, dtype="f32").struct()
+    assert lib.moe_pack_weights(ctypes.byref(f32), 0, f, ctypes.c_void_p(0x40000000), None) == B.MOE_ERR_UNSUPPORTED
+    cfg = B.LayerConfig(1000, 64, 8, 2, 64).struct()
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 2, f, ctypes.c_void_p(0x40000000), None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 0, f, ctypes.c_void_p(0x10010), None) == B.MOE_ERR_INVALID_ARG
+    # a tiled f32 layer, an unknown layout, and the training calls with tiled weights
+    tf32 = B.LayerConfig(1000, 64, 8, 2, 64, dtype="f32", weight_layout="tiled").struct()
+    st = lib.moe_expert_ffn(ctypes.byref(tf32), f, f, f, f, None, f, None, None, f, f, 1 << 40, None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    odd = B.LayerConfig(1000, 64, 8, 2, 64).struct()
+    odd.weight_layout = 7
+    st = lib.moe_expert_ffn(ctypes.byref(odd), f, f, f, f, None, f, None, None, f, f, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    tiled = B.LayerConfig(1000, 64, 8, 2, 64, weight_layout="tiled").struct()
+    st = lib.moe_forward_train(ctypes.byref(tiled), *([f] * 20), 1 << 40, None)
+    assert st == B.MOE_ERR_UNSUPPORTED

@@ -1,0 +1,105 @@
+"""Tiled weights (MOE_WEIGHTS_TILED): the re-layout against its definition in moe.h, and the
+layer and the expert FFN with tiled weights against the same calls with row-major weights,
+bit for bit (the grouped GEMM loads the same values into the same places either way)."""
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_19_amd import binding as B
+from mixture_experts_layer_19_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def tiled_definition(w: np.ndarray, rows=128, kslab=32) -> np.ndarray:
+    """The layout as moe.h defines it: per expert, 128-row blocks stored slab by slab of 32
+    reduction elements, zero padding up to multiples of 128 rows and 32 elements."""
+    E, N, K = w.shape
+    Np, Kp = -(-N // rows) * rows, -(-K // kslab) * kslab
+    p = np.zeros((E, Np, Kp), w.dtype)
+    p[:, :N, :K] = w
+    out = np.empty(E * Np * Kp, w.dtype)
+    for e in range(E):
+        for n in range(Np):
+            for s in range(Kp // kslab):
+                base = e * Np * Kp + (n // rows) * rows * Kp + s * rows * kslab + (n % rows) * kslab
+                out[base:base + kslab] = p[e, n, s * kslab:(s + 1) * kslab]
+    return out.reshape(E, Np, Kp)
+
+
+@pytest.mark.parametrize("E,N,K", [(2, 200, 136), (3, 256, 64), (1, 136, 1000)])
+def test_pack_matches_layout_definition(E, N, K):
+    cfg = B.LayerConfig(8, K, E, 1, N)  # which = 0: N = d_ff, K = d
+    g = torch.Generator().manual_seed(E * N + K)
+    w = torch.randn((E, N, K), generator=g).to(torch.bfloat16).cuda()
+    p = B.moe_pack_weights(cfg, 0, w)
+    torch.cuda.synchronize()
+    want = tiled_definition(w.cpu().view(torch.int16).numpy())
+    assert np.array_equal(p.cpu().view(torch.int16).numpy(), want)
+    # W2's orientation: N = d, K = d_ff
+    cfg2 = B.LayerConfig(8, N, E, 1, K)
+    p2 = B.moe_pack_weights(cfg2, 1, w)
+    assert np.array_equal(p2.cpu().view(torch.int16).numpy(), want)
+
+
+def tiled_inputs(cfg, inp):
+    t = {n: (B.moe_pack_weights(cfg, 1 if n == "w2" else 0, inp[n]) if inp[n] is not None else None)
+         for n in ("w1", "w3", "w2")}
+    return replace(cfg, weight_layout="tiled"), t
+
+
+SHAPES = {
+    "mixtral_small": ("mixtral", dict(n_tokens=640, d_model=256, d_ff=456)),
+    "deepseek_small": ("deepseek_v3", dict(n_tokens=300, d_model=256, d_ff=128)),   # narrow tiles
+    "gpt2_small": ("gpt2_small", dict(n_tokens=700, d_model=192, d_ff=392)),        # GELU + biases
+    "fine_small": ("fine_grained", dict(n_tokens=900, d_model=128, d_ff=96)),
+    "deepseek_shared_small": ("deepseek_v3_shared", dict(n_tokens=300, d_model=256, d_ff=128, d_ff_shared=128)),
+    "mixtral": ("mixtral", {}),
+    "deepseek_v3": ("deepseek_v3", {}),
+}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_tiled_equals_rowmajor(name):
+    base, kw = SHAPES[name]
+    w = W.WORKLOADS[base].scaled(**kw) if kw else W.WORKLOADS[base]
+    cfg = w.cfg
+    say(f"[tiled forward] {name} {cfg}")
+    inp = W.make_inputs(w, seed=3)
+    args = (inp["x"], inp["w_router"])
+    ref = B.moe_forward(cfg, *args, inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"], inp["logit_bias"],
+                        inp["sel_bias"], shared=inp["shared"])
+    tcfg, t = tiled_inputs(cfg, inp)
+    got = B.moe_forward(tcfg, *args, t["w1"], t["w3"], t["w2"], inp["b1"], inp["b2"], inp["logit_bias"],
+                        inp["sel_bias"], shared=inp["shared"])
+    torch.cuda.synchronize()
+    for key in ("y", "topk_ids", "topk_w", "counts", "stats"):
+        assert torch.equal(ref[key], got[key]), key
+
+
+@pytest.mark.parametrize("act,bias,d,f,counts", [("swiglu", False, 1984, 1000, [6000, 5120, 7000, 6500]),
+                                                 ("gelu", True, 1000, 1984, [6000, 5120, 7000, 6500]),
+                                                 ("swiglu", False, 200, 600, [0, 1, 127, 128, 129, 257, 640])])
+def test_expert_ffn_tiled_equals_rowmajor(act, bias, d, f, counts):
+    """Several items per workgroup, partial m- and n-tiles, a reduction length off the 32 grid
+    (the tiled copy's zero padding), and narrow tiles (the last case)."""
+    counts = np.array(counts)
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[tiled ffn] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act=act, has_bias=bias, dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_tiled", cfg, weight_std=0.05), seed=9)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=9)
+    gate = W.random_gates(rows, 1, seed=9).reshape(-1)
+    ref = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    tcfg, t = tiled_inputs(cfg, inp)
+    got = B.moe_expert_ffn(tcfg, xs, offsets, t["w1"], t["w3"], inp["b1"], t["w2"], inp["b2"], gate)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
