@@ -61,6 +61,9 @@ struct GemmArgs {
   int grid;             // tail_reduce_kernel: the GEMM launches' grid
   int pre_gated;        // down: a = gate * h already, so y = a W2^T + gate * b2
   int b_kp, b_np;       // B tiled (MOE_WEIGHTS_TILED): padded K and rows per expert; 0: row-major
+  int a_kp;             // A tiled like h below (its padded K); 0: row-major
+  int c_kp;             // the up projection writes h tiled: 128-row blocks of 32-column slabs,
+                        // row pitch c_kp (n_out rounded up to 32); 0: row-major
 };
 
 // ---------------------------------------------------------------------------------------
@@ -227,14 +230,20 @@ struct TileLoads {
     const bool tiled = g.b_kp > 0;
     const int Kb = tiled ? g.b_kp : K;
     const size_t b_off = ((size_t)e * (tiled ? g.b_np : n_out) + n0) * Kb * 2;
+    // tiled A: offsets from the 128-row block holding row0 (rows are those of the whole A)
+    const bool a_tiled = g.a_kp > 0;
+    const int rb = row0 & ~(kTiledRows - 1);
     Src r;
-    r.a = static_cast<const char*>(g.a) + (size_t)row0 * K * 2;
+    r.a = static_cast<const char*>(g.a) + (a_tiled ? (size_t)rb * g.a_kp * 2 : (size_t)row0 * K * 2);
     const char* b0_base = static_cast<const char*>(g.b0) + b_off;
     const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + b_off : b0_base;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
-      r.ao[i] = (uint32_t)(min(rr, rows - 1) * K + lchunk) * 2u;
+      const int rc = min(rr, rows - 1);
+      const int rel = row0 - rb + rc;  // tiled: row within the blocks from rb
+      r.ao[i] = a_tiled ? (uint32_t)((rel & ~(kTiledRows - 1)) * g.a_kp + (rel & (kTiledRows - 1)) * kTiledK + lchunk) * 2u
+                        : (uint32_t)(rc * K + lchunk) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -256,28 +265,28 @@ struct TileLoads {
     }
     return r;
   }
-  // byte offset of reduction index k0 (a multiple of 32) in B: row-major as for A; tiled,
-  // slab k0 / 32 of a block (128 x 32 elements each), where lanes past K read the padding
-  MOE_DEV uint32_t dma_kb(int k0, uint32_t ka) const { return g.b_kp > 0 ? (uint32_t)k0 * (kTiledRows * 2u) : ka; }
+  // byte offset of reduction index k0 (a multiple of 32) in a tiled operand: slab k0 / 32 of
+  // a block (128 x 32 elements each); lanes past K read the padding (zeroed in LDS later)
+  MOE_DEV uint32_t dma_kt(int k0) const { return (uint32_t)k0 * (kTiledRows * 2u); }
   // byte offset of reduction index k0 for this lane; lanes past K read inside the row (their
   // chunks are zeroed once they have landed)
   MOE_DEV uint32_t dma_k(int k0) const {
     const int K = g.K;
     return ((K % kBK) != 0 && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
   }
-  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) at byte offsets ka (A) and
-  // kb (B) into stage j
-  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kb) const {
+  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) into stage j, at byte offset
+  // ka (row-major operands) or kt (tiled ones) along K
+  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kt) const {
     const bool is_a = NAR ? c == 0 : (c & 1) == 0;
     const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
-    if (is_a) lds_dma16(sr.a + sr.ao[i] + ka, sa(j) + (wave * CA + i) * 16 * kBK);
-    else lds_dma16(sr.b[i] + sr.bo[i] + kb, sb(j) + (wave * CB + i) * 16 * kBK);
+    if (is_a) lds_dma16(sr.a + sr.ao[i] + (g.a_kp > 0 ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
+    else lds_dma16(sr.b[i] + sr.bo[i] + (g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
   }
   // every copy of slab k (from the start of K) into stage j
   MOE_DEV void refill(const Src& sr, int j, int k) const {
-    const uint32_t ka = dma_k(k * kBK), kb = dma_kb(k * kBK, ka);
+    const uint32_t ka = dma_k(k * kBK), kt = dma_kt(k * kBK);
 #pragma unroll
-    for (int c = 0; c < CPR; ++c) copy(sr, c, j, ka, kb);
+    for (int c = 0; c < CPR; ++c) copy(sr, c, j, ka, kt);
   }
 };
 
@@ -399,7 +408,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   // multiply the slab in registers while refilling stage j with `slab`: copy c after MFMA
   // number floor((c + 1) 16 / CPR) - 1, so the copies spread over the phase
   auto multiply_refill = [&](int j, int slab) {
-    const uint32_t ka = dma_k((kso + slab) * kBK), kb = L.dma_kb((kso + slab) * kBK, ka);
+    const uint32_t ka = dma_k((kso + slab) * kBK), kb = L.dma_kt((kso + slab) * kBK);
 #pragma unroll
     for (int mm = 0; mm < 16; ++mm) {
       const int ks = mm >> 3, i = (mm >> 1) & 3, jj = mm & 1;
@@ -529,7 +538,9 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   auto srow = [](int v) { return ((v >> 2) & 1) * 8 + (v & 3); };
   // each lane stores whole 16-byte chunks of the half's 16 staged rows to dst (row pitch
   // `pitch` elements, first column col_base)
-  auto flush = [&](int i, int h, uint16_t* dst, size_t pitch) {
+  // (ckp > 0: dst is tiled with row pitch ckp; a store instruction then writes 16 rows of one
+  // 32-column slab, 1 KiB contiguous within a 128-row block)
+  auto flush = [&](int i, int h, uint16_t* dst, size_t pitch, int ckp = 0) {
 #pragma unroll
     for (int it = 0; it < 16 * kWChunks / 64; ++it) {
       const int idx = it * 64 + lane;
@@ -537,7 +548,11 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
       const int trow = wm * 128 + i * 32 + h * 16 + prow;
       const int col = col_base + ch * 8;
       const uint4 val = *reinterpret_cast<const uint4*>(stage + prow * kStride + ch * 8);
-      if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + (size_t)(row0 + trow) * pitch + col) = val;
+      const int R = row0 + trow;
+      const size_t at = ckp > 0 ? (size_t)(R & ~(kTiledRows - 1)) * ckp + (size_t)(col >> 5) * (kTiledRows * kTiledK) +
+                                      (R & (kTiledRows - 1)) * kTiledK + (col & 31)
+                                : (size_t)R * pitch + col;
+      if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + at) = val;
     }
   };
 #pragma unroll
@@ -595,7 +610,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
             }
           }
         }
-        flush(i, h, C, n_out);
+        flush(i, h, C, n_out, g.c_kp);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each half block's registers short-lived
     }
@@ -885,7 +900,10 @@ void carve_ffn(const moe_config& c, WsCarver& w, WsLayout* L) {
   const size_t A = (size_t)(c.n_tokens * c.top_k);
   // the shared expert (run after the routed experts) reuses the tile table and h
   const size_t tiles_n = (size_t)std::max(ffn_max_m_tiles(c), shared_m_tiles(c));
-  const size_t h_elems = std::max(A * (size_t)c.d_ff, (size_t)c.n_tokens * (size_t)std::max(c.d_ff_shared, 0));
+  // h: row-major [A, d_ff], or tiled (bf16) over A rounded up to 128 rows and d_ff to 32
+  const size_t h_routed = ffn_h_tiled(c) ? (A + kTiledRows - 1) / kTiledRows * kTiledRows * (size_t)tiled_k(c, 1)
+                                         : A * (size_t)c.d_ff;
+  const size_t h_elems = std::max(h_routed, (size_t)c.n_tokens * (size_t)std::max(c.d_ff_shared, 0));
   int* tiles = w.take_t<int>((size_t)tile_table_ints((long long)tiles_n));
   void* h = w.take(h_elems * elem_size(c));
   // the down projection's tail partials (bfloat16 path, when its K allows several pieces)
@@ -929,6 +947,7 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
     g.b_kp = tiled_k(c, 0);
     g.b_np = tiled_n(c, 0);
   }
+  if (ffn_h_tiled(c)) g.c_kp = tiled_k(c, 1);  // h in the tiled layout (K of the down projection)
   const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
@@ -946,9 +965,10 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
 
 hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
                        const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
-                       hipStream_t stream, bool w2_tiled) {
+                       hipStream_t stream, bool w2_tiled, int h_kp) {
   GemmArgs g{};
   g.a = h;
+  g.a_kp = h_kp;
   g.b0 = w2;
   if (w2_tiled) {
     g.b_kp = tiled_k(c, 1);
@@ -987,7 +1007,7 @@ hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t
                            void* y_sorted, hipStream_t stream) {
   if (c.n_tokens * c.top_k == 0) return hipGetLastError();
   return launch_down(c, L.tiles, ffn_max_m_tiles(c), L.h, c.d_ff, w2, b2, gate_sorted, false, y_sorted, L.tail_part,
-                     stream, c.weight_layout == MOE_WEIGHTS_TILED);
+                     stream, c.weight_layout == MOE_WEIGHTS_TILED, ffn_h_tiled(c) ? tiled_k(c, 1) : 0);
 }
 
 hipError_t launch_dense_tiles(int n, int bm, int* tiles, hipStream_t stream) {

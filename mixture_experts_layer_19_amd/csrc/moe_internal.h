@@ -276,6 +276,9 @@ inline size_t packed_weight_elems(const moe_config& c, int which) {
   return (size_t)c.n_experts * (size_t)tiled_n(c, which) * (size_t)tiled_k(c, which);
 }
 hipError_t launch_pack_weights(const moe_config& c, int which, const void* w, void* w_tiled, hipStream_t stream);
+// The expert FFN's hidden activations h (moe_expert_ffn, moe_forward) in the same tiled layout
+// (rows of h in 128-row blocks of 32-column slabs): bf16.
+inline bool ffn_h_tiled(const moe_config& c) { return c.dtype == MOE_BF16; }
 // floor(k cf N / E) raised to the next even integer (the capacity-factor dispatch's capacity)
 long long expert_capacity(const moe_config& c, float capacity_factor);
 hipError_t launch_dispatch_capacity(const moe_config& c, const WsLayout& L, float capacity_factor, const void* x,
@@ -308,10 +311,11 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
 // Down projection y = h W2^T (+ b2) times gate over a tile table's rows, K = the hidden width:
 // (acc + b2) * gate, or with pre_gated (h already scaled by its row's gate) acc + gate * b2.
 // tail_part: the K-split tail's partials (bfloat16; null: one persistent launch).
-// w2_tiled: w2 is a moe_pack_weights copy (which = 1).
+// w2_tiled: w2 is a moe_pack_weights copy (which = 1). h_kp > 0: h is tiled (as the up
+// projection of moe_expert_ffn / moe_forward writes it) with that row pitch.
 hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, const void* h, int K, const void* w2,
                        const void* b2, const float* gate, bool pre_gated, void* y, float* tail_part,
-                       hipStream_t stream, bool w2_tiled = false);
+                       hipStream_t stream, bool w2_tiled = false, int h_kp = 0);
 // One persistent workgroup per CU: the CU count rounded up to a multiple of 8 (the XCDs).
 int persistent_grid();
 // Tile table of one dense "expert" covering rows [0, n) in tiles of bm rows.
