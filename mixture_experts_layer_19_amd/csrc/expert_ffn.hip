@@ -231,7 +231,7 @@ struct TileLoads {
     const int Kb = tiled ? g.b_kp : K;
     const size_t b_off = ((size_t)e * (tiled ? g.b_np : n_out) + n0) * Kb * 2;
     // tiled A: offsets from the 128-row block holding row0 (rows are those of the whole A)
-    const bool a_tiled = g.a_kp > 0;
+    const bool a_tiled = a_is_tiled();
     const int rb = row0 & ~(kTiledRows - 1);
     Src r;
     r.a = static_cast<const char*>(g.a) + (a_tiled ? (size_t)rb * g.a_kp * 2 : (size_t)row0 * K * 2);
@@ -268,6 +268,8 @@ struct TileLoads {
   // byte offset of reduction index k0 (a multiple of 32) in a tiled operand: slab k0 / 32 of
   // a block (128 x 32 elements each); lanes past K read the padding (zeroed in LDS later)
   MOE_DEV uint32_t dma_kt(int k0) const { return (uint32_t)k0 * (kTiledRows * 2u); }
+  // only the down projection reads a tiled A (h); the other epilogues keep it row-major
+  MOE_DEV bool a_is_tiled() const { return EPI == kEpiDown && g.a_kp > 0; }
   // byte offset of reduction index k0 for this lane; lanes past K read inside the row (their
   // chunks are zeroed once they have landed)
   MOE_DEV uint32_t dma_k(int k0) const {
@@ -279,7 +281,7 @@ struct TileLoads {
   MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kt) const {
     const bool is_a = NAR ? c == 0 : (c & 1) == 0;
     const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
-    if (is_a) lds_dma16(sr.a + sr.ao[i] + (g.a_kp > 0 ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
+    if (is_a) lds_dma16(sr.a + sr.ao[i] + (a_is_tiled() ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
     else lds_dma16(sr.b[i] + sr.bo[i] + (g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
   }
   // every copy of slab k (from the start of K) into stage j
@@ -610,7 +612,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
             }
           }
         }
-        flush(i, h, C, n_out, g.c_kp);
+        flush(i, h, C, n_out, EPI == kEpiDown ? 0 : g.c_kp);  // only h is written tiled
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each half block's registers short-lived
     }
