@@ -217,10 +217,12 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
 // Token-major row copy: x_sorted[inv_perm[n*k + j]] = x[n] for j < k. One wave per token:
 // the k destinations are wave-uniform, the lanes stream the row in 16-byte pieces, four
-// pieces per lane in flight, each read once and written k times.
+// pieces per lane in flight, each read once and written k times. kp > 0: x_sorted is tiled
+// (128-row blocks of 32-column slabs, row pitch kp elements; bf16), so four lanes write the
+// 64 bytes of one slab of the row.
 __global__ __launch_bounds__(256) void dispatch_copy_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ inv_perm, uint4* __restrict__ x_sorted,
-    long long n_tokens, int k, int vec_per_row) {
+    long long n_tokens, int k, int vec_per_row, int kp) {
   const int lane = threadIdx.x & 63;
   const long long wave0 = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long long n_waves = (long long)gridDim.x * 4;
@@ -236,11 +238,14 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(
       for (int j = 0; j < k; ++j) {
         const int dst = inv_perm[n * k + j];  // wave-uniform
         if (dst < 0) continue;
-        uint4* out = x_sorted + (size_t)dst * vec_per_row;
+        // row-major: row dst; tiled: row dst & 127 of block dst / 128 (16-byte units; a slab
+        // row is 4 of them and a block's slab 512)
+        uint4* out = kp > 0 ? x_sorted + ((size_t)(dst & ~(kTiledRows - 1)) * kp + (dst & (kTiledRows - 1)) * kTiledK) / 8
+                            : x_sorted + (size_t)dst * vec_per_row;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < vec_per_row) out[c] = v[u];
+          if (c < vec_per_row) out[kp > 0 ? (c >> 2) * (kTiledRows * kTiledK / 8) + (c & 3) : c] = v[u];
         }
       }
     }
@@ -253,12 +258,13 @@ static int id_bits_of(int E) {
   return b;
 }
 
-void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream) {
+void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream,
+                 int kp) {
   if (!x_sorted) return;
   const int vpr = (int)(c.d_model * elem_size(c) / 16);
   const int grid = (int)std::min<long long>((c.n_tokens + 3) / 4, 1 << 16);
   dispatch_copy_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(x), inv_perm,
-                                                 static_cast<uint4*>(x_sorted), c.n_tokens, c.top_k, vpr);
+                                                 static_cast<uint4*>(x_sorted), c.n_tokens, c.top_k, vpr, kp);
 }
 
 void carve_dispatch(const moe_config& c, WsCarver& w, WsLayout* L) {
@@ -333,7 +339,8 @@ hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x
 // bases (L.fbase), so only the scatter (one chunk per routing block) and the copy remain.
 hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const void* x,
                                    const int32_t* topk_ids, const float* topk_w, void* x_sorted,
-                                   int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream) {
+                                   int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream,
+                                   int xs_kp) {
   const int A = (int)(c.n_tokens * c.top_k);
   if (A == 0) return hipGetLastError();
   const int E = c.n_experts;
@@ -343,7 +350,7 @@ hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const
   dispatch_scatter_kernel<false, false><<<n_chunks, threads, 0, stream>>>(
       topk_ids, (gate_sorted && topk_w) ? topk_w : nullptr, A, E, id_bits_of(E), chunk, (int)c.n_tokens, c.top_k,
       L.fbase, perm, inv_perm, (gate_sorted && topk_w) ? gate_sorted : nullptr, CapArgs{});
-  launch_copy(c, x, inv_perm, x_sorted, stream);
+  launch_copy(c, x, inv_perm, x_sorted, stream, xs_kp);
   return hipGetLastError();
 }
 

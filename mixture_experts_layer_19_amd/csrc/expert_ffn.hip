@@ -268,8 +268,9 @@ struct TileLoads {
   // byte offset of reduction index k0 (a multiple of 32) in a tiled operand: slab k0 / 32 of
   // a block (128 x 32 elements each); lanes past K read the padding (zeroed in LDS later)
   MOE_DEV uint32_t dma_kt(int k0) const { return (uint32_t)k0 * (kTiledRows * 2u); }
-  // only the down projection reads a tiled A (h); the other epilogues keep it row-major
-  MOE_DEV bool a_is_tiled() const { return EPI == kEpiDown && g.a_kp > 0; }
+  // A may be tiled (h for the down projection, moe_forward's x_sorted for the up one); the
+  // save epilogues of the training path keep it row-major
+  MOE_DEV bool a_is_tiled() const { return !kSave<EPI> && g.a_kp > 0; }
   // byte offset of reduction index k0 for this lane; lanes past K read inside the row (their
   // chunks are zeroed once they have landed)
   MOE_DEV uint32_t dma_k(int k0) const {
@@ -933,7 +934,7 @@ hipError_t launch_ffn_tiles(const moe_config& c, const WsLayout& L, const int32_
 
 hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_sorted,
                          const int32_t* offsets, const void* w1, const void* w3, const void* b1,
-                         hipStream_t stream) {
+                         hipStream_t stream, int xs_kp) {
   const int A = (int)(c.n_tokens * c.top_k);
   if (A == 0) return hipGetLastError();
   GemmArgs g{};
@@ -950,6 +951,7 @@ hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_s
     g.b_np = tiled_n(c, 0);
   }
   if (ffn_h_tiled(c)) g.c_kp = tiled_k(c, 1);  // h in the tiled layout (K of the down projection)
+  g.a_kp = xs_kp;                                // x_sorted tiled (moe_forward, dropless bf16) or not
   const int mt = ffn_max_m_tiles(c);
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);

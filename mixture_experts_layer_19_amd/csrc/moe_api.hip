@@ -1,6 +1,7 @@
 // C ABI of the MoE layer forward: host-side validation, workspace carving and the launch
 // sequences. Nothing here allocates, frees or synchronises (except moe_get_device_error),
 // and no HIP call is made before the first launch, so the library loads without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -92,7 +93,10 @@ void carve_forward_buffers(const moe_config& c, WsCarver& w, WsLayout* L) {
   int* fbase = w.take_t<int>(route_base_ints(c));
   int* kept = w.take_t<int>((size_t)c.n_experts);
   float* gs = w.take_t<float>(A);
-  void* xs = w.take(A * row);
+  // x_sorted: row-major, or tiled (forward_xs_kp) over A rounded up to 128 rows
+  const size_t xs_tiled = forward_xs_kp(c) > 0 ? (A + kTiledRows - 1) / kTiledRows * kTiledRows *
+                                                     (size_t)forward_xs_kp(c) * elem_size(c) : 0;
+  void* xs = w.take(std::max(A * row, xs_tiled));
   void* ys = w.take(A * row);
   if (L) {
     L->perm = perm;
@@ -341,10 +345,11 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     MOE_TRY(hip_status(launch_ffn_tiles(*cfg, L, L.offsets, s)));
   } else {
     MOE_TRY(hip_status(launch_dispatch_scanned(*cfg, L, x, topk_ids, topk_w, L.x_sorted, L.perm, L.inv_perm,
-                                               L.gate_sorted, s)));
+                                               L.gate_sorted, s, forward_xs_kp(*cfg))));
   }
   MOE_TRY(mark(2));
-  MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s)));
+  // x_sorted is tiled on the dropless bf16 path (forward_xs_kp), row-major after a capacity dispatch
+  MOE_TRY(hip_status(launch_ffn_up(*cfg, L, L.x_sorted, L.offsets, w1, w3, b1, s, forward_xs_kp(*cfg))));
   MOE_TRY(mark(3));
   MOE_TRY(hip_status(launch_ffn_down(*cfg, L, L.offsets, w2, b2, L.gate_sorted, L.y_sorted, s)));
   // Shared(x) of the output equation: its output lands in x_sorted, free after the routed up

@@ -262,7 +262,8 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
                         float* gap_out, bool fuse_dispatch, hipStream_t stream);
 hipError_t launch_dispatch_scanned(const moe_config& c, const WsLayout& L, const void* x,
                                    const int32_t* topk_ids, const float* topk_w, void* x_sorted,
-                                   int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream);
+                                   int32_t* perm, int32_t* inv_perm, float* gate_sorted, hipStream_t stream,
+                                   int xs_kp = 0);
 int ffn_tile_rows(const moe_config& c);
 // rows at or below which an expert's last m-tile is narrow (0: no narrow tiles)
 int ffn_narrow_rows(const moe_config& c);
@@ -279,6 +280,14 @@ hipError_t launch_pack_weights(const moe_config& c, int which, const void* w, vo
 // The expert FFN's hidden activations h (moe_expert_ffn, moe_forward) in the same tiled layout
 // (rows of h in 128-row blocks of 32-column slabs): bf16.
 inline bool ffn_h_tiled(const moe_config& c) { return c.dtype == MOE_BF16; }
+// moe_forward's own x_sorted (dropless, bf16) in the tiled layout too, for rows of 4096 or
+// more elements: its row pitch, or 0. The dispatch copy then writes 64-byte pieces, which
+// costs more than the up projection's contiguous reads gain on shorter rows (same-box A/B:
+// d = 2048, k = 8: copy +31 us, up projection -23 us; d = 4096: +9 / -71 us; d = 7168:
+// +26 / -239 us).
+inline int forward_xs_kp(const moe_config& c) {
+  return (c.dtype == MOE_BF16 && c.capacity_factor <= 0.f && c.d_model >= 4096) ? tiled_k(c, 0) : 0;
+}
 // floor(k cf N / E) raised to the next even integer (the capacity-factor dispatch's capacity)
 long long expert_capacity(const moe_config& c, float capacity_factor);
 hipError_t launch_dispatch_capacity(const moe_config& c, const WsLayout& L, float capacity_factor, const void* x,
@@ -294,7 +303,8 @@ hipError_t launch_dispatch(const moe_config& c, const WsLayout& L, const void* x
 hipError_t launch_ffn_tiles(const moe_config& c, const WsLayout& L, const int32_t* offsets, hipStream_t stream);
 hipError_t launch_ffn_up(const moe_config& c, const WsLayout& L, const void* x_sorted,
                          const int32_t* offsets, const void* w1, const void* w3, const void* b1,
-                         hipStream_t stream);
+                         hipStream_t stream,
+                         int xs_kp = 0);
 hipError_t launch_ffn_down(const moe_config& c, const WsLayout& L, const int32_t* offsets,
                            const void* w2, const void* b2, const float* gate_sorted,
                            void* y_sorted, hipStream_t stream);
@@ -344,6 +354,8 @@ hipError_t launch_backward(const moe_config& c, const WsLayout& L, const BwdIn& 
 hipError_t launch_forward_train(const moe_config& c, const WsLayout& L, const BwdIn& in, void* y, const RouteOut& ro,
                                 hipStream_t stream);
 // rows of x copied to their sorted slots (x_sorted[inv_perm[n k + j]] = x[n])
-void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream);
+// kp > 0: write x_sorted tiled with that row pitch (moe_forward's dropless bf16 path)
+void launch_copy(const moe_config& c, const void* x, const int32_t* inv_perm, void* x_sorted, hipStream_t stream,
+                 int kp = 0);
 
 }  // namespace moe

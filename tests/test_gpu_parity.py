@@ -354,6 +354,14 @@ def test_forward_small(name):
     run_forward_and_check(W.WORKLOADS[name].scaled(**SMALL[name]))
 
 
+@pytest.mark.parametrize("name,kw", [("mixtral", dict(n_tokens=300, d_model=4096, d_ff=264)),
+                                     ("deepseek_v3", dict(n_tokens=200, d_model=4104, d_ff=136))])
+def test_forward_wide_rows(name, kw):
+    """Rows of 4096 elements or more: moe_forward's x_sorted in the tiled layout (4104: d off the
+    32-column slab grid; d_ff off it too, so both projections have a reduction tail)."""
+    run_forward_and_check(W.WORKLOADS[name].scaled(**kw))
+
+
 @pytest.mark.parametrize("case", ["n1", "k_eq_e", "e1", "k1", "identical_tokens", "skip_experts", "no_norm_scaled"])
 def test_forward_edge_cases(case):
     base = W.WORKLOADS["mixtral"].scaled(n_tokens=260, d_model=128, d_ff=200)
