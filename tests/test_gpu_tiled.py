@@ -63,6 +63,9 @@ SHAPES = {
     "deepseek_shared_small": ("deepseek_v3_shared", dict(n_tokens=300, d_model=256, d_ff=128, d_ff_shared=128)),
     "mixtral": ("mixtral", {}),
     "deepseek_v3": ("deepseek_v3", {}),
+    # capacity-factor dispatch (row-major x_kept) with tiled weights; and wide rows (tiled x_sorted)
+    "mixtral_capacity": ("mixtral", dict(n_tokens=640, d_model=256, d_ff=456, capacity_factor=1.0)),
+    "mixtral_wide": ("mixtral", dict(n_tokens=300, d_model=4096, d_ff=264)),
 }
 
 
