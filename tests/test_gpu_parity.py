@@ -362,6 +362,27 @@ def test_forward_wide_rows(name, kw):
     run_forward_and_check(W.WORKLOADS[name].scaled(**kw))
 
 
+def _wide_cases():
+    """Seeded irregular shapes on the tiled-x_sorted path: few tokens (fewer assignments than a
+    128-row block), one expert, k = E, widths off the slab grid, GELU with biases."""
+    rng = np.random.default_rng(11)
+    cases = [dict(n_tokens=1, d_model=4096, n_experts=4, top_k=2, d_ff=64),
+             dict(n_tokens=37, d_model=4160, n_experts=1, top_k=1, d_ff=136),
+             dict(n_tokens=50, d_model=4096, n_experts=3, top_k=3, d_ff=200)]
+    for _ in range(3):
+        E = int(rng.integers(2, 17))
+        cases.append(dict(n_tokens=int(rng.integers(60, 500)), d_model=4096 + 8 * int(rng.integers(0, 12)),
+                          n_experts=E, top_k=int(rng.integers(1, min(E, 6) + 1)),
+                          d_ff=8 * int(rng.integers(4, 50))))
+    return cases
+
+
+@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("base", ["mixtral", "gpt2_small"])
+def test_forward_wide_rows_irregular(base, i):
+    run_forward_and_check(W.WORKLOADS[base].scaled(**_wide_cases()[i]))
+
+
 @pytest.mark.parametrize("case", ["n1", "k_eq_e", "e1", "k1", "identical_tokens", "skip_experts", "no_norm_scaled"])
 def test_forward_edge_cases(case):
     base = W.WORKLOADS["mixtral"].scaled(n_tokens=260, d_model=128, d_ff=200)
