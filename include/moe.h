@@ -90,6 +90,8 @@ typedef enum {
   MOE_OP_SHARED_FFN = 5, MOE_OP_BACKWARD = 6
 } moe_op;
 
+/* One layer's configuration. Zero-initialise it (e.g. moe_config c = {0};) before setting
+ * fields: a field added at the end later then means its default, 0. */
 typedef struct {
   int64_t n_tokens;     /* N: tokens, every leading axis flattened ([L7.8] §2) */
   int32_t d_model;      /* d */
