@@ -170,11 +170,14 @@ def test_expert_ffn(dtype, act, bias, rows, E, d, f, empty):
 
 BOUNDARY_COUNTS = [0, 1, 127, 128, 129, 255, 256, 257, 384, 385, 640]   # 6 of 15 m-tiles narrow
 FEW_NARROW_COUNTS = [1000, 700, 513, 100, 0, 900, 0, 0]                 # 2 of 15
+# about 1020 rows per expert: narrow tiles in the up projection only
+UP_NARROW_COUNTS = [2000, 1500, 700, 100, 50, 1300, 2500, 10]
 
 
 @pytest.mark.parametrize("act,bias,d,f,counts", [("swiglu", False, 200, 600, BOUNDARY_COUNTS),
                                                  ("gelu", True, 264, 712, BOUNDARY_COUNTS),
-                                                 ("swiglu", False, 136, 520, FEW_NARROW_COUNTS)])
+                                                 ("swiglu", False, 136, 520, FEW_NARROW_COUNTS),
+                                                 ("swiglu", False, 136, 264, UP_NARROW_COUNTS)])
 def test_expert_ffn_tile_boundaries(act, bias, d, f, counts):
     """Per-expert row counts on both sides of the 128-row (narrow tile) and 256-row (full
     tile) boundaries; widths off both tile grids and K not a multiple of 32 (at most 512 rows
