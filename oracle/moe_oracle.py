@@ -271,15 +271,36 @@ def shared_output(x, params: Mapping[str, Any], act: str):
 # ([L7.8] §2.1 equation).
 # ----------------------------------------------------------------------------------------
 
-def forward_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_bias=None):
+def with_choice(r: Route, ids, spec: Spec) -> Route:
+    """The routing r with the chosen experts replaced by a given choice ids [N,k] (for
+    instance the device's, on a token whose k-th and (k+1)-th scores are within rounding of
+    each other): the gates are recomputed for that choice by the [L7.8] §2.1 routers table,
+    from the same logits. z, p, the scores and the tie margins (which describe the scores,
+    not a choice) are kept."""
+    ids = np.asarray(ids).astype(np.int64)
+    if ids.shape != r.ids.shape:
+        raise ValueError(f"choice shape {ids.shape} != {r.ids.shape}")
+    if ids.size and (ids.min() < 0 or ids.max() >= spec.n_experts):
+        raise ValueError("expert id out of range")
+    return Route(z=r.z, p=r.p, scores=r.scores, ids=ids, w=gate_weights(r.z, ids, spec), gap=r.gap,
+                 intra_gap=r.intra_gap)
+
+
+def forward_loop(x, params: Mapping[str, Any], spec: Spec, logit_bias=None, sel_bias=None, ids=None):
     """Per-token loop over the chosen experts, j ascending ([L7.8] §4 oracle recipe).
 
     params: w_g [E,d]; w1 [E,d_ff,d]; w3 [E,d_ff,d] (swiglu); w2 [E,d,d_ff];
             b1 [E,d_ff], b2 [E,d] (optional, gelu only); the shared expert's s_w1, s_w3,
-            s_w2, s_b1, s_b2 (optional, see shared_output). Returns (y [N,d], Route).
+            s_w2, s_b1, s_b2 (optional, see shared_output).
+    ids:    None (the oracle's own top-k), or a given choice [N,k] whose gates follow the
+            routers table (with_choice): y_n = sum_j w_{n,j} FFN_{ids[n,j]}(x_n) + Shared(x_n),
+            the [L7.8] §2.1 output equation for that choice.
+    Returns (y [N,d], Route); the Route carries the choice used.
     """
     x = np.asarray(x, f64)
     r = route(x, params["w_g"], spec, logit_bias, sel_bias)
+    if ids is not None:
+        r = with_choice(r, ids, spec)
     n, d = x.shape
     y = np.zeros((n, d), f64)
     for t in range(n):
@@ -401,12 +422,15 @@ def capacity_dispatch(ids, n_experts: int, cap: int):
 
 
 def forward_capacity(x, params: Mapping[str, Any], spec: Spec, capacity_factor: float, logit_bias=None,
-                     sel_bias=None):
+                     sel_bias=None, ids=None):
     """The layer with capacity-factor dispatch: dropped assignments contribute nothing, kept
     ones keep their router weight (no renormalisation over the survivors), plus Shared(x).
-    Returns (y, Route, slot, kept)."""
+    ids: None, or a given choice [N,k] (see forward_loop); the ranking and the drops then
+    follow that choice. Returns (y, Route, slot, kept)."""
     x = np.asarray(x, f64)
     r = route(x, params["w_g"], spec, logit_bias, sel_bias)
+    if ids is not None:
+        r = with_choice(r, ids, spec)
     n, d = x.shape
     cap = expert_capacity(spec.top_k, capacity_factor, n, spec.n_experts)
     slot, kept, _ = capacity_dispatch(r.ids, spec.n_experts, cap)

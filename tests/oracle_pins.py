@@ -122,6 +122,64 @@ def pin_worked_example_constant_experts(O):
         _close(y, np.array([[50 / 3] * d, [20.0] * d]), 1e-12, fwd.__name__)
 
 
+def pin_worked_example_gaps(O):
+    """The tie margins on the [L7.8] §3 worked example (selection on z = ln of the page's
+    exp_z). Token 0 picks ln 4, ln 2 over 0, 0: both margins are ln 2. Token 1 picks ln 3, ln 3
+    (the exact tie) over ln 2: the margin inside the top k is 0, the k-th / (k+1)-th one
+    ln 3 - ln 2."""
+    _, r = _worked_route(O)
+    gap, intra = O.topk_gaps(r.scores, r.ids)
+    _close(gap, [math.log(2), math.log(3) - math.log(2)], 1e-15, "k-th / (k+1)-th margins")
+    _close(intra, [math.log(2), 0.0], 1e-15, "smallest margin inside the top k")
+    _close(r.gap, gap, 0, "route() carries the margins")
+
+
+def pin_gpt2_moe_gaps(O):
+    """Margins on [GPT2-MoE]'s printed logits. The four-logit top-2 example keeps 0.5106 and
+    0.4254 over 0.1342: gap 0.4254 - 0.1342, intra 0.5106 - 0.4254. The six-logit walk-through
+    at k = 3 keeps 0.5106, 0.4254, 0.1342 over 0.0418: gap 0.1342 - 0.0418 and intra the
+    smaller of 0.0852 and 0.2912; k = 6 has no (k+1)-th score (gap +inf) and k = 1 no pair
+    inside the top k (intra +inf)."""
+    g = _load("gpt2_moe_router_printout.json")
+    s4 = np.array([g["topk_example_logits"]])
+    ids = O.topk_ids(s4, 2)
+    gap, intra = O.topk_gaps(s4, ids)
+    _close(gap, [0.4254 - 0.1342], 1e-15, "top-2 margin")
+    _close(intra, [0.5106 - 0.4254], 1e-15, "top-2 intra margin")
+    s6 = np.array([g["logits"]])
+    gap, intra = O.topk_gaps(s6, O.topk_ids(s6, 3))
+    _close(gap, [0.1342 - 0.0418], 1e-15, "top-3 margin")
+    _close(intra, [0.5106 - 0.4254], 1e-15, "top-3 intra margin (the smallest pair)")
+    gap, intra = O.topk_gaps(s6, O.topk_ids(s6, 6))
+    assert np.isinf(gap[0]) and gap[0] > 0, "k = E: no (k+1)-th score"
+    gap, intra = O.topk_gaps(s6, O.topk_ids(s6, 1))
+    assert np.isinf(intra[0]) and intra[0] > 0, "k = 1: no pair inside the top k"
+    _close(gap, [0.5106 - 0.4254], 1e-15, "top-1 margin")
+
+
+def pin_given_choice(O):
+    """The output for a given choice follows the [L7.8] §2.1 output equation with the routers
+    table's gates for THAT choice. Worked example logits, constant experts c = (10, 20, 30, 40)
+    (W2 = 0, b2_e = c_e): forcing token 0 onto experts (1, 3) renormalises p = (1/4, 1/2, 1/8,
+    1/8) over them to (4/5, 1/5), so y_0 = 4/5 20 + 1/5 40 = 24; forcing token 1's exact tie
+    the other way round, (2, 0), keeps the gates (1/2, 1/2) and y_1 = 20. With the oracle's own
+    choice given back, the result is the plain forward."""
+    g = _load("worked_example.json")
+    E, d, d_ff = 4, 4, 3
+    z = np.log(_q(g["exp_z"]))
+    c = np.array([10.0, 20.0, 30.0, 40.0])
+    rng = np.random.default_rng(6)
+    params = {"w_g": np.eye(E), "w1": rng.normal(size=(E, d_ff, d)), "b1": rng.normal(size=(E, d_ff)),
+              "w2": np.zeros((E, d, d_ff)), "b2": np.repeat(c[:, None], d, axis=1)}
+    spec = O.Spec(n_experts=E, top_k=2, router="softmax_topk", act="gelu")
+    y, r = O.forward_loop(z, params, spec, ids=np.array([[1, 3], [2, 0]]))
+    _close(r.w, [[4 / 5, 1 / 5], [1 / 2, 1 / 2]], 1e-15, "gates of the given choice")
+    _close(y, np.array([[24.0] * d, [20.0] * d]), 1e-12, "output of the given choice")
+    y_own, r_own = O.forward_loop(z, params, spec)
+    y_back, _ = O.forward_loop(z, params, spec, ids=r_own.ids)
+    _close(y_back, y_own, 0, "own choice given back")
+
+
 # ---------------------------------------------------------------------------------------
 # Printed router values on the other pages
 # ---------------------------------------------------------------------------------------
@@ -429,6 +487,27 @@ def pin_capacity_top_choices_win(O):
     y_ref, _ = O.forward_loop(x, params, spec)
     assert (slot >= 0).all()
     _close(y_cap, y_ref, 1e-12, "capacity >= load is dropless")
+
+
+def pin_capacity_drops(O):
+    """Dropped assignments contribute nothing and kept ones keep their gate ([nanoMoE] "Expert
+    Capacity"). The hand-ranked case of pin_capacity_worked_example (capacity 2: k cf N / E
+    = 2 * 0.6 * 5 / 3 = 2) with zero router logits (uniform p, so every kept gate is 1/2) and
+    constant experts c = (10, 20, 30): token 0 keeps both (10 + 20) / 2 = 15, token 1 both
+    (10 + 30) / 2 = 20, token 2 only its first choice 20 / 2 = 10, token 3 nothing, token 4
+    its first choice 30 / 2 = 15."""
+    ids = np.array([[0, 1], [0, 2], [1, 0], [0, 1], [2, 0]])
+    N, E, d, d_ff = 5, 3, 4, 3
+    c = np.array([10.0, 20.0, 30.0])
+    rng = np.random.default_rng(7)
+    params = {"w_g": np.zeros((E, d)), "w1": rng.normal(size=(E, d_ff, d)), "b1": rng.normal(size=(E, d_ff)),
+              "w2": np.zeros((E, d, d_ff)), "b2": np.repeat(c[:, None], d, axis=1)}
+    spec = O.Spec(n_experts=E, top_k=2, router="softmax_topk", act="gelu")
+    assert O.expert_capacity(2, 0.6, N, E) == 2
+    y, r, slot, kept = O.forward_capacity(rng.normal(size=(N, d)), params, spec, 0.6, ids=ids)
+    assert list(slot) == [0, 3, 1, 5, 2, -1, -1, -1, 4, -1] and list(kept) == [2, 2, 2]
+    _close(r.w, np.full((N, 2), 0.5), 1e-15, "kept gates are not renormalised over survivors")
+    _close(y, np.repeat([[15.0], [20.0], [10.0], [0.0], [15.0]], d, axis=1), 1e-12, "dropped rows add nothing")
 
 
 def _objective(O, x, params, spec, dy, aux, zc):

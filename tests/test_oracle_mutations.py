@@ -258,6 +258,79 @@ def m_logit_bias_dropped(O):
     O.router_logits = lambda x, w_g, logit_bias=None: np.asarray(x, float) @ np.asarray(w_g, float).T
 
 
+def m_gap_zero(O):  # every token taken for a near tie: nothing would be compared
+    O.topk_gaps = lambda scores, ids: (np.zeros(len(ids)), np.zeros(len(ids)))
+
+
+def m_gap_from_top(O):  # margin measured from the top choice instead of the k-th
+    orig = O.topk_gaps
+    def gaps(scores, ids):
+        gap, intra = orig(scores, ids)
+        s = np.asarray(scores, float)
+        top = s[np.arange(len(ids)), ids[:, 0]]
+        kth = s[np.arange(len(ids)), ids[:, -1]]
+        return gap + (top - kth), intra
+    O.topk_gaps = gaps
+
+
+def m_intra_gap_largest(O):  # the largest adjacent margin inside the top k instead of the smallest
+    orig = O.topk_gaps
+    def gaps(scores, ids):
+        gap, _ = orig(scores, ids)
+        s = np.asarray(scores, float)
+        ch = np.take_along_axis(s, ids, axis=1)
+        intra = np.max(ch[:, :-1] - ch[:, 1:], axis=1) if ids.shape[1] > 1 else np.full(len(ids), np.inf)
+        return gap, intra
+    O.topk_gaps = gaps
+
+
+def m_capacity_drops_ignored(O):  # the capacity ranks but nothing is dropped
+    orig = O.capacity_dispatch
+    def cd(ids, n_experts, cap):
+        slot, kept, offsets = orig(ids, n_experts, cap)
+        return np.abs(slot), kept, offsets
+    O.capacity_dispatch = cd
+    fc = O.forward_capacity
+    def forward_capacity(x, params, spec, capacity_factor, logit_bias=None, sel_bias=None, ids=None):
+        y, r, slot, kept = fc(x, params, spec, float(spec.n_experts) * 8, logit_bias, sel_bias, ids)
+        return y, r, orig(r.ids, spec.n_experts, O.expert_capacity(spec.top_k, capacity_factor, len(r.ids),
+                                                                   spec.n_experts))[0], kept
+    O.forward_capacity = forward_capacity
+
+
+def m_capacity_renormalised(O):  # the survivors' gates renormalised to sum to one
+    def forward_capacity(x, params, spec, capacity_factor, logit_bias=None, sel_bias=None, ids=None):
+        x = np.asarray(x, float)
+        r = O.route(x, params["w_g"], spec, logit_bias, sel_bias)
+        if ids is not None:
+            r = O.with_choice(r, ids, spec)
+        cap = O.expert_capacity(spec.top_k, capacity_factor, len(x), spec.n_experts)
+        slot, kept, _ = O.capacity_dispatch(r.ids, spec.n_experts, cap)
+        y = np.zeros_like(x)
+        keep = slot.reshape(r.ids.shape) >= 0
+        for t in range(len(x)):
+            wt = np.where(keep[t], r.w[t], 0.0)
+            if wt.sum() > 0:
+                wt = wt / wt.sum()
+            for j in range(spec.top_k):
+                if keep[t, j]:
+                    y[t] += wt[j] * O.expert_ffn(x[t][None, :], spec.act, **O._expert(params, int(r.ids[t, j])))[0]
+        return y + O.shared_output(x, params, spec.act), r, slot, kept
+    O.forward_capacity = forward_capacity
+
+
+def m_given_choice_ignored(O):  # a given choice silently replaced by the oracle's own
+    orig = O.forward_loop
+    O.forward_loop = lambda x, params, spec, logit_bias=None, sel_bias=None, ids=None: \
+        orig(x, params, spec, logit_bias, sel_bias)
+
+
+def m_given_choice_old_gates(O):  # a given choice weighed with the gates of the oracle's own choice
+    def with_choice(r, ids, spec):
+        return O.Route(z=r.z, p=r.p, scores=r.scores, ids=np.asarray(ids), w=r.w, gap=r.gap, intra_gap=r.intra_gap)
+    O.with_choice = with_choice
+
+
 MUTANTS = [v for k, v in sorted(globals().items()) if k.startswith("m_")]
 
 
