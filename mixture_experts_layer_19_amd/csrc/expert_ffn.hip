@@ -64,6 +64,9 @@ struct GemmArgs {
   int a_kp;             // A tiled like h below (its padded K); 0: row-major
   int c_kp;             // the up projection writes h tiled: 128-row blocks of 32-column slabs,
                         // row pitch c_kp (n_out rounded up to 32); 0: row-major
+  int nar_ok;           // the launch's kernel runs narrow tiles where the table lists them
+                        // (set by launch_bf16_gemm; read by tail_reduce_kernel, so that it
+                        // numbers the tail items exactly as the GEMM launches did)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -115,87 +118,7 @@ constexpr int kGemmThreads = 512;
 
 // lds_dma16, wait_vm_lds and stage_barrier: moe_common.h
 
-// Whether a launch runs narrow tiles. A narrow tile reads twice the B rows per item of a
-// full one, and its expert's B on its own; a launch that splits its tail (the down
-// projection, PART 1 / 2) runs all of its tail at once, so it uses them only when they are at
-// least a quarter of the m-tiles (then most tiles stream their weights anyway and the halved
-// MFMA work wins). Otherwise every m-tile runs with the full shape, in table order.
-MOE_DEV bool use_narrow(const int* tiles, bool split) {
-  const int n_nar = tiles[0] - tiles[1];
-  return n_nar > 0 && (!split || 4 * n_nar >= tiles[0]);
-}
-
-// Work items of a grouped GEMM with NT n-tiles per full m-tile: NT per m-tile, or with narrow
-// tiles NT per full m-tile and ceil(NT / 2) per narrow one.
-MOE_DEV long long gemm_items(const int* tiles, int NT, bool nar) {
-  return nar ? (long long)tiles[1] * NT + (long long)(tiles[0] - tiles[1]) * ((NT + 1) >> 1)
-             : (long long)tiles[0] * NT;
-}
-
-// Narrow items a launch of `grid` persistent workgroups that splits the tail (PART 1 / 2)
-// places last: as many as the tail (the last S mod grid items) holds, so that the whole
-// rounds are made of full items where possible (every workgroup then runs the same work) and
-// the narrow items' K pieces are balanced like any tail item's.
-MOE_DEV long long narrow_tail(const int* tiles, int NT, bool nar, int grid) {
-  if (!nar) return 0;
-  const long long S = gemm_items(tiles, NT, true);
-  const long long S_nar = (long long)(tiles[0] - tiles[1]) * ((NT + 1) >> 1);
-  return min(S_nar, S - S / grid * grid);
-}
-
-// Work item u (0 <= u < gemm_items): its m-tile (expert, first row, rows) and n-tile; returns
-// whether it is narrow. Without narrow tiles the items are expert-major, then in supertiles
-// of the expert's m-tiles. With them, the full m-tiles (fmap) are ordered that way; the last
-// n_tail items are narrow ones, and the other narrow items are spread evenly through the rest
-// (item u is the narrow item floor(u Sn / S) when that count steps at u), so that every XCD's
-// run and every round holds its share of them.
-MOE_DEV bool decode_tile(const int* tiles, long long u, int NT, bool use_nar, long long n_tail, int* e, int* row0,
-                         int* rows, int* nt) {
-  const int* T = tiles + kTileHdr;
-  int t, m;
-  if (!use_nar) {
-    const int* probe = T + kTileInts * (int)(u / NT);
-    const int ts = probe[3];
-    supertile(u - (long long)ts * NT, probe[4], NT, &m, nt);
-    t = ts + m;
-  } else {
-    const int NT2 = (NT + 1) >> 1;
-    const long long s_full = (long long)tiles[1] * NT;
-    const long long S_nar = (long long)(tiles[0] - tiles[1]) * NT2 - n_tail;  // interleaved ones
-    const long long S = s_full + S_nar;
-    long long nb;  // narrow items before u
-    bool nar;
-    if (u >= S) {
-      nb = S_nar + (u - S);
-      nar = true;
-    } else {
-      nb = u * S_nar / S;
-      nar = (u + 1) * S_nar / S > nb;
-    }
-    if (nar) {
-      const long long j = nb / NT2;
-      t = tiles[tiles[3] + (int)j];
-      *nt = (int)(nb - j * NT2);
-    } else {
-      const int* fmap = tiles + tiles[2];
-      const long long s = u - nb;  // full item
-      const int* probe = T + kTileInts * fmap[(int)(s / NT)];
-      const int fs = probe[5];
-      supertile(s - (long long)fs * NT, probe[6], NT, &m, nt);
-      t = fmap[fs + m];
-    }
-    const int* q = T + kTileInts * t;
-    *e = q[0];
-    *row0 = q[1];
-    *rows = q[2];
-    return nar;
-  }
-  const int* q = T + kTileInts * t;
-  *e = q[0];
-  *row0 = q[1];
-  *rows = q[2];
-  return false;
-}
+// The launch's work items and the operand addresses: gemm_sched.h.
 
 // A wave's share of a tile's operand copies into the LDS stages (full or narrow shape):
 // stage j holds A at sa(j) and B at sb(j); copy instruction i of the wave fills 16 rows of a
@@ -242,8 +165,7 @@ struct TileLoads {
       const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
       const int rc = min(rr, rows - 1);
       const int rel = row0 - rb + rc;  // tiled: row within the blocks from rb
-      r.ao[i] = a_tiled ? (uint32_t)((rel & ~(kTiledRows - 1)) * g.a_kp + (rel & (kTiledRows - 1)) * kTiledK + lchunk) * 2u
-                        : (uint32_t)(rc * K + lchunk) * 2u;
+      r.ao[i] = a_tiled ? tiled_row_off(rel, g.a_kp, lchunk) : rm_row_off(rc, K, lchunk);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -260,30 +182,26 @@ struct TileLoads {
       cl = min(cl, n_out - 1 - n0);
       // tiled: block cl / 128, row cl % 128 of its 32-element slab rows (the slab offset
       // is added per copy)
-      r.bo[i] = tiled ? (uint32_t)((cl & ~(kTiledRows - 1)) * Kb + (cl & (kTiledRows - 1)) * kTiledK + lchunk) * 2u
-                      : (uint32_t)(cl * K + lchunk) * 2u;
+      r.bo[i] = tiled ? tiled_row_off(cl, Kb, lchunk) : rm_row_off(cl, K, lchunk);
     }
     return r;
   }
   // byte offset of reduction index k0 (a multiple of 32) in a tiled operand: slab k0 / 32 of
   // a block (128 x 32 elements each); lanes past K read the padding (zeroed in LDS later)
-  MOE_DEV uint32_t dma_kt(int k0) const { return (uint32_t)k0 * (kTiledRows * 2u); }
+  MOE_DEV uint32_t dma_kt(int k0) const { return tiled_k_off(k0); }
   // A may be tiled (h for the down projection, moe_forward's x_sorted for the up one); the
   // save epilogues of the training path keep it row-major
   MOE_DEV bool a_is_tiled() const { return !kSave<EPI> && g.a_kp > 0; }
-  // byte offset of reduction index k0 for this lane; lanes past K read inside the row (their
-  // chunks are zeroed once they have landed)
-  MOE_DEV uint32_t dma_k(int k0) const {
-    const int K = g.K;
-    return ((K % kBK) != 0 && k0 + lchunk >= K) ? (uint32_t)(K - 8 - lchunk) * 2u : (uint32_t)k0 * 2u;
-  }
+  // byte offset of reduction index k0 for this lane in a row-major operand; lanes past K read
+  // the row's last chunk (zeroed once it has landed); a modular offset, added in 32 bits
+  MOE_DEV uint32_t dma_k(int k0) const { return rm_k_off(g.K, k0, lchunk); }
   // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) into stage j, at byte offset
   // ka (row-major operands) or kt (tiled ones) along K
   MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kt) const {
     const bool is_a = NAR ? c == 0 : (c & 1) == 0;
     const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
-    if (is_a) lds_dma16(sr.a + sr.ao[i] + (a_is_tiled() ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
-    else lds_dma16(sr.b[i] + sr.bo[i] + (g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
+    if (is_a) lds_dma16(sr.a + src_off(sr.ao[i], a_is_tiled() ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
+    else lds_dma16(sr.b[i] + src_off(sr.bo[i], g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
   }
   // every copy of slab k (from the start of K) into stage j
   MOE_DEV void refill(const Src& sr, int j, int k) const {
@@ -639,20 +557,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
   const int NT = g.n_tiles_n;
-  const bool nar = NAR && use_narrow(g.tiles, PART != 0);
-  const long long S_all = gemm_items(g.tiles, NT, nar);
   const int nk_all = (g.K + kBK - 1) / kBK;
-  const long long S_main = (PART == 0) ? S_all : S_all / gridDim.x * gridDim.x;
-  const int q = (PART == 2) ? tail_pieces(S_all - S_main, nk_all, gridDim.x) : 1;
-  const long long n_tail = (PART == 0) ? 0 : narrow_tail(g.tiles, NT, nar, gridDim.x);
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int per_xcd = gridDim.x >> 3;
-  const long long chunk = (S_main + 7) / 8;
-  // work items: [0, S_main) in per-XCD runs, or the tail's (item, piece) pairs
-  const long long w_begin = (PART == 2) ? (long long)blockIdx.x : (long long)xcd * chunk + slot;
-  const long long w_end = (PART == 2) ? (S_all - S_main) * q : min(S_main, (long long)xcd * chunk + chunk);
-  const int w_step = (PART == 2) ? (int)gridDim.x : per_xcd;
+  // this launch's items and this workgroup's run of them (gemm_sched.h)
+  const GemmPlan P = gemm_plan(g.tiles, NT, NAR && g.nar_ok, PART, gridDim.x, nk_all);
+  const GemmRange R = gemm_range(P, PART, blockIdx.x, gridDim.x);
+  const long long w_begin = R.begin, w_end = R.end;
+  const int w_step = R.step;
 
   if constexpr (!NAR && PART != 2) {
     // full-shape, whole-K items: each item issues the next one's first stages before its
@@ -682,15 +592,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     }
   } else {
   for (long long w = w_begin; w < w_end; w += w_step) {
-    long long s = w;       // work item (position in the sequence)
-    int kso = 0;           // first slab of this item
-    int nk = nk_all;       // slabs of this item
-    if (PART == 2) {
-      s = S_main + w / q;
-      const int piece = (int)(w % q);
-      kso = piece * nk_all / q;
-      nk = (piece + 1) * nk_all / q - kso;
-    }
+    int kso, nk, piece;  // this item's slabs [kso, kso + nk)
+    const long long s = plan_item(P, PART, w, nk_all, &kso, &nk, &piece);  // position in the sequence
     // Rebuilt / made opaque per item, so that what the two tile shapes derive from them is
     // computed per tile instead of being held (and spilled to memory) across the whole loop;
     // the thread index comes from the wave index and the lane's position in the wave.
@@ -698,13 +601,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     asm volatile("" : "+s"(wave_i), "+s"(NT_i));
     const int tid_i = wave_i * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     int e, row0, rows, nt;
-    const bool is_nar = decode_tile(g.tiles, s, NT_i, nar, n_tail, &e, &row0, &rows, &nt);
+    const bool is_nar = decode_tile(g.tiles, s, NT_i, P.nar, P.n_tail, &e, &row0, &rows, &nt);
     if constexpr (NAR) {
-      if (is_nar) gemm_tile<EPI, PART, 1>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
-      else gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
+      if (is_nar) gemm_tile<EPI, PART, 1>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
+      else gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
     } else {
       (void)is_nar;
-      gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, q);
+      gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
     }
   }
   }
@@ -715,16 +618,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
 // rows (4 of a full tile's 256, 2 of a narrow tile's 128), a thread per 4 columns.
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
   const int NT = g.n_tiles_n, K = g.K, n_out = g.n_out;
-  const bool use_nar = use_narrow(g.tiles, true);
-  const long long S_all = gemm_items(g.tiles, NT, use_nar);
-  const int G = g.grid;
-  const long long S_main = S_all / G * G;
-  const long long S_tail = S_all - S_main;
-  const int q = tail_pieces(S_tail, (K + kBK - 1) / kBK, G);
+  // the same plan as the PART 2 launch (same table, narrow decision and grid)
+  const GemmPlan P = gemm_plan(g.tiles, NT, g.nar_ok != 0, 2, g.grid, (K + kBK - 1) / kBK);
+  const long long S_tail = P.S_all - P.S_main;
+  const int q = P.q;
   if (q <= 1 || blockIdx.x >= S_tail) return;
   int e, row0, rows, nt;
-  const bool nar = decode_tile(g.tiles, S_main + blockIdx.x, NT, use_nar, narrow_tail(g.tiles, NT, use_nar, G), &e,
-                               &row0, &rows, &nt);
+  const bool nar = decode_tile(g.tiles, P.S_main + blockIdx.x, NT, P.nar, P.n_tail, &e, &row0, &rows, &nt);
   const int tbn = nar ? 512 : 256;  // the partial tile's columns
   const int r = nar ? blockIdx.y * 2 + (threadIdx.x >> 7) : blockIdx.y * 4 + (threadIdx.x >> 6);
   const int c4 = nar ? (threadIdx.x & 127) * 4 : (threadIdx.x & 63) * 4;
@@ -842,7 +742,7 @@ int ffn_tile_rows(const moe_config& c) { return c.dtype == MOE_BF16 ? kBM : kFBM
 // average (A / E <= 1024 rows). With more rows per expert they save little, and the narrow
 // shape's registers slow the full tiles of the same kernel.
 int ffn_narrow_rows(const moe_config& c) {
-  return (c.dtype == MOE_BF16 && c.n_tokens * c.top_k <= 1024LL * c.n_experts) ? kBM / 2 : 0;
+  return narrow_rows_for(c.n_tokens * c.top_k, c.n_experts, c.dtype == MOE_BF16);
 }
 // The down projection's split launches take narrow tiles only when they are a quarter of the
 // m-tiles (use_narrow), which between 512 and 1024 rows per expert they mostly are not: there
@@ -850,12 +750,13 @@ int ffn_narrow_rows(const moe_config& c) {
 // (fine-grained shape, same-box A/B: down 0.550 ms with the narrow-capable kernel, 0.542 ms
 // without).
 static bool down_narrow(const moe_config& c) {
-  return ffn_narrow_rows(c) > 0 && c.n_tokens * c.top_k <= 512LL * c.n_experts;
+  return down_narrow_for(c.n_tokens * c.top_k, c.n_experts, c.dtype == MOE_BF16);
 }
 
 // A bf16 grouped GEMM launch: the instantiation with narrow tiles when the table may hold them.
 template <int EPI, int PART = 0>
-void launch_bf16_gemm(bool narrow, int grid, const GemmArgs& g, hipStream_t stream) {
+void launch_bf16_gemm(bool narrow, int grid, GemmArgs g, hipStream_t stream) {
+  g.nar_ok = narrow ? 1 : 0;
   if (narrow) expert_gemm_bf16_kernel<EPI, PART, true><<<grid, kGemmThreads, 0, stream>>>(g);
   else expert_gemm_bf16_kernel<EPI, PART, false><<<grid, kGemmThreads, 0, stream>>>(g);
 }
@@ -1004,6 +905,7 @@ hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, c
       // chip, then the fixed-order sum of the pieces with the epilogue
       g.partial = tail_part;
       g.grid = grid;
+      g.nar_ok = down_narrow(c) ? 1 : 0;  // what the two GEMM launches use
       launch_bf16_gemm<kEpiDown, 1>(down_narrow(c), grid, g, stream);
       launch_bf16_gemm<kEpiDown, 2>(down_narrow(c), grid, g, stream);
       tail_reduce_kernel<<<dim3(grid, kBM / 4), 256, 0, stream>>>(g);

@@ -7,6 +7,7 @@
 
 #include "../../include/moe.h"
 #include "moe_common.h"
+#include "gemm_sched.h"
 
 namespace moe {
 
@@ -61,40 +62,6 @@ struct WsLayout {
   // backward (its own regions; see carve_backward)
   void* bwd = nullptr;
 };
-
-// m-tile table of the grouped GEMMs. Header: tiles[0] = m-tiles, tiles[1] = full m-tiles,
-// tiles[2] / tiles[3] = offsets (in ints, from tiles) of fmap / nmap, tiles[4..7] = 16 zero
-// bytes. m-tile t (experts in order, each expert's rows in order) is
-// tiles[kTileHdr + kTileInts t ..] = (expert, first row, rows in the tile, the expert's first
-// m-tile, the expert's m-tile count, the expert's first full m-tile in fmap, the expert's
-// full m-tiles). An expert's last m-tile is narrow when it has at most `narrow` rows;
-// fmap[i] is the table index of the i-th full m-tile and nmap[j] that of the j-th narrow one.
-constexpr int kTileHdr = 8, kTileInts = 8;
-// ints of a tile table for at most cap m-tiles
-constexpr long long tile_table_ints(long long cap) { return kTileHdr + (kTileInts + 2) * cap; }
-
-// K pieces of each tail tile: enough (tile, piece) pairs to fill the grid, at least 4 slabs
-// per piece, at most kMaxTailItems pairs (the partial buffer's size).
-constexpr int kMaxTailItems = 256;
-MOE_DEV int tail_pieces(long long s_tail, int nk_all, int grid) {
-  if (s_tail <= 0) return 1;
-  const long long q = min((long long)grid / s_tail, (long long)kMaxTailItems / s_tail);
-  return (int)max(1ll, min(q, (long long)(nk_all / 4)));
-}
-
-// Supertile order of a group of `me` m-tiles with NT n-tiles each: bands of kGM m-tiles, each
-// walked in groups of kGN n-tiles with the m-tile fastest, so the tiles that run at the same
-// time share A and B panels in L2. Local item l -> (m-tile within the group, n-tile).
-constexpr int kGM = 8, kGN = 4;
-MOE_DEV void supertile(long long l, int me, int NT, int* mt, int* nt) {
-  const int band = (int)(l / ((long long)kGM * NT));
-  const int lb = (int)(l - (long long)band * kGM * NT);
-  const int bm = min(kGM, me - kGM * band);
-  const int grpn = lb / (kGN * bm);
-  const int r = lb - grpn * kGN * bm;
-  *mt = kGM * band + r % bm;
-  *nt = grpn * kGN + r / bm;
-}
 
 // Builds the tile table with one workgroup of at least E threads (thread e owns expert e).
 // lo_e / hi_e are expert e's row range; ranges outside [0, rows] or decreasing are clamped,
@@ -270,7 +237,6 @@ int ffn_narrow_rows(const moe_config& c);
 // Tiled weights (MOE_WEIGHTS_TILED): rows per block and reduction elements per slab, the
 // padded sizes of weight `which` (0: W1 / W3, N = d_ff, K = d; 1: W2, N = d, K = d_ff), its
 // element count, and the re-layout kernel.
-constexpr int kTiledRows = 128, kTiledK = 32;
 inline int tiled_n(const moe_config& c, int which) { return ((which ? c.d_model : c.d_ff) + kTiledRows - 1) / kTiledRows * kTiledRows; }
 inline int tiled_k(const moe_config& c, int which) { return ((which ? c.d_ff : c.d_model) + kTiledK - 1) / kTiledK * kTiledK; }
 inline size_t packed_weight_elems(const moe_config& c, int which) {
