@@ -241,6 +241,11 @@ moe_status moe_shared_ffn(const moe_config* cfg, const void* x, const void* s_w1
  * statistics still describe the routing before any drop).
  * With cfg->weight_layout = MOE_WEIGHTS_TILED, w1, w3 and w2 are moe_pack_weights copies (the
  * shared expert's weights stay row-major); the results are the same.
+ * perm, inv_perm, offsets: NULL, or int32 buffers that receive the dispatch arrays the call
+ * itself used ([L7.8] §2.2): dropless, perm [A], inv_perm [A] and offsets [E+1] exactly as
+ * moe_dispatch defines them for topk_ids; with cfg->capacity_factor > 0, moe_dispatch_capacity's
+ * perm_kept (its first offsets[E] entries), slot and offsets. The call then writes them there
+ * instead of into its workspace, so asking for them costs nothing. Each may be given alone.
  * stage_events: NULL, or 6 hipEvent_t (as void*) recorded on `stream` at the start, after
  * routing, after dispatch, after the up projection, after the down projection (and the
  * shared expert, when there is one) and at the end.
@@ -252,6 +257,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const void* s_w1, const void* s_w3, const void* s_b1,
                        const void* s_w2, const void* s_b2,
                        void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                       int32_t* perm, int32_t* inv_perm, int32_t* offsets,
                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 
 /* Gradients written by moe_backward: device pointers owned by the caller, each shaped like

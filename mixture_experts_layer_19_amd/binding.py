@@ -128,7 +128,7 @@ def lib():
     L.moe_expert_ffn.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.moe_combine.argtypes = [S, _P, _P, _P, _P, _P, _P]
     L.moe_shared_ffn.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
-    L.moe_forward.argtypes = [S] + [_P] * 20 + [ctypes.c_size_t, _P, _P]
+    L.moe_forward.argtypes = [S] + [_P] * 23 + [ctypes.c_size_t, _P, _P]
     L.moe_get_device_error.argtypes = [_P, _P]
     L.moe_update_bias.argtypes = [S, _P, _P, ctypes.c_float, _P]
     L.moe_dispatch_capacity.argtypes = [S, ctypes.c_float] + [_P] * 10 + [ctypes.c_size_t, _P]
@@ -375,11 +375,14 @@ def moe_shared_ffn(cfg: LayerConfig, x, s_w1, s_w3, s_w2, s_b1=None, s_b2=None, 
 
 
 def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, logit_bias=None, sel_bias=None,
-                *, shared: Optional[dict] = None, ws=None, out=None, stage_events: Optional[Sequence[int]] = None):
+                *, shared: Optional[dict] = None, ws=None, out=None, stage_events: Optional[Sequence[int]] = None,
+                want_dispatch: bool = False):
     """The whole layer. Returns dict y [N,d], topk_ids, topk_w, counts, stats. `shared`: the
     shared expert's weights {s_w1, s_w3, s_w2, s_b1, s_b2} when cfg.d_ff_shared > 0. `out` may
     hold preallocated outputs (same keys) and `ws` a preallocated workspace, so that repeated
-    calls allocate nothing. stage_events: 6 raw hipEvent_t handles (ints) or None."""
+    calls allocate nothing. stage_events: 6 raw hipEvent_t handles (ints) or None.
+    want_dispatch: also return the dispatch arrays the call used, perm [A], inv_perm [A] and
+    offsets [E+1] (int32; with a capacity factor: perm_kept, slot and the kept offsets)."""
     N, d, E, k, f = cfg.n_tokens, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff
     T = cfg.torch_dtype
     sh = shared or {}
@@ -409,6 +412,11 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
             "counts": torch.empty((E,), dtype=torch.int32, device=dev),
             "stats": torch.empty((2 * E + 2,), dtype=torch.float32, device=dev),
         }
+    if want_dispatch and "perm" not in out:
+        dev = w_router.device
+        out["perm"] = torch.empty((N * k,), dtype=torch.int32, device=dev)
+        out["inv_perm"] = torch.empty((N * k,), dtype=torch.int32, device=dev)
+        out["offsets"] = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     if ws is None:
         ws = workspace(cfg, Op.FORWARD, w_router.device)
     ev = None
@@ -419,7 +427,8 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
     st = lib().moe_forward(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(sel_bias),
                            _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1), _ptr(s_w3), _ptr(s_b1),
                            _ptr(s_w2), _ptr(s_b2), _ptr(out["y"]), _ptr(out["topk_ids"]),
-                           _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]), _ptr(ws), ws.numel(),
+                           _ptr(out["topk_w"]), _ptr(out["counts"]), _ptr(out["stats"]), _ptr(out.get("perm")),
+                           _ptr(out.get("inv_perm")), _ptr(out.get("offsets")), _ptr(ws), ws.numel(),
                            ev, _stream())
     _check(st, "moe_forward")
     return out

@@ -301,9 +301,13 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        const void* w3, const void* b1, const void* w2, const void* b2,
                        const void* s_w1, const void* s_w3, const void* s_b1, const void* s_w2,
                        const void* s_b2, void* y, int32_t* topk_ids, float* topk_w, int32_t* counts,
-                       float* stats, void* ws, size_t ws_bytes, void* const* stage_events, void* stream) {
+                       float* stats, int32_t* perm_out, int32_t* inv_perm_out, int32_t* offsets_out, void* ws,
+                       size_t ws_bytes, void* const* stage_events, void* stream) {
   MOE_TRY(check_config(cfg, true));
   MOE_TRY(check_shared(cfg, s_w1, s_w3, s_b1, s_w2, s_b2));
+  MOE_TRY(opt_4(perm_out));
+  MOE_TRY(opt_4(inv_perm_out));
+  MOE_TRY(opt_4(offsets_out));
   if (cfg->n_tokens > 0) {
     MOE_TRY(need_t(x));
     MOE_TRY(need_t(y));
@@ -327,6 +331,10 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
       if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
   WsLayout L{};
   MOE_TRY(check_ws(*cfg, MOE_OP_FORWARD, ws, ws_bytes, &L));
+  // dispatch arrays the caller asked for are written in place of the workspace's copies
+  if (perm_out) L.perm = perm_out;
+  if (inv_perm_out) L.inv_perm = inv_perm_out;
+  if (offsets_out) L.offsets = offsets_out;
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto mark = [&](int i) -> moe_status {
     if (!stage_events) return MOE_OK;

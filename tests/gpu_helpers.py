@@ -98,3 +98,32 @@ def assert_close_rel(got, want, tol, what, rows=None):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert err <= tol * max(scale, 1e-30), f"{what}: max|err| {err:.3e} > {tol:.0e} * max|y| {scale:.3e}"
     return err, scale
+
+
+def check_forward_dispatch(out, gpu_ids, E):
+    """moe_forward's own dispatch arrays (want_dispatch=True) against the oracle's stable sort
+    of the device's ids ([L7.8] §2.2): perm, inv_perm, counts and offsets bit-exact, always
+    (an integer-only stage: a near-tie choice changes the ids, never how they are sorted)."""
+    perm, inv, counts, offsets = O.dispatch(np.asarray(gpu_ids), E)
+    assert np.array_equal(out["perm"].cpu().numpy(), perm), "moe_forward's perm differs from the stable sort"
+    assert np.array_equal(out["inv_perm"].cpu().numpy(), inv), "moe_forward's inv_perm differs"
+    assert np.array_equal(out["offsets"].cpu().numpy(), offsets), "moe_forward's offsets differ"
+    assert np.array_equal(out["counts"].cpu().numpy(), counts), "moe_forward's counts differ"
+    return perm, inv, counts, offsets
+
+
+def reference_on_device_choice(x64, params, spec, route, gpu_ids, y_own, logit_bias=None, sel_bias=None):
+    """The oracle output on the device's choice: rows where the device chose as the oracle did
+    keep the oracle's own output y_own; the others (a legitimate near-tie choice) are
+    recomputed by the oracle for the device's ids, with the routers table's gates for that
+    choice (forward_loop(ids=...)). Returns (y_ref, w_ref) for every token."""
+    gpu_ids = np.asarray(gpu_ids)
+    agree = (gpu_ids == route.ids).all(axis=1)
+    y_ref, w_ref = np.array(y_own, copy=True), np.array(route.w, copy=True)
+    rows = np.nonzero(~agree)[0]
+    if rows.size:
+        lb = None if logit_bias is None else logit_bias
+        y_r, r_r = O.forward_loop(x64[rows], params, spec, lb, sel_bias, ids=gpu_ids[rows])
+        y_ref[rows] = y_r
+        w_ref[rows] = r_r.w
+    return y_ref, w_ref

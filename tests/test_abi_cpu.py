@@ -81,7 +81,8 @@ def test_host_validation_codes(bad, status):
     lib = B.lib()
     fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
     st = lib.moe_forward(ctypes.byref(cfg), fake, fake, None, None, fake, fake, None, fake, None,
-                         None, None, None, None, None, fake, fake, fake, fake, fake, fake, 1 << 40, None, None)
+                         None, None, None, None, None, fake, fake, fake, fake, fake, None, None, None, fake, 1 << 40,
+                         None, None)
     assert st == status
 
 
@@ -105,12 +106,19 @@ def test_null_and_misaligned_pointers_and_small_workspace():
     # stage events must all be given when the array is
     ev = (ctypes.c_void_p * 6)(f, f, f, None, f, f)
     st = lib.moe_forward(ctypes.byref(cfg), f, f, None, None, f, f, None, f, None, None, None, None, None, None,
-                         f, f, f, f, f, f, 1 << 40, ev, None)
+                         f, f, f, f, f, None, None, None, f, 1 << 40, ev, None)
     assert st == B.MOE_ERR_INVALID_ARG
+    # the optional dispatch outputs are int32 arrays: 4-byte aligned when given
+    for i in range(3):
+        opt = [None, None, None]
+        opt[i] = ctypes.c_void_p(0x10002)
+        st = lib.moe_forward(ctypes.byref(cfg), f, f, None, None, f, f, None, f, None, None, None, None, None, None,
+                             f, f, f, f, f, *opt, f, 16, None, None)
+        assert st == B.MOE_ERR_UNSUPPORTED
     # shared-expert weights: required iff d_ff_shared > 0 (w3 too for SwiGLU), NULL otherwise
     scfg = B.LayerConfig(8192, 4096, 8, 2, 14336, d_ff_shared=2048).struct()
     fwd = lambda c, *sh: lib.moe_forward(ctypes.byref(c), f, f, None, None, f, f, None, f, None, *sh,
-                                         f, f, f, f, f, f, 1 << 40, None, None)
+                                         f, f, f, f, f, None, None, None, f, 1 << 40, None, None)
     assert fwd(scfg, f, None, None, f, None) == B.MOE_ERR_INVALID_ARG
     assert fwd(cfg, f, f, None, f, None) == B.MOE_ERR_INVALID_ARG
     bad = B.LayerConfig(8192, 4096, 8, 2, 14336, d_ff_shared=12).struct()

@@ -186,24 +186,25 @@ def test_forward_with_capacity(base, kw, cf):
     say(f"[forward capacity] {base} {cfg}")
     inp = W.make_inputs(w, seed=9)
     out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
-                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"])
+                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"], want_dispatch=True)
     torch.cuda.synchronize()
     spec = spec_of(cfg)
     params = oracle_params(inp)
     x64 = f64(inp["x"])
-    r = O.route(x64, params["w_g"], spec, f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    lb, sb = f64(inp["logit_bias"]), f64(inp["sel_bias"])
+    r = O.route(x64, params["w_g"], spec, lb, sb)
     ids = out["topk_ids"].cpu().numpy()
     near, intra, agree = compare_ids(ids, r, cfg.top_k)
-    w_dev_ids = O.gate_weights(r.z, ids, spec)
+    # the oracle's capacity layer on the device's choice: its ranking, drops and gates
+    y_ref, r_dev, slot, kept = O.forward_capacity(x64, params, spec, float(np.float32(cf)), lb, sb, ids=ids)
     cap = O.expert_capacity(cfg.top_k, float(np.float32(cf)), cfg.n_tokens, cfg.n_experts)
-    slot, kept, _ = O.capacity_dispatch(ids, cfg.n_experts, cap)
-    y_ref = np.zeros_like(x64)
-    for t in range(cfg.n_tokens):
-        for j in range(cfg.top_k):
-            if slot[t * cfg.top_k + j] >= 0:
-                e = int(ids[t, j])
-                y_ref[t] += w_dev_ids[t, j] * O.expert_ffn(x64[t][None, :], cfg.act, **O._expert(params, e))[0]
-    y_ref += O.shared_output(x64, params, cfg.act)
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy(), r_dev.w, rtol=1e-5, atol=1e-6)
+    # the dispatch arrays moe_forward used: perm_kept, slot, kept offsets
+    assert np.array_equal(out["inv_perm"].cpu().numpy(), slot), "moe_forward's slots differ from the oracle's"
+    offsets = np.concatenate([[0], np.cumsum(kept)])
+    assert np.array_equal(out["offsets"].cpu().numpy(), offsets)
+    keep = np.nonzero(slot >= 0)[0]
+    assert np.array_equal(out["perm"].cpu().numpy()[slot[keep]], keep)
     dropped = int((slot < 0).sum())
     err, scale = assert_close_rel(f64(out["y"]), y_ref, TOL[cfg.dtype], f"y with capacity ({base})")
     say(f"    capacity {cap}: dropped {dropped} of {slot.size}; max|err| {err:.3e} max|y| {scale:.3e}")

@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (NEAR_TIE, TOL, assert_close_rel, check_dispatch_valid, compare_ids, f64,
-                         oracle_params, spec_of)
+from gpu_helpers import (NEAR_TIE, TOL, assert_close_rel, check_dispatch_valid, check_forward_dispatch,
+                         compare_ids, f64, oracle_params, reference_on_device_choice, spec_of)
 from mixture_experts_layer_19_amd import binding as B
 from mixture_experts_layer_19_amd import workload as W
 from oracle import moe_oracle as O
@@ -31,22 +31,25 @@ def _gpu():
 
 
 def run_forward_and_check(w: W.Workload, seed=0, check_stats=True):
+    """The layer against the oracle: ids bit-exact outside near ties (counted), moe_forward's
+    own dispatch arrays bit-exact against the stable sort of the device's ids, and y on EVERY
+    token, near-tie tokens included, against the oracle on the device's choice."""
     cfg = w.cfg
     say(f"[forward] {w.name} {cfg}")
     inp = W.make_inputs(w, seed=seed)
     out = B.moe_forward(cfg, inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], inp["b1"], inp["b2"],
-                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"])
+                        inp["logit_bias"], inp["sel_bias"], shared=inp["shared"], want_dispatch=True)
     torch.cuda.synchronize()
     params = oracle_params(inp)
     spec = spec_of(cfg)
-    y_ref, r = O.forward_loop(f64(inp["x"]), params, spec, f64(inp["logit_bias"]), f64(inp["sel_bias"]))
+    x64, lb, sb = f64(inp["x"]), f64(inp["logit_bias"]), f64(inp["sel_bias"])
+    y_own, r = O.forward_loop(x64, params, spec, lb, sb)
     ids = out["topk_ids"].cpu().numpy()
     near, intra, agree = compare_ids(ids, r, cfg.top_k)
-    gw = out["topk_w"].cpu().numpy()
-    if agree.any():
-        np.testing.assert_allclose(gw[agree], r.w[agree], rtol=1e-5, atol=1e-6)
+    check_forward_dispatch(out, ids, cfg.n_experts)
+    y_ref, w_ref = reference_on_device_choice(x64, params, spec, r, ids, y_own, lb, sb)
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy(), w_ref, rtol=1e-5, atol=1e-6)
     counts = out["counts"].cpu().numpy()
-    assert np.array_equal(counts, np.bincount(ids.reshape(-1), minlength=cfg.n_experts))
     if agree.all():
         assert np.array_equal(counts, np.bincount(r.ids.reshape(-1), minlength=cfg.n_experts))
     if check_stats:
@@ -56,11 +59,16 @@ def run_forward_and_check(w: W.Workload, seed=0, check_stats=True):
         if agree.all():
             np.testing.assert_allclose(st[:E], f, rtol=1e-6, atol=1e-7)
             np.testing.assert_allclose(st[2 * E], L, rtol=1e-5)
+        else:  # f and L on the device's choice
+            f_dev, _, L_dev = O.load_balance(r.p, ids, E)
+            np.testing.assert_allclose(st[:E], f_dev, rtol=1e-6, atol=1e-7)
+            np.testing.assert_allclose(st[2 * E], L_dev, rtol=1e-5)
         np.testing.assert_allclose(st[E:2 * E], P, rtol=1e-5, atol=1e-7)
         np.testing.assert_allclose(st[2 * E + 1], O.z_loss(r.z), rtol=1e-5, atol=1e-6)
     y = f64(out["y"])
-    err, scale = assert_close_rel(y[agree], y_ref[agree], TOL[cfg.dtype], f"y ({w.name})")
-    say(f"    near-ties {int(near.sum())} intra {int(intra.sum())} max|err| {err:.3e} max|y| {scale:.3e}")
+    err, scale = assert_close_rel(y, y_ref, TOL[cfg.dtype], f"y ({w.name})")
+    say(f"    near-ties {int(near.sum())} intra {int(intra.sum())} recomputed on the device's choice "
+        f"{int((~agree).sum())}; max|err| {err:.3e} max|y| {scale:.3e}")
     return out, r
 
 
@@ -203,6 +211,74 @@ def test_expert_ffn_tile_boundaries(act, bias, d, f, counts):
             ex = {n: (None if p[n] is None else p[n][e]) for n in ("w1", "w2", "w3", "b1", "b2")}
             ref[lo:hi] = O.expert_ffn(xs64[lo:hi], act, **ex) * g64[lo:hi, None]
     err, scale = assert_close_rel(f64(ys), ref, TOL["bf16"], "y_sorted")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
+def _ffn_reference(cfg, inp, xs, offsets, gate, act):
+    """y_sorted by the oracle, expert by expert over the slices offsets gives."""
+    xs64, g64 = f64(xs), (None if gate is None else f64(gate))
+    p = oracle_params(inp)
+    rows = xs.shape[0]
+    ref = np.zeros((rows, cfg.d_model))
+    off = offsets.cpu().numpy()
+    for e in range(cfg.n_experts):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            ex = {n: (None if p[n] is None else p[n][e]) for n in ("w1", "w2", "w3", "b1", "b2")}
+            ref[lo:hi] = O.expert_ffn(xs64[lo:hi], act, **ex) * (1.0 if g64 is None else g64[lo:hi, None])
+    return ref
+
+
+@pytest.mark.parametrize("act,bias,d,f", [("swiglu", False, 8, 8), ("swiglu", False, 16, 24),
+                                          ("gelu", True, 24, 16), ("swiglu", False, 8, 264),
+                                          ("gelu", False, 264, 8), ("swiglu", False, 24, 4104)])
+def test_expert_ffn_short_reduction(act, bias, d, f):
+    """Reductions shorter than one 32-element slab (d or d_ff of 8, 16 or 24): every lane whose
+    chunk lies past K re-reads the row's last chunk (zeroed in LDS), and its source must stay
+    inside the row (gemm_sched.h; checked for every K on the host by tests/sched_check.cpp)."""
+    counts = np.array([300, 0, 129, 40, 1, 256])
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[ffn short K] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act=act, has_bias=bias, dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_short_k", cfg, weight_std=0.3), seed=12)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=12)
+    gate = W.random_gates(rows, 1, seed=12).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    err, scale = assert_close_rel(f64(ys), _ffn_reference(cfg, inp, xs, offsets, gate, act), TOL["bf16"], "y_sorted")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
+@pytest.mark.parametrize("base,kw", [("mixtral", dict(n_tokens=500, d_model=8, d_ff=16)),
+                                     ("mixtral", dict(n_tokens=333, d_model=24, d_ff=8)),
+                                     ("gpt2_small", dict(n_tokens=400, d_model=16, d_ff=24)),
+                                     ("deepseek_v3_shared", dict(n_tokens=200, d_model=16, n_experts=16, top_k=4,
+                                                                 d_ff=24, d_ff_shared=8))])
+def test_forward_short_reduction(base, kw):
+    """The whole layer with d, d_ff and the shared expert's width below one 32-element slab."""
+    run_forward_and_check(W.WORKLOADS[base].scaled(**kw))
+
+
+DOWN_BAND_COUNTS = [600] * 8   # 600 rows per expert: narrow tiles listed, not run by the down projection
+
+
+@pytest.mark.parametrize("d,f", [(256, 264), (1024, 1000), (4096, 520)])
+def test_expert_ffn_down_split_band(d, f):
+    """Between 512 and 1024 rows per expert the tile table lists narrow m-tiles (the up
+    projection runs them) but the down projection's split launches run every m-tile with the
+    full shape; the K pieces of its tail must be summed for exactly the tiles the split launch
+    computed."""
+    counts = np.array(DOWN_BAND_COUNTS)
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[ffn down band] d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act="swiglu", dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_band", cfg, weight_std=0.05), seed=13)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=13)
+    gate = W.random_gates(rows, 1, seed=13).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    err, scale = assert_close_rel(f64(ys), _ffn_reference(cfg, inp, xs, offsets, gate, "swiglu"), TOL["bf16"],
+                                  "y_sorted")
     say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
 
 
