@@ -1,13 +1,15 @@
 """MoE layer benchmark on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
-                [--mode forward|backward] [--weights tiled|rowmajor]
+                [--no-extras] [--mode forward|backward|train] [--weights tiled|rowmajor]
 
 Forward (the default): a step is one whole layer forward (moe_forward: route, dispatch,
 expert up and down projections, combine, statistics) over one batch of synthetic tokens
 already resident in HBM. Prints ONE JSON line: tokens/s plus the roofline of the dominant
 kernel (the fused gate/up expert projection) timed with HIP events that the library records
-on its own stream, and the CPU oracle timed on a bounded sample of the same workload. The
+on its own stream, the near-tie count, the HBM-bound stages timed alone after a MALL flush,
+and the CPU baselines: the float64 oracle on a bounded sample (all cores and one core) and a
+float32 sorted-dispatch CPU reference on all tokens. The
 routed experts' bf16 weights are re-laid out once, before the timed region, into the grouped
 GEMM's tiled layout (moe_pack_weights); --weights rowmajor times them as given instead.
 
@@ -96,16 +98,39 @@ def algorithmic_backward(cfg):
             "router_dx_combine": 4 * N * d * E}
 
 
-def cpu_baseline(w, inp, n_sample=0, target_s=15.0):
-    """The float64 CPU oracle, as it stands, on the first n_sample tokens of the workload
-    (n_sample = 0: sized from an 8-token probe to take about target_s seconds)."""
-    import numpy as np
-    from oracle import moe_oracle as O
+def host_info():
+    """The host the CPU baselines run on: model name, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count()
+        return os.cpu_count()
+
+
+def cpu_baseline(w, inp, n_sample=0, target_s=10.0, target_1core_s=8.0, reference=True):
+    """The float64 CPU oracle, as it stands, on the first n_sample tokens of the workload
+    (n_sample = 0: sized from an 8-token probe to take about target_s seconds), with BLAS on
+    every host core; the same on one core (its own sample, sized the same way); and the
+    float32 sorted-dispatch CPU reference (oracle/cpu_reference.py) on all N tokens."""
+    import numpy as np
+    from oracle import moe_oracle as O
     f64 = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
     cfg = w.cfg
     params = {"w_g": f64(inp["w_router"])}
@@ -116,19 +141,106 @@ def cpu_baseline(w, inp, n_sample=0, target_s=15.0):
     spec = O.Spec(n_experts=cfg.n_experts, top_k=cfg.top_k, router=cfg.router, norm_topk=cfg.norm_topk,
                   routed_scaling=cfg.routed_scaling, act=cfg.act)
     lb, sb = f64(inp["logit_bias"]), f64(inp["sel_bias"])
-    if not n_sample:
+
+    def timed(n_req, n_probe, target):
+        if not n_req:
+            t0 = time.perf_counter()
+            O.forward_loop(f64(inp["x"][:n_probe]), params, spec, lb, sb)
+            per_tok = (time.perf_counter() - t0) / n_probe
+            n_req = int(min(cfg.n_tokens, max(n_probe, target / max(per_tok, 1e-9))))
+        x = f64(inp["x"][:n_req])
         t0 = time.perf_counter()
-        O.forward_loop(f64(inp["x"][:8]), params, spec, lb, sb)
-        per_tok = (time.perf_counter() - t0) / 8
-        n_sample = int(min(cfg.n_tokens, max(8, target_s / max(per_tok, 1e-9))))
-    x = f64(inp["x"][:n_sample])
+        O.forward_loop(x, params, spec, lb, sb)
+        return n_req, time.perf_counter() - t0
+
+    threads = _blas_threads()
+    n_all, dt = timed(n_sample, 8, target_s)
+    res = {"value": n_all / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": (f"per-token float64 oracle (routing, {cfg.top_k} expert FFNs per token, combine) on the "
+                      f"first {n_all} of {cfg.n_tokens} tokens; {dt:.1f} s; weights widened to float64 "
+                      f"before the timed region")}
+    res.update(host_info())
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, dt1 = timed(0, 2, target_1core_s)
+        res["one_core"] = {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"the same oracle on the first {n1} tokens with BLAS limited to one thread; "
+                                     f"{dt1:.1f} s"}
+    except Exception as exc:  # threadpoolctl missing: say so rather than guess
+        res["one_core"] = {"value": None, "note": f"not measured: {exc}"}
+    del params
+    if reference:
+        res["reference_f32"] = cpu_reference_f32(w, inp)
+    return res
+
+
+def cpu_reference_f32(w, inp):
+    """The float32 sorted-dispatch CPU reference (oracle/cpu_reference.py) on all N tokens,
+    BLAS on every host core; the weights are converted to float32 before the timed region."""
+    import numpy as np
+    from oracle import cpu_reference as R
+    cfg = w.cfg
+    f32 = lambda t: None if t is None else t.float().cpu().numpy()
+    params = {"w_g": f32(inp["w_router"])}
+    for name in ("w1", "w3", "w2", "b1", "b2"):
+        params[name] = None if inp[name] is None else [f32(inp[name][e]) for e in range(cfg.n_experts)]
+    for name, t in (inp.get("shared") or {}).items():
+        params[name] = f32(t)
+    x = f32(inp["x"])
+    lb, sb = f32(inp["logit_bias"]), f32(inp["sel_bias"])
     t0 = time.perf_counter()
-    O.forward_loop(x, params, spec, lb, sb)
+    R.forward_f32(x, params, cfg.n_experts, cfg.top_k, cfg.act, cfg.router, cfg.norm_topk, cfg.routed_scaling,
+                  lb, sb)
     dt = time.perf_counter() - t0
-    return {"value": n_sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"per-token float64 oracle (routing, {cfg.top_k} expert FFNs per token, combine) on the "
-                       f"first {n_sample} of {cfg.n_tokens} tokens; {dt:.1f} s; weights widened to float64 "
-                       f"before the timed region")}
+    return {"value": cfg.n_tokens / dt, "unit": "tokens/s", "cores": int(_blas_threads()), "kind": "cpu reference",
+            "sample": f"NumPy float32 sorted dispatch, one matrix product per expert, all {cfg.n_tokens} tokens; "
+                      f"{dt:.2f} s"}
+
+
+def near_tie_count(cfg, inp):
+    """Tokens whose k-th and (k+1)-th selection scores are within 1e-4 on the device (moe_route's
+    margin output, same kernels and inputs as the timed forward): their choice may legitimately
+    differ from the oracle's, and the parity tests check them on the device's choice."""
+    from mixture_experts_layer_19_amd import binding as B
+    r = B.moe_route(cfg, inp["x"], inp["w_router"], inp["logit_bias"], inp["sel_bias"], want_gap=True)
+    return int((r["gap"] < 1e-4).sum().item())
+
+
+def isolated_hbm_stages(cfg, inp, out, reps=10, flush_bytes=1 << 30):
+    """The HBM-bound stages timed on their own, each repetition preceded by a write of
+    flush_bytes of scratch so that the 256 MB MALL holds none of their inputs: moe_dispatch
+    (the standalone call: histogram, scan, scatter and row copy of the forward's own ids) and
+    moe_combine (the forward's combine: y_sorted already gate-scaled). HIP events on the
+    library's stream; median and minimum over reps. GB/s use the algorithmic bytes."""
+    import torch
+    from mixture_experts_layer_19_amd import binding as B
+    work = algorithmic(cfg)
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    ev = B.HipEvents(2)
+    d = B.moe_dispatch(cfg, inp["x"], out["topk_ids"])
+    res = {}
+    for name in ("dispatch", "combine"):
+        ms = []
+        for i in range(reps):
+            scratch.fill_(i)
+            ev.record(0)
+            if name == "dispatch":
+                d = B.moe_dispatch(cfg, inp["x"], out["topk_ids"], ws=d["ws"])
+            else:
+                B.moe_combine(cfg, d["x_sorted"], None, d["inv_perm"])
+            ev.record(1)
+            ms.append(ev.elapsed_ms(0, 1))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        nbytes = work[f"{name}_bytes"]
+        res[name] = {"median_us": round(med * 1e3, 2), "min_us": round(ms[0] * 1e3, 2),
+                     "gbs": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                     "algorithmic_bytes": nbytes}
+    res["note"] = (f"each of {reps} runs after writing {flush_bytes >> 20} MiB of scratch; dispatch is the "
+                   f"standalone moe_dispatch (it also histograms and scans the ids, which the forward's "
+                   f"routing does for it); x_sorted row-major")
+    return res
 
 
 def cpu_baseline_backward(w, inp, dy, n_sample=0, target_s=15.0, aux_coef=0.0, z_coef=0.0):
@@ -273,6 +385,9 @@ def main():
                     help="forward: routed experts' weights re-laid out once into the tiled layout "
                          "(moe_pack_weights, outside the timed region) or row-major as given")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="forward: skip the near-tie count and the MALL-flushed isolated stage timings "
+                         "(so that a kernel trace holds only the timed forward's kernels)")
     ap.add_argument("--mode", choices=("forward", "backward", "train"), default="forward")
     ap.add_argument("--recompute", action="store_true",
                     help="backward: recompute routing, dispatch and the up projection instead of a saved forward")
@@ -408,6 +523,9 @@ def main():
         "expert_rows": {"min": int(counts.min()), "max": int(counts.max()), "empty": int((counts == 0).sum())},
         "events_vs_wall": fwd_ms_events / ms_per_step,
     }
+    if not args.no_extras:
+        res["near_ties"] = near_tie_count(cfg, inp)
+        res["isolated_stages"] = isolated_hbm_stages(cfg, inp, out)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample)
     print(json.dumps(res), flush=True)
