@@ -260,6 +260,26 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        int32_t* perm, int32_t* inv_perm, int32_t* offsets,
                        void* ws, size_t ws_bytes, void* const* stage_events, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_forward with the same arguments minus the
+ * workspace, perm / inv_perm / offsets and stage events. Its scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds from module load to process
+ * end; the call allocates and frees nothing. Configurations whose moe_workspace_size(cfg,
+ * MOE_OP_FORWARD) exceeds MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_ERR_WORKSPACE before
+ * anything is enqueued: 128 MiB covers about 700 tokens at Mixtral width (d = 4096, E = 8, k = 2,
+ * d_ff = 14336), of which 64 MiB are the down projection's split-K partials at any size. Every call on one GPU uses that GPU's single array, which keeps the last call's
+ * contents: calls that overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and must not be issued. Results equal moe_forward's, bit for bit. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* logit_bias, const float* sel_bias,
+                               const void* w1, const void* w3, const void* b1,
+                               const void* w2, const void* b2,
+                               const void* s_w1, const void* s_w3, const void* s_b1,
+                               const void* s_w2, const void* s_b2,
+                               void* y, int32_t* topk_ids, float* topk_w, int32_t* counts, float* stats,
+                               void* stream);
+
 /* Gradients written by moe_backward: device pointers owned by the caller, each shaped like
  * the tensor it is the gradient of, element type T unless stated. */
 typedef struct {

@@ -129,6 +129,7 @@ def lib():
     L.moe_combine.argtypes = [S, _P, _P, _P, _P, _P, _P]
     L.moe_shared_ffn.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.moe_forward.argtypes = [S] + [_P] * 23 + [ctypes.c_size_t, _P, _P]
+    L.moe_forward_noalloc.argtypes = [S] + [_P] * 20
     L.moe_get_device_error.argtypes = [_P, _P]
     L.moe_update_bias.argtypes = [S, _P, _P, ctypes.c_float, _P]
     L.moe_dispatch_capacity.argtypes = [S, ctypes.c_float] + [_P] * 10 + [ctypes.c_size_t, _P]
@@ -144,7 +145,7 @@ def lib():
     L.moe_status_string.restype = ctypes.c_char_p
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_get_device_error",
                  "moe_update_bias", "moe_shared_ffn", "moe_dispatch_capacity", "moe_backward",
-                 "moe_forward_train", "moe_pack_weights"):
+                 "moe_forward_train", "moe_pack_weights", "moe_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -431,6 +432,25 @@ def moe_forward(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, log
                            _ptr(out.get("inv_perm")), _ptr(out.get("offsets")), _ptr(ws), ws.numel(),
                            ev, _stream())
     _check(st, "moe_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(cfg: LayerConfig, x, w_router, w1, w3, w2, b1=None, b2=None, logit_bias=None, sel_bias=None,
+                        *, shared: Optional[dict] = None, out: dict):
+    """moe_forward on the library's static device scratch: the call allocates nothing (the
+    outputs in `out` are the caller's: y, topk_ids, topk_w, counts, stats). Calls on one GPU
+    must not overlap."""
+    sh = shared or {}
+    s_w1, s_w3, s_w2, s_b1, s_b2 = (sh.get(n) for n in ("s_w1", "s_w3", "s_w2", "s_b1", "s_b2"))
+    st = lib().moe_forward_noalloc(ctypes.byref(cfg.struct()), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                   _ptr(sel_bias), _ptr(w1), _ptr(w3), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(s_w1),
+                                   _ptr(s_w3), _ptr(s_b1), _ptr(s_w2), _ptr(s_b2), _ptr(out["y"]),
+                                   _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["counts"]),
+                                   _ptr(out["stats"]), _stream())
+    _check(st, "moe_forward_noalloc")
     return out
 
 

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
                "moe_workspace_size", "moe_get_device_error", "moe_status_string", "moe_update_bias",
                "moe_shared_ffn", "moe_dispatch_capacity", "moe_expert_capacity", "moe_backward",
-               "moe_forward_train", "moe_packed_weight_size", "moe_pack_weights"):
+               "moe_forward_train", "moe_packed_weight_size", "moe_pack_weights", "moe_forward_noalloc"):
         assert fn in names
 
 
@@ -252,3 +252,19 @@ def test_tiled_weight_sizes_and_rejections():
     tiled = B.LayerConfig(1000, 64, 8, 2, 64, weight_layout="tiled").struct()
     st = lib.moe_forward_train(ctypes.byref(tiled), *([f] * 20), 1 << 40, None)
     assert st == B.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_refuses_beyond_its_scratch():
+    """moe_forward_noalloc refuses, on the host, a configuration whose forward workspace exceeds
+    MOE_NOALLOC_SCRATCH_BYTES (the Mixtral-shaped layer at N = 8192 needs about 0.74 GB), and
+    reports an invalid configuration like moe_forward; no pointer is dereferenced."""
+    from mixture_experts_layer_19_amd import workload as W
+    lib = B.lib()
+    f = ctypes.c_void_p(0x10000)
+    call = lambda c: lib.moe_forward_noalloc(ctypes.byref(c.struct()), f, f, None, None, f, f, None, f, None,
+                                             None, None, None, None, None, f, f, f, f, f, None)
+    cfg = W.WORKLOADS["mixtral"].cfg
+    assert B.moe_workspace_size(cfg, B.Op.FORWARD) > B.NOALLOC_SCRATCH_BYTES
+    assert call(cfg) == B.MOE_ERR_WORKSPACE
+    assert call(B.LayerConfig(64, 64, 8, 9, 64)) == B.MOE_ERR_INVALID_ARG      # k > E
+    assert call(B.LayerConfig(64, 60, 8, 2, 64)) == B.MOE_ERR_UNSUPPORTED      # d not a multiple of 8
