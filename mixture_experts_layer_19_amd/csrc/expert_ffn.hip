@@ -11,6 +11,7 @@
 // so the GEMM grids are sized from the worst case on the host and idle experts cost
 // nothing: they own no tile and their weights are never read.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -613,6 +614,377 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// bfloat16 grouped GEMM, 4-wave shape: the launches without narrow tiles.
+//
+// A 256 x 256 tile per workgroup of 4 waves (2 x 2), each wave 128 rows x 128 B-rows on
+// v_mfma_f32_16x16x32_bf16: 8 x 8 blocks of 16 x 16, 256 float32 accumulators per lane.
+// Operands stream through kW4Stages LDS stages of one 32-element K slab (A 16 KiB + B 16 KiB,
+// written by global_load_lds_dwordx4 as in the 8-wave kernel, same swizzle), and a 32 KiB
+// epilogue area follows them (160 KiB in all).
+//
+// Slab pipeline, per wave: while slab s multiplies (64 MFMAs), the wave reads slab s+1's
+// operand fragments into its other register set (16 ds_read_b128, one after every other MFMA
+// of the first half) and refills slab s's stage with slab s + kW4Stages (8 copies, after MFMAs
+// of the second half). One barrier per slab, at its end, once slab s+2 has landed: it makes
+// slab s+2 visible and frees slab s+1's stage (its fragments are in registers by then). A
+// fragment is thus read a whole slab (1024 MFMA cycles) before it is used, and the MFMA pipe
+// sees one barrier per 64 MFMAs.
+//
+// SwiGLU: the wave's 8 B-row blocks alternate 16 gate rows and the 16 up rows of the same
+// output columns, so gate and up of an output land in the same lane (64 output columns per
+// wave, 128 per tile). GELU / down: 128 output columns per wave.
+// ---------------------------------------------------------------------------------------
+constexpr int kW4Threads = 256;
+constexpr int kW4Stages = 4;
+constexpr int kW4StageElems = 2 * kStageElems;  // A [256][32] then B [256][32]
+constexpr int kW4Pitch = 136;                   // staged row pitch (elements) for 128 columns
+constexpr int kW4WaveStage = 16 * kW4Pitch;     // elements of a wave's 16-row staging buffer
+template <int EPI> constexpr int kW4Cols = kSwi<EPI> ? 64 : 128;  // output columns per wave
+// global store instructions per wave in the epilogue of a tile whose rows and columns are all
+// in range: 8 blocks x the flushes of a block x (columns / 32)
+template <int EPI> constexpr int kW4Stores =
+    8 * (EPI == kEpiSwigluSave ? 3 : EPI == kEpiGeluSave ? 2 : 1) * (kW4Cols<EPI> / 32);
+// the next item's first stages go ahead of the epilogue stores when the relaxed wait
+// (2 slabs of copies + the stores) fits the counter
+template <int EPI> constexpr bool kW4Defer = 8 * (kW4Stages - 2) + kW4Stores<EPI> <= 63;
+
+template <int EPI>
+struct W4Loads {
+  static constexpr int kCols = kSwi<EPI> ? 128 : 256;  // output columns per tile
+  struct Src {
+    const char* a;
+    const char* b[4];
+    uint32_t ao[4], bo[4];
+  };
+  const GemmArgs& g;
+  uint16_t* smem;
+  int wave, lchunk, lrow;
+  MOE_DEV W4Loads(const GemmArgs& g_, uint16_t* smem_, int wave_, int lane)
+      : g(g_), smem(smem_), wave(wave_), lchunk(((lane & 3) ^ ((lane >> 4) & 3)) * 8), lrow(lane >> 2) {}
+  MOE_DEV uint16_t* sa(int j) const { return smem + j * kW4StageElems; }
+  MOE_DEV uint16_t* sb(int j) const { return smem + j * kW4StageElems + kBM * kBK; }
+  MOE_DEV bool a_tiled() const { return !kSave<EPI> && g.a_kp > 0; }
+  // copy i (0..3) of A / B covers stage rows (wave * 4 + i) * 16 .. + 15
+  MOE_DEV Src src(int e, int row0, int rows, int nt) const {
+    const int K = g.K, n_out = g.n_out, n0 = nt * kCols;
+    const bool tiled = g.b_kp > 0;
+    const int Kb = tiled ? g.b_kp : K;
+    const size_t b_off = ((size_t)e * (tiled ? g.b_np : n_out) + n0) * Kb * 2;
+    const int rb = row0 & ~(kTiledRows - 1);
+    Src r;
+    r.a = static_cast<const char*>(g.a) + (a_tiled() ? (size_t)rb * g.a_kp * 2 : (size_t)row0 * K * 2);
+    const char* b0_base = static_cast<const char*>(g.b0) + b_off;
+    const char* b1_base = kSwi<EPI> ? static_cast<const char*>(g.b1) + b_off : b0_base;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (wave * 4 + i) * 16 + lrow;
+      const int rc = min(rr, rows - 1);
+      r.ao[i] = a_tiled() ? tiled_row_off(row0 - rb + rc, g.a_kp, lchunk) : rm_row_off(rc, K, lchunk);
+      int cl;
+      if (kSwi<EPI>) {
+        // B-rows 32 c .. 32 c + 15: gate of output columns 16 c ..; the next 16: up of the same
+        cl = (rr >> 5) * 16 + (rr & 15);
+        r.b[i] = (((wave * 4 + i) & 1) != 0) ? b1_base : b0_base;  // uniform per copy
+      } else {
+        cl = rr;
+        r.b[i] = b0_base;
+      }
+      cl = min(cl, n_out - 1 - n0);
+      r.bo[i] = tiled ? tiled_row_off(cl, Kb, lchunk) : rm_row_off(cl, K, lchunk);
+    }
+    return r;
+  }
+  // copy c of a refill (0..3: A, 4..7: B) of global slab k into stage j
+  MOE_DEV void copy(const Src& sr, int c, int j, int k) const {
+    const uint32_t ka = rm_k_off(g.K, k * kBK, lchunk), kt = tiled_k_off(k * kBK);
+    if (c < 4) lds_dma16(sr.a + src_off(sr.ao[c], a_tiled() ? kt : ka), sa(j) + (wave * 4 + c) * 16 * kBK);
+    else lds_dma16(sr.b[c - 4] + src_off(sr.bo[c - 4], g.b_kp > 0 ? kt : ka), sb(j) + (wave * 4 + c - 4) * 16 * kBK);
+  }
+  MOE_DEV void refill(const Src& sr, int j, int k) const {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) copy(sr, c, j, k);
+  }
+  // zero this wave's landed chunks of stage j that lie past K (global slab k is the last one)
+  MOE_DEV void zero_tail(int j, int k, int nk_all, int lane) const {
+    const int K = g.K;
+    if ((K % kBK) == 0 || k != nk_all - 1 || k * kBK + lchunk < K) return;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      *reinterpret_cast<uint4*>(sa(j) + (wave * 4 + c) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sb(j) + (wave * 4 + c) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);
+    }
+  }
+};
+
+// One work item on the 4-wave shape: tile (e, row0, rows, nt) over slabs [kso, kso + nk) of
+// nk_all. PART 2 with q > 1 writes the float32 partial tile of item w. DEFER / RLX and the
+// returned value as for gemm_tile (the relaxed waits count kW4Stores<EPI> stores).
+template <int EPI, int PART, bool DEFER = false, bool RLX = false>
+MOE_DEV int gemm_tile_w4(const GemmArgs& g, uint16_t* smem, int tid, int wave, int e, int row0, int rows, int nt,
+                         int kso, int nk, int nk_all, long long w, int q, long long s_next = -1, int NT = 0,
+                         int* ne = nullptr, int* nrow0 = nullptr, int* nrows = nullptr, int* nnt = nullptr) {
+  using TL = W4Loads<EPI>;
+  constexpr int NST = kW4Stages;
+  constexpr int kCols = TL::kCols;
+  constexpr int kWn = 8 * (NST - 2);                      // copies younger than slab s+2
+  constexpr int kWr = kWn + (RLX ? kW4Stores<EPI> : 0);   // ... with the previous tile's stores
+  static_assert(!DEFER || (PART != 2 && kW4Defer<EPI>), "deferred stores: whole-K items that fit the counter");
+  static_assert(DEFER || !RLX, "relaxed waits follow deferred stores");
+  const int n_out = g.n_out;
+  const int wm = wave & 1, wn = wave >> 1;
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const TL L(g, smem, wave, lane);
+  const typename TL::Src cur = L.src(e, row0, rows, nt);
+  // 16x16x32 operand read: row lane & 15 of a 16-row block, logical chunk lane >> 4
+  const int r16 = (lane & 15) * kBK + (((lane >> 4) ^ (((lane & 15) >> 2) & 3)) * 8);
+  const int a_rd = wm * 128 * kBK + r16, b_rd = wn * 128 * kBK + r16;
+  // the slab held by pipeline position t (copies past the item's end repeat its last slab)
+  auto slab_at = [&](int t) { return kso + min(t, nk - 1); };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 fa[2][8], fb[2][8];
+
+  if (!RLX) {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) L.refill(cur, t, slab_at(t));
+  }
+  L.refill(cur, NST - 1, slab_at(NST - 1));
+  // slabs 0 and 1 landed (the younger copies: slabs 2 .. NST-1, and with RLX the previous
+  // item's stores, issued after this item's first NST-1 slabs); K tails zeroed
+  wait_vm_lds<kWr>();
+  L.zero_tail(0, slab_at(0), nk_all, lane);
+  L.zero_tail(1, slab_at(1), nk_all, lane);
+  wait_vm_lds<63>();
+  stage_barrier();
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    fa[0][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(L.sa(0) + a_rd + t * 16 * kBK));
+    fb[0][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(L.sb(0) + b_rd + t * 16 * kBK));
+  }
+  // every wave's reads of stage 0 are done before slab 0's body refills it
+  wait_vm_lds<kWr>();
+  stage_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // slab s (fragments in set P) multiplies; slab s+1 is read into set 1-P; stage s % NST is
+  // refilled with pipeline position s + NST; at the end slab s+2 has landed and is visible
+  auto body = [&](int s, auto P_, auto W_) {
+    constexpr int P = decltype(P_)::value;
+    constexpr int W = decltype(W_)::value;
+    const int st = s % NST;
+    const int nst = (s + 1) % NST;
+    const uint16_t* ra = L.sa(nst) + a_rd;
+    const uint16_t* rb = L.sb(nst) + b_rd;
+    const int rslab = slab_at(s + NST);
+#pragma unroll
+    for (int mm = 0; mm < 64; ++mm) {
+      const int i = mm >> 3, j = mm & 7;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[P][i], fb[P][j], acc[i][j], 0, 0, 0);
+      if ((mm & 1) == 0 && mm < 32) {
+        const int t = mm >> 1;
+        if (t < 8) fa[1 - P][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ra + t * 16 * kBK));
+        else fb[1 - P][t - 8] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rb + (t - 8) * 16 * kBK));
+      } else if ((mm & 3) == 1 && mm >= 32) {
+        L.copy(cur, (mm - 32) >> 2, st, rslab);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_lds<W>();
+    L.zero_tail((s + 2) % NST, slab_at(s + 2), nk_all, lane);
+    wait_vm_lds<63>();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  body(0, I0{}, std::integral_constant<int, kWr>{});
+  for (int s = 1; s < nk; s += 2) {
+    body(s, I1{}, std::integral_constant<int, kWn>{});
+    if (s + 1 < nk) body(s + 1, I0{}, std::integral_constant<int, kWn>{});
+  }
+  // every copy landed (those past the end included) and every wave is done with the stages
+  wait_vm_lds<0>();
+  __syncthreads();
+
+  if (PART == 2 && q > 1) {
+    // a K piece of a tail tile: raw float32 accumulators to this item's partial tile
+    // [256 rows][256 B-rows] (summed with the epilogue by tail_reduce_kernel)
+    float* pt = g.partial + (size_t)w * (kBM * kBNB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = wm * 128 + i * 16 + 4 * (lane >> 4) + v;
+          const int col = wn * 128 + j * 16 + (lane & 15);
+          pt[row * kBNB + col] = acc[i][j][v];
+        }
+    return 0;
+  }
+  const bool has_next = DEFER && s_next >= 0;
+  if (has_next) decode_tile(g.tiles, s_next, NT, false, 0, ne, nrow0, nrows, nnt);
+  const int n0 = nt * kCols;
+  const bool pre_issue = has_next && rows == kBM && n0 + kCols <= n_out && nk_all >= NST;
+
+  // epilogue area: each wave's 16-row staging buffer, then the tile's row gates and column biases
+  uint16_t* epi = smem + NST * kW4StageElems;
+  float* s_gate = reinterpret_cast<float*>(epi + 4 * kW4WaveStage);
+  float* s_bias = s_gate + kBM;
+  s_gate[tid] = ((EPI == kEpiDown || kSave<EPI>) && g.gate && tid < rows) ? g.gate[row0 + tid] : 1.f;
+  if (tid < kCols)
+    s_bias[tid] = (!kSwi<EPI> && g.bias && n0 + tid < n_out)
+                      ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[(size_t)e * n_out + n0 + tid]) : 0.f;
+  if (pre_issue) {
+    const typename TL::Src nx = L.src(*ne, *nrow0, *nrows, *nnt);
+    const int nk_next = nk_all;  // whole-K items
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) L.refill(nx, t, min(t, nk_next - 1));
+  }
+  __syncthreads();
+
+  // ---- epilogue: per 16-row block i, the wave's outputs are staged as bf16 in its own LDS
+  // buffer and written with 16-byte row stores (tiled h: a store covers 16 rows of one slab)
+  uint16_t* C = static_cast<uint16_t*>(g.c);
+  constexpr int kWC = kW4Cols<EPI>;
+  uint16_t* stg = epi + wave * kW4WaveStage;
+  const int col_base = n0 + wn * kWC;
+  auto put = [&](int v, int c, float x) {  // lane's value for staged row 4 (lane >> 4) + v, column c
+    stg[(4 * (lane >> 4) + v) * kW4Pitch + c] = f32_to_bf16(x);
+  };
+  auto flush = [&](int i, uint16_t* dst, size_t pitch, int ckp = 0) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's staging writes are done
+#pragma unroll
+    for (int it = 0; it < kWC / 32; ++it) {
+      const int idx = it * 64 + lane;
+      const int prow = idx / (kWC / 8), ch = idx % (kWC / 8);
+      const int trow = wm * 128 + i * 16 + prow;
+      const int col = col_base + ch * 8;
+      const uint4 val = *reinterpret_cast<const uint4*>(stg + prow * kW4Pitch + ch * 8);
+      const int R = row0 + trow;
+      const size_t at = ckp > 0 ? (size_t)(R & ~(kTiledRows - 1)) * ckp + (size_t)(col >> 5) * (kTiledRows * kTiledK) +
+                                      (R & (kTiledRows - 1)) * kTiledK + (col & 31)
+                                : (size_t)R * pitch + col;
+      if (trow < rows && col < n_out) *reinterpret_cast<uint4*>(dst + at) = val;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the staging reads are done before the next writes
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rbase = wm * 128 + i * 16 + 4 * (lane >> 4);  // tile row of v = 0
+    if (kSwi<EPI>) {
+      if (EPI == kEpiSwigluSave) {
+        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) put(v, c * 16 + (lane & 15), acc[i][2 * c][v]);
+        flush(i, C2, 2 * (size_t)n_out);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) put(v, c * 16 + (lane & 15), acc[i][2 * c + 1][v]);
+        flush(i, C2 + n_out, 2 * (size_t)n_out);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float h = silu_f(acc[i][2 * c][v]) * acc[i][2 * c + 1][v];
+          put(v, c * 16 + (lane & 15), EPI == kEpiSwigluSave ? s_gate[rbase + v] * h : h);
+        }
+      flush(i, C, n_out, EPI == kEpiSwiglu ? g.c_kp : 0);
+    } else {
+      if (EPI == kEpiGeluSave) {
+        uint16_t* C2 = static_cast<uint16_t*>(g.c2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            put(v, j * 16 + (lane & 15), acc[i][j][v] + s_bias[wn * 128 + j * 16 + (lane & 15)]);
+        flush(i, C2, n_out);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float bj = s_bias[wn * 128 + j * 16 + (lane & 15)];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gs = s_gate[rbase + v];
+          float val;
+          if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
+          else if (EPI == kEpiGeluSave) val = gs * gelu_erf(acc[i][j][v] + bj);
+          else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
+          put(v, j * 16 + (lane & 15), val);
+        }
+      }
+      flush(i, C, n_out, EPI == kEpiGelu ? g.c_kp : 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each block's registers short-lived
+  }
+  if (!DEFER) {
+    __syncthreads();  // the epilogue area before the next item's gates and biases
+    return 0;
+  }
+  return pre_issue ? 2 : 1;
+}
+
+// The 4-wave grouped GEMM (launches without narrow tiles). PART as for
+// expert_gemm_bf16_kernel.
+template <int EPI, int PART = 0>
+__global__ __launch_bounds__(kW4Threads, 1) void expert_gemm_w4_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kW4Stages * kW4StageElems + 2 * kStageElems];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..3
+  const int NT = g.n_tiles_n;
+  const int nk_all = (g.K + kBK - 1) / kBK;
+  const GemmPlan P = gemm_plan(g.tiles, NT, false, PART, gridDim.x, nk_all);
+  const GemmRange R = gemm_range(P, PART, blockIdx.x, gridDim.x);
+  const long long w_begin = R.begin, w_end = R.end;
+  const int w_step = R.step;
+  if constexpr (PART != 2 && kW4Defer<EPI>) {
+    if (w_begin >= w_end) return;
+    int e, row0, rows, nt;
+    decode_tile(g.tiles, w_begin, NT, false, 0, &e, &row0, &rows, &nt);
+    int pre = 1;
+    for (long long w = w_begin;; w += w_step) {
+      int wave_i = wave, NT_i = NT;
+      asm volatile("" : "+s"(wave_i), "+s"(NT_i));
+      const int tid_i = wave_i * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const long long w2 = w + w_step;
+      const long long sn = w2 < w_end ? w2 : -1;
+      int ne = 0, nrow0 = 0, nrows = 0, nnt = 0;
+      if (pre == 2)
+        pre = gemm_tile_w4<EPI, PART, true, true>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w, 1,
+                                                  sn, NT_i, &ne, &nrow0, &nrows, &nnt);
+      else
+        pre = gemm_tile_w4<EPI, PART, true, false>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w,
+                                                   1, sn, NT_i, &ne, &nrow0, &nrows, &nnt);
+      if (w2 >= w_end) break;
+      e = ne;
+      row0 = nrow0;
+      rows = nrows;
+      nt = nnt;
+    }
+  } else {
+    for (long long w = w_begin; w < w_end; w += w_step) {
+      int kso, nk, piece;
+      const long long s = plan_item(P, PART, w, nk_all, &kso, &nk, &piece);
+      int wave_i = wave, NT_i = NT;
+      asm volatile("" : "+s"(wave_i), "+s"(NT_i));
+      const int tid_i = wave_i * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      int e, row0, rows, nt;
+      decode_tile(g.tiles, s, NT_i, false, 0, &e, &row0, &rows, &nt);
+      gemm_tile_w4<EPI, PART>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
+    }
+  }
+}
+
 // The down projection's tail items (PART 2 with q > 1): y_s = (sum of the q partials, in
 // piece order, + b2) * gate, rounded once. Workgroup (t, rg) covers 1 / 64 of tail item t's
 // rows (4 of a full tile's 256, 2 of a narrow tile's 128), a thread per 4 columns.
@@ -754,10 +1126,19 @@ static bool down_narrow(const moe_config& c) {
 }
 
 // A bf16 grouped GEMM launch: the instantiation with narrow tiles when the table may hold them.
+// Which kernel a launch runs. Launches that may run narrow tiles take the 8-wave kernel. The
+// others take the 4-wave kernel when the reduction is long (K >= kW4MinK), where its fewer
+// barriers per MFMA and its slab-ahead operand reads pay, and the 8-wave kernel otherwise, whose
+// per-tile costs (pipeline fill, an epilogue spread over twice the waves) are lower.
+// Same-box A/B (20 steps, 3 rounds): Mixtral-shaped down projection (K = 14336) 1.585 -> 1.497
+// ms with the 4-wave kernel, up projection (K = 4096) 3.34 ms either way; at K = 768 (GPT-2-small
+// up, fine-grained down) the 4-wave kernel was 31 % and 14 % slower.
+constexpr int kW4MinK = 8192;
 template <int EPI, int PART = 0>
 void launch_bf16_gemm(bool narrow, int grid, GemmArgs g, hipStream_t stream) {
   g.nar_ok = narrow ? 1 : 0;
   if (narrow) expert_gemm_bf16_kernel<EPI, PART, true><<<grid, kGemmThreads, 0, stream>>>(g);
+  else if (g.K >= kW4MinK) expert_gemm_w4_kernel<EPI, PART><<<grid, kW4Threads, 0, stream>>>(g);
   else expert_gemm_bf16_kernel<EPI, PART, false><<<grid, kGemmThreads, 0, stream>>>(g);
 }
 
@@ -973,8 +1354,8 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
   g.n_out = c.d_ff_shared;
   if (c.dtype == MOE_BF16) {
     g.n_tiles_n = (c.d_ff_shared + (c.act == MOE_ACT_SWIGLU ? 127 : 255)) / (c.act == MOE_ACT_SWIGLU ? 128 : 256);
-    if (c.act == MOE_ACT_SWIGLU) expert_gemm_bf16_kernel<kEpiSwiglu><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
-    else expert_gemm_bf16_kernel<kEpiGelu><<<persistent_grid(), kGemmThreads, 0, stream>>>(g);
+    if (c.act == MOE_ACT_SWIGLU) launch_bf16_gemm<kEpiSwiglu>(false, persistent_grid(), g, stream);
+    else launch_bf16_gemm<kEpiGelu>(false, persistent_grid(), g, stream);
   } else {
     dim3 grid(mt, (c.d_ff_shared + kFBN - 1) / kFBN);
     if (c.act == MOE_ACT_SWIGLU) expert_gemm_f32_kernel<kEpiSwiglu><<<grid, 256, 0, stream>>>(g);
@@ -991,7 +1372,7 @@ hipError_t launch_shared(const moe_config& c, const WsLayout& L, const void* x, 
   d.n_out = c.d_model;
   if (c.dtype == MOE_BF16) {
     d.n_tiles_n = (c.d_model + 255) / 256;
-    expert_gemm_bf16_kernel<kEpiDown><<<persistent_grid(), kGemmThreads, 0, stream>>>(d);
+    launch_bf16_gemm<kEpiDown>(false, persistent_grid(), d, stream);
   } else {
     dim3 grid(mt, (c.d_model + kFBN - 1) / kFBN);
     expert_gemm_f32_kernel<kEpiDown><<<grid, 256, 0, stream>>>(d);

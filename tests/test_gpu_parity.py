@@ -259,6 +259,30 @@ def test_forward_short_reduction(base, kw):
     run_forward_and_check(W.WORKLOADS[base].scaled(**kw))
 
 
+@pytest.mark.parametrize("act,bias,d,f", [("swiglu", False, 256, 8200), ("gelu", True, 8200, 264),
+                                          ("swiglu", False, 8192, 136)])
+def test_expert_ffn_long_reduction(act, bias, d, f):
+    """Reductions of 8192 elements or more run the 4-wave grouped GEMM: the down projection
+    with a K tail (8200), its split tail and partial tiles; the GELU up projection with biases
+    writing the tiled h; the SwiGLU up projection (8192). Ragged experts, one empty."""
+    counts = np.array([700, 0, 300, 129, 1000, 1])
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[ffn long K] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act=act, has_bias=bias, dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_long_k", cfg, weight_std=0.02), seed=14)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=14)
+    gate = W.random_gates(rows, 1, seed=14).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    err, scale = assert_close_rel(f64(ys), _ffn_reference(cfg, inp, xs, offsets, gate, act), TOL["bf16"], "y_sorted")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
+def test_forward_long_reduction():
+    """The layer at d = 8192 (tiled x_sorted read by the 4-wave up projection)."""
+    run_forward_and_check(W.WORKLOADS["mixtral"].scaled(n_tokens=200, d_model=8192, d_ff=200))
+
+
 DOWN_BAND_COUNTS = [600] * 8   # 600 rows per expert: narrow tiles listed, not run by the down projection
 
 
