@@ -620,8 +620,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
 // A 256 x 256 tile per workgroup of 4 waves (2 x 2), each wave 128 rows x 128 B-rows on
 // v_mfma_f32_16x16x32_bf16: 8 x 8 blocks of 16 x 16, 256 float32 accumulators per lane.
 // Operands stream through kW4Stages LDS stages of one 32-element K slab (A 16 KiB + B 16 KiB,
-// written by global_load_lds_dwordx4 as in the 8-wave kernel, same swizzle), and a 32 KiB
-// epilogue area follows them (160 KiB in all).
+// written by global_load_lds_dwordx4 as in the 8-wave kernel, with a swizzle suited to the
+// 16x16x32 reads), and a 32 KiB epilogue area follows them (160 KiB in all).
 //
 // Slab pipeline, per wave: while slab s multiplies (64 MFMAs), the wave reads slab s+1's
 // operand fragments into its other register set (16 ds_read_b128, one after every other MFMA
@@ -660,8 +660,13 @@ struct W4Loads {
   const GemmArgs& g;
   uint16_t* smem;
   int wave, lchunk, lrow;
+  // lane l writes row l >> 2 of a copy's 16 rows at physical chunk l & 3, which holds logical
+  // chunk (l & 3) ^ ((row >> 1) & 3): the swizzle under which the 16x16x32 operand reads (16
+  // consecutive rows at one logical chunk per 16 lanes) hit no bank conflict (measured with a
+  // read-pattern probe: (row >> 2) & 3, the 8-wave kernel's, costs 0.8 conflict cycles per
+  // ds_read_b128 of this pattern)
   MOE_DEV W4Loads(const GemmArgs& g_, uint16_t* smem_, int wave_, int lane)
-      : g(g_), smem(smem_), wave(wave_), lchunk(((lane & 3) ^ ((lane >> 4) & 3)) * 8), lrow(lane >> 2) {}
+      : g(g_), smem(smem_), wave(wave_), lchunk(((lane & 3) ^ ((lane >> 3) & 3)) * 8), lrow(lane >> 2) {}
   MOE_DEV uint16_t* sa(int j) const { return smem + j * kW4StageElems; }
   MOE_DEV uint16_t* sb(int j) const { return smem + j * kW4StageElems + kBM * kBK; }
   MOE_DEV bool a_tiled() const { return !kSave<EPI> && g.a_kp > 0; }
@@ -738,7 +743,7 @@ MOE_DEV int gemm_tile_w4(const GemmArgs& g, uint16_t* smem, int tid, int wave, i
   const TL L(g, smem, wave, lane);
   const typename TL::Src cur = L.src(e, row0, rows, nt);
   // 16x16x32 operand read: row lane & 15 of a 16-row block, logical chunk lane >> 4
-  const int r16 = (lane & 15) * kBK + (((lane >> 4) ^ (((lane & 15) >> 2) & 3)) * 8);
+  const int r16 = (lane & 15) * kBK + (((lane >> 4) ^ (((lane & 15) >> 1) & 3)) * 8);
   const int a_rd = wm * 128 * kBK + r16, b_rd = wn * 128 * kBK + r16;
   // the slab held by pipeline position t (copies past the item's end repeat its last slab)
   auto slab_at = [&](int t) { return kso + min(t, nk - 1); };
@@ -1130,10 +1135,12 @@ static bool down_narrow(const moe_config& c) {
 // others take the 4-wave kernel when the reduction is long (K >= kW4MinK), where its fewer
 // barriers per MFMA and its slab-ahead operand reads pay, and the 8-wave kernel otherwise, whose
 // per-tile costs (pipeline fill, an epilogue spread over twice the waves) are lower.
-// Same-box A/B (20 steps, 3 rounds): Mixtral-shaped down projection (K = 14336) 1.585 -> 1.497
-// ms with the 4-wave kernel, up projection (K = 4096) 3.34 ms either way; at K = 768 (GPT-2-small
-// up, fine-grained down) the 4-wave kernel was 31 % and 14 % slower.
-constexpr int kW4MinK = 8192;
+// Same-box A/B at the Mixtral shape, 20 steps, 3 rounds (layer ms): both projections on the
+// 4-wave kernel 4.96-4.99; only the down projection (K = 14336) 5.02-5.03; neither 5.03-5.07.
+// The up projection alone (K = 4096) runs 1 % slower on the 4-wave kernel (3.33-3.36 against
+// 3.30-3.31 ms), but the down projection that follows it then takes 1.48 instead of 1.56-1.58
+// ms. At K = 768 (GPT-2-small up, fine-grained down) the 4-wave kernel was 31 % and 14 % slower.
+constexpr int kW4MinK = 4096;
 template <int EPI, int PART = 0>
 void launch_bf16_gemm(bool narrow, int grid, GemmArgs g, hipStream_t stream) {
   g.nar_ok = narrow ? 1 : 0;

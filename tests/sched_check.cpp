@@ -31,7 +31,10 @@ static long long n_checks = 0;
     }                                     \
   } while (0)
 
-static int lane_chunk(int lane) { return ((lane & 3) ^ ((lane >> 4) & 3)) * 8; }
+// the chunk a copy lane reads: the 8-wave kernel's swizzle (map 0) and the 4-wave kernel's (map 1)
+static int lane_chunk(int lane, int map = 0) {
+  return ((lane & 3) ^ (map ? ((lane >> 3) & 3) : ((lane >> 4) & 3))) * 8;
+}
 
 static void check_addresses() {
   for (int K = 8; K <= 65536; K += 8) {
@@ -42,8 +45,8 @@ static void check_addresses() {
       const int k = slabs[si];
       if (k < 0 || k >= nk) continue;
       const int k0 = k * kSchedBK;
-      for (int lane = 0; lane < 64; ++lane) {
-        const int lc = lane_chunk(lane);
+      for (int lm = 0; lm < 128; ++lm) {
+        const int lane = lm & 63, lc = lane_chunk(lane, lm >> 6);
         const bool inside = k0 + lc < K;
         // row-major [rows][K], rows 0, 1 and 255 of a tile
         const int rcs[3] = {0, 1, 255};
