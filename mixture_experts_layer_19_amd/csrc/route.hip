@@ -36,7 +36,30 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
 
   const bool a_ok = (t0 + row) < n_tokens;
   const bf16_t* arow = x + (size_t)(a_ok ? t0 + row : 0) * d;
-  for (int k = kb; k < ke; k += 32) {
+  int k = kb;
+  // four 32-wide steps at a time: every load of the four is in flight before the first
+  // multiply (the same products in the same order as one step at a time)
+  constexpr int kU = 4;
+  for (; k + kU * 32 <= ke; k += kU * 32) {
+    uint4 av[kU], bv[NB][kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int kk = k + u * 32 + kq;
+      av[u] = a_ok ? *reinterpret_cast<const uint4*>(arow + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int e = e0 + b * 16 + row;
+        bv[b][u] = e < n_experts ? *reinterpret_cast<const uint4*>(wg + (size_t)e * d + kk) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                         __builtin_bit_cast(bf16x8, bv[b][u]), acc[b], 0, 0, 0);
+  }
+  for (; k < ke; k += 32) {
     const int kk = k + kq;
     uint4 av = make_uint4(0, 0, 0, 0);
     if (a_ok && kk < ke) av = *reinterpret_cast<const uint4*>(arow + kk);
@@ -374,16 +397,19 @@ __global__ __launch_bounds__(route_waves(EPL) * kWave) void route_tokens_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Final reduction over the routing blocks, one workgroup of 1024 threads. Thread (g, e)
-// with g < G = 1024 / E sums expert e's partials over a contiguous range of blocks
+// Final reduction over the routing blocks, one workgroup of T threads (T = 256 up to 64
+// experts, else 1024). Thread (g, e) with g < G = T / E sums expert e's partials over a
+// contiguous range of blocks
 // (coalesced over e); the G range sums are then combined in a fixed order, so counts, f, P,
 // L and the z-loss are bitwise reproducible. With offsets != null it goes on to the
 // dispatch scan of [L7.8] §2.2 over the same blocks: offsets = exclusive scan of counts,
 // and base[b][e] = offsets[e] + (assignments of expert e in blocks before b), the first
 // sorted slot of block b's run of expert e; then the grouped GEMM's m-tile table.
 // ---------------------------------------------------------------------------------------
-constexpr int kFinThreads = 1024;
-
+// 1024 threads above 64 experts; 256 up to 64 (fewer, cheaper barriers for its ~50 steps:
+// routing stage at the Mixtral shape 46 -> 41 us together with the router projection's batched
+// loads, same-box A/B).
+template <int NT>
 MOE_DEV double block_sum_f64(double v, double* s_red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -392,10 +418,11 @@ MOE_DEV double block_sum_f64(double v, double* s_red) {
   if (lane == 0) s_red[wave] = v;
   __syncthreads();
   double r = 0.0;
-  for (int w = 0; w < kFinThreads / kWave; ++w) r += s_red[w];
+  for (int w = 0; w < NT / kWave; ++w) r += s_red[w];
   return r;
 }
 
+template <int kFinThreads>
 __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArgs a) {
   __shared__ double s_p[kFinThreads];
   __shared__ int s_c[kFinThreads];
@@ -451,10 +478,10 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
     a.stats[E + tid] = (float)P;
     fp = f * P;
   }
-  const double fp_sum = block_sum_f64(fp, s_red);
+  const double fp_sum = block_sum_f64<kFinThreads>(fp, s_red);
   double zl = 0.0;
   for (int b = tid; b < nb; b += kFinThreads) zl += (double)a.part_zl[b];
-  const double zl_sum = block_sum_f64(zl, s_red);
+  const double zl_sum = block_sum_f64<kFinThreads>(zl, s_red);
   if (tid == 0) {
     a.stats[2 * E] = (float)((double)E * fp_sum);
     a.stats[2 * E + 1] = (float)(zl_sum * inv_n);
@@ -685,7 +712,8 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
     fa.tile_narrow = ffn_narrow_rows(c);
     fa.max_tiles = ffn_max_m_tiles(c);
   }
-  route_finalize_kernel<<<1, kFinThreads, 0, stream>>>(fa);
+  if (E <= 64) route_finalize_kernel<256><<<1, 256, 0, stream>>>(fa);
+  else route_finalize_kernel<1024><<<1, 1024, 0, stream>>>(fa);
   return hipGetLastError();
 }
 
