@@ -71,19 +71,29 @@ def file_sha(path):
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def traffic_for(kernel_src, workload, kernel=None):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
-    current source of the kernel; else None. `kernel`: the entry of a per-kernel file."""
+def traffic_for(kernel_src, workload, kernel):
+    """HBM bytes per launch of `kernel` (its short name) from committed rocprofv3 counter runs,
+    if they were taken on the current text of the file that holds it; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("source_sha") != file_sha(kernel_src):
+    if t.get("sources", {}).get(os.path.basename(kernel_src)) != file_sha(kernel_src):
         return None
-    if kernel is not None:
-        return (t.get("kernels", {}).get(kernel) or {}).get("hbm_bytes_per_launch")
-    return t.get("hbm_bytes_per_launch")
+    return (t.get("kernels", {}).get(kernel) or {}).get("hbm_bytes_per_launch")
+
+
+def expert_gemm_kernel(cfg, epi, K):
+    """Short name of the grouped GEMM kernel that runs a bf16 expert-projection launch with
+    epilogue `epi` (0 GELU up, 1 SwiGLU up, 3 / 4 their saving variants) and reduction K,
+    by the library's own rule: the 8-wave kernel with narrow tiles up to 1024 rows per expert,
+    else the 4-wave kernel for K >= 4096, else the 8-wave kernel with full tiles only."""
+    if cfg.n_tokens * cfg.top_k <= 1024 * cfg.n_experts:
+        return f"expert_gemm_bf16_kernel<{epi}, 0, true>"
+    if K >= 4096:
+        return f"expert_gemm_w4_kernel<{epi}, 0>"
+    return f"expert_gemm_bf16_kernel<{epi}, 0, false>"
 
 
 def algorithmic_backward(cfg):
@@ -335,7 +345,7 @@ def run_backward(args, w, inp):
              if stage_ms[s] > 0 and work[s] > 0}
     dom = max((s for s in gemm_stages if work[s] > 0), key=lambda s: stage_ms[s])
     swi = cfg.act == "swiglu"
-    kernel = {"up_recompute": "expert_gemm_bf16_kernel<3>" if swi else "expert_gemm_bf16_kernel<4>",
+    kernel = {"up_recompute": expert_gemm_kernel(cfg, 3 if swi else 4, cfg.d_model),
               "act_backward": "bwd_gemm_kernel<0, 2>" if swi else "bwd_gemm_kernel<0, 3>",
               "dx_rows": "bwd_gemm_kernel<0, 0>", "dw2": "bwd_gemm_kernel<1, 0>", "dw13": "bwd_gemm_kernel<1, 0>"}[dom]
     csrc = os.path.join(ROOT, "mixture_experts_layer_19_amd", "csrc")
@@ -396,8 +406,8 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer has no multi-GPU "
-              f"path in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library runs one "
+              f"GPU's share of the layer and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -479,7 +489,7 @@ def main():
     intensity = work["up_flops"] / ub
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     up_s = stage_ms["expert_up"] * 1e-3
-    kname = "expert_gemm_bf16_kernel<SwiGLU up>" if cfg.act == "swiglu" else "expert_gemm up"
+    kname = expert_gemm_kernel(cfg, 1 if cfg.act == "swiglu" else 0, cfg.d_model)
     src = os.path.join(ROOT, "mixture_experts_layer_19_amd", "csrc", "expert_ffn.hip")
     if intensity >= ridge:
         roof = {"kernel": kname, "bound": "mfma", "achieved": up_tflops, "peak": peak, "unit": "TFLOP/s",
@@ -488,7 +498,7 @@ def main():
         gbs = ub / up_s / 1e9
         roof = {"kernel": kname, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "tflops": up_tflops}
-    roof.update({"traffic": traffic_for(src, w.name), "flops_per_launch": work["up_flops"],
+    roof.update({"traffic": traffic_for(src, w.name, kname), "flops_per_launch": work["up_flops"],
                  "bytes_per_launch": ub, "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
                  "avg_launch_ms": stage_ms["expert_up"]})
     res = {

@@ -23,7 +23,7 @@ Pages cited (by title, section / table / figure):
            MLPExperts listings (nn.GELU, optional biases), "Expert Capacity" and "Computing
            the expert capacity" (capacity_dispatch), the z-loss.
 
-Readings taken where the pages are silent or ambiguous (each also listed in the design doc):
+Readings taken where the pages are silent or ambiguous:
   * selection for the softmax routers uses the logits z (softmax is monotone, so the chosen
     set equals "top k of p"); ties go to the lowest expert id; the k chosen experts are
     stored largest first.
