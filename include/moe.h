@@ -15,8 +15,11 @@
  *
  * Conventions shared by every entry point
  *   - Memory: every tensor pointer is a DEVICE pointer owned by the caller. The library
- *     never allocates, frees or keeps device memory, and keeps no state between calls:
- *     scratch memory comes from the caller's workspace `ws` of `ws_bytes` bytes.
+ *     never allocates or frees device memory, and scratch memory comes from the caller's
+ *     workspace `ws` of `ws_bytes` bytes (moe_forward_noalloc alone uses a static device
+ *     array instead). No call's results depend on an earlier call. The only process-wide
+ *     state is a per-device cache of the compute-unit count (read once per device, it sizes
+ *     the persistent GEMM grids) and moe_forward_noalloc's per-device scratch address.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
  *     enqueue kernels on it and return without synchronising (moe_get_device_error is the
  *     one exception). Outputs are valid once the stream reaches that point.

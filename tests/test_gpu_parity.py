@@ -262,9 +262,10 @@ def test_forward_short_reduction(base, kw):
 @pytest.mark.parametrize("act,bias,d,f", [("swiglu", False, 256, 8200), ("gelu", True, 8200, 264),
                                           ("swiglu", False, 8192, 136)])
 def test_expert_ffn_long_reduction(act, bias, d, f):
-    """Reductions of 8192 elements or more run the 4-wave grouped GEMM: the down projection
-    with a K tail (8200), its split tail and partial tiles; the GELU up projection with biases
-    writing the tiled h; the SwiGLU up projection (8192). Ragged experts, one empty."""
+    """Reductions of 8192 elements or more with few rows per expert (narrow tiles): the down
+    projection with a K tail (8200), its split tail and partial tiles; the GELU up projection
+    with biases writing the tiled h; the SwiGLU up projection (8192). Ragged experts, one
+    empty."""
     counts = np.array([700, 0, 300, 129, 1000, 1])
     rows, E = int(counts.sum()), len(counts)
     say(f"[ffn long K] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
@@ -273,6 +274,31 @@ def test_expert_ffn_long_reduction(act, bias, d, f):
     offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
     xs = W.random_rows(rows, d, cfg.torch_dtype, seed=14)
     gate = W.random_gates(rows, 1, seed=14).reshape(-1)
+    ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
+    err, scale = assert_close_rel(f64(ys), _ffn_reference(cfg, inp, xs, offsets, gate, act), TOL["bf16"], "y_sorted")
+    say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
+
+
+# Experts ending in m-tiles of 20, 50, 100 and 200 rows (the 4-wave kernel multiplies them
+# with 1, 2, 4 and 8 row blocks per wave), one empty expert, and more than 1024 rows per
+# expert on average, so no launch takes the narrow-tile kernel.
+ROW_BLOCK_COUNTS = [1044, 0, 1074, 1124, 1224, 3000]
+
+
+@pytest.mark.parametrize("act,bias,d,f", [("swiglu", False, 4096, 264), ("gelu", True, 264, 4104),
+                                          ("swiglu", False, 4096, 4096)])
+def test_expert_ffn_four_wave_row_blocks(act, bias, d, f):
+    """The 4-wave grouped GEMM (reductions of 4096 or more, no narrow tiles) on partial
+    m-tiles of every row-block class: the SwiGLU up projection (K = 4096), the down projection
+    with a K tail, its split tail and GELU biases (K = 4104), and both at once."""
+    counts = np.array(ROW_BLOCK_COUNTS)
+    rows, E = int(counts.sum()), len(counts)
+    say(f"[ffn 4-wave row blocks] {act} bias={bias} d={d} f={f} counts={counts.tolist()}")
+    cfg = B.LayerConfig(rows, d, E, 1, f, act=act, has_bias=bias, dtype="bf16")
+    inp = W.make_inputs(W.Workload("ffn_row_blocks", cfg, weight_std=0.02), seed=15)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    xs = W.random_rows(rows, d, cfg.torch_dtype, seed=15)
+    gate = W.random_gates(rows, 1, seed=15).reshape(-1)
     ys = B.moe_expert_ffn(cfg, xs, offsets, inp["w1"], inp["w3"], inp["b1"], inp["w2"], inp["b2"], gate)
     err, scale = assert_close_rel(f64(ys), _ffn_reference(cfg, inp, xs, offsets, gate, act), TOL["bf16"], "y_sorted")
     say(f"    max|err| {err:.3e} max|y| {scale:.3e}")
