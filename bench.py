@@ -247,9 +247,27 @@ def isolated_hbm_stages(cfg, inp, out, reps=10, flush_bytes=1 << 30):
         res[name] = {"median_us": round(med * 1e3, 2), "min_us": round(ms[0] * 1e3, 2),
                      "gbs": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
                      "algorithmic_bytes": nbytes}
+    # the chip's practical rate for the same traffic: a plain device copy (torch) of half the
+    # dispatch's bytes into the other half, timed the same way
+    half = work["dispatch_bytes"] // 2 // 16 * 16
+    src = torch.empty(half // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms = []
+    for i in range(reps):
+        scratch.fill_(i)
+        ev.record(0)
+        dst.copy_(src)
+        ev.record(1)
+        ms.append(ev.elapsed_ms(0, 1))
+    ms.sort()
+    med = ms[len(ms) // 2]
+    res["plain_copy"] = {"median_us": round(med * 1e3, 2), "gbs": round(2 * half / (med * 1e-3) / 1e9, 1),
+                         "frac_of_hbm": round(2 * half / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 3), "bytes": 2 * half}
     res["note"] = (f"each of {reps} runs after writing {flush_bytes >> 20} MiB of scratch; dispatch is the "
                    f"standalone moe_dispatch (it also histograms and scans the ids, which the forward's "
-                   f"routing does for it); x_sorted row-major")
+                   f"routing does for it); x_sorted row-major; plain_copy is torch's device copy of the "
+                   f"same number of bytes (half read, half written), the rate a plain copy reaches")
     return res
 
 
