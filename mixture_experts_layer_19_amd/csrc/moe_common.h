@@ -101,6 +101,14 @@ MOE_DEV void lds_dma16(const void* src, uint16_t* lds_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_base;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
+// The same copy with the address as a 64-bit scalar base plus a 32-bit per-lane offset
+// (global_load_lds_dwordx4's saddr form), so a copy whose per-lane part is fixed for a tile
+// needs no vector address arithmetic.
+MOE_DEV void lds_dma16_s(const void* sbase, uint32_t voff, uint16_t* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 // s_waitcnt vmcnt(N) lgkmcnt(0): this wave's loads older than its last N have landed in LDS
 // and its own LDS accesses are done.
 template <int N> MOE_DEV void wait_vm_lds() {

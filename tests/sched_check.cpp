@@ -237,9 +237,25 @@ static void check_schedule(const std::vector<int>& counts, int NT, int grid, int
   }
 }
 
+// supertile is a bijection of a group's items onto its (m-tile, n-tile) cells
+static void check_supertile() {
+  for (int me = 1; me <= 40; ++me)
+    for (int NT : {1, 2, 3, 4, 5, 7, 16, 28, 112}) {
+      std::vector<int> seen((size_t)me * NT, 0);
+      for (long long l = 0; l < (long long)me * NT; ++l) {
+        int mt, nt;
+        supertile(l, me, NT, &mt, &nt);
+        CHECK(mt >= 0 && mt < me && nt >= 0 && nt < NT, "supertile(%lld, %d, %d) = (%d, %d)", l, me, NT, mt, nt);
+        ++seen[(size_t)mt * NT + nt];
+      }
+      for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i] == 1, "supertile %d x %d: cell %zu taken %d times", me, NT, i, seen[i]);
+    }
+}
+
 int main() {
   check_addresses();
   const long long after_addr = n_checks;
+  check_supertile();
 
   // The launch decisions of the down projection (narrow-capable kernel iff down_narrow_for)
   // over shapes that cross A / E = 512 and 1024, and skewed ones.
