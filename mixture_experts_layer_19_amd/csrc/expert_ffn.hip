@@ -199,17 +199,27 @@ struct TileLoads {
   MOE_DEV uint32_t dma_k(int k0) const { return rm_k_off(g.K, k0, lchunk); }
   // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) into stage j, at byte offset
   // ka (row-major operands) or kt (tiled ones) along K
-  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kt) const {
+  // SA: every copy's K part is uniform (tiled operands, or K a multiple of 32; ku = k0 * 2
+  // for row-major ones), taken into the scalar base of the saddr form (no per-copy vector
+  // address arithmetic)
+  template <bool SA>
+  MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kt, uint32_t ku) const {
     const bool is_a = NAR ? c == 0 : (c & 1) == 0;
     const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
-    if (is_a) lds_dma16(sr.a + src_off(sr.ao[i], a_is_tiled() ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
-    else lds_dma16(sr.b[i] + src_off(sr.bo[i], g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
+    if constexpr (SA) {
+      if (is_a) lds_dma16_s(sr.a + (a_is_tiled() ? kt : ku), sr.ao[i], sa(j) + (wave * CA + i) * 16 * kBK);
+      else lds_dma16_s(sr.b[i] + (g.b_kp > 0 ? kt : ku), sr.bo[i], sb(j) + (wave * CB + i) * 16 * kBK);
+    } else {
+      if (is_a) lds_dma16(sr.a + src_off(sr.ao[i], a_is_tiled() ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
+      else lds_dma16(sr.b[i] + src_off(sr.bo[i], g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
+    }
   }
   // every copy of slab k (from the start of K) into stage j
+  template <bool SA>
   MOE_DEV void refill(const Src& sr, int j, int k) const {
-    const uint32_t ka = dma_k(k * kBK), kt = dma_kt(k * kBK);
+    const uint32_t ka = dma_k(k * kBK), kt = dma_kt(k * kBK), ku = (uint32_t)k * kBK * 2u;
 #pragma unroll
-    for (int c = 0; c < CPR; ++c) copy(sr, c, j, ka, kt);
+    for (int c = 0; c < CPR; ++c) copy<SA>(sr, c, j, ka, kt, ku);
   }
 };
 
@@ -231,7 +241,7 @@ template <int EPI> constexpr int kStores =
 // stages were issued by the previous item, followed by exactly kStores<EPI> stores that may
 // still be in flight. Without RLX an item issues its own first stages. Returns for the next
 // item: 2 = RLX, 1 = not.
-template <int EPI, int PART, int NAR, bool DEFER = false, bool RLX = false>
+template <int EPI, int PART, int NAR, bool SA, bool DEFER = false, bool RLX = false>
 MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int e, int row0, int rows, int nt,
                       int kso, int nk, int nk_all, long long w, int q, long long s_next = -1, int NT = 0,
                       int* ne = nullptr, int* nrow0 = nullptr, int* nrows = nullptr, int* nnt = nullptr) {
@@ -278,10 +288,10 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   // count is a compile-time constant at every boundary (the first NST slabs are peeled).
   int relax = RLX ? 3 : 0;
   const typename TL::Src cur = L.src(e, row0, rows, nt);
-  auto copy = [&](int c, int j, uint32_t ka, uint32_t kb) { L.copy(cur, c, j, ka, kb); };
+  auto copy = [&](int c, int j, uint32_t ka, uint32_t kb, uint32_t ku) { L.template copy<SA>(cur, c, j, ka, kb, ku); };
   auto dma_k = [&](int k0) { return L.dma_k(k0); };
   auto refill = [&](int j, int slab) {
-    L.refill(cur, j, kso + slab);
+    L.template refill<SA>(cur, j, kso + slab);
     relax -= relax > 0;
   };
   // zero this wave's copied chunks of the last slab that lie past K (after they landed)
@@ -332,6 +342,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   // number floor((c + 1) 16 / CPR) - 1, so the copies spread over the phase
   auto multiply_refill = [&](int j, int slab) {
     const uint32_t ka = dma_k((kso + slab) * kBK), kb = L.dma_kt((kso + slab) * kBK);
+    const uint32_t ku = (uint32_t)(kso + slab) * kBK * 2u;
 #pragma unroll
     for (int mm = 0; mm < 16; ++mm) {
       const int ks = mm >> 3, i = (mm >> 1) & 3, jj = mm & 1;
@@ -339,7 +350,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
 #pragma unroll
       for (int c = 0; c < CPR; ++c)
         if (mm == (c + 1) * 16 / CPR - 1) {
-          copy(c, j, ka, kb);
+          copy(c, j, ka, kb, ku);
           __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -441,7 +452,7 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
   if (pre_issue) {
     const typename TL::Src nx = L.src(*ne, *nrow0, *nrows, *nnt);
 #pragma unroll
-    for (int j = 0; j < NST - 1; ++j) L.refill(nx, j, min(j, nk_all - 1));
+    for (int j = 0; j < NST - 1; ++j) L.template refill<SA>(nx, j, min(j, nk_all - 1));
   }
   __syncthreads();
 
@@ -553,9 +564,8 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
 // (tail_reduce_kernel sums them and applies the epilogue).
 // NAR: whether the launch may run narrow tiles; without them the narrow shape is not
 // compiled in, and the kernel keeps the registers of the full shape alone.
-template <int EPI, int PART = 0, bool NAR = false>
-__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[10 * kStageElems];
+template <int EPI, int PART, bool NAR, bool SA>
+MOE_DEV void bf16_run(const GemmArgs& g, uint16_t* smem) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
   const int NT = g.n_tiles_n;
@@ -581,10 +591,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
       const long long sn = w2 < w_end ? w2 : -1;
       int ne = 0, nrow0 = 0, nrows = 0, nnt = 0;
       if (pre == 2)
-        pre = gemm_tile<EPI, PART, 0, true, true>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w, 1,
+        pre = gemm_tile<EPI, PART, 0, SA, true, true>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w, 1,
                                                   sn, NT_i, &ne, &nrow0, &nrows, &nnt);
       else
-        pre = gemm_tile<EPI, PART, 0, true, false>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w,
+        pre = gemm_tile<EPI, PART, 0, SA, true, false>(g, smem, tid_i, wave_i, e, row0, rows, nt, 0, nk_all, nk_all, w,
                                                    1, sn, NT_i, &ne, &nrow0, &nrows, &nnt);
       if (w2 >= w_end) break;
       e = ne;
@@ -605,14 +615,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmA
     int e, row0, rows, nt;
     const bool is_nar = decode_tile(g.tiles, s, NT_i, P.nar, P.n_tail, &e, &row0, &rows, &nt);
     if constexpr (NAR) {
-      if (is_nar) gemm_tile<EPI, PART, 1>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
-      else gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
+      if (is_nar) gemm_tile<EPI, PART, 1, SA>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
+      else gemm_tile<EPI, PART, 0, SA>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
     } else {
       (void)is_nar;
-      gemm_tile<EPI, PART, 0>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
+      gemm_tile<EPI, PART, 0, SA>(g, smem, tid_i, wave_i, e, row0, rows, nt, kso, nk, nk_all, w, P.q);
     }
   }
   }
+}
+
+template <int EPI, int PART = 0, bool NAR = false>
+__global__ __launch_bounds__(kGemmThreads, 1) void expert_gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[10 * kStageElems];
+  // copies in saddr form where every copy's K part is uniform (as in the 4-wave kernel).
+  // Same-box A/B, 2 rounds: GPT-2-small layer 0.307-0.308 -> 0.296-0.301 ms, fine-grained
+  // 1.769 -> 1.716-1.720 ms; DeepSeek-V3 (weight-stream bound) unchanged.
+  const bool k_whole = (g.K % kBK) == 0;
+  const bool a_uniform = (!kSave<EPI> && g.a_kp > 0) || k_whole;
+  const bool b_uniform = g.b_kp > 0 || k_whole;
+  if (a_uniform && b_uniform) bf16_run<EPI, PART, NAR, true>(g, smem);
+  else bf16_run<EPI, PART, NAR, false>(g, smem);
 }
 
 // ---------------------------------------------------------------------------------------

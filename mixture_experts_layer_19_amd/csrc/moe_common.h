@@ -70,7 +70,12 @@ MOE_DEV uint4 pack16(const float* in, bf16_t) {
 
 MOE_DEV float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752440f)); }
 MOE_DEV float sigmoid_f(float u) { return 1.0f / (1.0f + expf(-u)); }
-MOE_DEV float silu_f(float u) { return u / (1.0f + expf(-u)); }
+// silu(u) = u sigmoid(u) with the hardware exponential and reciprocal (about 1 ulp each; the
+// result is rounded to bfloat16 at once): 5 vector instructions instead of about 20 for a
+// correctly rounded exp and division, in the up projection's epilogue. A large negative u
+// gives -0, as the exact form does. Same-box A/B, 3 rounds: Mixtral-shaped up projection
+// 3.09 -> 2.94 ms (layer 4.64 -> 4.50 ms), fine-grained layer 1.72 -> 1.66 ms.
+MOE_DEV float silu_f(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
 
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
