@@ -528,22 +528,30 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
         }
         flush(i, h, C, n_out);
       } else {
+        // the half block's values first, as independent chains the scheduler can overlap
+        // (the activations' exp, rcp and erf have latencies of their own), then their
+        // staging writes
+        constexpr int kJ = kSwi<EPI> ? 1 : 2;
+        float val[8][kJ];
 #pragma unroll
-        for (int v = 8 * h; v < 8 * h + 8; ++v) {
+        for (int v = 0; v < 8; ++v) {
+          const int vv = 8 * h + v;
           if (EPI == kEpiSwiglu) {
-            st_lane[srow(v) * kStride] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+            val[v][0] = silu_f(acc[i][0][vv]) * acc[i][1][vv];
           } else {
-            const float gs = gate_of(v);
+            const float gs = gate_of(vv);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kJ; ++j) {
               const float bj = s_bias[wc * kWCols + j * 32 + (lane & 31)];
-              float val;
-              if (EPI == kEpiGelu) val = gelu_erf(acc[i][j][v] + bj);
-              else val = g.pre_gated ? acc[i][j][v] + bj * gs : (acc[i][j][v] + bj) * gs;
-              st_lane[srow(v) * kStride + j * 32] = f32_to_bf16(val);
+              if (EPI == kEpiGelu) val[v][j] = gelu_erf(acc[i][j][vv] + bj);
+              else val[v][j] = g.pre_gated ? acc[i][j][vv] + bj * gs : (acc[i][j][vv] + bj) * gs;
             }
           }
         }
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+#pragma unroll
+          for (int j = 0; j < kJ; ++j) st_lane[srow(8 * h + v) * kStride + j * 32] = f32_to_bf16(val[v][j]);
         flush(i, h, C, n_out, EPI == kEpiDown ? 0 : g.c_kp);  // only h is written tiled
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each half block's registers short-lived
@@ -948,13 +956,18 @@ MOE_DEV int gemm_tile_w4(const GemmArgs& g, uint16_t* smem, int tid, int wave, i
           for (int v = 0; v < 4; ++v) put(v, c * 16 + (lane & 15), acc[i][2 * c + 1][v]);
         flush(i, C2 + n_out, 2 * (size_t)n_out);
       }
+      // the block's 16 activations first, as independent chains the scheduler can overlap
+      // (exp and rcp have latencies of their own), then their staging writes
+      float hv[4][4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float h = silu_f(acc[i][2 * c][v]) * acc[i][2 * c + 1][v];
-          put(v, c * 16 + (lane & 15), EPI == kEpiSwigluSave ? s_gate[rbase + v] * h : h);
-        }
+        for (int v = 0; v < 4; ++v) hv[c][v] = silu_f(acc[i][2 * c][v]) * acc[i][2 * c + 1][v];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          put(v, c * 16 + (lane & 15), EPI == kEpiSwigluSave ? s_gate[rbase + v] * hv[c][v] : hv[c][v]);
       flush(i, C, n_out, EPI == kEpiSwiglu ? g.c_kp : 0);
     } else {
       if (EPI == kEpiGeluSave) {
