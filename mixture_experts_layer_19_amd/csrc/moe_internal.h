@@ -63,11 +63,6 @@ struct WsLayout {
   void* bwd = nullptr;
 };
 
-// Builds the tile table with one workgroup of at least E threads (thread e owns expert e).
-// lo_e / hi_e are expert e's row range; ranges outside [0, rows] or decreasing are clamped,
-// the list is capped at max_tiles (so no access leaves the buffers) and *bad is set.
-// An expert's rows are cut into m-tiles of bm rows; a last tile of at most `narrow` rows
-// (0: none) is narrow. s_scan: kMaxExperts ints of LDS. Every thread of the block must call it.
 // Exclusive prefix sum of v over the threads of the block in thread order (threads without
 // a value pass 0), and the block's total in *total. Every thread of the block calls it; the
 // block size is a multiple of 64. An inclusive scan within each wave by shuffles, then each
@@ -116,20 +111,39 @@ MOE_DEV int expert_excl_scan(int v, int E, int* s_tmp, int* total) {
   return ex;
 }
 
-MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narrow, int max_tiles, int* tiles,
-                              int* s_scan, int* bad) {
-  const int e = threadIdx.x;
+// Exclusive prefix sum of v over the lanes of one wave in lane order, and the wave's total in
+// *total: shuffles only, every lane of the wave calls it.
+MOE_DEV int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  *total = __shfl(x, 63, 64);
+  return x - v;
+}
+
+// The m-tile table, filled by E owners: the caller with e < E owns expert e, whose rows are
+// [lo, hi); callers with e >= E only join the scans. Ranges outside [0, rows] or decreasing
+// are clamped and the list is capped at max_tiles (so no access leaves the buffers); the
+// return value says whether this caller met either. An expert's rows are cut into m-tiles of
+// bm rows; a last tile of at most `narrow` rows (0: none) is narrow. scan(v, &total) is an
+// exclusive prefix sum over the experts in order that every caller makes alike.
+template <class Scan>
+MOE_DEV bool tile_table_fill(int e, int lo, int hi, int E, int rows, int bm, int narrow, int max_tiles, int* tiles,
+                             Scan scan) {
+  bool bad = false;
   if (e < 4) tiles[4 + e] = 0;
   int n = 0, n_nar = 0;
   if (e < E) {
-    if (lo < 0 || hi > rows || hi < lo || (e == 0 && lo != 0)) *bad = 1;
+    if (lo < 0 || hi > rows || hi < lo || (e == 0 && lo != 0)) bad = true;
     lo = min(max(lo, 0), rows);
     hi = min(max(hi, lo), rows);
     n = (hi - lo + bm - 1) / bm;
     n_nar = (n > 0 && hi - lo - (n - 1) * bm <= narrow) ? 1 : 0;
   }
-  // exclusive prefix over experts of v (through s_scan); *total = the sum
-  auto scan = [&](int v, int* total) -> int { return expert_excl_scan(e < E ? v : 0, E, s_scan, total); };
   int total, total_full, total_nar;
   const int start = scan(n, &total);
   const int fstart = scan(n - n_nar, &total_full);
@@ -152,7 +166,7 @@ MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narro
     }
     if (n_nar && nstart < max_tiles && start + n - 1 < max_tiles) nmap[nstart] = start + n - 1;
     if (e == E - 1) {
-      if (total > max_tiles) *bad = 1;
+      if (total > max_tiles) bad = true;
       // with a clamped list every kept m-tile is counted full (their narrow entries may be gone)
       const bool ok = total <= max_tiles;
       tiles[0] = min(total, max_tiles);
@@ -161,7 +175,26 @@ MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narro
       tiles[3] = kTileHdr + (kTileInts + 1) * max_tiles;
     }
   }
+  return bad;
+}
+
+// The tile table from one workgroup of at least E threads (thread e owns expert e); sets *bad
+// (LDS) on a clamped range or list. s_scan: kMaxExperts ints of LDS. Every thread of the
+// block calls it.
+MOE_DEV void build_tile_table(int lo, int hi, int E, int rows, int bm, int narrow, int max_tiles, int* tiles,
+                              int* s_scan, int* bad) {
+  const int e = threadIdx.x;
+  auto scan = [&](int v, int* total) -> int { return expert_excl_scan(e < E ? v : 0, E, s_scan, total); };
+  if (tile_table_fill(e, lo, hi, E, rows, bm, narrow, max_tiles, tiles, scan)) *bad = 1;
   __syncthreads();
+}
+
+// The same from the 64 lanes of one wave (E <= 64, lane e owns expert e), with no barrier;
+// returns whether any lane met a clamped range or list.
+MOE_DEV bool build_tile_table_wave(int lo, int hi, int E, int rows, int bm, int narrow, int max_tiles, int* tiles) {
+  const int e = threadIdx.x & 63;
+  auto scan = [&](int v, int* total) -> int { return wave_excl_scan(e < E ? v : 0, total); };
+  return __ballot(tile_table_fill(e, lo, hi, E, rows, bm, narrow, max_tiles, tiles, scan)) != 0;
 }
 
 // Routing launch shape. A token is handled by a group of lpt lanes (a power of two: E rounded
