@@ -1104,19 +1104,32 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
   const int col = nt * tbn + c4;
   if (r >= rows || col >= n_out) return;
   const float* pt = g.partial + (size_t)blockIdx.x * q * (kBM * kBNB) + r * tbn + c4;
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < q; ++p) {
-    const float4 x = *reinterpret_cast<const float4*>(pt + (size_t)p * (kBM * kBNB));
-    v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
-  }
   const float gs = g.gate ? g.gate[row0 + r] : 1.f;
   const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
+  float b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = bias ? bf16_to_f32(bias[(size_t)e * n_out + col + i]) : 0.f;
+  // the pieces in order; up to kBatch of them requested before the first add
+  constexpr int kBatch = 8;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < q; p0 += kBatch) {
+    float4 x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      x[j] = p0 + j < q ? *reinterpret_cast<const float4*>(pt + (size_t)(p0 + j) * (kBM * kBNB))
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (p0 + j < q) {
+        v[0] += x[j].x;
+        v[1] += x[j].y;
+        v[2] += x[j].z;
+        v[3] += x[j].w;
+      }
+  }
   float o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float b = bias ? bf16_to_f32(bias[(size_t)e * n_out + col + i]) : 0.f;
-    o[i] = g.pre_gated ? v[i] + b * gs : (v[i] + b) * gs;
-  }
+  for (int i = 0; i < 4; ++i) o[i] = g.pre_gated ? v[i] + b[i] * gs : (v[i] + b[i]) * gs;
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + (size_t)(row0 + r) * n_out + col) =
       make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
 }
