@@ -132,6 +132,7 @@ struct TileLoads {
   static constexpr int TBN = NAR ? 512 : 256;           // tile B-rows
   static constexpr int CA = TBM / 128, CB = TBN / 128;  // copies of A / B per wave and slab
   static constexpr int CPR = CA + CB;                   // copies per refill
+  static_assert(CA <= 4 && CB <= 4, "a copy group holds at most four copies");
   static constexpr int kCols = kSwi<EPI> ? TBN / 2 : TBN;  // output columns per tile
   // uniform bases (bytes) and 32-bit per-lane offsets of the wave's A and B copies of a tile
   struct Src {
@@ -167,7 +168,7 @@ struct TileLoads {
       const int rr = (wave * CA + i) * 16 + lrow;  // stage row 0 .. TBM-1
       const int rc = min(rr, rows - 1);
       const int rel = row0 - rb + rc;  // tiled: row within the blocks from rb
-      r.ao[i] = a_tiled ? tiled_row_off(rel, g.a_kp, lchunk) : rm_row_off(rc, K, lchunk);
+      r.ao[i] = (a_tiled ? tiled_row_off(rel, g.a_kp, lchunk) : rm_row_off(rc, K, lchunk)) + (uint32_t)(3 - i) * 1024u;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -184,7 +185,7 @@ struct TileLoads {
       cl = min(cl, n_out - 1 - n0);
       // tiled: block cl / 128, row cl % 128 of its 32-element slab rows (the slab offset
       // is added per copy)
-      r.bo[i] = tiled ? tiled_row_off(cl, Kb, lchunk) : rm_row_off(cl, K, lchunk);
+      r.bo[i] = (tiled ? tiled_row_off(cl, Kb, lchunk) : rm_row_off(cl, K, lchunk)) + (uint32_t)(3 - i) * 1024u;
     }
     return r;
   }
@@ -197,21 +198,40 @@ struct TileLoads {
   // byte offset of reduction index k0 for this lane in a row-major operand; lanes past K read
   // the row's last chunk (zeroed once it has landed); a modular offset, added in 32 bits
   MOE_DEV uint32_t dma_k(int k0) const { return rm_k_off(g.K, k0, lchunk); }
-  // copy c of a refill (full: A0 B0 A1 B1; narrow: A0 B0 B1 B2 B3) into stage j, at byte offset
-  // ka (row-major operands) or kt (tiled ones) along K
+  // copy c of a refill (full: A0 A1 B0 B1; narrow: A0 B0 B1 B2 B3) into stage j, at byte offset
+  // ka (row-major operands) or kt (tiled ones) along K. A wave's copies of one operand fill
+  // consecutive 1 KiB blocks of the stage and form a group with one M0 write (lds_m0, at the
+  // group's first copy; immediate offset 1024 i for copy i, the row offsets being stored
+  // 1024 (3 - i) higher and the base taken 3072 bytes lower), so a refill's copies are issued
+  // in order c = 0 .. CPR - 1.
   // SA: every copy's K part is uniform (tiled operands, or K a multiple of 32; ku = k0 * 2
   // for row-major ones), taken into the scalar base of the saddr form (no per-copy vector
   // address arithmetic)
   template <bool SA>
   MOE_DEV void copy(const Src& sr, int c, int j, uint32_t ka, uint32_t kt, uint32_t ku) const {
-    const bool is_a = NAR ? c == 0 : (c & 1) == 0;
-    const int i = NAR ? (c == 0 ? 0 : c - 1) : (c >> 1);
+    const bool is_a = NAR ? c == 0 : c < CA;
+    const int i = is_a ? c : c - CA;
+    if (c == 0) lds_m0(sa(j) + wave * CA * 16 * kBK);
+    if (c == CA) lds_m0(sb(j) + wave * CB * 16 * kBK);
+    const char* base = is_a ? sr.a : sr.b[i];
+    const uint32_t row = is_a ? sr.ao[i] : sr.bo[i];
+    const bool tl = is_a ? a_is_tiled() : g.b_kp > 0;
     if constexpr (SA) {
-      if (is_a) lds_dma16_s(sr.a + (a_is_tiled() ? kt : ku), sr.ao[i], sa(j) + (wave * CA + i) * 16 * kBK);
-      else lds_dma16_s(sr.b[i] + (g.b_kp > 0 ? kt : ku), sr.bo[i], sb(j) + (wave * CB + i) * 16 * kBK);
+      const char* sbase = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(base) + (tl ? kt : ku) - 3072u);
+      switch (i) {
+        case 0: lds_dma16_sg<0>(sbase, row); break;
+        case 1: lds_dma16_sg<1>(sbase, row); break;
+        case 2: lds_dma16_sg<2>(sbase, row); break;
+        default: lds_dma16_sg<3>(sbase, row); break;
+      }
     } else {
-      if (is_a) lds_dma16(sr.a + src_off(sr.ao[i], a_is_tiled() ? kt : ka), sa(j) + (wave * CA + i) * 16 * kBK);
-      else lds_dma16(sr.b[i] + src_off(sr.bo[i], g.b_kp > 0 ? kt : ka), sb(j) + (wave * CB + i) * 16 * kBK);
+      const char* src = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(base) - 3072u) + src_off(row, tl ? kt : ka);
+      switch (i) {
+        case 0: lds_dma16_g<0>(src); break;
+        case 1: lds_dma16_g<1>(src); break;
+        case 2: lds_dma16_g<2>(src); break;
+        default: lds_dma16_g<3>(src); break;
+      }
     }
   }
   // every copy of slab k (from the start of K) into stage j
@@ -295,8 +315,10 @@ MOE_DEV int gemm_tile(const GemmArgs& g, uint16_t* smem, int tid, int wave, int 
     relax -= relax > 0;
   };
   // zero this wave's copied chunks of the last slab that lie past K (after they landed)
+  // (the uniform slab test first: a launch with K a multiple of 32 pays a scalar compare)
   auto zero_tail = [&](int j, int slab) {
-    if (!k_tail || kso + slab != nk_all - 1 || (kso + slab) * kBK + L.lchunk < K) return;
+    if (__builtin_expect(!k_tail || kso + slab != nk_all - 1, 1)) return;
+    if ((kso + slab) * kBK + L.lchunk < K) return;
 #pragma unroll
     for (int i = 0; i < CA; ++i)
       *reinterpret_cast<uint4*>(sa(j) + (wave * CA + i) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);
@@ -703,12 +725,18 @@ struct W4Loads {
   // consecutive rows at one logical chunk per 16 lanes) hit no bank conflict (measured with a
   // read-pattern probe: (row >> 2) & 3, the 8-wave kernel's, costs 0.8 conflict cycles per
   // ds_read_b128 of this pattern)
+  // the launch's last slab when it runs past K (its chunks past K are zeroed once landed), else -1
+  int ktail;
   MOE_DEV W4Loads(const GemmArgs& g_, uint16_t* smem_, int wave_, int lane)
-      : g(g_), smem(smem_), wave(wave_), lchunk(((lane & 3) ^ ((lane >> 3) & 3)) * 8), lrow(lane >> 2) {}
+      : g(g_), smem(smem_), wave(wave_), lchunk(((lane & 3) ^ ((lane >> 3) & 3)) * 8), lrow(lane >> 2),
+        ktail((g_.K % kBK) != 0 ? (g_.K + kBK - 1) / kBK - 1 : -1) {}
   MOE_DEV uint16_t* sa(int j) const { return smem + j * kW4StageElems; }
   MOE_DEV uint16_t* sb(int j) const { return smem + j * kW4StageElems + kBM * kBK; }
   MOE_DEV bool a_tiled() const { return !kSave<EPI> && g.a_kp > 0; }
-  // copy i (0..3) of A / B covers stage rows (wave * 4 + i) * 16 .. + 15
+  // copy i (0..3) of A / B covers stage rows (wave * 4 + i) * 16 .. + 15. The four copies of
+  // an operand form one group (one M0 write, immediate offsets 1024 i; lds_dma16_sg): the row
+  // offsets are stored 1024 (3 - i) higher and the group's base is taken 3072 bytes lower, so
+  // copy i reads base + row offset exactly, with no offset below zero.
   MOE_DEV Src src(int e, int row0, int rows, int nt) const {
     const int K = g.K, n_out = g.n_out, n0 = nt * kCols;
     const bool tiled = g.b_kp > 0;
@@ -735,23 +763,44 @@ struct W4Loads {
       }
       cl = min(cl, n_out - 1 - n0);
       r.bo[i] = tiled ? tiled_row_off(cl, Kb, lchunk) : rm_row_off(cl, K, lchunk);
+      r.ao[i] += (uint32_t)(3 - i) * 1024u;
+      r.bo[i] += (uint32_t)(3 - i) * 1024u;
     }
     return r;
   }
-  // copy c of a refill (0..3: A, 4..7: B) of global slab k into stage j
+  // copy c of a refill (0..3: A, 4..7: B) of global slab k into stage j; copies 0 and 4 set
+  // their group's M0, so a refill's copies are issued in order c = 0 .. 7 with no other M0
+  // write between them.
   // SA: the K part of every copy of the launch is uniform (tiled operands, or K a multiple of
   // 32), so it goes into the scalar base of the saddr form and a copy needs no vector address
   // arithmetic; otherwise the 64-bit per-lane address of the K-tail rule (rm_k_off).
   template <bool SA>
   MOE_DEV void copy(const Src& sr, int c, int j, int k) const {
+    if (c == 0) lds_m0(sa(j) + wave * 4 * 16 * kBK);
+    if (c == 4) lds_m0(sb(j) + wave * 4 * 16 * kBK);
+    const bool isa = c < 4;
+    const uint32_t kt = tiled_k_off(k * kBK);
+    const char* base = isa ? sr.a : sr.b[c - 4];
+    const uint32_t row = isa ? sr.ao[c] : sr.bo[c - 4];
+    const bool tl = isa ? a_tiled() : g.b_kp > 0;
     if constexpr (SA) {
-      const uint32_t ku = (uint32_t)k * kBK * 2u, kt = tiled_k_off(k * kBK);
-      if (c < 4) lds_dma16_s(sr.a + (a_tiled() ? kt : ku), sr.ao[c], sa(j) + (wave * 4 + c) * 16 * kBK);
-      else lds_dma16_s(sr.b[c - 4] + (g.b_kp > 0 ? kt : ku), sr.bo[c - 4], sb(j) + (wave * 4 + c - 4) * 16 * kBK);
+      const uint32_t ku = (uint32_t)k * kBK * 2u;
+      const char* sbase = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(base) + (tl ? kt : ku) - 3072u);
+      switch (c & 3) {
+        case 0: lds_dma16_sg<0>(sbase, row); break;
+        case 1: lds_dma16_sg<1>(sbase, row); break;
+        case 2: lds_dma16_sg<2>(sbase, row); break;
+        default: lds_dma16_sg<3>(sbase, row); break;
+      }
     } else {
-      const uint32_t ka = rm_k_off(g.K, k * kBK, lchunk), kt = tiled_k_off(k * kBK);
-      if (c < 4) lds_dma16(sr.a + src_off(sr.ao[c], a_tiled() ? kt : ka), sa(j) + (wave * 4 + c) * 16 * kBK);
-      else lds_dma16(sr.b[c - 4] + src_off(sr.bo[c - 4], g.b_kp > 0 ? kt : ka), sb(j) + (wave * 4 + c - 4) * 16 * kBK);
+      const uint32_t ka = rm_k_off(g.K, k * kBK, lchunk);
+      const char* src = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(base) - 3072u) + src_off(row, tl ? kt : ka);
+      switch (c & 3) {
+        case 0: lds_dma16_g<0>(src); break;
+        case 1: lds_dma16_g<1>(src); break;
+        case 2: lds_dma16_g<2>(src); break;
+        default: lds_dma16_g<3>(src); break;
+      }
     }
   }
   template <bool SA>
@@ -759,10 +808,12 @@ struct W4Loads {
 #pragma unroll
     for (int c = 0; c < 8; ++c) copy<SA>(sr, c, j, k);
   }
-  // zero this wave's landed chunks of stage j that lie past K (global slab k is the last one)
+  // zero this wave's landed chunks of stage j that lie past K (global slab k is the last one).
+  // The slab test is uniform and comes first, so a launch with K a multiple of 32 pays one
+  // scalar compare per slab (the combined per-lane test cost ~60 cycles a slab in a probe).
   MOE_DEV void zero_tail(int j, int k, int nk_all, int lane) const {
-    const int K = g.K;
-    if ((K % kBK) == 0 || k != nk_all - 1 || k * kBK + lchunk < K) return;
+    if (__builtin_expect(k != ktail, 1)) return;
+    if (k * kBK + lchunk < g.K) return;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       *reinterpret_cast<uint4*>(sa(j) + (wave * 4 + c) * 16 * kBK + lane * 8) = make_uint4(0, 0, 0, 0);

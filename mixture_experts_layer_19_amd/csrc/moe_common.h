@@ -114,6 +114,30 @@ MOE_DEV void lds_dma16_s(const void* sbase, uint32_t voff, uint16_t* lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
+
+// Grouped copies: four copies whose LDS destinations are consecutive 1 KiB blocks share one
+// M0 write. The instruction's immediate offset is added to both the global and the LDS
+// address (checked on gfx950), so copy c (0..3) of a group carries offset 1024 c, and its
+// global address is passed 1024 c lower to cancel it. Each M0 write costs the wave about as
+// much as a copy's own issue (probe: 64 MFMAs and 8 copies per slab, 1275 -> 1220 cycles).
+// lds_m0 sets M0 to the group's first destination; nothing between it and the group's last
+// copy may write M0 (the kernels' loops use no other M0-based instruction).
+MOE_DEV void lds_m0(uint16_t* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_base;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(m0) : "memory", "m0");
+}
+// copy C of a group, saddr form: reads sbase + voff + 1024 C, writes M0 + 1024 C + 16 lane.
+template <int C>
+MOE_DEV void lds_dma16_sg(const void* sbase, uint32_t voff) {
+  static_assert(C >= 0 && C < 4, "four copies per M0");
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(C * 1024) : "memory");
+}
+// copy C of a group, 64-bit per-lane address: reads src + 1024 C, writes M0 + 1024 C + 16 lane.
+template <int C>
+MOE_DEV void lds_dma16_g(const void* src) {
+  static_assert(C >= 0 && C < 4, "four copies per M0");
+  asm volatile("global_load_lds_dwordx4 %0, off offset:%1" ::"v"(src), "i"(C * 1024) : "memory");
+}
 // s_waitcnt vmcnt(N) lgkmcnt(0): this wave's loads older than its last N have landed in LDS
 // and its own LDS accesses are done.
 template <int N> MOE_DEV void wait_vm_lds() {
