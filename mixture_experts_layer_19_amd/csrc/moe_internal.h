@@ -202,6 +202,7 @@ MOE_DEV bool build_tile_table_wave(int lo, int hi, int E, int rows, int bm, int 
 // each lane holding epl experts, so a wave routes 64/lpt tokens at once; tokens_per_wave is a
 // multiple of 64/lpt.
 struct RoutePlan {
+  bool fused;  // bfloat16 with up to 64 experts: projection and routing in one launch
   int lpt, epl;
   int tokens_per_wave, tokens_per_block, n_blocks;
   int n_split, k_chunk;

@@ -11,13 +11,14 @@
 
 namespace moe {
 
-// The router projection splits its reduction into at most this many partial sums (a power
-// of two): 8 for the LDS-tiled projection (E > 64), 4 for the one of up to 64 experts, whose
-// lanes keep eight 32-wide steps of loads in flight. Mixtral shape, same-box A/B of the
-// routing stage: split 8 with four steps in flight 39.2-39.5 us, split 4 with eight 37.4 us
-// (split 2 39.1, split 1 47.5, split 2 with sixteen steps 39.3).
+// The router projection splits its reduction into partial sums added in a fixed order: at
+// most 8 (a power of two) for the LDS-tiled projection (E > 64); always kFusedQuarters, one
+// per wave pair, in the fused kernel of up to 64 experts, whose lanes keep eight 32-wide
+// steps of loads in flight. Before the fusion, Mixtral shape, same-box A/B of the routing
+// stage: split 8 with four steps in flight 39.2-39.5 us, split 4 with eight 37.4 us (split 2
+// 39.1, split 1 47.5, split 2 with sixteen steps 39.3).
 constexpr int kRouterMaxSplit = 8;
-constexpr int kRouterMaxSplitNarrow = 4;
+constexpr int kFusedQuarters = 4;
 
 // z = the sum of a token's S split partials of one expert, in split order; every partial is
 // requested before the first add.
@@ -33,45 +34,44 @@ MOE_DEV float split_sum(const float* zp, size_t stride) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Router projection, bfloat16 inputs, float32 accumulation on MFMA (v_mfma_f32_16x16x32_bf16).
-// Workgroup = 4 waves; each wave owns 16 tokens and NB blocks of 16 experts; grid.z splits
-// the reduction axis into independent chunks whose partial sums land in zpart[split][N][E]
-// and are added in split order by the epilogue kernel (deterministic, no atomics).
+// Router projection, bfloat16 inputs, float32 accumulation on MFMA (v_mfma_f32_16x16x32_bf16),
+// up to 64 experts: route_fused_kernel (below) runs it and the per-token routing in one launch.
 // ---------------------------------------------------------------------------------------
+// Partial logits of 16 tokens (t0 ..) x 16 NB experts (e0 ..) over the reduction range
+// [kb, ke), on v_mfma_f32_16x16x32_bf16: lane l ends with token t0 + 4 (l >> 4) + r of
+// acc[b][r], expert e0 + 16 b + (l & 15). Rows past the last token or expert read the last
+// one's row, an in-range address, so no load sits behind a per-lane branch (a load there is
+// waited for before the next is issued); their outputs are never used. Steps past ke (a
+// partial 32-wide step) multiply zeros.
+//
+// Loads go in batches of kU steps, left to the compiler's schedule, which issues each step's
+// loads a few steps ahead of its product (about eight 16-byte loads in flight per lane).
+// Same-box A/B at the Mixtral shape (routing kernel, moe_forward): this form 18.7 us; every
+// batch's loads issued before its first product 21.0; two batches in flight (the next
+// batch's loads issued ahead of this batch's products) 24.2; bounds-checked buffer loads for
+// the rows past N or E instead of the clamped rows 20.3.
 template <int NB>
-__global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, float* __restrict__ zpart,
-    int n_tokens, int d, int n_experts, int k_chunk) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 64 + wave * 16;
-  const int e0 = blockIdx.y * (16 * NB);
-  const int kb = blockIdx.z * k_chunk;
-  const int ke = min(d, kb + k_chunk);
+MOE_DEV void router_mfma16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, int t0, int e0, int kb, int ke,
+                           int n_tokens, int d, int n_experts, int lane, f32x4 (&acc)[NB]) {
   const int row = lane & 15;
   const int kq = (lane >> 4) * 8;
-
-  f32x4 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16_t* arow = x + (size_t)min(t0 + row, n_tokens - 1) * d + kq;
+  const bf16_t* brow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) brow[b] = wg + (size_t)min(e0 + b * 16 + row, n_experts - 1) * d + kq;
 
-  const bool a_ok = (t0 + row) < n_tokens;
-  const bf16_t* arow = x + (size_t)(a_ok ? t0 + row : 0) * d;
-  int k = kb;
-  // eight 32-wide steps at a time: every load of the eight is in flight before the first
-  // multiply (the same products in the same order as one step at a time)
-  constexpr int kU = 8;
-  for (; k + kU * 32 <= ke; k += kU * 32) {
-    uint4 av[kU], bv[NB][kU];
+  constexpr int kU = NB >= 4 ? 4 : 8;
+  const int nb = max(0, ke - kb) / (kU * 32);
+  uint4 av[kU], bv[NB][kU];
+  for (int i = 0; i < nb; ++i) {
+    const int k0 = kb + i * (kU * 32);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int kk = k + u * 32 + kq;
-      av[u] = a_ok ? *reinterpret_cast<const uint4*>(arow + kk) : make_uint4(0, 0, 0, 0);
+      av[u] = *reinterpret_cast<const uint4*>(arow + k0 + u * 32);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int e = e0 + b * 16 + row;
-        bv[b][u] = e < n_experts ? *reinterpret_cast<const uint4*>(wg + (size_t)e * d + kk) : make_uint4(0, 0, 0, 0);
-      }
+      for (int b = 0; b < NB; ++b) bv[b][u] = *reinterpret_cast<const uint4*>(brow[b] + k0 + u * 32);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -80,27 +80,19 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
         acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
                                                          __builtin_bit_cast(bf16x8, bv[b][u]), acc[b], 0, 0, 0);
   }
-  for (; k < ke; k += 32) {
-    const int kk = k + kq;
-    uint4 av = make_uint4(0, 0, 0, 0);
-    if (a_ok && kk < ke) av = *reinterpret_cast<const uint4*>(arow + kk);
-    bf16x8 a = __builtin_bit_cast(bf16x8, av);
+  for (int k = kb + nb * kU * 32; k < ke; k += 32) {  // uniform trip count
+    const bool in = k + kq < ke;  // ke is a multiple of 8, so a chunk is wholly in or out
+    const int kc = in ? k : ke - 8 - kq;  // lanes past ke re-read the chunk ke - 8 (in range)
+    uint4 a1 = *reinterpret_cast<const uint4*>(arow + kc);
+    uint4 b1[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) b1[b] = *reinterpret_cast<const uint4*>(brow[b] + kc);
+    if (!in) a1 = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int e = e0 + b * 16 + row;
-      uint4 bv = make_uint4(0, 0, 0, 0);
-      if (e < n_experts && kk < ke) bv = *reinterpret_cast<const uint4*>(wg + (size_t)e * d + kk);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[b], 0, 0, 0);
-    }
-  }
-  float* zp = zpart + (size_t)blockIdx.z * n_tokens * n_experts;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int e = e0 + b * 16 + (lane & 15);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + (lane >> 4) * 4 + r;
-      if (t < n_tokens && e < n_experts) zp[(size_t)t * n_experts + e] = acc[b][r];
+      if (!in) b1[b] = make_uint4(0, 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1[b]),
+                                                       acc[b], 0, 0, 0);
     }
   }
 }
@@ -259,6 +251,151 @@ template <int W> MOE_DEV float group_max(float v) {
 // Waves per routing workgroup: 16, or 4 when every lane holds 16 experts (register budget).
 constexpr int route_waves(int epl) { return epl >= 16 ? 4 : 16; }
 
+// One pass of a wave's token groups: group grp routes token t (valid when tok; the trip is
+// uniform over the wave, so a group past the last token computes on -inf / zeros and writes
+// nothing). zf(e) is the token's logit of expert e before the logit bias. Adds the token's
+// probabilities to psum and its squared log-sum-exp to zl_acc (lane 0 of the group), and its
+// chosen ids to the block histogram s_hist.
+template <int LPT, int EPL, typename ZF>
+MOE_DEV void route_token(const RouteArgs& a, int t, bool tok, int sub, int grp, ZF&& zf, float (&psum)[EPL],
+                         float& zl_acc, int* s_hist) {
+  const int E = a.n_experts;
+  const int k = a.top_k;
+  const bool sigm = a.router == MOE_ROUTER_SIGMOID;
+  float z[EPL], s[EPL], ex[EPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = sub + LPT * i;
+    const bool ok = e < E;
+    float v = 0.f;
+    if (ok && tok) {
+      v = zf(e);
+      if (a.logit_bias) v += a.logit_bias[e];
+      if (a.logits_out) a.logits_out[(size_t)t * E + e] = v;
+    }
+    z[i] = ok ? v : -INFINITY;
+    m = fmaxf(m, z[i]);
+  }
+  m = group_max<LPT>(m);
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    ex[i] = (sub + LPT * i < E) ? expf(z[i] - m) : 0.f;
+    lsum += ex[i];
+  }
+  const float sum = group_sum<LPT>(lsum);
+  const float inv_sum = 1.0f / sum;
+  if (tok && sub == 0) {
+    const float lse = m + logf(sum);
+    zl_acc += lse * lse;
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = sub + LPT * i;
+    const bool ok = e < E;
+    psum[i] += (ok && tok) ? ex[i] * inv_sum : 0.f;
+    float sc = sigm ? sigmoid_f(z[i]) : z[i];
+    if (ok && a.sel_bias) sc += a.sel_bias[e];
+    if (sc != sc) sc = -INFINITY;  // a NaN score ranks last, so k valid ids are still chosen
+    s[i] = ok ? sc : -INFINITY;
+  }
+
+  // k rounds of a group arg-max on (score desc, id asc); one more for the margin. Some
+  // lane of the group always holds an untaken valid expert (k <= E), and -inf loses
+  // only to a lower id, so the winner is always a valid id.
+  uint32_t taken = 0;
+  int my_id = -1;
+  float my_u = 0.f, last_s = 0.f, gap = INFINITY;
+  const int rounds = (k < E) ? k + 1 : k;
+  for (int j = 0; j < rounds; ++j) {
+    float bs = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = sub + LPT * i;
+      if (e < E && !((taken >> i) & 1u) && beats(s[i], e, bs, bi)) {
+        bs = s[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = LPT / 2; o >= 1; o >>= 1) {
+      const float os = __shfl_xor(bs, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (beats(os, oi, bs, bi)) {
+        bs = os;
+        bi = oi;
+      }
+    }
+    if (j == k) {  // the best unchosen expert
+      gap = last_s - bs;
+      break;
+    }
+    last_s = bs;
+    // raw gate of the chosen expert: exp(z - m) for the softmax routers, sigmoid(z) else
+    const int slot = bi / LPT;
+    const int owner = bi & (LPT - 1);
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (i == slot) mine = sigm ? sigmoid_f(z[i]) : ex[i];
+    const float u = __shfl(mine, grp * LPT + owner, kWave);
+    if (sub == owner) taken |= 1u << slot;
+    if (sub == j) {
+      my_id = bi;
+      my_u = u;
+    }
+  }
+  // gates ([L7.8] §2.1): the softmax routers renormalise exp(z - m) over the chosen set
+  // (= p_T / sum p_T = softmax over the chosen logits); without renormalisation the
+  // softmax_topk gate is p itself. The sigmoid router renormalises sigmoid(z_T).
+  const float usum = group_sum<LPT>(sub < k ? my_u : 0.f);
+  if (tok && sub < k) {
+    float w;
+    if (a.router == MOE_ROUTER_TOPK_SOFTMAX || a.norm_topk) w = my_u / usum;
+    else if (a.router == MOE_ROUTER_SOFTMAX_TOPK) w = my_u * inv_sum;
+    else w = my_u;
+    w *= a.routed_scaling;
+    a.topk_ids[(size_t)t * k + sub] = my_id;
+    a.topk_w[(size_t)t * k + sub] = w;
+    atomicAdd(&s_hist[my_id], 1);  // integer adds: order-independent
+  }
+  if (a.gap_out && tok && sub == 0) a.gap_out[t] = gap;
+}
+
+// Deterministic block partials of NW waves: the groups of a wave combined by a fixed
+// butterfly, then the waves in wave order. Every thread of the block calls it.
+template <int LPT, int EPL, int NW>
+MOE_DEV void route_block_partials(const RouteArgs& a, int lane, int wave, float (&psum)[EPL], float zl_acc,
+                                  float (*s_psum)[LPT * EPL], float* s_zl, const int* s_hist) {
+  const int E = a.n_experts;
+  const int sub = lane & (LPT - 1);
+  const int grp = lane / LPT;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+#pragma unroll
+    for (int o = 32; o >= LPT; o >>= 1) psum[i] += __shfl_xor(psum[i], o, kWave);
+    const int e = sub + LPT * i;
+    if (grp == 0 && e < E) s_psum[wave][e] = psum[i];
+  }
+  const float zl = wave_sum(zl_acc);
+  if (lane == 0) s_zl[wave] = zl;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += NW * kWave) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += s_psum[w][e];
+    a.part_p[(size_t)blockIdx.x * E + e] = v;
+    a.part_hist[(size_t)blockIdx.x * E + e] = s_hist[e];
+  }
+  if (threadIdx.x == 0) {
+    float v = 0.f;
+    for (int w = 0; w < NW; ++w) v += s_zl[w];
+    a.part_zl[blockIdx.x] = v;
+  }
+}
+
 template <int LPT, int EPL>
 __global__ __launch_bounds__(route_waves(EPL) * kWave) void route_tokens_kernel(RouteArgs a) {
   constexpr int kRouteWaves = route_waves(EPL);
@@ -272,8 +409,6 @@ __global__ __launch_bounds__(route_waves(EPL) * kWave) void route_tokens_kernel(
   const int sub = lane & (LPT - 1);  // lane within the token's group
   const int grp = lane / LPT;
   const int E = a.n_experts;
-  const int k = a.top_k;
-  const bool sigm = a.router == MOE_ROUTER_SIGMOID;
 
   for (int e = threadIdx.x; e < E; e += kRouteWaves * kWave) s_hist[e] = 0;
   __syncthreads();
@@ -284,144 +419,85 @@ __global__ __launch_bounds__(route_waves(EPL) * kWave) void route_tokens_kernel(
   float zl_acc = 0.f;
 
   const int wave_tok0 = blockIdx.x * a.tokens_per_block + wave * a.tokens_per_wave;
-  // Uniform trip count over the wave: groups past the last token compute on zeros and
-  // write nothing.
+  const size_t zs = (size_t)a.n_tokens * E;
   for (int it = 0; it < a.tokens_per_wave; it += kTpw) {
     const int t = wave_tok0 + it + grp;
-    const bool tok = t < a.n_tokens;
-    float z[EPL], s[EPL], ex[EPL];
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = sub + LPT * i;
-      const bool ok = e < E;
-      float v = 0.f;
-      if (ok && tok) {
-        const float* zp = a.zpart + (size_t)t * E + e;
-        const size_t zs = (size_t)a.n_tokens * E;
-        switch (a.n_split) {  // a power of two up to kRouterMaxSplit
-          case 1: v = split_sum<1>(zp, zs); break;
-          case 2: v = split_sum<2>(zp, zs); break;
-          case 4: v = split_sum<4>(zp, zs); break;
-          default: v = split_sum<8>(zp, zs); break;
-        }
-        if (a.logit_bias) v += a.logit_bias[e];
-        if (a.logits_out) a.logits_out[(size_t)t * E + e] = v;
+    const float* zp = a.zpart + (size_t)t * E;
+    auto zf = [&](int e) {
+      switch (a.n_split) {  // a power of two up to kRouterMaxSplit
+        case 1: return split_sum<1>(zp + e, zs);
+        case 2: return split_sum<2>(zp + e, zs);
+        case 4: return split_sum<4>(zp + e, zs);
+        default: return split_sum<8>(zp + e, zs);
       }
-      z[i] = ok ? v : -INFINITY;
-      m = fmaxf(m, z[i]);
-    }
-    m = group_max<LPT>(m);
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      ex[i] = (sub + LPT * i < E) ? expf(z[i] - m) : 0.f;
-      lsum += ex[i];
-    }
-    const float sum = group_sum<LPT>(lsum);
-    const float inv_sum = 1.0f / sum;
-    if (tok && sub == 0) {
-      const float lse = m + logf(sum);
-      zl_acc += lse * lse;
-    }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = sub + LPT * i;
-      const bool ok = e < E;
-      psum[i] += (ok && tok) ? ex[i] * inv_sum : 0.f;
-      float sc = sigm ? sigmoid_f(z[i]) : z[i];
-      if (ok && a.sel_bias) sc += a.sel_bias[e];
-      if (sc != sc) sc = -INFINITY;  // a NaN score ranks last, so k valid ids are still chosen
-      s[i] = ok ? sc : -INFINITY;
-    }
+    };
+    route_token<LPT, EPL>(a, t, t < a.n_tokens, sub, grp, zf, psum, zl_acc, s_hist);
+  }
+  route_block_partials<LPT, EPL, kRouteWaves>(a, lane, wave, psum, zl_acc, s_psum, s_zl, s_hist);
+}
 
-    // k rounds of a group arg-max on (score desc, id asc); one more for the margin. Some
-    // lane of the group always holds an untaken valid expert (k <= E), and -inf loses
-    // only to a lower id, so the winner is always a valid id.
-    uint32_t taken = 0;
-    int my_id = -1;
-    float my_u = 0.f, last_s = 0.f, gap = INFINITY;
-    const int rounds = (k < E) ? k + 1 : k;
-    for (int j = 0; j < rounds; ++j) {
-      float bs = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = sub + LPT * i;
-        if (e < E && !((taken >> i) & 1u) && beats(s[i], e, bs, bi)) {
-          bs = s[i];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int o = LPT / 2; o >= 1; o >>= 1) {
-        const float os = __shfl_xor(bs, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (beats(os, oi, bs, bi)) {
-          bs = os;
-          bi = oi;
-        }
-      }
-      if (j == k) {  // the best unchosen expert
-        gap = last_s - bs;
-        break;
-      }
-      last_s = bs;
-      // raw gate of the chosen expert: exp(z - m) for the softmax routers, sigmoid(z) else
-      const int slot = bi / LPT;
-      const int owner = bi & (LPT - 1);
-      float mine = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (i == slot) mine = sigm ? sigmoid_f(z[i]) : ex[i];
-      const float u = __shfl(mine, grp * LPT + owner, kWave);
-      if (sub == owner) taken |= 1u << slot;
-      if (sub == j) {
-        my_id = bi;
-        my_u = u;
-      }
-    }
-    // gates ([L7.8] §2.1): the softmax routers renormalise exp(z - m) over the chosen set
-    // (= p_T / sum p_T = softmax over the chosen logits); without renormalisation the
-    // softmax_topk gate is p itself. The sigmoid router renormalises sigmoid(z_T).
-    const float usum = group_sum<LPT>(sub < k ? my_u : 0.f);
-    if (tok && sub < k) {
-      float w;
-      if (a.router == MOE_ROUTER_TOPK_SOFTMAX || a.norm_topk) w = my_u / usum;
-      else if (a.router == MOE_ROUTER_SOFTMAX_TOPK) w = my_u * inv_sum;
-      else w = my_u;
-      w *= a.routed_scaling;
-      a.topk_ids[(size_t)t * k + sub] = my_id;
-      a.topk_w[(size_t)t * k + sub] = w;
-      atomicAdd(&s_hist[my_id], 1);  // integer adds: order-independent
-    }
-    if (a.gap_out && tok && sub == 0) a.gap_out[t] = gap;
-  }
+// ---------------------------------------------------------------------------------------
+// Router projection and routing in one launch, bfloat16, up to 64 experts (LPT = E rounded up
+// to a power of two, one expert per lane; NB = the 16-expert blocks of the projection). A
+// workgroup of 8 waves is one routing block, taken in runs of kFusedTokens = 32 tokens: wave
+// w multiplies tokens 16 (w & 1) .. + 15 of the run against every expert over reduction
+// quarter w >> 1, the quarter sums of each logit land in LDS and are added in quarter order
+// (the order of the split projection's partials), and the token groups then route the run's
+// tokens. The block's partials are written as route_tokens_kernel writes them. No logits
+// pass through HBM and one launch is saved.
+// ---------------------------------------------------------------------------------------
+constexpr int kFusedTokens = 32, kFusedWaves = 8;
+template <int NB, int LPT>
+__global__ __launch_bounds__(kFusedWaves * kWave) void route_fused_kernel(const bf16_t* __restrict__ x,
+                                                                          const bf16_t* __restrict__ wg, RouteArgs a,
+                                                                          int d, int k_chunk) {
+  static_assert(16 * NB >= LPT, "the projection covers every expert slot");
+  constexpr int kTpw = kWave / LPT;
+  __shared__ float s_z[kFusedQuarters][kFusedTokens][16 * NB];
+  __shared__ float s_psum[kFusedWaves][LPT];
+  __shared__ int s_hist[LPT];
+  __shared__ float s_zl[kFusedWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int E = a.n_experts;
+  const int N = a.n_tokens;
+  for (int e = threadIdx.x; e < E; e += kFusedWaves * kWave) s_hist[e] = 0;
 
-  // Deterministic block partials: the groups of a wave combined by a fixed butterfly, then
-  // the waves in wave order.
+  const int sub = lane & (LPT - 1);
+  const int grp = lane / LPT;
+  float psum[1] = {0.f};
+  float zl_acc = 0.f;
+  // the block's runs of kFusedTokens tokens (uniform over the workgroup)
+  for (int r0 = 0; r0 < a.tokens_per_block; r0 += kFusedTokens) {
+    const int tb = blockIdx.x * a.tokens_per_block + r0;
+    if (tb >= N) break;
+    {
+      const int half = wave & 1, quarter = wave >> 1;
+      const int kb = quarter * k_chunk;
+      const int ke = min(d, kb + k_chunk);
+      f32x4 acc[NB];
+      router_mfma16<NB>(x, wg, tb + 16 * half, 0, kb, ke, N, d, E, lane, acc);
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int o = 32; o >= LPT; o >>= 1) psum[i] += __shfl_xor(psum[i], o, kWave);
-    const int e = sub + LPT * i;
-    if (grp == 0 && e < E) s_psum[wave][e] = psum[i];
-  }
-  const float zl = wave_sum(zl_acc);
-  if (lane == 0) s_zl[wave] = zl;
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteWaves * kWave) {
-    float v = 0.f;
+        for (int r = 0; r < 4; ++r) s_z[quarter][16 * half + (lane >> 4) * 4 + r][b * 16 + (lane & 15)] = acc[b][r];
+    }
+    __syncthreads();  // (the first time also the histogram's zeros)
+    constexpr int kPasses = (kFusedTokens + kTpw - 1) / kTpw;  // one for E <= 2 (half a pass for E = 1)
+    for (int p = wave; p < kPasses; p += kFusedWaves) {  // wave-uniform trip count
+      const int tl = p * kTpw + grp;
+      const bool tok = tl < kFusedTokens && tb + tl < N;
+      auto zf = [&](int e) {
+        float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kRouteWaves; ++w) v += s_psum[w][e];
-    a.part_p[(size_t)blockIdx.x * E + e] = v;
-    a.part_hist[(size_t)blockIdx.x * E + e] = s_hist[e];
+        for (int q = 0; q < kFusedQuarters; ++q) v += s_z[q][tl][e];
+        return v;
+      };
+      route_token<LPT, 1>(a, tb + tl, tok, sub, grp, zf, psum, zl_acc, s_hist);
+    }
+    __syncthreads();  // every wave is done with s_z before the next run's projection
   }
-  if (threadIdx.x == 0) {
-    float v = 0.f;
-    for (int w = 0; w < kRouteWaves; ++w) v += s_zl[w];
-    a.part_zl[blockIdx.x] = v;
-  }
+  route_block_partials<LPT, 1, kFusedWaves>(a, lane, wave, psum, zl_acc, s_psum, s_zl, s_hist);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -552,7 +628,7 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
 // kFinWaveBlocks long: one wave, lane (g, e) = g E + e (g < G = 64 / E) summing expert e over
 // group g's blocks, with every cross-lane step a shuffle, so the kernel has no barrier and no
 // LDS. All of a lane's partials (counts, P, z-loss) are requested before the first add.
-constexpr int kFinWaveBlocks = 16;
+constexpr int kFinWaveBlocks = 32;
 
 MOE_DEV double wave_sum_f64(double v) {
 #pragma unroll
@@ -572,14 +648,32 @@ __global__ __launch_bounds__(kWave) void route_finalize_wave_kernel(FinalizeArgs
   const int nmine = act ? nb * (g + 1) / G - b0 : 0;  // <= kFinWaveBlocks (checked by the host)
   int hb[kFinWaveBlocks];
   float pb[kFinWaveBlocks], zb[kFinWaveBlocks];
+  // Unconditional loads (an entry past the lane's run reads the last block's, in range, and is
+  // zeroed after), so all of them are in flight together: a load behind a per-lane condition
+  // is waited for before the next is issued.
+  if (nb > 0) {
+#pragma unroll
+    for (int j = 0; j < kFinWaveBlocks; ++j) {
+      const size_t o = (size_t)min(b0 + j, nb - 1) * E + e;  // e < E on every lane
+      hb[j] = a.part_hist[o];
+      pb[j] = a.part_p[o];
+      zb[j] = a.part_zl[min(lane + kWave * j, nb - 1)];  // nb <= G kFinWaveBlocks <= 64 kFinWaveBlocks
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kFinWaveBlocks; ++j) {
+      hb[j] = 0;
+      pb[j] = 0.f;
+      zb[j] = 0.f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kFinWaveBlocks; ++j) {
-    const bool in = j < nmine;
-    const size_t o = (size_t)(b0 + j) * E + e;
-    hb[j] = in ? a.part_hist[o] : 0;
-    pb[j] = in ? a.part_p[o] : 0.f;
-    const int bz = lane + kWave * j;  // nb <= G kFinWaveBlocks <= 64 kFinWaveBlocks
-    zb[j] = bz < nb ? a.part_zl[bz] : 0.f;
+    if (j >= nmine) {
+      hb[j] = 0;
+      pb[j] = 0.f;
+    }
+    if (lane + kWave * j >= nb) zb[j] = 0.f;
   }
   int c = 0;
   double p = 0.0, zl = 0.0;
@@ -697,8 +791,20 @@ RoutePlan plan_route(const moe_config& c) {
   }
   p.epl = 1;
   while (p.lpt * p.epl < E) p.epl <<= 1;
-  // Tokens per wave: enough that the per-block partial arrays ([blocks][E]) stay within
-  // 64K entries, which the single-workgroup final reduction reads twice.
+  // Blocks of tokens: enough tokens per block that the per-block partial arrays ([blocks][E])
+  // stay within 64K entries, which the single-workgroup final reduction reads twice.
+  p.fused = c.dtype == MOE_BF16 && E <= kWave;
+  if (p.fused) {
+    // route_fused_kernel: a block is `iters` consecutive runs of kFusedTokens tokens, the
+    // reduction cut into kFusedQuarters quarters of whole 32-wide steps
+    const long long iters = std::max<long long>(1, (N * E + 65536ll * kFusedTokens - 1) / (65536ll * kFusedTokens));
+    p.tokens_per_block = (int)(kFusedTokens * iters);
+    p.tokens_per_wave = p.tokens_per_block;
+    p.n_blocks = (int)((N + p.tokens_per_block - 1) / p.tokens_per_block);
+    p.n_split = kFusedQuarters;
+    p.k_chunk = ((c.d_model + kFusedQuarters - 1) / kFusedQuarters + 31) / 32 * 32;
+    return p;
+  }
   const int tpw = kWave / p.lpt;
   const int waves = route_waves(p.epl);
   const long long per_block_min = (long long)waves * tpw;
@@ -710,13 +816,10 @@ RoutePlan plan_route(const moe_config& c) {
   if (c.dtype == MOE_BF16) {
     // Split the reduction so that the projection launches several workgroups per CU even
     // for a few thousand tokens; each split writes its own partial z.
-    const bool tiled = E > 64;
-    const int e_blocks = tiled ? (E + router_tile_experts(E) - 1) / router_tile_experts(E) : (E + 255) / 256;
+    const int e_blocks = (E + router_tile_experts(E) - 1) / router_tile_experts(E);
     const long long base = ((N + 63) / 64) * e_blocks;
-    const long long want = tiled ? 512 : 1024;
     int split = 1;
-    const int max_split = tiled ? kRouterMaxSplit : kRouterMaxSplitNarrow;
-    while (split < max_split && base * split < want && (c.d_model / (split * 2)) >= 256) split *= 2;
+    while (split < kRouterMaxSplit && base * split < 512 && (c.d_model / (split * 2)) >= 256) split *= 2;
     p.n_split = split;
     p.k_chunk = ((c.d_model / split) + 31) / 32 * 32;
   } else {
@@ -729,7 +832,7 @@ RoutePlan plan_route(const moe_config& c) {
 void carve_route(const moe_config& c, WsCarver& w, WsLayout* L) {
   const RoutePlan p = plan_route(c);
   const size_t N = (size_t)c.n_tokens, E = (size_t)c.n_experts;
-  float* zpart = w.take_t<float>((size_t)p.n_split * N * E);
+  float* zpart = w.take_t<float>(p.fused ? 0 : (size_t)p.n_split * N * E);  // the fused kernel keeps z in LDS
   float* part_p = w.take_t<float>((size_t)p.n_blocks * E);
   int* part_hist = w.take_t<int>((size_t)p.n_blocks * E);
   float* part_zl = w.take_t<float>((size_t)p.n_blocks);
@@ -757,27 +860,6 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   const RoutePlan p = plan_route(c);
   const int N = (int)c.n_tokens, E = c.n_experts, d = c.d_model;
   if (N > 0) {
-    if (c.dtype == MOE_BF16) {
-      auto xb = static_cast<const bf16_t*>(x);
-      auto wb = static_cast<const bf16_t*>(w_router);
-      if (E > 64) {
-        const int te = router_tile_experts(E);
-        dim3 grid((N + 63) / 64, (E + te - 1) / te, p.n_split);
-        if (te == 128) router_gemm_tiled_kernel<2><<<grid, 128, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk);
-        else router_gemm_tiled_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk);
-      } else {
-        const int eb = (E <= 16) ? 1 : (E <= 32) ? 2 : 4;
-        dim3 grid((N + 63) / 64, (E + 16 * eb - 1) / (16 * eb), p.n_split);
-        switch (eb) {
-          case 1: router_gemm_bf16_kernel<1><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-          case 2: router_gemm_bf16_kernel<2><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-          default: router_gemm_bf16_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk); break;
-        }
-      }
-    } else {
-      router_gemm_f32_kernel<<<(N + 3) / 4, 256, 0, stream>>>(
-          static_cast<const float*>(x), static_cast<const float*>(w_router), L.zpart, N, d, E);
-    }
     RouteArgs ra{};
     ra.zpart = L.zpart;
     ra.n_split = p.n_split;
@@ -798,24 +880,50 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
     ra.part_p = L.part_p;
     ra.part_hist = L.part_hist;
     ra.part_zl = L.part_zl;
-    switch (p.lpt * 100 + p.epl) {
-      case 101: launch_tokens<1, 1>(p, ra, stream); break;
-      case 201: launch_tokens<2, 1>(p, ra, stream); break;
-      case 401: launch_tokens<4, 1>(p, ra, stream); break;
-      case 801: launch_tokens<8, 1>(p, ra, stream); break;
-      case 1601: launch_tokens<16, 1>(p, ra, stream); break;
-      case 3201: launch_tokens<32, 1>(p, ra, stream); break;
-      case 6401: launch_tokens<64, 1>(p, ra, stream); break;
-      case 816: launch_tokens<8, 16>(p, ra, stream); break;
-      case 1608: launch_tokens<16, 8>(p, ra, stream); break;
-      case 1616: launch_tokens<16, 16>(p, ra, stream); break;
-      case 3204: launch_tokens<32, 4>(p, ra, stream); break;
-      case 3208: launch_tokens<32, 8>(p, ra, stream); break;
-      case 3216: launch_tokens<32, 16>(p, ra, stream); break;
-      case 6402: launch_tokens<64, 2>(p, ra, stream); break;
-      case 6404: launch_tokens<64, 4>(p, ra, stream); break;
-      case 6408: launch_tokens<64, 8>(p, ra, stream); break;
-      default: launch_tokens<64, 16>(p, ra, stream); break;
+    if (p.fused) {
+      auto xb = static_cast<const bf16_t*>(x);
+      auto wb = static_cast<const bf16_t*>(w_router);
+      const dim3 grid(p.n_blocks), block(kFusedWaves * kWave);
+      switch (p.lpt) {
+        case 1: route_fused_kernel<1, 1><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+        case 2: route_fused_kernel<1, 2><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+        case 4: route_fused_kernel<1, 4><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+        case 8: route_fused_kernel<1, 8><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+        case 16: route_fused_kernel<1, 16><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+        case 32: route_fused_kernel<2, 32><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+        default: route_fused_kernel<4, 64><<<grid, block, 0, stream>>>(xb, wb, ra, d, p.k_chunk); break;
+      }
+    } else {
+      if (c.dtype == MOE_BF16) {  // E > 64
+        auto xb = static_cast<const bf16_t*>(x);
+        auto wb = static_cast<const bf16_t*>(w_router);
+        const int te = router_tile_experts(E);
+        dim3 grid((N + 63) / 64, (E + te - 1) / te, p.n_split);
+        if (te == 128) router_gemm_tiled_kernel<2><<<grid, 128, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk);
+        else router_gemm_tiled_kernel<4><<<grid, 256, 0, stream>>>(xb, wb, L.zpart, N, d, E, p.k_chunk);
+      } else {
+        router_gemm_f32_kernel<<<(N + 3) / 4, 256, 0, stream>>>(
+            static_cast<const float*>(x), static_cast<const float*>(w_router), L.zpart, N, d, E);
+      }
+      switch (p.lpt * 100 + p.epl) {
+        case 101: launch_tokens<1, 1>(p, ra, stream); break;
+        case 201: launch_tokens<2, 1>(p, ra, stream); break;
+        case 401: launch_tokens<4, 1>(p, ra, stream); break;
+        case 801: launch_tokens<8, 1>(p, ra, stream); break;
+        case 1601: launch_tokens<16, 1>(p, ra, stream); break;
+        case 3201: launch_tokens<32, 1>(p, ra, stream); break;
+        case 6401: launch_tokens<64, 1>(p, ra, stream); break;
+        case 816: launch_tokens<8, 16>(p, ra, stream); break;
+        case 1608: launch_tokens<16, 8>(p, ra, stream); break;
+        case 1616: launch_tokens<16, 16>(p, ra, stream); break;
+        case 3204: launch_tokens<32, 4>(p, ra, stream); break;
+        case 3208: launch_tokens<32, 8>(p, ra, stream); break;
+        case 3216: launch_tokens<32, 16>(p, ra, stream); break;
+        case 6402: launch_tokens<64, 2>(p, ra, stream); break;
+        case 6404: launch_tokens<64, 4>(p, ra, stream); break;
+        case 6408: launch_tokens<64, 8>(p, ra, stream); break;
+        default: launch_tokens<64, 16>(p, ra, stream); break;
+      }
     }
   }
   FinalizeArgs fa{};

@@ -441,6 +441,20 @@ def test_route_lane_layouts(router, E, k, N):
     check_route(router, True, 1.0, E, k, "bf16", N, 128)
 
 
+# Shapes of the fused projection-and-routing kernel (bf16, up to 64 experts): every lanes-per-
+# token width from 1 to 64 (one, two and four 16-expert projection blocks), a reduction whose
+# last quarter is a partial 32-wide step (d = 200), one whose last quarters are empty (d = 64),
+# and token counts that make a routing block two runs of 32 tokens (N E above 2^21), with the
+# workgroup finalize.
+@pytest.mark.parametrize("router,E,k,N,d", [
+    ("softmax_topk", 1, 1, 1500, 384), ("topk_softmax", 2, 2, 777, 200), ("sigmoid", 3, 2, 1500, 384),
+    ("softmax_topk", 24, 3, 1500, 384), ("sigmoid", 64, 8, 1500, 384), ("softmax_topk", 64, 6, 40000, 64),
+    ("softmax_topk", 16, 2, 140000, 32),
+])
+def test_route_fused_shapes(router, E, k, N, d):
+    check_route(router, True, 1.0, E, k, "bf16", N, d)
+
+
 def check_route(router, norm, scale, E, k, dtype, N, d):
     cfg = B.LayerConfig(N, d, E, k, 64, router=router, norm_topk=norm, routed_scaling=scale, dtype=dtype)
     wl = W.Workload("route", cfg, logit_offset="zipf1.2" if E == 128 else None,
