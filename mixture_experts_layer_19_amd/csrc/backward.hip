@@ -508,26 +508,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gemm_kernel(BwdGemm g) {
 }
 
 // The split tail of a grouped bf16 product: out = bf16(sum of the tail tile's pieces, in
-// piece order). Workgroup (t, rg): rows 4 rg .. 4 rg + 3 of tail tile t, a thread per 4
-// columns.
-__global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdGemm g) {
+// piece order). Unit (t, rg): rows 4 rg .. 4 rg + 3 of tail tile t, a thread per 4 columns;
+// a fixed grid walks the units (the tail's size is known on the device only).
+constexpr int kBwdTailReduceGrid = 2048;
+MOE_DEV void bwd_tail_reduce_unit(const BwdGemm& g, long long S_main, int q, int t, int rg) {
   const int NT = g.n_tiles_n;
-  const long long S = (long long)g.tiles[0] * NT;
-  const long long S_main = S / g.cu_grid * g.cu_grid;
-  const int q = tail_pieces(S - S_main, grouped_slabs(g), g.cu_grid);
-  if (q <= 1 || blockIdx.x >= S - S_main) return;
-  const long long s = S_main + blockIdx.x;
+  const long long s = S_main + t;
   const int* probe = g.tiles + kTileHdr + kTileInts * (int)(s / NT);
   const int ts = probe[3], me = probe[4];
   int mt, nt;
   supertile(s - (long long)ts * NT, me, NT, &mt, &nt);
   const int* tq = g.tiles + kTileHdr + kTileInts * (ts + mt);
   const int row0 = tq[1], rows = tq[2];
-  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int r = rg * 4 + (threadIdx.x >> 6);
   const int c4 = (threadIdx.x & 63) * 4;
   const int col = nt * kBN + c4;
   if (r >= rows || col >= g.N) return;
-  const float* pt = g.tpart + (size_t)blockIdx.x * q * (kBM * kBN) + (size_t)r * kBN + c4;
+  const float* pt = g.tpart + (size_t)t * q * (kBM * kBN) + (size_t)r * kBN + c4;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < q; ++p) {
     const float4 x = *reinterpret_cast<const float4*>(pt + (size_t)p * (kBM * kBN));
@@ -535,6 +532,16 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdGemm g) {
   }
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + (size_t)(row0 + r) * g.ldc + col) =
       make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdGemm g) {
+  const long long S = (long long)g.tiles[0] * g.n_tiles_n;
+  const long long S_main = S / g.cu_grid * g.cu_grid;
+  const int q = tail_pieces(S - S_main, grouped_slabs(g), g.cu_grid);
+  if (q <= 1) return;
+  constexpr int kGroups = kBM / 4;  // row groups of a tail tile
+  const long long units = (S - S_main) * kGroups;
+  for (long long u = blockIdx.x; u < units; u += gridDim.x)
+    bwd_tail_reduce_unit(g, S_main, q, (int)(u / kGroups), (int)(u % kGroups));
 }
 
 // Cost prefix of the weight-gradient schedule: sched[e] = sum over experts e' < e of
@@ -943,7 +950,7 @@ hipError_t dx_rows(const moe_config& c, const uint16_t* zero, const int* tiles, 
   g.grid_static = (int)((S_max + 7) / 8 * 8);
   bwd_gemm_kernel<kGrouped, EPI><<<(unsigned)(g.grid_static + kMaxTailItems), kThreads, 0, stream>>>(g);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  bwd_tail_reduce_kernel<<<dim3(g.cu_grid, kBM / 4), 256, 0, stream>>>(g);
+  bwd_tail_reduce_kernel<<<kBwdTailReduceGrid, 256, 0, stream>>>(g);
   return hipGetLastError();
 }
 

@@ -1138,23 +1138,22 @@ __global__ __launch_bounds__(kW4Threads, 1) void expert_gemm_w4_kernel(GemmArgs 
 }
 
 // The down projection's tail items (PART 2 with q > 1): y_s = (sum of the q partials, in
-// piece order, + b2) * gate, rounded once. Workgroup (t, rg) covers 1 / 64 of tail item t's
-// rows (4 of a full tile's 256, 2 of a narrow tile's 128), a thread per 4 columns.
-__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
-  const int NT = g.n_tiles_n, K = g.K, n_out = g.n_out;
-  // the same plan as the PART 2 launch (same table, narrow decision and grid)
-  const GemmPlan P = gemm_plan(g.tiles, NT, g.nar_ok != 0, 2, g.grid, (K + kBK - 1) / kBK);
-  const long long S_tail = P.S_all - P.S_main;
+// piece order, + b2) * gate, rounded once. Unit (t, rg) covers 1 / 64 of tail item t's rows
+// (4 of a full tile's 256, 2 of a narrow tile's 128), a thread per 4 columns. The tail's size
+// is known on the device only, so a fixed grid walks the units (a grid sized for the largest
+// tail left most workgroups to decode the plan and exit: Mixtral shape 22.8 us).
+constexpr int kTailReduceGrid = 2048;
+MOE_DEV void tail_reduce_unit(const GemmArgs& g, const GemmPlan& P, int t, int rg) {
+  const int NT = g.n_tiles_n, n_out = g.n_out;
   const int q = P.q;
-  if (q <= 1 || blockIdx.x >= S_tail) return;
   int e, row0, rows, nt;
-  const bool nar = decode_tile(g.tiles, P.S_main + blockIdx.x, NT, P.nar, P.n_tail, &e, &row0, &rows, &nt);
+  const bool nar = decode_tile(g.tiles, P.S_main + t, NT, P.nar, P.n_tail, &e, &row0, &rows, &nt);
   const int tbn = nar ? 512 : 256;  // the partial tile's columns
-  const int r = nar ? blockIdx.y * 2 + (threadIdx.x >> 7) : blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int r = nar ? rg * 2 + (threadIdx.x >> 7) : rg * 4 + (threadIdx.x >> 6);
   const int c4 = nar ? (threadIdx.x & 127) * 4 : (threadIdx.x & 63) * 4;
   const int col = nt * tbn + c4;
   if (r >= rows || col >= n_out) return;
-  const float* pt = g.partial + (size_t)blockIdx.x * q * (kBM * kBNB) + r * tbn + c4;
+  const float* pt = g.partial + (size_t)t * q * (kBM * kBNB) + r * tbn + c4;
   const float gs = g.gate ? g.gate[row0 + r] : 1.f;
   const uint16_t* bias = static_cast<const uint16_t*>(g.bias);
   float b[4];
@@ -1183,6 +1182,14 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i) o[i] = g.pre_gated ? v[i] + b[i] * gs : (v[i] + b[i]) * gs;
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + (size_t)(row0 + r) * n_out + col) =
       make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+}
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g) {
+  // the same plan as the PART 2 launch (same table, narrow decision and grid)
+  const GemmPlan P = gemm_plan(g.tiles, g.n_tiles_n, g.nar_ok != 0, 2, g.grid, (g.K + kBK - 1) / kBK);
+  if (P.q <= 1) return;
+  constexpr int kGroups = kBM / 4;  // row groups of a tail item
+  const long long units = (P.S_all - P.S_main) * kGroups;
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) tail_reduce_unit(g, P, (int)(u / kGroups), (int)(u % kGroups));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1460,7 +1467,7 @@ hipError_t launch_down(const moe_config& c, const int* tiles, int max_m_tiles, c
       g.nar_ok = down_narrow(c) ? 1 : 0;  // what the two GEMM launches use
       launch_bf16_gemm<kEpiDown, 1>(down_narrow(c), grid, g, stream);
       launch_bf16_gemm<kEpiDown, 2>(down_narrow(c), grid, g, stream);
-      tail_reduce_kernel<<<dim3(grid, kBM / 4), 256, 0, stream>>>(g);
+      tail_reduce_kernel<<<kTailReduceGrid, 256, 0, stream>>>(g);
     }
   } else {
     dim3 grid(max_m_tiles, (c.d_model + kFBN - 1) / kFBN);
