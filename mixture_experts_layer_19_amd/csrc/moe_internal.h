@@ -113,15 +113,20 @@ MOE_DEV int expert_excl_scan(int v, int E, int* s_tmp, int* total) {
 
 // Exclusive prefix sum of v over the lanes of one wave in lane order, and the wave's total in
 // *total: shuffles only, every lane of the wave calls it.
+// The inclusive scan is six DPP moves: row_shr 1, 2, 4, 8 within each row of 16 lanes (lanes
+// with no source add the 0 passed as `old`), then row_bcast 15 (lane 15 of rows 0 and 2 into
+// rows 1 and 3) and row_bcast 31 (lane 31 into rows 2 and 3). Each is a register move of a
+// few cycles, where a shuffle is an LDS-unit permute of about a hundred; the routing
+// finalize chains a dozen of these scans.
 MOE_DEV int wave_excl_scan(int v, int* total) {
-  const int lane = threadIdx.x & 63;
   int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  *total = __shfl(x, 63, 64);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  *total = __builtin_amdgcn_readlane(x, 63);
   return x - v;
 }
 
