@@ -63,19 +63,36 @@ struct WsLayout {
   void* bwd = nullptr;
 };
 
+// Exclusive prefix sum of v over the lanes of one wave in lane order, and the wave's total in
+// *total, with no LDS; every lane of the wave calls it. The inclusive scan is six DPP moves: row_shr 1, 2, 4, 8 within each row of 16 lanes (lanes
+// with no source add the 0 passed as `old`), then row_bcast 15 (lane 15 of rows 0 and 2 into
+// rows 1 and 3) and row_bcast 31 (lane 31 into rows 2 and 3). Each is a register move of a
+// few cycles, where a shuffle is an LDS-unit permute of about a hundred; the routing
+// finalize chains a dozen of these scans.
+MOE_DEV int wave_incl_scan(int v) {
+  int x = v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+MOE_DEV int wave_excl_scan(int v, int* total) {
+  const int x = wave_incl_scan(v);
+  *total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
 // Exclusive prefix sum of v over the threads of the block in thread order (threads without
 // a value pass 0), and the block's total in *total. Every thread of the block calls it; the
-// block size is a multiple of 64. An inclusive scan within each wave by shuffles, then each
+// block size is a multiple of 64. An inclusive scan within each wave (DPP moves), then each
 // thread adds the totals of the waves before its own: two barriers at any block size.
 // s_tmp: one int per wave.
 MOE_DEV int block_excl_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_tmp[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
@@ -89,46 +106,14 @@ MOE_DEV int block_excl_scan(int v, int* s_tmp, int* total) {
   return before + x - v;
 }
 
-// The same over the first E threads (v = 0 beyond), with E <= blockDim.x: up to 64 experts
-// a step-doubling scan through s_tmp (E ints; log2 E steps of two barriers, cheaper than the
-// shuffles there), beyond them block_excl_scan (s_tmp: one int per wave). Every thread of the
-// block calls it and receives *total.
+// The same over the first E threads (v = 0 beyond), with E <= blockDim.x (s_tmp: one int per
+// wave). Every thread of the block calls it and receives *total. (Up to 64 experts this was a
+// step-doubling scan through LDS, log2 E steps of two barriers, while the in-wave scan was
+// made of shuffles; with DPP moves the two-barrier block scan is shorter at every E.)
 MOE_DEV int expert_excl_scan(int v, int E, int* s_tmp, int* total) {
-  if (E > 64) return block_excl_scan(v, s_tmp, total);
-  const int e = threadIdx.x;
-  if (e < E) s_tmp[e] = v;
-  __syncthreads();
-  for (int o = 1; o < E; o <<= 1) {
-    int u = 0;
-    if (e < E && e >= o) u = s_tmp[e - o];
-    __syncthreads();
-    if (e < E) s_tmp[e] += u;
-    __syncthreads();
-  }
-  const int ex = e < E ? s_tmp[e] - v : 0;
-  *total = s_tmp[E - 1];
-  __syncthreads();
-  return ex;
+  return block_excl_scan(threadIdx.x < E ? v : 0, s_tmp, total);
 }
 
-// Exclusive prefix sum of v over the lanes of one wave in lane order, and the wave's total in
-// *total: shuffles only, every lane of the wave calls it.
-// The inclusive scan is six DPP moves: row_shr 1, 2, 4, 8 within each row of 16 lanes (lanes
-// with no source add the 0 passed as `old`), then row_bcast 15 (lane 15 of rows 0 and 2 into
-// rows 1 and 3) and row_bcast 31 (lane 31 into rows 2 and 3). Each is a register move of a
-// few cycles, where a shuffle is an LDS-unit permute of about a hundred; the routing
-// finalize chains a dozen of these scans.
-MOE_DEV int wave_excl_scan(int v, int* total) {
-  int x = v;
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
-  *total = __builtin_amdgcn_readlane(x, 63);
-  return x - v;
-}
 
 // The m-tile table, filled by E owners: the caller with e < E owns expert e, whose rows are
 // [lo, hi); callers with e >= E only join the scans. Ranges outside [0, rows] or decreasing

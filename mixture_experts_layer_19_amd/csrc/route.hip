@@ -528,6 +528,7 @@ MOE_DEV double block_sum_f64(double v, double* s_red) {
   return r;
 }
 
+constexpr int kFinChunk = 16;
 template <int kFinThreads>
 __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArgs a) {
   __shared__ double s_p[kFinThreads];
@@ -548,12 +549,26 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
   const int b1 = act ? (int)((long long)nb * (g + 1) / G) : 0;
   if (tid == 0) s_bad = 0;
 
+  // the thread's blocks in chunks of kFinChunk, every load of a chunk unconditional (an index
+  // past the thread's range reads its last block, in range, and is dropped), so a chunk is one
+  // round trip: a load behind a per-thread condition is waited for before the next is issued
   int c = 0;
   double p = 0.0;
-#pragma unroll 8
-  for (int b = b0; b < b1; ++b) {
-    c += a.part_hist[(size_t)b * E + e];
-    p += (double)a.part_p[(size_t)b * E + e];
+  for (int j0 = b0; j0 < b1; j0 += kFinChunk) {  // b1 > b0 only for active threads
+    int hv[kFinChunk];
+    float pv[kFinChunk];
+#pragma unroll
+    for (int j = 0; j < kFinChunk; ++j) {
+      const size_t o = (size_t)min(j0 + j, b1 - 1) * E + e;
+      hv[j] = a.part_hist[o];
+      pv[j] = a.part_p[o];
+    }
+#pragma unroll
+    for (int j = 0; j < kFinChunk; ++j)
+      if (j0 + j < b1) {
+        c += hv[j];
+        p += (double)pv[j];
+      }
   }
   s_c[tid] = c;
   s_cs[tid] = c;
@@ -586,7 +601,14 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
   }
   const double fp_sum = block_sum_f64<kFinThreads>(fp, s_red);
   double zl = 0.0;
-  for (int b = tid; b < nb; b += kFinThreads) zl += (double)a.part_zl[b];
+  for (int b0z = 0; b0z < nb; b0z += kFinThreads * kFinChunk) {  // uniform trip count
+    float zv[kFinChunk];
+#pragma unroll
+    for (int j = 0; j < kFinChunk; ++j) zv[j] = a.part_zl[min(b0z + j * kFinThreads + tid, nb - 1)];
+#pragma unroll
+    for (int j = 0; j < kFinChunk; ++j)
+      if (b0z + j * kFinThreads + tid < nb) zl += (double)zv[j];
+  }
   const double zl_sum = block_sum_f64<kFinThreads>(zl, s_red);
   if (tid == 0) {
     a.stats[2 * E] = (float)((double)E * fp_sum);
@@ -609,10 +631,16 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(FinalizeArg
   // per-block bases: this thread's block range continues after the earlier groups' rows
   if (act) {
     int run = s_off[e] + (s_cs[tid] - s_c[tid]);
-#pragma unroll 8
-    for (int b = b0; b < b1; ++b) {
-      a.base[(size_t)b * E + e] = run;
-      run += a.part_hist[(size_t)b * E + e];
+    for (int j0 = b0; j0 < b1; j0 += kFinChunk) {
+      int hv[kFinChunk];
+#pragma unroll
+      for (int j = 0; j < kFinChunk; ++j) hv[j] = a.part_hist[(size_t)min(j0 + j, b1 - 1) * E + e];
+#pragma unroll
+      for (int j = 0; j < kFinChunk; ++j)
+        if (j0 + j < b1) {
+          a.base[(size_t)(j0 + j) * E + e] = run;
+          run += hv[j];
+        }
     }
   }
   if (a.tiles) {
